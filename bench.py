@@ -1,0 +1,191 @@
+#!/usr/bin/env python3
+"""Benchmark of the mixed-precision MoE layer on one MI355X.
+
+A step is one pass of the hot path over one batch: moe_route (router GEMV,
+softmax, top-K) followed by moe_ffn (grouping, gate_up + SwiGLU, down,
+weighted combine), reading every expert weight from its bit-planes and lookup
+table at the block's committed bitwidth. The workload is the decode-shaped
+layer shaped like Qwen1.5-MoE-A2.7B (PagedWeight §4, Table 1): H=2048,
+I=1408, 60 routed + 4 shared experts, top-4, 64 tokens, per-block bitwidths
+3..8 with the hot 20% of experts floored at 5 bits. Inputs are synthetic and
+already resident in HBM when the timed region starts. R copies of the layer's
+weights are rotated so the weight bytes streamed per rotation exceed 1 GB and
+the 256 MB last-level cache cannot hold them.
+
+Prints one JSON line (tokens/s, HBM GB/s of the step, a roofline entry for the
+gate_up kernel timed with HIP events inside the timed region, and the CPU
+oracle timed on a bounded sample on rank 0).
+"""
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+METRIC = "MoE-layer tokens/s and achieved HBM GB/s (% of peak) at mixed bitwidths"
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_gate_up_qwen15moe_decode.json")
+KERNEL_SRCS = ["k_ffn_decode.hip", "mpb_device.h"]
+
+
+def kernel_hash():
+    h = hashlib.sha256()
+    for f in KERNEL_SRCS:
+        with open(os.path.join(ROOT, "mixed_precision_bit_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def block_bytes(N, Kd, b):
+    return N * Kd * b // 8 + N * (1 << b) * 2
+
+
+def algorithmic_bytes(L, idx, T):
+    """Bytes the method must move per step: touched blocks at q_i (planes +
+    q_i-bit table), activations in, output out, router weights. Also the gate_up
+    kernel's share: touched gate_up blocks + activations."""
+    touched = np.zeros(L.E + L.S, bool)
+    touched[np.unique(idx[(idx >= 0) & (idx < L.E)])] = True
+    touched[L.E:] = True
+    blocks_gu = sum(block_bytes(*L.shape(2 * e), int(L.q[2 * e])) for e in np.nonzero(touched)[0])
+    blocks_dn = sum(block_bytes(*L.shape(2 * e + 1), int(L.q[2 * e + 1])) for e in np.nonzero(touched)[0])
+    x_bytes = T * L.H * 2
+    step = blocks_gu + blocks_dn + x_bytes + T * L.H * 4 + L.E * L.H * 4 + (4 * L.E if L.bias is not None else 0)
+    return step, blocks_gu + x_bytes, int(touched.sum())
+
+
+def cpu_baseline(L, Xbits, n_tokens):
+    import oracle as O
+    import mpb_synth as S
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    except Exception:
+        cores = os.cpu_count() or 1
+    X = S.x_bits_to_f64(Xbits[:n_tokens], L.cfg["xdtype"])
+    t = time.perf_counter()
+    z, r, _ = O.route(X, L.W_r, L.bias, L.K)
+    O.moe_ffn(X, z, r, L)
+    dt = time.perf_counter() - t
+    return {"value": round(n_tokens / dt, 3), "unit": "tokens/s", "cores": int(cores), "kind": "oracle",
+            "sample": f"first {n_tokens} of the {Xbits.shape[0]} tokens of the same layer (route + FFN "
+                      f"with dequantisation of every touched block), fp64 numpy, {dt:.1f} s"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--config", type=int, default=1)
+    ap.add_argument("--rotate", type=int, default=0, help="layer copies (0: enough for >= 1 GB)")
+    ap.add_argument("--cpu-tokens", type=int, default=8)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (got --gpus {args.gpus}); this layer is measured at N=1.",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import mpb_synth as S
+    from mixed_precision_bit_amd import _lib as M
+    from mixed_precision_bit_amd.layer import DeviceLayer
+
+    rank = int(os.environ.get("RANK", "0"))
+    cfg = args.config
+    c = S.layer_config(cfg)
+    L = S.make_layer(cfg)
+    Xbits = S.make_tokens(cfg)
+    T = Xbits.shape[0]
+    xdt = c["xdtype"]
+
+    D0 = DeviceLayer.from_synth(L)
+    wbytes = D0.weight_bytes()
+    R = args.rotate or max(1, int(np.ceil(1.0e9 / (0.5 * wbytes))))
+    layers = [D0] + [DeviceLayer.from_synth(L, q_dev=D0.q_dev) for _ in range(R - 1)]
+    X = torch.from_numpy(Xbits.view(np.int16)).cuda()
+    bufs = []
+    for D in layers:
+        idx, w = D.alloc_route(T)
+        out, ws = D.alloc_ffn(T)
+        bufs.append((idx, w, out, ws))
+    stream = torch.cuda.current_stream()
+
+    def step(k):
+        D = layers[k % R]
+        idx, w, out, ws = bufs[k % R]
+        D.route(X, xdt, idx, w, stream)
+        D.ffn(X, xdt, idx, w, out, ws, stream)
+
+    for k in range(args.warmup):
+        step(k)
+    torch.cuda.synchronize()
+    idx_host = bufs[0][0].cpu().numpy()
+    step_bytes, gu_bytes, n_touched = algorithmic_bytes(L, idx_host, T)
+
+    # per-step phase events recorded by moe_ffn inside the timed region
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
+    for row in evs:              # torch creates the HIP event on first record
+        for e in row:
+            e.record(stream)
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record(stream)
+    for k in range(args.steps):
+        M.mpb_set_kernel_events([e.cuda_event for e in evs[k]])
+        step(args.warmup + k)
+    end.record(stream)
+    torch.cuda.synchronize()
+    M.mpb_set_kernel_events([])
+    ms = start.elapsed_time(end) / args.steps
+    phase = np.array([[evs[k][j].elapsed_time(evs[k][j + 1]) for j in range(4)] for k in range(args.steps)])
+    gu_ms = float(phase[:, 1].mean())
+
+    tok_s = T / (ms * 1e-3)
+    step_gbs = step_bytes / (ms * 1e-3) / 1e9
+    gu_gbs = gu_bytes / (gu_ms * 1e-3) / 1e9
+    traffic = None
+    if os.path.exists(TRAFFIC_FILE):
+        tf = json.load(open(TRAFFIC_FILE))
+        if tf.get("kernel_hash") == kernel_hash() and tf.get("workload") == c["name"]:
+            traffic = tf.get("bytes_per_launch")
+    res = {
+        "metric": METRIC,
+        "value": round(tok_s, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f16",
+        "data": "synthetic",
+        "config": {"workload": f"{c['name']}: H={c['H']} I={c['I']} E={c['E']}+{c['S']} shared K={c['K']} "
+                               f"T={T} x={xdt}, per-block q_i 3..8 (hot 20% floored at 5)",
+                   "global_batch": T, "layer_copies_rotated": R, "touched_experts": n_touched,
+                   "committed_weight_bytes": int(M.mpb_committed_bytes())},
+        "hbm_gbs": round(step_gbs, 1),
+        "hbm_frac": round(step_gbs / HBM_PEAK_GBS, 4),
+        "phase_ms": {"group": round(float(phase[:, 0].mean()), 5), "gate_up": round(gu_ms, 5),
+                     "down": round(float(phase[:, 2].mean()), 5), "combine": round(float(phase[:, 3].mean()), 5)},
+        "roofline": {"kernel": "k_gate_up_decode", "bound": "hbm", "achieved": round(gu_gbs, 1),
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(gu_gbs / HBM_PEAK_GBS, 4),
+                     "traffic": traffic, "algorithmic_bytes_per_launch": int(gu_bytes)},
+    }
+    if rank == 0 and not args.no_cpu_baseline:
+        res["cpu_baseline"] = cpu_baseline(L, Xbits, args.cpu_tokens)
+    if rank == 0:
+        print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,201 @@
+/*
+ * mpb.h -- C ABI of libmpb, the MI355X (gfx950) mixed-precision MoE layer.
+ *
+ * The layer is the one PagedWeight runs inside its serving loop ("PagedWeight:
+ * Efficient MoE LLM Serving with Dynamic Quality-Aware Weight Quantization",
+ * §3.3 "Fused Mixed-Precision MoE Kernel"): top-K routing, expert gate_up with
+ * SwiGLU, the down projection and the routing-weighted output accumulation,
+ * with every expert weight read straight from Any-Precision bit-planes and
+ * per-row lookup tables at the bitwidth q_i committed for its linear-block
+ * (§3.1 "Paged Weight Representation").
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * - Return value: 0 on success, a negative MPB_E_* code on failure. No C++
+ *   exception crosses the ABI. mpb_last_error() gives a message for the last
+ *   failure of the calling thread.
+ * - Pointers named *_dev / device arrays are device (HBM) addresses; *_host are
+ *   host addresses. All buffers are owned by the caller and only borrowed: the
+ *   caller keeps them alive until the stream has passed the enqueued work. The
+ *   library allocates no device memory.
+ * - stream is a hipStream_t passed as void* (NULL = the default stream). Work is
+ *   enqueued asynchronously; argument validation happens synchronously on the
+ *   host before anything is enqueued, so a failed call enqueues nothing. Device
+ *   faults surface at the caller's next synchronisation of that stream.
+ * - One controlling thread; the library takes no locks.
+ *
+ * Linear-blocks. For a layer with E routed and S shared experts, block
+ * i = 2*e + u, e in [0, E+S) (routed first), u = 0 for gate_up ([N=2I rows,
+ * Kd=H]; rows 0..I-1 gate, rows I..2I-1 up) and u = 1 for down ([N=H, Kd=I]).
+ * Supported bitwidths B_i = {3,...,8} for every block.
+ *
+ * Canonical bit-plane format (the interchange format mpb_pack_block reads):
+ * planes[p][n][w], uint32, p = 0..7 with plane 0 the code's most significant
+ * bit; bit j of word w holds element k = 32*w + j of row n. The b-bit index of
+ * an element is formed from planes 0..b-1 (the top b planes, §2.2 and §3.1).
+ * Canonical LUT of bitwidth b: [N][2^b] fp16 (one centroid table per row),
+ * indexed by that b-bit index.
+ */
+#ifndef MPB_H
+#define MPB_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum {
+    MPB_OK = 0,
+    MPB_E_ARG = -1,          /* null pointer, bad enum, bad count */
+    MPB_E_SHAPE = -2,        /* dimension not supported (see each call) */
+    MPB_E_RANGE = -3,        /* block index i or bitwidth b out of range */
+    MPB_E_NOT_RESIDENT = -4, /* bitwidth above the block's resident planes */
+    MPB_E_WS = -5,           /* workspace too small */
+    MPB_E_HIP = -6,          /* a HIP launch or API call failed */
+    MPB_E_UNINIT = -7        /* mpb_init has not bound a layer */
+};
+
+enum { MPB_F16 = 0, MPB_BF16 = 1 }; /* activation dtypes */
+
+typedef struct {
+    int32_t H; /* hidden size, multiple of 64 */
+    int32_t I; /* expert intermediate size, multiple of 64 */
+    int32_t E; /* routed experts, 1..512 */
+    int32_t S; /* shared (always-on) experts, 0..64 */
+    int32_t K; /* experts per token, 1..min(E,16) */
+} mpb_layer_desc;
+
+/*
+ * Bind a layer: its geometry and the weight page table of committed bitwidths
+ * q_i (§3.1: one table row per linear-block; q_i is "the precision currently
+ * used in inference"). q_dev is a caller-owned device int32 array of
+ * 2*(E+S) entries that the FFN kernels read; q_init_host (2*(E+S) values in
+ * 3..8) is copied into it on `stream` and into the host mirror, and all planes
+ * of every block are marked resident. `stream` becomes the stream on which
+ * set_committed_bits enqueues its updates. Rebinding replaces the previous
+ * layer. Errors: MPB_E_ARG (null pointer), MPB_E_SHAPE (geometry outside the
+ * ranges above), MPB_E_RANGE (an initial q outside 3..8), MPB_E_HIP.
+ */
+int mpb_init(const mpb_layer_desc* d, int32_t* q_dev, const int32_t* q_init_host, void* stream);
+
+/* Bytes of one packed plane page of an [N][Kd] block (= N*Kd/8). */
+size_t mpb_plane_page_bytes(int N, int Kd);
+
+/*
+ * Packer (bit-plane layout for the kernels). Reads one block's canonical planes
+ * canon_dev ([8][N][Kd/32] uint32, device) and writes 8 packed plane pages,
+ * plane_pages_host[p] (host array of 8 device pointers, each
+ * mpb_plane_page_bytes(N, Kd) bytes). Packed pages are plane-major, so a block
+ * at bitwidth b is read through its first b pages only (§3.1: a b-bit block
+ * consists of b bit-planes and the b-bit table). The packed layout inside a
+ * page is private to this library. Needs N % 32 == 0 and Kd % 64 == 0, else
+ * MPB_E_SHAPE. Does not need mpb_init.
+ */
+int mpb_pack_block(const uint32_t* canon_dev, int N, int Kd, uint32_t* const* plane_pages_host,
+                   void* stream);
+
+/*
+ * Router (§2.1: "the router assigns routing weights to E experts and selects
+ * the top K experts for each token"). X_dev: [T][H] activations of x_dtype
+ * (MPB_F16 or MPB_BF16); W_router_dev: [E][H] fp32; bias_dev: [E] fp32 added
+ * to the logits, or NULL. Logits are accumulated in fp64 (every product of an
+ * activation and a router weight is exact in fp64). Writes topk_idx_dev [T][K]
+ * int32 (descending logit, ties to the lower expert index) and topk_w_dev
+ * [T][K] fp32 = softmax over all E experts restricted to the K winners and
+ * renormalised (equal to a softmax over the K winning logits). Needs
+ * 1 <= K <= min(E, 16), E <= 512, H % 64 == 0; T == 0 is a no-op.
+ * Does not need mpb_init.
+ */
+int moe_route(const void* X_dev, int x_dtype, const float* W_router_dev, const float* bias_dev,
+              int T, int H, int E, int K, int32_t* topk_idx_dev, float* topk_w_dev, void* stream);
+
+/* Workspace bytes moe_ffn needs for T tokens of the bound layer (0 if unbound). */
+size_t moe_ffn_workspace_bytes(int T);
+
+/*
+ * Fused MoE FFN of the bound layer (§3.3): groups the T tokens by expert,
+ * runs gate_up + SwiGLU (h = SiLU(gate) * up) and the down projection of
+ * every expert with tokens, and accumulates
+ *   out[t] = sum_k topk_w[t][k] * FFN_{topk_idx[t][k]}(x_t) + sum_s FFN_{E+s}(x_t).
+ * Each block's weights are dequantised on the fly from its first q_i packed
+ * plane pages and its q_i-bit LUT, with q_i read from q_dev on the device.
+ *   X_dev       [T][H] x_dtype activations
+ *   topk_idx_dev/topk_w_dev  [T][K] as produced by moe_route; expert ids
+ *               outside [0, E) contribute nothing
+ *   planes_dev  device array of 2*(E+S)*8 device pointers: entry i*8 + p is
+ *               plane page p of block i (written by mpb_pack_block). Only pages
+ *               p < q_i are dereferenced.
+ *   luts_dev    device array of 2*(E+S)*6 device pointers: entry i*6 + (b-3) is
+ *               block i's canonical [N][2^b] fp16 LUT. Only b == q_i is read.
+ *   q_dev       the bound page table (2*(E+S) int32, values 3..8)
+ *   out_dev     [T][H] fp32, overwritten
+ *   ws_dev      workspace of ws_bytes >= moe_ffn_workspace_bytes(T)
+ * Results are deterministic for T <= 256 (no order-dependent atomics).
+ * Errors: MPB_E_UNINIT, MPB_E_ARG, MPB_E_WS, MPB_E_HIP.
+ */
+int moe_ffn(const void* X_dev, int x_dtype, int T, const int32_t* topk_idx_dev,
+            const float* topk_w_dev, const uint32_t* const* planes_dev,
+            const uint16_t* const* luts_dev, const int32_t* q_dev, float* out_dev, void* ws_dev,
+            size_t ws_bytes, void* stream);
+
+/*
+ * Commit bitwidth b for linear-block i (§3.1 and §3.3: the planner lowers or
+ * raises q_i at a safe boundary; a reload raises q_i only once its pages are
+ * GPU-resident). Validates 0 <= i < 2*(E+S), b in 3..8 and b <= the block's
+ * resident plane count, updates the host mirror and enqueues the device write
+ * of q_dev[i] on the bound stream: FFN launches enqueued before it read the old
+ * value, later ones the new value. Errors: MPB_E_UNINIT, MPB_E_RANGE,
+ * MPB_E_NOT_RESIDENT, MPB_E_HIP.
+ */
+int set_committed_bits(int i, int b);
+
+/*
+ * Weight bytes the committed bitwidths hold (§3.1, Eq. 3: M_i^b counts the b
+ * bit-planes and the b-bit LUT of block i): sum over blocks of
+ * N_i*Kd_i*q_i/8 + N_i*2^q_i*2, from the host mirror. touched_host, if not
+ * NULL, is a host array of 2*(E+S) flags restricting the sum. Returns the byte
+ * count, or MPB_E_UNINIT.
+ */
+int64_t mpb_committed_bytes(const uint8_t* touched_host);
+
+/* Host mirror of q_i (test and planner use); MPB_E_UNINIT / MPB_E_RANGE. */
+int mpb_get_committed_bits(int i);
+
+/*
+ * Test export: dequantise one block through the same device index assembly and
+ * LUT lookup the FFN kernels use. pages_host: host array of b device pointers
+ * (packed plane pages 0..b-1); lut_b_dev: canonical [N][2^b] fp16 LUT; writes
+ * out_f16_dev [N][Kd] fp16 in canonical element order. Shapes as for
+ * mpb_pack_block; b in 3..8 else MPB_E_RANGE.
+ */
+int mpb_dequant_block(const uint32_t* const* pages_host, const uint16_t* lut_b_dev, int N, int Kd,
+                      int b, uint16_t* out_f16_dev, void* stream);
+
+/*
+ * Test hook: set how many of block i's planes are GPU-resident (3..8), to
+ * model an offloaded or in-transfer page; set_committed_bits then refuses
+ * b > r (§3.1: q_i is raised only when the page state is GPU-resident).
+ * Lowering r below the committed q_i is refused with MPB_E_NOT_RESIDENT
+ * (offload lowers q_i first). MPB_E_UNINIT / MPB_E_RANGE.
+ */
+int mpb_set_resident_planes(int i, int r);
+
+/*
+ * Profiling hook: with n == 5, every following moe_ffn records
+ * events_host[0..4] (host array of hipEvent_t handles, caller-created) on its
+ * stream before the grouping kernels, before gate_up, before down, before the
+ * combine and after the combine, so the caller can time each phase with
+ * hipEventElapsedTime. n == 0 turns recording off. The handles are borrowed
+ * until the hook is changed. MPB_E_ARG for any other n or a null handle.
+ */
+int mpb_set_kernel_events(void* const* events_host, int n);
+
+/* Message of the calling thread's last failure ("" if none). */
+const char* mpb_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* MPB_H */

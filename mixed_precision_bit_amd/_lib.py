@@ -1,0 +1,154 @@
+"""ctypes binding of libmpb (include/mpb.h). Argument marshalling only: every
+step of the layer runs in the library's HIP kernels. Functions keep the C
+names; tensors are passed as device pointers, streams as raw HIP handles."""
+import ctypes
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libmpb.so")
+
+MPB_F16, MPB_BF16 = 0, 1
+ERRORS = {-1: "MPB_E_ARG", -2: "MPB_E_SHAPE", -3: "MPB_E_RANGE", -4: "MPB_E_NOT_RESIDENT",
+          -5: "MPB_E_WS", -6: "MPB_E_HIP", -7: "MPB_E_UNINIT"}
+
+
+class MpbError(RuntimeError):
+    def __init__(self, name, code, msg):
+        super().__init__(f"{name}: {ERRORS.get(code, code)}: {msg}")
+        self.code = code
+
+
+class LayerDesc(ctypes.Structure):
+    _fields_ = [("H", ctypes.c_int32), ("I", ctypes.c_int32), ("E", ctypes.c_int32),
+                ("S", ctypes.c_int32), ("K", ctypes.c_int32)]
+
+
+_lib = None
+_P = ctypes.c_void_p
+_I = ctypes.c_int
+
+
+def lib() -> ctypes.CDLL:
+    """Load libmpb.so; raises if it has not been built (there is no fallback)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with "
+                               "`python -m mixed_precision_bit_amd.build` (hipcc, gfx950)")
+        L = ctypes.CDLL(LIB_PATH)
+        sig = {
+            "mpb_init": (_I, [ctypes.POINTER(LayerDesc), _P, _P, _P]),
+            "mpb_plane_page_bytes": (ctypes.c_size_t, [_I, _I]),
+            "mpb_pack_block": (_I, [_P, _I, _I, _P, _P]),
+            "moe_route": (_I, [_P, _I, _P, _P, _I, _I, _I, _I, _P, _P, _P]),
+            "moe_ffn_workspace_bytes": (ctypes.c_size_t, [_I]),
+            "moe_ffn": (_I, [_P, _I, _I, _P, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P]),
+            "set_committed_bits": (_I, [_I, _I]),
+            "mpb_committed_bytes": (ctypes.c_int64, [_P]),
+            "mpb_get_committed_bits": (_I, [_I]),
+            "mpb_dequant_block": (_I, [_P, _P, _I, _I, _I, _P, _P]),
+            "mpb_set_resident_planes": (_I, [_I, _I]),
+            "mpb_last_error": (ctypes.c_char_p, []),
+            "mpb_set_kernel_events": (_I, [_P, _I]),
+        }
+        for name, (res, args) in sig.items():
+            f = getattr(L, name)
+            f.restype, f.argtypes = res, args
+        _lib = L
+    return _lib
+
+
+def _check(name, rc):
+    if rc < 0:
+        raise MpbError(name, rc, lib().mpb_last_error().decode())
+    return rc
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _host_ptrs(ptrs):
+    arr = (ctypes.c_void_p * len(ptrs))(*ptrs)
+    return arr
+
+
+def mpb_last_error() -> str:
+    return lib().mpb_last_error().decode()
+
+
+def mpb_init(H, I, E, S, K, q_dev: torch.Tensor, q_init, stream=None):
+    import numpy as np
+    q_init = np.ascontiguousarray(q_init, dtype=np.int32)
+    d = LayerDesc(H, I, E, S, K)
+    return _check("mpb_init", lib().mpb_init(ctypes.byref(d), _ptr(q_dev),
+                                             q_init.ctypes.data_as(ctypes.c_void_p), _stream(stream)))
+
+
+def mpb_plane_page_bytes(N, Kd) -> int:
+    return lib().mpb_plane_page_bytes(N, Kd)
+
+
+def mpb_pack_block(canon: torch.Tensor, N, Kd, pages, stream=None):
+    arr = _host_ptrs([p.data_ptr() for p in pages])
+    return _check("mpb_pack_block", lib().mpb_pack_block(_ptr(canon), N, Kd, arr, _stream(stream)))
+
+
+def moe_route(X, x_dtype, W_router, bias, K, topk_idx, topk_w, stream=None):
+    T, H = X.shape
+    E = W_router.shape[0]
+    return _check("moe_route", lib().moe_route(_ptr(X), x_dtype, _ptr(W_router), _ptr(bias), T, H, E, K,
+                                               _ptr(topk_idx), _ptr(topk_w), _stream(stream)))
+
+
+def moe_ffn_workspace_bytes(T) -> int:
+    return lib().moe_ffn_workspace_bytes(T)
+
+
+def moe_ffn(X, x_dtype, topk_idx, topk_w, planes_table, luts_table, q, out, ws, stream=None):
+    T = X.shape[0]
+    nbytes = ws.numel() * ws.element_size()
+    return _check("moe_ffn", lib().moe_ffn(_ptr(X), x_dtype, T, _ptr(topk_idx), _ptr(topk_w),
+                                           _ptr(planes_table), _ptr(luts_table), _ptr(q), _ptr(out),
+                                           _ptr(ws), nbytes, _stream(stream)))
+
+
+def set_committed_bits(i, b):
+    return _check("set_committed_bits", lib().set_committed_bits(i, b))
+
+
+def mpb_committed_bytes(touched=None) -> int:
+    import numpy as np
+    if touched is None:
+        return _check("mpb_committed_bytes", lib().mpb_committed_bytes(None))
+    t = np.ascontiguousarray(touched, dtype=np.uint8)
+    return _check("mpb_committed_bytes", lib().mpb_committed_bytes(t.ctypes.data_as(ctypes.c_void_p)))
+
+
+def mpb_get_committed_bits(i) -> int:
+    return _check("mpb_get_committed_bits", lib().mpb_get_committed_bits(i))
+
+
+def mpb_dequant_block(pages, lut, N, Kd, b, out, stream=None):
+    arr = _host_ptrs([p.data_ptr() for p in pages[:b]])
+    return _check("mpb_dequant_block", lib().mpb_dequant_block(arr, _ptr(lut), N, Kd, b, _ptr(out),
+                                                               _stream(stream)))
+
+
+def mpb_set_kernel_events(events):
+    """events: list of 5 raw hipEvent_t handles (ints), or [] to turn recording off."""
+    if not events:
+        return _check("mpb_set_kernel_events", lib().mpb_set_kernel_events(None, 0))
+    return _check("mpb_set_kernel_events", lib().mpb_set_kernel_events(_host_ptrs(events), 5))
+
+
+def mpb_set_resident_planes(i, r):
+    return _check("mpb_set_resident_planes", lib().mpb_set_resident_planes(i, r))

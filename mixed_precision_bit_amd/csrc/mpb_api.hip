@@ -1,0 +1,265 @@
+// libmpb host side: argument validation, the host mirror of the weight page
+// table, workspace layout and launch sequencing. Every export validates on the
+// host before enqueuing anything and never lets a C++ exception escape.
+#include <string>
+#include <vector>
+
+#include "mpb.h"
+#include "mpb_internal.h"
+
+namespace {
+
+struct State {
+  bool init = false;
+  int H = 0, I = 0, E = 0, S = 0, K = 0;
+  int32_t* q_dev = nullptr;
+  std::vector<int> q;         // host mirror of committed bitwidths
+  std::vector<int> resident;  // GPU-resident planes per block
+  hipStream_t stream = nullptr;
+  int nb() const { return 2 * (E + S); }
+};
+
+State g;
+thread_local std::string g_err;
+hipEvent_t g_ev[5];
+int g_nev = 0;
+
+void mark(int k, hipStream_t s) {
+  if (g_nev == 5) (void)hipEventRecord(g_ev[k], s);
+}
+
+int fail(int code, const std::string& msg) {
+  g_err = msg;
+  return code;
+}
+
+int hip_fail(hipError_t e, const char* where) {
+  return fail(MPB_E_HIP, std::string(where) + ": " + hipGetErrorString(e));
+}
+
+bool geometry_ok(int H, int I, int E, int S, int K, std::string* why) {
+  if (H <= 0 || H % 64 || H > 65536) { *why = "H must be a positive multiple of 64 (<= 65536)"; return false; }
+  if (I <= 0 || I % 64 || I > 65536) { *why = "I must be a positive multiple of 64 (<= 65536)"; return false; }
+  if (E < 1 || E > 512) { *why = "E must be in 1..512"; return false; }
+  if (S < 0 || S > 64) { *why = "S must be in 0..64"; return false; }
+  if (K < 1 || K > 16 || K > E) { *why = "K must be in 1..min(E,16)"; return false; }
+  return true;
+}
+
+void block_shape(int i, int* N, int* Kd) {
+  if (i % 2 == 0) { *N = 2 * g.I; *Kd = g.H; }
+  else { *N = g.H; *Kd = g.I; }
+}
+
+int64_t block_bytes(int N, int Kd, int b) {
+  return (int64_t)N * Kd * b / 8 + (int64_t)N * (1 << b) * 2;
+}
+
+}  // namespace
+
+namespace mpb {
+
+static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+WsLayout ws_layout(int T, int H, int I, int E, int S, int K) {
+  WsLayout L{};
+  const size_t NB = (size_t)E + S, P = (size_t)T * (K + S);
+  size_t off = 0;
+  L.counts = off;  off += align256(NB * 4);
+  L.offsets = off; off += align256((NB + 1) * 4);
+  L.ptok = off;    off += align256(P * 4);
+  L.pw = off;      off += align256(P * 4);
+  L.inv = off;     off += align256(P * 4);
+  L.h = off;       off += align256(P * (size_t)I * 4);
+  L.y = off;       off += align256(P * (size_t)H * 4);
+  L.total = off;
+  return L;
+}
+
+}  // namespace mpb
+
+extern "C" {
+
+const char* mpb_last_error(void) { return g_err.c_str(); }
+
+int mpb_init(const mpb_layer_desc* d, int32_t* q_dev, const int32_t* q_init_host, void* stream) try {
+  if (!d || !q_dev || !q_init_host) return fail(MPB_E_ARG, "mpb_init: null pointer");
+  std::string why;
+  if (!geometry_ok(d->H, d->I, d->E, d->S, d->K, &why)) return fail(MPB_E_SHAPE, "mpb_init: " + why);
+  const int nb = 2 * (d->E + d->S);
+  for (int i = 0; i < nb; ++i)
+    if (q_init_host[i] < 3 || q_init_host[i] > 8)
+      return fail(MPB_E_RANGE, "mpb_init: initial q[" + std::to_string(i) + "] outside 3..8");
+  hipStream_t s = (hipStream_t)stream;
+  hipError_t e = hipMemcpyAsync(q_dev, q_init_host, nb * sizeof(int32_t), hipMemcpyHostToDevice, s);
+  if (e != hipSuccess) return hip_fail(e, "mpb_init: copy of q");
+  e = hipStreamSynchronize(s);
+  if (e != hipSuccess) return hip_fail(e, "mpb_init: stream sync");
+  g.init = true;
+  g.H = d->H; g.I = d->I; g.E = d->E; g.S = d->S; g.K = d->K;
+  g.q_dev = q_dev;
+  g.q.assign(q_init_host, q_init_host + nb);
+  g.resident.assign(nb, 8);
+  g.stream = s;
+  return MPB_OK;
+} catch (...) {
+  return fail(MPB_E_HIP, "mpb_init: unexpected exception");
+}
+
+size_t mpb_plane_page_bytes(int N, int Kd) {
+  if (N <= 0 || Kd <= 0) return 0;
+  return (size_t)N * Kd / 8;
+}
+
+int mpb_pack_block(const uint32_t* canon_dev, int N, int Kd, uint32_t* const* plane_pages_host,
+                   void* stream) try {
+  if (!canon_dev || !plane_pages_host) return fail(MPB_E_ARG, "mpb_pack_block: null pointer");
+  for (int p = 0; p < 8; ++p)
+    if (!plane_pages_host[p]) return fail(MPB_E_ARG, "mpb_pack_block: null page pointer");
+  if (N <= 0 || N % 32 || Kd <= 0 || Kd % 64)
+    return fail(MPB_E_SHAPE, "mpb_pack_block: need N % 32 == 0 and Kd % 64 == 0");
+  hipError_t e = mpb::launch_pack(canon_dev, N, Kd, plane_pages_host, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "mpb_pack_block");
+  return MPB_OK;
+} catch (...) {
+  return fail(MPB_E_HIP, "mpb_pack_block: unexpected exception");
+}
+
+int mpb_dequant_block(const uint32_t* const* pages_host, const uint16_t* lut_b_dev, int N, int Kd, int b,
+                      uint16_t* out_f16_dev, void* stream) try {
+  if (!pages_host || !lut_b_dev || !out_f16_dev) return fail(MPB_E_ARG, "mpb_dequant_block: null pointer");
+  if (b < 3 || b > 8) return fail(MPB_E_RANGE, "mpb_dequant_block: b outside 3..8");
+  for (int p = 0; p < b; ++p)
+    if (!pages_host[p]) return fail(MPB_E_ARG, "mpb_dequant_block: null page pointer");
+  if (N <= 0 || N % 32 || Kd <= 0 || Kd % 64)
+    return fail(MPB_E_SHAPE, "mpb_dequant_block: need N % 32 == 0 and Kd % 64 == 0");
+  hipError_t e = mpb::launch_dequant(pages_host, lut_b_dev, N, Kd, b, out_f16_dev, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "mpb_dequant_block");
+  return MPB_OK;
+} catch (...) {
+  return fail(MPB_E_HIP, "mpb_dequant_block: unexpected exception");
+}
+
+int moe_route(const void* X_dev, int x_dtype, const float* W_router_dev, const float* bias_dev, int T, int H,
+              int E, int K, int32_t* topk_idx_dev, float* topk_w_dev, void* stream) try {
+  if (x_dtype != MPB_F16 && x_dtype != MPB_BF16) return fail(MPB_E_ARG, "moe_route: bad x_dtype");
+  if (T < 0) return fail(MPB_E_ARG, "moe_route: T < 0");
+  if (H <= 0 || H % 64) return fail(MPB_E_SHAPE, "moe_route: H must be a positive multiple of 64");
+  if (E < 1 || E > 512) return fail(MPB_E_SHAPE, "moe_route: E must be in 1..512");
+  if (K < 1 || K > 16 || K > E) return fail(MPB_E_SHAPE, "moe_route: K must be in 1..min(E,16)");
+  if (T == 0) return MPB_OK;
+  if (!X_dev || !W_router_dev || !topk_idx_dev || !topk_w_dev) return fail(MPB_E_ARG, "moe_route: null pointer");
+  hipError_t e = mpb::launch_route((const uint16_t*)X_dev, x_dtype, W_router_dev, bias_dev, T, H, E, K,
+                                   topk_idx_dev, topk_w_dev, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "moe_route");
+  return MPB_OK;
+} catch (...) {
+  return fail(MPB_E_HIP, "moe_route: unexpected exception");
+}
+
+size_t moe_ffn_workspace_bytes(int T) {
+  if (!g.init || T < 0) return 0;
+  return mpb::ws_layout(T, g.H, g.I, g.E, g.S, g.K).total;
+}
+
+int moe_ffn(const void* X_dev, int x_dtype, int T, const int32_t* topk_idx_dev, const float* topk_w_dev,
+            const uint32_t* const* planes_dev, const uint16_t* const* luts_dev, const int32_t* q_dev,
+            float* out_dev, void* ws_dev, size_t ws_bytes, void* stream) try {
+  if (!g.init) return fail(MPB_E_UNINIT, "moe_ffn: no layer bound (mpb_init)");
+  if (x_dtype != MPB_F16 && x_dtype != MPB_BF16) return fail(MPB_E_ARG, "moe_ffn: bad x_dtype");
+  if (T < 0) return fail(MPB_E_ARG, "moe_ffn: T < 0");
+  if (T == 0) return MPB_OK;
+  if (T > (1 << 20)) return fail(MPB_E_SHAPE, "moe_ffn: T above 2^20");
+  if (!X_dev || !topk_idx_dev || !topk_w_dev || !planes_dev || !luts_dev || !q_dev || !out_dev || !ws_dev)
+    return fail(MPB_E_ARG, "moe_ffn: null pointer");
+  const mpb::WsLayout L = mpb::ws_layout(T, g.H, g.I, g.E, g.S, g.K);
+  if (ws_bytes < L.total)
+    return fail(MPB_E_WS, "moe_ffn: workspace " + std::to_string(ws_bytes) + " < " + std::to_string(L.total));
+  char* ws = (char*)ws_dev;
+  mpb::FfnParams p{};
+  p.X = (const uint16_t*)X_dev;
+  p.T = T; p.H = g.H; p.I = g.I; p.E = g.E; p.S = g.S; p.K = g.K; p.NB = g.E + g.S;
+  p.topk_idx = topk_idx_dev; p.topk_w = topk_w_dev;
+  p.planes = planes_dev; p.luts = luts_dev; p.q = q_dev;
+  p.counts = (int32_t*)(ws + L.counts);
+  p.offsets = (int32_t*)(ws + L.offsets);
+  p.ptok = (int32_t*)(ws + L.ptok);
+  p.pw = (float*)(ws + L.pw);
+  p.inv = (int32_t*)(ws + L.inv);
+  p.h = (float*)(ws + L.h);
+  p.y = (float*)(ws + L.y);
+  p.out = out_dev;
+  hipStream_t s = (hipStream_t)stream;
+  mark(0, s);
+  hipError_t e = mpb::launch_permute(p, s);
+  if (e != hipSuccess) return hip_fail(e, "moe_ffn: permute");
+  mark(1, s);
+  e = mpb::launch_gate_up(p, x_dtype, s);
+  if (e != hipSuccess) return hip_fail(e, "moe_ffn: gate_up");
+  mark(2, s);
+  e = mpb::launch_down(p, s);
+  if (e != hipSuccess) return hip_fail(e, "moe_ffn: down");
+  mark(3, s);
+  e = mpb::launch_combine(p, s);
+  if (e != hipSuccess) return hip_fail(e, "moe_ffn: combine");
+  mark(4, s);
+  return MPB_OK;
+} catch (...) {
+  return fail(MPB_E_HIP, "moe_ffn: unexpected exception");
+}
+
+int set_committed_bits(int i, int b) try {
+  if (!g.init) return fail(MPB_E_UNINIT, "set_committed_bits: no layer bound");
+  if (i < 0 || i >= g.nb()) return fail(MPB_E_RANGE, "set_committed_bits: block index out of range");
+  if (b < 3 || b > 8) return fail(MPB_E_RANGE, "set_committed_bits: bitwidth outside 3..8");
+  if (b > g.resident[i])
+    return fail(MPB_E_NOT_RESIDENT, "set_committed_bits: block " + std::to_string(i) + " has only " +
+                                        std::to_string(g.resident[i]) + " resident planes");
+  hipError_t e = mpb::launch_set_q(g.q_dev, i, b, g.stream);
+  if (e != hipSuccess) return hip_fail(e, "set_committed_bits");
+  g.q[i] = b;
+  return MPB_OK;
+} catch (...) {
+  return fail(MPB_E_HIP, "set_committed_bits: unexpected exception");
+}
+
+int mpb_set_kernel_events(void* const* events_host, int n) {
+  if (n == 0) { g_nev = 0; return MPB_OK; }
+  if (n != 5 || !events_host) return fail(MPB_E_ARG, "mpb_set_kernel_events: need 5 events or 0");
+  for (int k = 0; k < 5; ++k) {
+    if (!events_host[k]) return fail(MPB_E_ARG, "mpb_set_kernel_events: null event");
+    g_ev[k] = (hipEvent_t)events_host[k];
+  }
+  g_nev = 5;
+  return MPB_OK;
+}
+
+int64_t mpb_committed_bytes(const uint8_t* touched_host) {
+  if (!g.init) return fail(MPB_E_UNINIT, "mpb_committed_bytes: no layer bound");
+  int64_t tot = 0;
+  for (int i = 0; i < g.nb(); ++i) {
+    if (touched_host && !touched_host[i]) continue;
+    int N, Kd;
+    block_shape(i, &N, &Kd);
+    tot += block_bytes(N, Kd, g.q[i]);
+  }
+  return tot;
+}
+
+int mpb_get_committed_bits(int i) {
+  if (!g.init) return fail(MPB_E_UNINIT, "mpb_get_committed_bits: no layer bound");
+  if (i < 0 || i >= g.nb()) return fail(MPB_E_RANGE, "mpb_get_committed_bits: block index out of range");
+  return g.q[i];
+}
+
+int mpb_set_resident_planes(int i, int r) {
+  if (!g.init) return fail(MPB_E_UNINIT, "mpb_set_resident_planes: no layer bound");
+  if (i < 0 || i >= g.nb()) return fail(MPB_E_RANGE, "mpb_set_resident_planes: block index out of range");
+  if (r < 3 || r > 8) return fail(MPB_E_RANGE, "mpb_set_resident_planes: plane count outside 3..8");
+  if (r < g.q[i])
+    return fail(MPB_E_NOT_RESIDENT, "mpb_set_resident_planes: lower q_i before offloading its planes");
+  g.resident[i] = r;
+  return MPB_OK;
+}
+
+}  // extern "C"

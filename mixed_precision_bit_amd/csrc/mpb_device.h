@@ -1,0 +1,149 @@
+// Device-side building blocks shared by every kernel that reads Any-Precision
+// weights: the packed bit-plane word layout, index assembly from the top q
+// planes, the LDS staging of per-row centroid tables and the table lookup.
+//
+// Source: "PagedWeight: Efficient MoE LLM Serving with Dynamic Quality-Aware
+// Weight Quantization", §2.2 (a b-bit weight is a subset of the bit-planes
+// plus the b-bit lookup table) and §3.3 (the fused kernel reads the planes and
+// tables directly at each block's committed bitwidth).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint16_t u16x8 __attribute__((ext_vector_type(8)));
+
+namespace mpb {
+
+// ----------------------------------------------------------------------------
+// Packed plane word layout.
+//
+// A packed page stores, for every 32-row tile and every 32-element word of a
+// row, one uint32 per row: page[((n/32) * W + w) * 32 + n%32], W = Kd/32. A
+// wave that reads word w of 32 consecutive rows therefore reads 128 contiguous
+// bytes.
+//
+// Inside the word, element e = 4*s + b (s = 0..7, b = 0..3) of plane p sits at
+// bit (8*b + s + p) mod 32. With that placement the q-bit indices of four
+// elements {4s..4s+3} come out of q plane words with one AND per plane and one
+// rotation: OR_p (P_p & rotl(0x01010101, s+p)), rotated right by s, holds in
+// byte b the bits of element 4s+b with plane p at bit p.
+// ----------------------------------------------------------------------------
+__host__ __device__ constexpr int packed_pos(int e, int p) { return (8 * (e & 3) + (e >> 2) + p) & 31; }
+
+__host__ __device__ constexpr uint32_t rotl_c(uint32_t x, int r) {
+  return (r & 31) ? (x << (r & 31)) | (x >> (32 - (r & 31))) : x;
+}
+
+// Index assembly. P[p] = plane-p word (p < Q) of one (row, word). On return
+// byte b of O[s] is u = sum_p bit_p(e=4s+b) << p, the Q-bit index with its bit
+// order reversed (plane 0, the code MSB, lands in bit 0). Tables are staged in
+// the same reversed order, so no per-weight reversal is needed.
+template <int Q>
+__device__ __forceinline__ void assemble(const uint32_t (&P)[Q], uint32_t (&O)[8]) {
+#pragma unroll
+  for (int s = 0; s < 8; ++s) {
+    uint32_t c;
+    if constexpr (Q == 8) {
+      // the eight masks of one s partition the word: a bit-field-insert chain
+      c = P[7];
+#pragma unroll
+      for (int p = 6; p >= 0; --p) {
+        const uint32_t m = rotl_c(0x01010101u, s + p);
+        c = (P[p] & m) | (c & ~m);
+      }
+    } else {
+      c = P[0] & rotl_c(0x01010101u, s);
+#pragma unroll
+      for (int p = 1; p < Q; ++p) c |= P[p] & rotl_c(0x01010101u, s + p);
+    }
+    O[s] = s ? __builtin_amdgcn_alignbit(c, c, s) : c;
+  }
+}
+
+template <int Q>
+__device__ __forceinline__ uint32_t bitrev(uint32_t v) {
+  return __builtin_bitreverse32(v) >> (32 - Q);
+}
+
+// ----------------------------------------------------------------------------
+// LDS centroid tables.
+//
+// A workgroup of up to 4 waves keeps, for each wave, the tables of the 32 rows
+// it is dequantising. Entry u (reversed index, see assemble) of row r of wave w
+// is the fp16 at byte
+//     u * 256 + slot(r, w),   slot(r, w) = 4*r + 2*(w & 1) + 128*(w >> 1).
+// Row r always lives in LDS bank r (dword address = 64u + r + 32*(w>>1)), so the
+// 32 lanes of a half-wave, which hold 32 different rows, never conflict. The
+// table region starts at LDS byte 0 and spans 2^Q * 256 bytes (64 KiB at Q=8).
+// ----------------------------------------------------------------------------
+__device__ __forceinline__ uint32_t lut_slot(int r, int w) {
+  return 4u * r + 2u * (w & 1) + 128u * (w >> 1);
+}
+
+// Stage the Q-bit tables of rows row0..row0+31 (canonical [N][2^Q] fp16 at
+// lut, canonical index order) for wave w. Called by all 64 lanes of the wave.
+template <int Q>
+__device__ __forceinline__ void stage_luts(uint16_t* lds, const uint16_t* __restrict__ lut, int row0,
+                                           int lane, int w) {
+  const int r = lane & 31;
+  const uint32_t slot = lut_slot(r, w);
+  const uint16_t* src = lut + (size_t)(row0 + r) * (1u << Q);
+#pragma unroll 4
+  for (int v = lane >> 5; v < (1 << Q); v += 2) {
+    const uint32_t u = bitrev<Q>(v);
+    lds[(u * 256u + slot) >> 1] = src[v];
+  }
+}
+
+// LDS byte address of the entry named by byte b of an assembled word O.
+__device__ __forceinline__ uint32_t lut_addr(uint32_t O, uint32_t slot, int b) {
+  // result byte 0 = slot, byte 1 = O.byte[b], bytes 2..3 = 0
+  return __builtin_amdgcn_perm(O, slot, 0x0c0c0000u | ((4u + (uint32_t)b) << 8));
+}
+
+__device__ __forceinline__ _Float16 lut_read(const uint16_t* lds, uint32_t addr) {
+  return __builtin_bit_cast(_Float16, *(const uint16_t*)((const char*)lds + addr));
+}
+
+// Eight dequantised weights, elements 8m..8m+7 of the word (O0 = O[2m],
+// O1 = O[2m+1]), as an MFMA A-operand.
+__device__ __forceinline__ f16x8 lookup8(const uint16_t* lds, uint32_t O0, uint32_t O1, uint32_t slot) {
+  f16x8 a;
+#pragma unroll
+  for (int b = 0; b < 4; ++b) a[b] = lut_read(lds, lut_addr(O0, slot, b));
+#pragma unroll
+  for (int b = 0; b < 4; ++b) a[4 + b] = lut_read(lds, lut_addr(O1, slot, b));
+  return a;
+}
+
+// ----------------------------------------------------------------------------
+// Activations as MFMA B-operands (8 consecutive elements, 16-byte aligned).
+// ----------------------------------------------------------------------------
+__device__ __forceinline__ f16x8 load_x8_f16(const uint16_t* p) { return *(const f16x8*)p; }
+
+// bf16 -> fp16 (exact for |x| in the fp16 normal range; rounded below it).
+__device__ __forceinline__ f16x8 load_x8_bf16(const uint16_t* p) {
+  const u16x8 v = *(const u16x8*)p;
+  f16x8 r;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) r[j] = (_Float16)__builtin_bit_cast(float, (uint32_t)v[j] << 16);
+  return r;
+}
+
+template <int XDT>
+__device__ __forceinline__ f16x8 load_x8(const uint16_t* p) {
+  if constexpr (XDT == 0) return load_x8_f16(p);
+  else return load_x8_bf16(p);
+}
+
+__device__ __forceinline__ f32x16 mfma32(f16x8 a, f16x8 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ float silu(float g) { return g / (1.0f + __expf(-g)); }
+
+}  // namespace mpb

@@ -48,6 +48,12 @@ CONFIGS = {
     # the config-1 layer driven with 256 decode tokens through bitwidth states
     4: dict(name="qwen15moe_bitsweep", layer_of=1, T=256, xdtype="f16",
             seed=1004),
+    # parity-only shapes: ragged row tiles (I % 128 != 0, H % 128 != 0), a
+    # ragged token chunk, shared experts, and many empty experts
+    10: dict(name="ragged_small", H=384, I=320, E=12, S=2, K=3, T=72, xdtype="f16",
+             q_mode="uniform", bias=False, seed=1010),
+    11: dict(name="sparse_bf16", H=192, I=192, E=40, S=0, K=1, T=9, xdtype="bf16",
+             q_mode="uniform", bias=True, seed=1011, zipf=1.1),
 }
 
 LUT_STD = 0.02  # centroid draws ~ N(0, 0.02)

@@ -41,18 +41,17 @@ def unpack_indices(planes: np.ndarray, b: int) -> np.ndarray:
     """b-bit centroid indices from the top b bit-planes [PW §2.2, §3.1].
 
     idx[n][k] = sum_{p<b} bit_p(n, k) * 2**(b-1-p), where bit_p(n, k) is bit
-    (k mod 32) of word k//32 of plane p.  planes: [>=b][N][W] uint32.
+    j = k mod 32 of word k//32 of plane p (evaluated for all j at once by
+    broadcasting the 32 shifts).  planes: [>=b][N][W] uint32.
     """
     assert 3 <= b <= 8
     _, N, W = planes.shape
-    k = np.arange(32 * W)
-    word = k >> 5
-    shift = (k & 31).astype(np.uint32)
-    idx = np.zeros((N, 32 * W), dtype=np.int64)
+    j = np.arange(32, dtype=np.uint32)
+    idx = np.zeros((N, W, 32), dtype=np.uint8)
     for p in range(b):
-        bit = (planes[p][:, word] >> shift) & np.uint32(1)
-        idx += bit.astype(np.int64) << (b - 1 - p)
-    return idx
+        bit = ((planes[p][:, :, None] >> j) & np.uint32(1)).astype(np.uint8)
+        idx |= bit << np.uint8(b - 1 - p)
+    return idx.reshape(N, 32 * W)
 
 
 def dequant(planes: np.ndarray, lut_bits: np.ndarray, b: int) -> np.ndarray:
@@ -63,7 +62,7 @@ def dequant(planes: np.ndarray, lut_bits: np.ndarray, b: int) -> np.ndarray:
     idx = unpack_indices(planes, b)
     lut = np.ascontiguousarray(lut_bits, dtype=np.uint16).view(np.float16).astype(np.float64)
     assert lut.shape == (planes.shape[1], 1 << b)
-    return np.take_along_axis(lut, idx, axis=1)
+    return lut[np.arange(lut.shape[0])[:, None], idx]
 
 
 def dequant_block(layer, i: int, b: int = None, rows=None) -> np.ndarray:

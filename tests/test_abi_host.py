@@ -1,0 +1,59 @@
+"""C ABI checks that need no GPU: the library loads, exports every function
+include/mpb.h declares, and its host-side validation rejects bad arguments
+before touching the device."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "mpb.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    names = re.findall(r"^\s*(?:const\s+)?[A-Za-z_][A-Za-z0-9_]*\s*\**\s*([A-Za-z_][A-Za-z0-9_]*)\s*\(",
+                       text, flags=re.M)
+    return sorted(set(names))
+
+
+@pytest.fixture(scope="module")
+def L():
+    from mixed_precision_bit_amd import _lib
+    return _lib.lib()
+
+
+def test_header_declares_the_calls():
+    names = declared_functions()
+    for n in ("moe_route", "moe_ffn", "set_committed_bits", "mpb_init", "mpb_pack_block",
+              "mpb_committed_bytes", "mpb_dequant_block", "mpb_last_error"):
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol(L):
+    for n in declared_functions():
+        assert hasattr(L, n), n
+
+
+def test_host_validation_without_device(L):
+    from mixed_precision_bit_amd import _lib as M
+    # nothing bound yet in this process
+    assert L.set_committed_bits(0, 4) == -7
+    assert L.mpb_committed_bytes(None) == -7
+    assert L.moe_ffn_workspace_bytes(16) == 0
+    assert "no layer bound" in M.mpb_last_error()
+    d = M.LayerDesc(100, 128, 8, 0, 2)   # H not a multiple of 64
+    assert L.mpb_init(ctypes.byref(d), ctypes.c_void_p(1), ctypes.c_void_p(1), None) == -2
+    d = M.LayerDesc(256, 128, 8, 0, 9)   # K > E
+    assert L.mpb_init(ctypes.byref(d), ctypes.c_void_p(1), ctypes.c_void_p(1), None) == -2
+    assert L.mpb_init(None, None, None, None) == -1
+    one = ctypes.c_void_p(1)
+    assert L.moe_route(one, 2, one, None, 4, 256, 8, 2, one, one, None) == -1      # dtype
+    assert L.moe_route(one, 0, one, None, 4, 250, 8, 2, one, one, None) == -2      # H % 64
+    assert L.moe_route(one, 0, one, None, 4, 256, 8, 17, one, one, None) == -2     # K
+    assert L.moe_route(one, 0, one, None, 0, 256, 8, 2, one, one, None) == 0       # T = 0
+    assert L.mpb_pack_block(one, 48, 128, (ctypes.c_void_p * 8)(*[1] * 8), None) == -2
+    assert L.mpb_dequant_block((ctypes.c_void_p * 8)(*[1] * 8), one, 64, 128, 9, one, None) == -3
+    assert L.mpb_plane_page_bytes(64, 128) == 64 * 128 // 8

@@ -1,0 +1,350 @@
+"""GPU parity: libmpb (through its C ABI) against the CPU oracle.
+
+Bit-exact: dequantised weights (uint16 compare) and top-K expert indices.
+Floating point: topk_w and out within |gpu - ref| <= 1e-3 + 1e-2 |ref| for
+every element (the stated tolerance). The full-size decode and prefill layers
+are checked on sampled tokens; the small and ragged layers on every element.
+"""
+import numpy as np
+import pytest
+
+import mpb_synth as S
+import oracle as O
+from helpers import assert_close, oracle_route, say, to_dev_x, tol_ratio
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+
+@pytest.fixture(scope="module", autouse=True)
+def need_gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import mixed_precision_bit_amd  # noqa: F401  (fails loudly if libmpb.so is missing)
+
+
+def M():
+    from mixed_precision_bit_amd import _lib
+    return _lib
+
+
+_dev_layers = {}
+
+
+def dev_layer(layer_cache, cfg):
+    from mixed_precision_bit_amd.layer import DeviceLayer
+    L = layer_cache(cfg)
+    key = cfg
+    if key not in _dev_layers:
+        _dev_layers.clear()
+        torch.cuda.empty_cache()
+        _dev_layers[key] = DeviceLayer.from_synth(L)
+    D = _dev_layers[key]
+    # rebind this layer's page table and restore its initial bitwidths
+    M().mpb_init(D.H, D.I, D.E, D.S, D.K, D.q_dev, L.q)
+    return L, D
+
+
+def run_layer(D, Xbits, xdtype):
+    X = to_dev_x(Xbits)
+    idx, w, out = D.forward(X, xdtype)
+    torch.cuda.synchronize()
+    return idx.cpu().numpy(), w.cpu().numpy(), out.cpu().numpy()
+
+
+# ---------------------------------------------------------------- dequant
+@pytest.mark.parametrize("N,Kd", [(64, 128), (256, 2048), (2816, 64)])
+def test_dequant_bit_exact_all_bitwidths(N, Kd):
+    blk = S.make_block(77, N + Kd, N, Kd)
+    canon = torch.from_numpy(blk.planes.view(np.int32)).cuda()
+    nw = M().mpb_plane_page_bytes(N, Kd) // 4
+    pages = [torch.empty(nw, dtype=torch.int32, device="cuda") for _ in range(8)]
+    M().mpb_pack_block(canon, N, Kd, pages)
+    for b in S.BITS:
+        lut = torch.from_numpy(blk.luts[b - 3].view(np.int16)).cuda()
+        out = torch.empty((N, Kd), dtype=torch.int16, device="cuda")
+        M().mpb_dequant_block(pages, lut, N, Kd, b, out)
+        torch.cuda.synchronize()
+        got = out.cpu().numpy().view(np.uint16)
+        ref = O.dequant(blk.planes, blk.luts[b - 3], b).astype(np.float16).view(np.uint16)
+        assert np.array_equal(got, ref), f"b={b}: {np.count_nonzero(got != ref)} mismatches"
+
+
+def test_pack_round_trip_integer_table():
+    rng = np.random.default_rng(11)
+    N, Kd = 96, 192
+    codes = rng.integers(0, 256, size=(N, Kd), dtype=np.uint8)
+    planes = S.codes_to_planes(codes)
+    canon = torch.from_numpy(planes.view(np.int32)).cuda()
+    pages = [torch.empty(N * Kd // 32, dtype=torch.int32, device="cuda") for _ in range(8)]
+    M().mpb_pack_block(canon, N, Kd, pages)
+    lut = np.tile(np.arange(256) - 128.0, (N, 1)).astype(np.float16)
+    out = torch.empty((N, Kd), dtype=torch.int16, device="cuda")
+    M().mpb_dequant_block(pages, torch.from_numpy(lut.view(np.int16)).cuda(), N, Kd, 8, out)
+    torch.cuda.synchronize()
+    got = out.cpu().numpy().view(np.float16).astype(np.int64)
+    assert np.array_equal(got, codes.astype(np.int64) - 128)
+    # lower bitwidths read only the top planes: code >> (8-b) indexes the table
+    for b in (3, 5, 7):
+        lut_b = np.tile(np.arange(1 << b, dtype=np.float64), (N, 1)).astype(np.float16)
+        M().mpb_dequant_block(pages, torch.from_numpy(lut_b.view(np.int16)).cuda(), N, Kd, b, out)
+        torch.cuda.synchronize()
+        got = out.cpu().numpy().view(np.float16).astype(np.int64)
+        assert np.array_equal(got, codes.astype(np.int64) >> (8 - b))
+
+
+# ---------------------------------------------------------------- routing
+@pytest.mark.parametrize("cfg", [0, 1, 2, 3, 4, 10, 11])
+def test_route_bit_exact(cfg):
+    c = S.layer_config(cfg)
+    L = S.make_layer(cfg, blocks=[])
+    Xb = S.make_tokens(cfg)
+    say(f"route cfg{cfg}: T={Xb.shape[0]} H={c['H']} E={c['E']} K={c['K']}")
+    X, z, r = oracle_route(L, Xb)
+    W = torch.from_numpy(L.W_r).cuda()
+    bias = None if L.bias is None else torch.from_numpy(L.bias).cuda()
+    T = Xb.shape[0]
+    idx = torch.empty((T, L.K), dtype=torch.int32, device="cuda")
+    w = torch.empty((T, L.K), dtype=torch.float32, device="cuda")
+    M().moe_route(to_dev_x(Xb), 0 if c["xdtype"] == "f16" else 1, W, bias, L.K, idx, w)
+    torch.cuda.synchronize()
+    gi = idx.cpu().numpy()
+    assert np.array_equal(gi, z), f"{np.count_nonzero((gi != z).any(1))} tokens differ"
+    assert_close(w.cpu().numpy(), r, f"cfg{cfg} topk_w")
+
+
+def test_route_ties_lowest_index():
+    rng = np.random.default_rng(12)
+    H, E, K, T = 256, 24, 6, 40
+    Wr = (rng.standard_normal((E, H)) / 16).astype(np.float32)
+    Wr[7] = Wr[3]
+    Wr[19] = Wr[3]
+    Wr[20] = Wr[11]
+    Xb = rng.standard_normal((T, H)).astype(np.float16).view(np.uint16)
+    X = S.f16_bits_to_f64(Xb)
+    for Wt in (Wr, np.zeros_like(Wr)):
+        z, r, _ = O.route(X, Wt, None, K)
+        idx = torch.empty((T, K), dtype=torch.int32, device="cuda")
+        w = torch.empty((T, K), dtype=torch.float32, device="cuda")
+        M().moe_route(to_dev_x(Xb), 0, torch.from_numpy(Wt).cuda(), None, K, idx, w)
+        torch.cuda.synchronize()
+        assert np.array_equal(idx.cpu().numpy(), z)
+        assert_close(w.cpu().numpy(), r, "tie topk_w")
+
+
+# ---------------------------------------------------------------- FFN, every element
+@pytest.mark.parametrize("cfg", [0, 10, 11])
+def test_ffn_small_every_element(cfg, layer_cache):
+    L, D = dev_layer(layer_cache, cfg)
+    Xb = S.make_tokens(cfg)
+    say(f"ffn cfg{cfg}: T={Xb.shape[0]} q={L.q.tolist()}")
+    gi, gw, gout = run_layer(D, Xb, L.cfg["xdtype"])
+    X, z, r = oracle_route(L, Xb)
+    assert np.array_equal(gi, z)
+    ref = O.moe_ffn(X, z, r, L)
+    assert_close(gout, ref, f"cfg{cfg} out")
+
+
+def test_ffn_qwen_decode_every_element(layer_cache):
+    L, D = dev_layer(layer_cache, 1)
+    Xb = S.make_tokens(1)
+    say(f"ffn cfg1 full: T={Xb.shape[0]}")
+    gi, gw, gout = run_layer(D, Xb, "f16")
+    X, z, r = oracle_route(L, Xb)
+    assert np.array_equal(gi, z)
+    ref = O.moe_ffn(X, z, r, L)
+    assert_close(gout, ref, "cfg1 out")
+
+
+def test_ffn_deterministic_and_block_independent(layer_cache):
+    L, D = dev_layer(layer_cache, 10)
+    Xb = S.make_tokens(10)
+    _, _, a = run_layer(D, Xb, "f16")
+    gi, _, b = run_layer(D, Xb, "f16")
+    assert np.array_equal(a.view(np.uint32), b.view(np.uint32)), "two runs differ"
+    # lower one routed gate_up block: only tokens routed to that expert change
+    e = int(gi[0, 0])
+    i = 2 * e
+    newb = 3 if L.q[i] != 3 else 4
+    M().set_committed_bits(i, newb)
+    _, _, c = run_layer(D, Xb, "f16")
+    routed = (gi == e).any(axis=1)
+    assert np.array_equal(c[~routed].view(np.uint32), a[~routed].view(np.uint32))
+    assert (c[routed] != a[routed]).any(axis=1).all()
+    X, z, r = oracle_route(L, Xb)
+    q2 = L.q.copy()
+    q2[i] = newb
+    assert_close(c, O.moe_ffn(X, z, r, L, q=q2), "after set_committed_bits")
+    M().set_committed_bits(i, int(L.q[i]))
+
+
+def test_set_committed_bits_is_stream_ordered(layer_cache):
+    L, D = dev_layer(layer_cache, 0)
+    Xb = S.make_tokens(0)
+    X = to_dev_x(Xb)
+    T = Xb.shape[0]
+    idx, w = D.alloc_route(T)
+    out1, ws1 = D.alloc_ffn(T)
+    out2, ws2 = D.alloc_ffn(T)
+    D.route(X, "f16", idx, w)
+    q2 = L.q.copy()
+    D.ffn(X, "f16", idx, w, out1, ws1)
+    for i in range(L.n_blocks):          # enqueued behind the first FFN
+        q2[i] = 8 if L.q[i] < 8 else 3
+        M().set_committed_bits(i, int(q2[i]))
+    D.ffn(X, "f16", idx, w, out2, ws2)
+    torch.cuda.synchronize()
+    Xf, z, r = oracle_route(L, Xb)
+    assert_close(out1.cpu().numpy(), O.moe_ffn(Xf, z, r, L), "before commit")
+    assert_close(out2.cpu().numpy(), O.moe_ffn(Xf, z, r, L, q=q2), "after commit")
+    assert [M().mpb_get_committed_bits(i) for i in range(L.n_blocks)] == q2.tolist()
+
+
+# ---------------------------------------------------------------- full-size layers, sampled
+def test_ffn_mixtral_decode_sampled(layer_cache):
+    L, D = dev_layer(layer_cache, 2)
+    Xb = S.make_tokens(2)
+    say(f"ffn cfg2 full: T={Xb.shape[0]} (sampled check)")
+    gi, gw, gout = run_layer(D, Xb, "f16")
+    X, z, r = oracle_route(L, Xb)
+    assert np.array_equal(gi, z)
+    toks = [0, 77, 127]
+    cols = np.arange(0, L.H, 7)
+    ref = O.moe_ffn_sampled(X, z, r, L, toks, cols)
+    assert_close(gout[np.ix_(toks, cols)], ref, "cfg2 sampled out")
+
+
+def test_ffn_prefill_sampled(layer_cache):
+    L, D = dev_layer(layer_cache, 3)
+    Xb = S.make_tokens(3)
+    say(f"ffn cfg3 full: T={Xb.shape[0]} (sampled check)")
+    gi, gw, gout = run_layer(D, Xb, "bf16")
+    X, z, r = oracle_route(L, Xb)
+    assert np.array_equal(gi, z)
+    toks = np.arange(0, Xb.shape[0], 171)
+    ref = O.moe_ffn(X[toks], z[toks], r[toks], L)
+    assert_close(gout[toks], ref, "cfg3 sampled out")
+
+
+# ---------------------------------------------------------------- bitwidth sweep
+def test_bitwidth_sweep_states(layer_cache):
+    L, D = dev_layer(layer_cache, 1)   # the config-4 layer is the config-1 layer
+    Xb = S.make_tokens(4)
+    T = Xb.shape[0]
+    X, z, r = oracle_route(L, Xb)
+    s = S.make_sensitivity(4, L.n_blocks)
+    states = [("initial", L.q.copy())]
+    for f in (0.25, 0.5, 0.75):
+        red, short = O.greedy_reductions(L, s, f)
+        q = L.q.copy()
+        for i, b2 in red:
+            q[i] = b2
+        states.append((f"lowered {int(f * 100)}% (short {short})", q))
+    states.append(("all 8-bit", np.full(L.n_blocks, 8, np.int32)))
+    wcache = {}
+    Xd = to_dev_x(Xb)
+    idx, w = D.alloc_route(T)
+    out, ws = D.alloc_ffn(T)
+    D.route(Xd, "f16", idx, w)
+    torch.cuda.synchronize()
+    assert np.array_equal(idx.cpu().numpy(), z)
+    prev = L.q.copy()
+    for name, q in states:
+        for i in np.nonzero(q != prev)[0]:
+            M().set_committed_bits(int(i), int(q[i]))
+        prev = q
+        D.ffn(Xd, "f16", idx, w, out, ws)
+        torch.cuda.synchronize()
+        assert M().mpb_committed_bytes() == O.committed_bytes(L, q=q)
+        ref = O.moe_ffn(X, z, r, L, q=q, wcache=wcache)
+        r_ = tol_ratio(out.cpu().numpy(), ref)
+        say(f"  state {name}: committed {O.committed_bytes(L, q=q) / 1e6:.1f} MB, max err/tol {r_:.4f}")
+        assert r_ <= 1.0
+
+
+# ---------------------------------------------------------------- edge cases
+def test_edge_token_counts(layer_cache):
+    L, D = dev_layer(layer_cache, 10)
+    for T in (1, 33, 200):
+        Xb = S.make_tokens(10, T=T, seed=5000 + T)
+        _, _, gout = run_layer(D, Xb, "f16")
+        X, z, r = oracle_route(L, Xb)
+        assert_close(gout, O.moe_ffn(X, z, r, L), f"T={T}")
+    X0 = torch.empty((0, L.H), dtype=torch.int16, device="cuda")
+    idx, w = D.alloc_route(0)
+    out, ws = D.alloc_ffn(0)
+    D.route(X0, "f16", idx, w)
+    D.ffn(X0, "f16", idx, w, out, ws)
+    torch.cuda.synchronize()
+
+
+def test_edge_one_expert_takes_all_and_extreme_bitwidths(layer_cache):
+    L, D = dev_layer(layer_cache, 10)
+    T = 150
+    Xb = S.make_tokens(10, T=T, seed=99)
+    X = S.f16_bits_to_f64(Xb)
+    # every token picks experts 0..K-1 (zero logits tie), one group of 150 tokens
+    z = np.tile(np.arange(L.K), (T, 1))
+    r = np.full((T, L.K), 1.0 / L.K)
+    idx = torch.from_numpy(z.astype(np.int32)).cuda()
+    w = torch.from_numpy(r.astype(np.float32)).cuda()
+    out, ws = D.alloc_ffn(T)
+    for qv in (3, 8):
+        for i in range(L.n_blocks):
+            M().set_committed_bits(i, qv)
+        D.ffn(to_dev_x(Xb), "f16", idx, w, out, ws)
+        torch.cuda.synchronize()
+        assert_close(out.cpu().numpy(), O.moe_ffn(X, z, r, L, q=np.full(L.n_blocks, qv)), f"all q={qv}")
+
+
+def test_edge_out_of_range_expert_ids_contribute_nothing(layer_cache):
+    L, D = dev_layer(layer_cache, 10)
+    T = 20
+    Xb = S.make_tokens(10, T=T, seed=7)
+    X, z, r = oracle_route(L, Xb)
+    zb = z.copy()
+    zb[3, 1] = -1
+    zb[8, 0] = L.E + 5
+    idx = torch.from_numpy(zb.astype(np.int32)).cuda()
+    w = torch.from_numpy(r.astype(np.float32)).cuda()
+    out, ws = D.alloc_ffn(T)
+    D.ffn(to_dev_x(Xb), "f16", idx, w, out, ws)
+    torch.cuda.synchronize()
+    rr = r.copy()
+    rr[3, 1] = 0.0
+    rr[8, 0] = 0.0
+    zz = zb.copy()
+    zz[3, 1] = 0
+    zz[8, 0] = 0
+    assert_close(out.cpu().numpy(), O.moe_ffn(X, zz, rr, L), "bad ids")
+
+
+def test_abi_errors_after_init(layer_cache):
+    L, D = dev_layer(layer_cache, 0)
+    E = M().MpbError
+    nb = L.n_blocks
+    with pytest.raises(E) as ei:
+        M().set_committed_bits(nb, 4)
+    assert ei.value.code == -3
+    with pytest.raises(E):
+        M().set_committed_bits(0, 9)
+    i = 1
+    M().set_committed_bits(i, 4)
+    M().mpb_set_resident_planes(i, 5)
+    with pytest.raises(E) as ei:
+        M().set_committed_bits(i, 6)   # planes 5..7 are not resident
+    assert ei.value.code == -4
+    M().set_committed_bits(i, 5)
+    with pytest.raises(E) as ei:
+        M().mpb_set_resident_planes(i, 4)  # offload must lower q_i first
+    assert ei.value.code == -4
+    M().mpb_set_resident_planes(i, 8)
+    M().set_committed_bits(i, int(L.q[i]))
+    Xb = S.make_tokens(0)
+    idx, w = D.alloc_route(16)
+    out, _ = D.alloc_ffn(16)
+    small = torch.empty(16, dtype=torch.uint8, device="cuda")
+    with pytest.raises(E) as ei:
+        D.ffn(to_dev_x(Xb), "f16", idx, w, out, small)
+    assert ei.value.code == -5
