@@ -80,7 +80,8 @@ typedef struct {
  */
 int mpb_init(const mpb_layer_desc* d, int32_t* q_dev, const int32_t* q_init_host, void* stream);
 
-/* Bytes of one packed plane page of an [N][Kd] block (= N*Kd/8). */
+/* Bytes of one packed plane page of an [N][Kd] block: N * ceil(Kd/128) * 16
+ * (= N*Kd/8 when Kd is a multiple of 128; rows are padded to 128 elements). */
 size_t mpb_plane_page_bytes(int N, int Kd);
 
 /*
@@ -105,7 +106,8 @@ int mpb_pack_block(const uint32_t* canon_dev, int N, int Kd, uint32_t* const* pl
  * int32 (descending logit, ties to the lower expert index) and topk_w_dev
  * [T][K] fp32 = softmax over all E experts restricted to the K winners and
  * renormalised (equal to a softmax over the K winning logits). Needs
- * 1 <= K <= min(E, 16), E <= 512, H % 64 == 0; T == 0 is a no-op.
+ * 1 <= K <= min(E, 16), E <= 512, H a multiple of 64 up to 4096; T == 0 is a
+ * no-op.
  * Does not need mpb_init.
  */
 int moe_route(const void* X_dev, int x_dtype, const float* W_router_dev, const float* bias_dev,

@@ -2,19 +2,25 @@
 //
 // "PagedWeight", §2.1: the router assigns routing weights to the E experts and
 // selects the top K for each token. Logits are accumulated in fp64: an fp16 or
-// bf16 activation times an fp32 router weight is exact in fp64, and each logit
-// is summed in one fixed order, so two identical router rows give bit-identical
-// logits and the lower expert index wins the tie. The routing weights are the
-// softmax over all experts restricted to the K winners and renormalised, which
-// equals a softmax over the K winning logits.
+// bf16 activation times an fp32 router weight is exact in fp64, and every
+// logit is summed in one fixed order (per-lane partials over a fixed set of
+// hidden indices, then a butterfly reduction whose pairwise adds are
+// commutative), so two identical router rows give bit-identical logits and the
+// lower expert index wins the tie. The routing weights are the softmax over
+// all experts restricted to the K winners and renormalised, which equals a
+// softmax over the K winning logits.
+//
+// Mapping: one workgroup (4 waves) per token. Wave w scores experts w, w+4,
+// ...; lane l owns hidden indices 4l + 256i + {0..3}, holds the token's
+// activations for them in fp64 registers, and streams the matching float4
+// pieces of each router row (one coalesced 1 KiB read per wave per piece).
 #include "mpb_device.h"
 #include "mpb_internal.h"
 
 namespace mpb {
 
-constexpr int kRT = 16;      // tokens per workgroup
-constexpr int kHC = 64;      // activations staged per step
-constexpr int kEMax = 512;   // experts supported by the LDS logit tile
+constexpr int kEMax = 512;   // experts supported by the LDS logit row
+constexpr int kHMax = 4096;  // hidden sizes held in registers (16 float4 pieces)
 
 template <int XDT>
 __device__ __forceinline__ double x_to_f64(uint16_t v) {
@@ -26,96 +32,100 @@ __device__ __forceinline__ bool better(double v, int i, double bv, int bi) {
   return v > bv || (v == bv && i < bi);
 }
 
-template <int XDT>
+template <int XDT, int NPC>
 __global__ __launch_bounds__(256) void k_route(const uint16_t* __restrict__ X, const float* __restrict__ W,
                                                const float* __restrict__ bias, int T, int H, int E, int K,
                                                int32_t* __restrict__ idx_out, float* __restrict__ w_out) {
-  __shared__ double xs[kRT][kHC + 1];  // +1: the 16 token rows fall in distinct banks
-  __shared__ double lg[kRT][kEMax];
-  __shared__ double tv[4][16];
-  __shared__ int ti[4][16];
-  const int tid = threadIdx.x;
-  const int t0 = blockIdx.x * kRT;
-  const int tl = tid & 15, eg = tid >> 4;
-
-  // logits: thread (tl, eg) owns experts ep + eg + 16*j, j < 8
-  for (int ep = 0; ep < E; ep += 128) {
-    double acc[8];
+  __shared__ double lg[kEMax];
+  const int t = blockIdx.x, tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const uint16_t* xr = X + (size_t)t * H;
+  double x[NPC][4];
 #pragma unroll
-    for (int j = 0; j < 8; ++j) acc[j] = 0.0;
-    for (int h0 = 0; h0 < H; h0 += kHC) {
-      __syncthreads();
-      for (int j = tid; j < kRT * kHC; j += 256) {
-        const int t = j / kHC, hh = j % kHC;
-        xs[t][hh] = (t0 + t < T) ? x_to_f64<XDT>(X[(size_t)(t0 + t) * H + h0 + hh]) : 0.0;
-      }
-      __syncthreads();
+  for (int i = 0; i < NPC; ++i) {
+    const int h = 4 * lane + 256 * i;
+    const bool ok = h < H;
+    const ushort4 v = ok ? *(const ushort4*)(xr + h) : make_ushort4(0, 0, 0, 0);
+    x[i][0] = x_to_f64<XDT>(v.x);
+    x[i][1] = x_to_f64<XDT>(v.y);
+    x[i][2] = x_to_f64<XDT>(v.z);
+    x[i][3] = x_to_f64<XDT>(v.w);
+  }
+  for (int e = w; e < E; e += 4) {
+    const float* wr = W + (size_t)e * H;
+    double a = 0.0;
 #pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const int e = ep + eg + 16 * j;
-        if (e < E) {
-          const float4* wr = (const float4*)(W + (size_t)e * H + h0);
-          double a = acc[j];
-          for (int h4 = 0; h4 < kHC / 4; ++h4) {
-            const float4 wv = wr[h4];
-            a = fma(xs[tl][4 * h4 + 0], (double)wv.x, a);
-            a = fma(xs[tl][4 * h4 + 1], (double)wv.y, a);
-            a = fma(xs[tl][4 * h4 + 2], (double)wv.z, a);
-            a = fma(xs[tl][4 * h4 + 3], (double)wv.w, a);
-          }
-          acc[j] = a;
-        }
+    for (int i = 0; i < NPC; ++i) {
+      const int h = 4 * lane + 256 * i;
+      if (h < H) {
+        const float4 wv = *(const float4*)(wr + h);
+        a = fma(x[i][0], (double)wv.x, a);
+        a = fma(x[i][1], (double)wv.y, a);
+        a = fma(x[i][2], (double)wv.z, a);
+        a = fma(x[i][3], (double)wv.w, a);
       }
     }
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const int e = ep + eg + 16 * j;
-      if (e < E) lg[tl][e] = acc[j] + (bias ? (double)bias[e] : 0.0);
-    }
+    for (int off = 32; off >= 1; off >>= 1) a += __shfl_xor(a, off);
+    if (lane == 0) lg[e] = a + (bias ? (double)bias[e] : 0.0);
   }
   __syncthreads();
-
-  // top-K: wave w handles token slots w, w+4, w+8, w+12
-  const int lane = tid & 63, w = tid >> 6;
-  for (int tt = w; tt < kRT; tt += 4) {
-    const int t = t0 + tt;
-    if (t >= T) break;
-    uint32_t taken = 0;
-    for (int k = 0; k < K; ++k) {
-      double bv = -__builtin_inf();
-      int bi = 0x7fffffff;
-      for (int i = 0; i < kEMax / 64; ++i) {
-        const int e = lane + 64 * i;
-        if (e < E && !((taken >> i) & 1u)) {
-          const double v = lg[tt][e];
-          if (better(v, e, bv, bi)) { bv = v; bi = e; }
-        }
+  if (w != 0) return;
+  // top-K on wave 0; lane holds experts lane + 64i
+  uint32_t taken = 0;
+  double tv[16];
+  int ti[16];
+  for (int k = 0; k < K; ++k) {
+    double bv = -__builtin_inf();
+    int bi = 0x7fffffff;
+    for (int i = 0; i < kEMax / 64; ++i) {
+      const int e = lane + 64 * i;
+      if (e < E && !((taken >> i) & 1u)) {
+        const double v = lg[e];
+        if (better(v, e, bv, bi)) { bv = v; bi = e; }
       }
+    }
 #pragma unroll
-      for (int off = 32; off >= 1; off >>= 1) {
-        const double ov = __shfl_xor(bv, off);
-        const int oi = __shfl_xor(bi, off);
-        if (better(ov, oi, bv, bi)) { bv = ov; bi = oi; }
-      }
-      if (bi < E && (bi & 63) == lane) taken |= 1u << (bi >> 6);
-      if (lane == 0) { tv[w][k] = bv; ti[w][k] = bi; }
+    for (int off = 32; off >= 1; off >>= 1) {
+      const double ov = __shfl_xor(bv, off);
+      const int oi = __shfl_xor(bi, off);
+      if (better(ov, oi, bv, bi)) { bv = ov; bi = oi; }
     }
-    if (lane == 0) {
-      double sum = 0.0;
-      for (int k = 0; k < K; ++k) sum += exp(tv[w][k] - tv[w][0]);
-      for (int k = 0; k < K; ++k) {
-        idx_out[(size_t)t * K + k] = ti[w][k];
-        w_out[(size_t)t * K + k] = (float)(exp(tv[w][k] - tv[w][0]) / sum);
-      }
-    }
+    if (bi < E && (bi & 63) == lane) taken |= 1u << (bi >> 6);
+#pragma unroll
+    for (int kk = 0; kk < 16; ++kk)
+      if (kk == k) { tv[kk] = bv; ti[kk] = bi; }
   }
+  if (lane < K) {
+    double sum = 0.0, mine = 0.0;
+    int myi = 0;
+#pragma unroll
+    for (int kk = 0; kk < 16; ++kk) {
+      if (kk < K) {
+        const double ex = exp(tv[kk] - tv[0]);
+        sum += ex;
+        if (kk == lane) { mine = ex; myi = ti[kk]; }
+      }
+    }
+    idx_out[(size_t)t * K + lane] = myi;
+    w_out[(size_t)t * K + lane] = (float)(mine / sum);
+  }
+}
+
+template <int XDT>
+static void launch_route_x(const uint16_t* X, const float* W, const float* bias, int T, int H, int E, int K,
+                           int32_t* idx, float* w, hipStream_t s) {
+  const int npc = (H + 255) / 256;
+  const dim3 grid(T), block(256);
+  if (npc <= 4) hipLaunchKernelGGL((k_route<XDT, 4>), grid, block, 0, s, X, W, bias, T, H, E, K, idx, w);
+  else if (npc <= 8) hipLaunchKernelGGL((k_route<XDT, 8>), grid, block, 0, s, X, W, bias, T, H, E, K, idx, w);
+  else if (npc <= 12) hipLaunchKernelGGL((k_route<XDT, 12>), grid, block, 0, s, X, W, bias, T, H, E, K, idx, w);
+  else hipLaunchKernelGGL((k_route<XDT, 16>), grid, block, 0, s, X, W, bias, T, H, E, K, idx, w);
 }
 
 hipError_t launch_route(const uint16_t* X, int xdt, const float* W, const float* bias, int T, int H, int E,
                         int K, int32_t* idx, float* w, hipStream_t s) {
-  const dim3 grid((T + kRT - 1) / kRT);
-  if (xdt == 0) hipLaunchKernelGGL(k_route<0>, grid, dim3(256), 0, s, X, W, bias, T, H, E, K, idx, w);
-  else hipLaunchKernelGGL(k_route<1>, grid, dim3(256), 0, s, X, W, bias, T, H, E, K, idx, w);
+  if (xdt == 0) launch_route_x<0>(X, W, bias, T, H, E, K, idx, w, s);
+  else launch_route_x<1>(X, W, bias, T, H, E, K, idx, w, s);
   return hipGetLastError();
 }
 

@@ -5,6 +5,7 @@
 #include <vector>
 
 #include "mpb.h"
+#include "mpb_device.h"
 #include "mpb_internal.h"
 
 namespace {
@@ -61,7 +62,7 @@ namespace mpb {
 
 static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
-WsLayout ws_layout(int T, int H, int I, int E, int S, int K) {
+WsLayout ws_layout(int T, int H, int I, int E, int S, int K, bool bf16) {
   WsLayout L{};
   const size_t NB = (size_t)E + S, P = (size_t)T * (K + S);
   size_t off = 0;
@@ -70,8 +71,10 @@ WsLayout ws_layout(int T, int H, int I, int E, int S, int K) {
   L.ptok = off;    off += align256(P * 4);
   L.pw = off;      off += align256(P * 4);
   L.inv = off;     off += align256(P * 4);
-  L.h = off;       off += align256(P * (size_t)I * 4);
+  L.hhi = off;     off += align256(P * (size_t)I * 2);
+  L.hlo = off;     off += align256(P * (size_t)I * 2);
   L.y = off;       off += align256(P * (size_t)H * 4);
+  L.xh = off;      off += bf16 ? align256((size_t)T * H * 2) : 0;
   L.total = off;
   return L;
 }
@@ -108,7 +111,7 @@ int mpb_init(const mpb_layer_desc* d, int32_t* q_dev, const int32_t* q_init_host
 
 size_t mpb_plane_page_bytes(int N, int Kd) {
   if (N <= 0 || Kd <= 0) return 0;
-  return (size_t)N * Kd / 8;
+  return (size_t)N * mpb::page_chunks(Kd) * 16;
 }
 
 int mpb_pack_block(const uint32_t* canon_dev, int N, int Kd, uint32_t* const* plane_pages_host,
@@ -144,7 +147,7 @@ int moe_route(const void* X_dev, int x_dtype, const float* W_router_dev, const f
               int E, int K, int32_t* topk_idx_dev, float* topk_w_dev, void* stream) try {
   if (x_dtype != MPB_F16 && x_dtype != MPB_BF16) return fail(MPB_E_ARG, "moe_route: bad x_dtype");
   if (T < 0) return fail(MPB_E_ARG, "moe_route: T < 0");
-  if (H <= 0 || H % 64) return fail(MPB_E_SHAPE, "moe_route: H must be a positive multiple of 64");
+  if (H <= 0 || H % 64 || H > 4096) return fail(MPB_E_SHAPE, "moe_route: H must be a multiple of 64 in 64..4096");
   if (E < 1 || E > 512) return fail(MPB_E_SHAPE, "moe_route: E must be in 1..512");
   if (K < 1 || K > 16 || K > E) return fail(MPB_E_SHAPE, "moe_route: K must be in 1..min(E,16)");
   if (T == 0) return MPB_OK;
@@ -159,7 +162,8 @@ int moe_route(const void* X_dev, int x_dtype, const float* W_router_dev, const f
 
 size_t moe_ffn_workspace_bytes(int T) {
   if (!g.init || T < 0) return 0;
-  return mpb::ws_layout(T, g.H, g.I, g.E, g.S, g.K).total;
+  // sized for bf16 activations (the larger case)
+  return mpb::ws_layout(T, g.H, g.I, g.E, g.S, g.K, true).total;
 }
 
 int moe_ffn(const void* X_dev, int x_dtype, int T, const int32_t* topk_idx_dev, const float* topk_w_dev,
@@ -172,12 +176,12 @@ int moe_ffn(const void* X_dev, int x_dtype, int T, const int32_t* topk_idx_dev, 
   if (T > (1 << 20)) return fail(MPB_E_SHAPE, "moe_ffn: T above 2^20");
   if (!X_dev || !topk_idx_dev || !topk_w_dev || !planes_dev || !luts_dev || !q_dev || !out_dev || !ws_dev)
     return fail(MPB_E_ARG, "moe_ffn: null pointer");
-  const mpb::WsLayout L = mpb::ws_layout(T, g.H, g.I, g.E, g.S, g.K);
+  const mpb::WsLayout L = mpb::ws_layout(T, g.H, g.I, g.E, g.S, g.K, x_dtype == MPB_BF16);
   if (ws_bytes < L.total)
     return fail(MPB_E_WS, "moe_ffn: workspace " + std::to_string(ws_bytes) + " < " + std::to_string(L.total));
   char* ws = (char*)ws_dev;
   mpb::FfnParams p{};
-  p.X = (const uint16_t*)X_dev;
+  p.xh = x_dtype == MPB_BF16 ? (const uint16_t*)(ws + L.xh) : (const uint16_t*)X_dev;
   p.T = T; p.H = g.H; p.I = g.I; p.E = g.E; p.S = g.S; p.K = g.K; p.NB = g.E + g.S;
   p.topk_idx = topk_idx_dev; p.topk_w = topk_w_dev;
   p.planes = planes_dev; p.luts = luts_dev; p.q = q_dev;
@@ -186,15 +190,21 @@ int moe_ffn(const void* X_dev, int x_dtype, int T, const int32_t* topk_idx_dev, 
   p.ptok = (int32_t*)(ws + L.ptok);
   p.pw = (float*)(ws + L.pw);
   p.inv = (int32_t*)(ws + L.inv);
-  p.h = (float*)(ws + L.h);
+  p.hhi = (uint16_t*)(ws + L.hhi);
+  p.hlo = (uint16_t*)(ws + L.hlo);
   p.y = (float*)(ws + L.y);
   p.out = out_dev;
   hipStream_t s = (hipStream_t)stream;
   mark(0, s);
-  hipError_t e = mpb::launch_permute(p, s);
+  hipError_t e = hipSuccess;
+  if (x_dtype == MPB_BF16) {
+    e = mpb::launch_x_to_f16((const uint16_t*)X_dev, (uint16_t*)(ws + L.xh), (size_t)T * g.H, s);
+    if (e != hipSuccess) return hip_fail(e, "moe_ffn: activation conversion");
+  }
+  e = mpb::launch_permute(p, s);
   if (e != hipSuccess) return hip_fail(e, "moe_ffn: permute");
   mark(1, s);
-  e = mpb::launch_gate_up(p, x_dtype, s);
+  e = mpb::launch_gate_up(p, s);
   if (e != hipSuccess) return hip_fail(e, "moe_ffn: gate_up");
   mark(2, s);
   e = mpb::launch_down(p, s);

@@ -19,20 +19,28 @@ typedef uint16_t u16x8 __attribute__((ext_vector_type(8)));
 namespace mpb {
 
 // ----------------------------------------------------------------------------
-// Packed plane word layout.
+// Packed plane page layout.
 //
-// A packed page stores, for every 32-row tile and every 32-element word of a
-// row, one uint32 per row: page[((n/32) * W + w) * 32 + n%32], W = Kd/32. A
-// wave that reads word w of 32 consecutive rows therefore reads 128 contiguous
-// bytes.
+// A page holds one bit-plane of an [N][Kd] block. Rows are grouped in tiles of
+// 32; each row's W = Kd/32 words are grouped in chunks of 4 (128 elements),
+// NC = ceil(W/4) chunks per row, the last one zero-padded. Chunk c of row n is
+// 16 contiguous bytes at word ((n/32 * NC + c) * 32 + n%32) * 4, so a wave whose
+// 32 lanes hold 32 rows reads one chunk of each with a single 512-byte
+// dwordx4 access.
 //
-// Inside the word, element e = 4*s + b (s = 0..7, b = 0..3) of plane p sits at
+// Inside a word, element e = 4*s + b (s = 0..7, b = 0..3) of plane p sits at
 // bit (8*b + s + p) mod 32. With that placement the q-bit indices of four
 // elements {4s..4s+3} come out of q plane words with one AND per plane and one
 // rotation: OR_p (P_p & rotl(0x01010101, s+p)), rotated right by s, holds in
 // byte b the bits of element 4s+b with plane p at bit p.
 // ----------------------------------------------------------------------------
 __host__ __device__ constexpr int packed_pos(int e, int p) { return (8 * (e & 3) + (e >> 2) + p) & 31; }
+
+__host__ __device__ constexpr int page_chunks(int Kd) { return (Kd / 32 + 3) / 4; }
+
+__host__ __device__ constexpr size_t page_word(int n, int w, int NC) {
+  return (((size_t)(n >> 5) * NC + (w >> 2)) * 32 + (n & 31)) * 4 + (w & 3);
+}
 
 __host__ __device__ constexpr uint32_t rotl_c(uint32_t x, int r) {
   return (r & 31) ? (x << (r & 31)) | (x >> (32 - (r & 31))) : x;
@@ -85,17 +93,30 @@ __device__ __forceinline__ uint32_t lut_slot(int r, int w) {
 }
 
 // Stage the Q-bit tables of rows row0..row0+31 (canonical [N][2^Q] fp16 at
-// lut, canonical index order) for wave w. Called by all 64 lanes of the wave.
+// lut, canonical index order) into table slot set w. Called by all 64 lanes of
+// one wave; lane (r, half) copies 16-byte pieces half, half+2, ... of row r.
 template <int Q>
 __device__ __forceinline__ void stage_luts(uint16_t* lds, const uint16_t* __restrict__ lut, int row0,
                                            int lane, int w) {
-  const int r = lane & 31;
+  constexpr int NP = (1 << Q) / 8;  // 16-byte pieces per row
+  const int r = lane & 31, half = lane >> 5;
   const uint32_t slot = lut_slot(r, w);
-  const uint16_t* src = lut + (size_t)(row0 + r) * (1u << Q);
-#pragma unroll 4
-  for (int v = lane >> 5; v < (1 << Q); v += 2) {
-    const uint32_t u = bitrev<Q>(v);
-    lds[(u * 256u + slot) >> 1] = src[v];
+  const uint4* src = (const uint4*)(lut + (size_t)(row0 + r) * (1u << Q));
+  constexpr int NI = (NP + 1) / 2;
+  uint4 v[NI];
+#pragma unroll
+  for (int i = 0; i < NI; ++i)
+    if (half + 2 * i < NP) v[i] = src[half + 2 * i];
+#pragma unroll
+  for (int i = 0; i < NI; ++i) {
+    if (half + 2 * i < NP) {
+      const uint32_t wd[4] = {v[i].x, v[i].y, v[i].z, v[i].w};
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const uint32_t u = bitrev<Q>(8 * (half + 2 * i) + j);
+        lds[(u * 256u + slot) >> 1] = (uint16_t)(wd[j >> 1] >> (16 * (j & 1)));
+      }
+    }
   }
 }
 
@@ -145,5 +166,19 @@ __device__ __forceinline__ f32x16 mfma32(f16x8 a, f16x8 b, f32x16 c) {
 }
 
 __device__ __forceinline__ float silu(float g) { return g / (1.0f + __expf(-g)); }
+
+// h = hi + lo with hi = fp16(h) and lo = fp16(h - hi). h is pinned to one fp32
+// value first: otherwise floating-point contraction may fold the product that
+// produced h into the two conversions separately (v_fma_mix), rounding hi two
+// different ways and making hi + lo wrong by one fp16 ulp near rounding ties.
+struct split16 {
+  _Float16 hi, lo;
+};
+__device__ __forceinline__ split16 split_hi_lo(float h) {
+  asm volatile("" : "+v"(h));
+  const _Float16 hi = (_Float16)h;
+  const float r = h - (float)hi;  // exact: hi is within half an fp16 ulp of h
+  return {hi, (_Float16)r};
+}
 
 }  // namespace mpb

@@ -77,7 +77,8 @@ def test_pack_round_trip_integer_table():
     codes = rng.integers(0, 256, size=(N, Kd), dtype=np.uint8)
     planes = S.codes_to_planes(codes)
     canon = torch.from_numpy(planes.view(np.int32)).cuda()
-    pages = [torch.empty(N * Kd // 32, dtype=torch.int32, device="cuda") for _ in range(8)]
+    nw = M().mpb_plane_page_bytes(N, Kd) // 4
+    pages = [torch.empty(nw, dtype=torch.int32, device="cuda") for _ in range(8)]
     M().mpb_pack_block(canon, N, Kd, pages)
     lut = np.tile(np.arange(256) - 128.0, (N, 1)).astype(np.float16)
     out = torch.empty((N, Kd), dtype=torch.int16, device="cuda")
