@@ -30,7 +30,7 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
 METRIC = "MoE-layer tokens/s and achieved HBM GB/s (% of peak) at mixed bitwidths"
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_gate_up_qwen15moe_decode.json")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_gate_up_qwen15moe_decode.md")
 KERNEL_SRCS = ["k_ffn_decode.hip", "mpb_device.h"]
 
 
@@ -78,6 +78,26 @@ def cpu_baseline(L, Xbits, n_tokens):
                       f"with dequantisation of every touched block), fp64 numpy, {dt:.1f} s"}
 
 
+def copy_calibration(torch, nbytes, steps):
+    """Time a plain copy kernel (torch's device copy) of known size: the
+    reference rocprofv3's FETCH_SIZE / WRITE_SIZE are scaled by, and the
+    measured copy bandwidth of the device."""
+    a = torch.empty(nbytes // 4, dtype=torch.int32, device="cuda").fill_(1)
+    b = torch.empty_like(a)
+    for _ in range(3):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    s.record()
+    for _ in range(steps):
+        b.copy_(a)
+    e.record()
+    torch.cuda.synchronize()
+    ms = s.elapsed_time(e) / steps
+    print(json.dumps({"copy_bytes": nbytes, "ms_per_copy": round(ms, 5),
+                      "copy_gbs": round(2 * nbytes / (ms * 1e-3) / 1e9, 1)}), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -87,6 +107,10 @@ def main():
     ap.add_argument("--rotate", type=int, default=0, help="layer copies (0: enough for >= 1 GB)")
     ap.add_argument("--cpu-tokens", type=int, default=8)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-bytes", type=int, default=0,
+                    help="only time a plain device-to-device copy of this many bytes (counter calibration)")
+    ap.add_argument("--no-graph", dest="graph", action="store_false",
+                    help="launch the timed steps eagerly instead of replaying them as one HIP graph")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (got --gpus {args.gpus}); this layer is measured at N=1.",
@@ -94,6 +118,9 @@ def main():
         sys.exit(2)
 
     import torch
+    if args.copy_bytes:
+        copy_calibration(torch, args.copy_bytes, args.steps)
+        return
     import mpb_synth as S
     from mixed_precision_bit_amd import _lib as M
     from mixed_precision_bit_amd.layer import DeviceLayer
@@ -121,8 +148,8 @@ def main():
     def step(k):
         D = layers[k % R]
         idx, w, out, ws = bufs[k % R]
-        D.route(X, xdt, idx, w, stream)
-        D.ffn(X, xdt, idx, w, out, ws, stream)
+        D.route(X, xdt, idx, w)        # on torch's current stream
+        D.ffn(X, xdt, idx, w, out, ws)
 
     for k in range(args.warmup):
         step(k)
@@ -130,21 +157,52 @@ def main():
     idx_host = bufs[0][0].cpu().numpy()
     step_bytes, gu_bytes, n_touched = algorithmic_bytes(L, idx_host, T)
 
-    # per-step phase events recorded by moe_ffn inside the timed region
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+
+    # Timed region 1 (the headline): K steps. With --graph (default) the K
+    # steps are captured once as a HIP graph, replayed once untimed, then
+    # replayed inside the timed region.
+    if args.graph:
+        cap = torch.cuda.Stream()
+        cap.wait_stream(stream)
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.stream(cap):
+            with torch.cuda.graph(graph, stream=cap):
+                for k in range(args.steps):
+                    step(args.warmup + k)
+        stream.wait_stream(cap)
+        graph.replay()
+        torch.cuda.synchronize()
+        start.record(stream)
+        graph.replay()
+        end.record(stream)
+    else:
+        torch.cuda.synchronize()
+        start.record(stream)
+        for k in range(args.steps):
+            step(args.warmup + k)
+        end.record(stream)
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(end) / args.steps
+
+    # Timed region 2 (per-kernel times): the same K steps launched eagerly, with
+    # moe_ffn recording HIP events on its stream before grouping, gate_up, down
+    # and combine and after the combine (event records inside a graph do not
+    # order against its kernel nodes, so kernel times come from this pass).
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
     for row in evs:              # torch creates the HIP event on first record
         for e in row:
             e.record(stream)
-    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
-    start.record(stream)
+    start2, end2 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start2.record(stream)
     for k in range(args.steps):
         M.mpb_set_kernel_events([e.cuda_event for e in evs[k]])
         step(args.warmup + k)
-    end.record(stream)
-    torch.cuda.synchronize()
     M.mpb_set_kernel_events([])
-    ms = start.elapsed_time(end) / args.steps
+    end2.record(stream)
+    torch.cuda.synchronize()
+    ms_eager = start2.elapsed_time(end2) / args.steps
     phase = np.array([[evs[k][j].elapsed_time(evs[k][j + 1]) for j in range(4)] for k in range(args.steps)])
     gu_ms = float(phase[:, 1].mean())
 
@@ -153,7 +211,7 @@ def main():
     gu_gbs = gu_bytes / (gu_ms * 1e-3) / 1e9
     traffic = None
     if os.path.exists(TRAFFIC_FILE):
-        tf = json.load(open(TRAFFIC_FILE))
+        tf = json.loads([ln for ln in open(TRAFFIC_FILE) if ln.strip().startswith("{")][-1])
         if tf.get("kernel_hash") == kernel_hash() and tf.get("workload") == c["name"]:
             traffic = tf.get("bytes_per_launch")
     res = {
@@ -172,7 +230,9 @@ def main():
         "config": {"workload": f"{c['name']}: H={c['H']} I={c['I']} E={c['E']}+{c['S']} shared K={c['K']} "
                                f"T={T} x={xdt}, per-block q_i 3..8 (hot 20% floored at 5)",
                    "global_batch": T, "layer_copies_rotated": R, "touched_experts": n_touched,
-                   "committed_weight_bytes": int(M.mpb_committed_bytes())},
+                   "committed_weight_bytes": int(M.mpb_committed_bytes()),
+                   "launch": "hip_graph" if args.graph else "eager",
+                   "ms_per_step_eager": round(ms_eager, 5)},
         "hbm_gbs": round(step_gbs, 1),
         "hbm_frac": round(step_gbs / HBM_PEAK_GBS, 4),
         "phase_ms": {"group": round(float(phase[:, 0].mean()), 5), "gate_up": round(gu_ms, 5),

@@ -349,3 +349,36 @@ def test_abi_errors_after_init(layer_cache):
     with pytest.raises(E) as ei:
         D.ffn(to_dev_x(Xb), "f16", idx, w, out, small)
     assert ei.value.code == -5
+
+
+def test_graph_replay_matches_eager(layer_cache):
+    """moe_route + moe_ffn captured in a HIP graph: every replay, with eager
+    work and synchronisation in between, reproduces the eager result bitwise."""
+    L, D = dev_layer(layer_cache, 10)
+    Xb = S.make_tokens(10)
+    X = to_dev_x(Xb)
+    T = Xb.shape[0]
+    idx, w = D.alloc_route(T)
+    out, ws = D.alloc_ffn(T)
+    D.route(X, "f16", idx, w)
+    D.ffn(X, "f16", idx, w, out, ws)
+    torch.cuda.synchronize()
+    eager = out.cpu().numpy().copy()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(s):
+        with torch.cuda.graph(g, stream=s):
+            D.route(X, "f16", idx, w)
+            D.ffn(X, "f16", idx, w, out, ws)
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    for rep in range(4):
+        out.fill_(float("nan"))
+        junk = torch.randn(1 << 16, device="cuda").sum()   # eager work between replays
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        got = out.cpu().numpy()
+        assert np.array_equal(got.view(np.uint32), eager.view(np.uint32)), f"replay {rep} differs"
+        del junk
