@@ -131,9 +131,14 @@ size_t moe_ffn_workspace_bytes(int T);
  *               p < q_i are dereferenced.
  *   luts_dev    device array of 2*(E+S)*6 device pointers: entry i*6 + (b-3) is
  *               block i's canonical [N][2^b] fp16 LUT. Only b == q_i is read.
- *   q_dev       the bound page table (2*(E+S) int32, values 3..8)
+ *   q_dev       the page table bound by mpb_init (MPB_E_ARG for any other);
+ *               values 3..8
  *   out_dev     [T][H] fp32, overwritten
  *   ws_dev      workspace of ws_bytes >= moe_ffn_workspace_bytes(T)
+ * The kernels' on-chip table space is sized at enqueue time for the highest
+ * bitwidth in the host mirror; a graph captured from this call must be
+ * captured again after a block is raised above that bitwidth (its outputs
+ * would otherwise be NaN, never silently wrong).
  * Results are deterministic for T <= 256 (no order-dependent atomics).
  * Errors: MPB_E_UNINIT, MPB_E_ARG, MPB_E_WS, MPB_E_HIP.
  */

@@ -7,6 +7,10 @@
 // Every workgroup builds the whole expert histogram in LDS (integer counts,
 // order-free), takes its own offset from it, then places its entries with a
 // ballot-ordered scan, so the grouping is identical on every run.
+//
+// The same pass lists the work items of the decode FFN kernels: one per
+// 32-token split of every group with tokens, in group order, so that those
+// kernels launch no workgroup without work in front of busy ones.
 #include "mpb_device.h"
 #include "mpb_internal.h"
 
@@ -16,7 +20,7 @@ constexpr int kMaxGroups = 512 + 64;
 
 __global__ __launch_bounds__(256) void k_group(FfnParams p) {
   __shared__ int hist[kMaxGroups];
-  __shared__ int s_off;
+  __shared__ int s_off, s_ioff;
   __shared__ int wtot[4];
   const int e = blockIdx.x, tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int T = p.T, K = p.K, S = p.S, E = p.E, KS = K + S, TK = T * K;
@@ -28,16 +32,29 @@ __global__ __launch_bounds__(256) void k_group(FfnParams p) {
   }
   __syncthreads();
   if (tid == 0) {
-    int off = 0;
-    for (int j = 0; j < e; ++j) off += j < E ? hist[j] : T;
+    int off = 0, ioff = 0;
+    for (int j = 0; j < e; ++j) {
+      const int c = j < E ? hist[j] : T;
+      off += c;
+      ioff += (c + kDecodeTokensPerWG - 1) / kDecodeTokensPerWG;
+    }
     const int mine = e < E ? hist[e] : T;
     s_off = off;
+    s_ioff = ioff;
     p.offsets[e] = off;
     p.counts[e] = mine;
-    if (e == p.NB - 1) p.offsets[p.NB] = off + mine;
+    if (e == p.NB - 1) {
+      p.offsets[p.NB] = off + mine;
+      p.n_items[0] = ioff + (mine + kDecodeTokensPerWG - 1) / kDecodeTokensPerWG;
+    }
   }
   __syncthreads();
   const int off = s_off;
+  {
+    const int mine = e < E ? hist[e] : T;
+    const int ni = (mine + kDecodeTokensPerWG - 1) / kDecodeTokensPerWG;
+    for (int sp = tid; sp < ni; sp += 256) p.items[s_ioff + sp] = (e << 16) | sp;
+  }
   if (e < E) {
     int run = 0;
     for (int b0 = 0; b0 < TK; b0 += 256) {

@@ -1,6 +1,7 @@
 // libmpb host side: argument validation, the host mirror of the weight page
 // table, workspace layout and launch sequencing. Every export validates on the
 // host before enqueuing anything and never lets a C++ exception escape.
+#include <algorithm>
 #include <string>
 #include <vector>
 
@@ -71,6 +72,9 @@ WsLayout ws_layout(int T, int H, int I, int E, int S, int K, bool bf16) {
   L.ptok = off;    off += align256(P * 4);
   L.pw = off;      off += align256(P * 4);
   L.inv = off;     off += align256(P * 4);
+  L.max_items = max_decode_items(T, E, S, K);
+  L.items = off;   off += align256((size_t)L.max_items * 4);
+  L.n_items = off; off += 256;
   L.hhi = off;     off += align256(P * (size_t)I * 2);
   L.hlo = off;     off += align256(P * (size_t)I * 2);
   L.y = off;       off += align256(P * (size_t)H * 4);
@@ -176,7 +180,10 @@ int moe_ffn(const void* X_dev, int x_dtype, int T, const int32_t* topk_idx_dev, 
   if (T > (1 << 20)) return fail(MPB_E_SHAPE, "moe_ffn: T above 2^20");
   if (!X_dev || !topk_idx_dev || !topk_w_dev || !planes_dev || !luts_dev || !q_dev || !out_dev || !ws_dev)
     return fail(MPB_E_ARG, "moe_ffn: null pointer");
+  if (q_dev != g.q_dev) return fail(MPB_E_ARG, "moe_ffn: q_dev is not the bound page table");
   const mpb::WsLayout L = mpb::ws_layout(T, g.H, g.I, g.E, g.S, g.K, x_dtype == MPB_BF16);
+  const long long ntile = std::max(g.I / 64, (g.H + 127) / 128);
+  if ((long long)L.max_items * ntile >= (1ll << 31)) return fail(MPB_E_SHAPE, "moe_ffn: T too large for this layer");
   if (ws_bytes < L.total)
     return fail(MPB_E_WS, "moe_ffn: workspace " + std::to_string(ws_bytes) + " < " + std::to_string(L.total));
   char* ws = (char*)ws_dev;
@@ -190,6 +197,9 @@ int moe_ffn(const void* X_dev, int x_dtype, int T, const int32_t* topk_idx_dev, 
   p.ptok = (int32_t*)(ws + L.ptok);
   p.pw = (float*)(ws + L.pw);
   p.inv = (int32_t*)(ws + L.inv);
+  p.items = (int32_t*)(ws + L.items);
+  p.n_items = (int32_t*)(ws + L.n_items);
+  p.max_items = L.max_items;
   p.hhi = (uint16_t*)(ws + L.hhi);
   p.hlo = (uint16_t*)(ws + L.hlo);
   p.y = (float*)(ws + L.y);
@@ -204,10 +214,15 @@ int moe_ffn(const void* X_dev, int x_dtype, int T, const int32_t* topk_idx_dev, 
   e = mpb::launch_permute(p, s);
   if (e != hipSuccess) return hip_fail(e, "moe_ffn: permute");
   mark(1, s);
-  e = mpb::launch_gate_up(p, s);
+  int qmax_gu = 3, qmax_dn = 3;
+  for (int i = 0; i < g.nb(); i += 2) {
+    qmax_gu = std::max(qmax_gu, g.q[i]);
+    qmax_dn = std::max(qmax_dn, g.q[i + 1]);
+  }
+  e = mpb::launch_gate_up(p, qmax_gu, s);
   if (e != hipSuccess) return hip_fail(e, "moe_ffn: gate_up");
   mark(2, s);
-  e = mpb::launch_down(p, s);
+  e = mpb::launch_down(p, qmax_dn, s);
   if (e != hipSuccess) return hip_fail(e, "moe_ffn: down");
   mark(3, s);
   e = mpb::launch_combine(p, s);

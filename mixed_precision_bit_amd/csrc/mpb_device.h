@@ -46,10 +46,24 @@ __host__ __device__ constexpr uint32_t rotl_c(uint32_t x, int r) {
   return (r & 31) ? (x << (r & 31)) | (x >> (32 - (r & 31))) : x;
 }
 
+// (a & m) | c and (a & m) | (c & ~m) as single instructions (v_and_or_b32,
+// v_bfi_b32); left to itself the compiler splits these chains into and + or3.
+__device__ __forceinline__ uint32_t and_or(uint32_t a, uint32_t m, uint32_t c) {
+  uint32_t d;
+  asm("v_and_or_b32 %0, %1, %2, %3" : "=v"(d) : "v"(a), "s"(m), "v"(c));
+  return d;
+}
+__device__ __forceinline__ uint32_t bfi(uint32_t m, uint32_t a, uint32_t c) {
+  uint32_t d;
+  asm("v_bfi_b32 %0, %1, %2, %3" : "=v"(d) : "s"(m), "v"(a), "v"(c));
+  return d;
+}
+
 // Index assembly. P[p] = plane-p word (p < Q) of one (row, word). On return
 // byte b of O[s] is u = sum_p bit_p(e=4s+b) << p, the Q-bit index with its bit
 // order reversed (plane 0, the code MSB, lands in bit 0). Tables are staged in
-// the same reversed order, so no per-weight reversal is needed.
+// the same reversed order, so no per-weight reversal is needed. Cost per four
+// elements: Q and-or (bit-field-insert for Q = 8) plus one rotate.
 template <int Q>
 __device__ __forceinline__ void assemble(const uint32_t (&P)[Q], uint32_t (&O)[8]) {
 #pragma unroll
@@ -59,14 +73,11 @@ __device__ __forceinline__ void assemble(const uint32_t (&P)[Q], uint32_t (&O)[8
       // the eight masks of one s partition the word: a bit-field-insert chain
       c = P[7];
 #pragma unroll
-      for (int p = 6; p >= 0; --p) {
-        const uint32_t m = rotl_c(0x01010101u, s + p);
-        c = (P[p] & m) | (c & ~m);
-      }
+      for (int p = 6; p >= 0; --p) c = bfi(rotl_c(0x01010101u, s + p), P[p], c);
     } else {
       c = P[0] & rotl_c(0x01010101u, s);
 #pragma unroll
-      for (int p = 1; p < Q; ++p) c |= P[p] & rotl_c(0x01010101u, s + p);
+      for (int p = 1; p < Q; ++p) c = and_or(P[p], rotl_c(0x01010101u, s + p), c);
     }
     O[s] = s ? __builtin_amdgcn_alignbit(c, c, s) : c;
   }
@@ -95,22 +106,32 @@ __device__ __forceinline__ uint32_t lut_slot(int r, int w) {
 // Stage the Q-bit tables of rows row0..row0+31 (canonical [N][2^Q] fp16 at
 // lut, canonical index order) into table slot set w. Called by all 64 lanes of
 // one wave; lane (r, half) copies 16-byte pieces half, half+2, ... of row r.
+// Split in a load phase and a store phase so that a caller can issue other
+// loads between them.
 template <int Q>
-__device__ __forceinline__ void stage_luts(uint16_t* lds, const uint16_t* __restrict__ lut, int row0,
-                                           int lane, int w) {
-  constexpr int NP = (1 << Q) / 8;  // 16-byte pieces per row
+struct LutPieces {
+  static constexpr int NP = (1 << Q) / 8;  // 16-byte pieces per row
+  static constexpr int NI = (NP + 1) / 2;  // pieces per lane
+  uint4 v[NI];
+};
+
+template <int Q>
+__device__ __forceinline__ void load_luts(LutPieces<Q>& L, const uint16_t* __restrict__ lut, int row0, int lane) {
+  const int r = lane & 31, half = lane >> 5;
+  const uint4* src = (const uint4*)(lut + (size_t)(row0 + r) * (1u << Q));
+#pragma unroll
+  for (int i = 0; i < LutPieces<Q>::NI; ++i)
+    if (half + 2 * i < LutPieces<Q>::NP) L.v[i] = src[half + 2 * i];
+}
+
+template <int Q>
+__device__ __forceinline__ void store_luts(uint16_t* lds, const LutPieces<Q>& L, int lane, int w) {
   const int r = lane & 31, half = lane >> 5;
   const uint32_t slot = lut_slot(r, w);
-  const uint4* src = (const uint4*)(lut + (size_t)(row0 + r) * (1u << Q));
-  constexpr int NI = (NP + 1) / 2;
-  uint4 v[NI];
 #pragma unroll
-  for (int i = 0; i < NI; ++i)
-    if (half + 2 * i < NP) v[i] = src[half + 2 * i];
-#pragma unroll
-  for (int i = 0; i < NI; ++i) {
-    if (half + 2 * i < NP) {
-      const uint32_t wd[4] = {v[i].x, v[i].y, v[i].z, v[i].w};
+  for (int i = 0; i < LutPieces<Q>::NI; ++i) {
+    if (half + 2 * i < LutPieces<Q>::NP) {
+      const uint32_t wd[4] = {L.v[i].x, L.v[i].y, L.v[i].z, L.v[i].w};
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
         const uint32_t u = bitrev<Q>(8 * (half + 2 * i) + j);
@@ -118,6 +139,14 @@ __device__ __forceinline__ void stage_luts(uint16_t* lds, const uint16_t* __rest
       }
     }
   }
+}
+
+template <int Q>
+__device__ __forceinline__ void stage_luts(uint16_t* lds, const uint16_t* __restrict__ lut, int row0,
+                                           int lane, int w) {
+  LutPieces<Q> L;
+  load_luts<Q>(L, lut, row0, lane);
+  store_luts<Q>(lds, L, lane, w);
 }
 
 // LDS byte address of the entry named by byte b of an assembled word O.

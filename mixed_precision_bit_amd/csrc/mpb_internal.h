@@ -7,9 +7,9 @@
 
 namespace mpb {
 
-// Token chunks of 32 held per workgroup by the decode FFN kernels.
-constexpr int kDecodeChunks = 2;
-constexpr int kDecodeTokensPerWG = 32 * kDecodeChunks;
+// Tokens of one expert held per workgroup by the decode FFN kernels (the N
+// dimension of one 32x32 MFMA tile).
+constexpr int kDecodeTokensPerWG = 32;
 
 struct FfnParams {
   const uint16_t* xh;         // [T][H] fp16 activations (converted copy for bf16 input)
@@ -25,6 +25,9 @@ struct FfnParams {
   int32_t* ptok;              // [P] token of each grouped entry
   float* pw;                  // [P] routing weight of each entry
   int32_t* inv;               // [T][K+S] entry position of (t, slot)
+  int32_t* items;             // [max_items] decode work items: (group << 16) | token split
+  int32_t* n_items;           // [1] number of valid items
+  int max_items;              // capacity of items (host bound)
   uint16_t* hhi;              // [P][I] fp16 high part of h = SiLU(gate) * up
   uint16_t* hlo;              // [P][I] fp16 remainder h - hi
   float* y;                   // [P][H] per-entry down projection
@@ -32,8 +35,15 @@ struct FfnParams {
 };
 
 struct WsLayout {
-  size_t counts, offsets, ptok, pw, inv, hhi, hlo, y, xh, total;
+  size_t counts, offsets, ptok, pw, inv, items, n_items, hhi, hlo, y, xh, total;
+  int max_items;
 };
+// Upper bound on decode work items (one per 32-token split of a group with
+// tokens): sum_g ceil(cnt_g / 32) <= min(NB, P) + P / 32 for P grouped entries.
+inline int max_decode_items(int T, int E, int S, int K) {
+  const long long P = (long long)T * (K + S), NB = (long long)E + S;
+  return (int)((P < NB ? P : NB) + P / kDecodeTokensPerWG);
+}
 WsLayout ws_layout(int T, int H, int I, int E, int S, int K, bool bf16);
 
 hipError_t launch_pack(const uint32_t* canon, int N, int Kd, uint32_t* const* pages, hipStream_t s);
@@ -43,8 +53,10 @@ hipError_t launch_route(const uint16_t* X, int xdt, const float* W, const float*
                         int E, int K, int32_t* idx, float* w, hipStream_t s);
 hipError_t launch_permute(const FfnParams& p, hipStream_t s);
 hipError_t launch_x_to_f16(const uint16_t* x, uint16_t* y, size_t n, hipStream_t s);
-hipError_t launch_gate_up(const FfnParams& p, hipStream_t s);
-hipError_t launch_down(const FfnParams& p, hipStream_t s);
+// qmax: highest committed bitwidth among the launch's blocks (sizes the LDS
+// table region; a block above it yields NaN)
+hipError_t launch_gate_up(const FfnParams& p, int qmax, hipStream_t s);
+hipError_t launch_down(const FfnParams& p, int qmax, hipStream_t s);
 hipError_t launch_combine(const FfnParams& p, hipStream_t s);
 hipError_t launch_set_q(int32_t* q, int i, int b, hipStream_t s);
 

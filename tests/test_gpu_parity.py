@@ -349,6 +349,13 @@ def test_abi_errors_after_init(layer_cache):
     with pytest.raises(E) as ei:
         D.ffn(to_dev_x(Xb), "f16", idx, w, out, small)
     assert ei.value.code == -5
+    # a page table other than the bound one is refused (the host mirror that
+    # sizes the kernels' table space describes the bound table only)
+    _, ws = D.alloc_ffn(16)
+    other = D.q_dev.clone()
+    with pytest.raises(E) as ei:
+        M().moe_ffn(to_dev_x(Xb), 0, idx, w, D.planes_table, D.luts_table, other, out, ws)
+    assert ei.value.code == -1
 
 
 def test_graph_replay_matches_eager(layer_cache):
