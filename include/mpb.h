@@ -98,6 +98,24 @@ int mpb_pack_block(const uint32_t* canon_dev, int N, int Kd, uint32_t* const* pl
                    void* stream);
 
 /*
+ * Table images (§2.2: a b-bit weight is its b-bit index plus the b-bit lookup
+ * table; §3.3: the fused kernel reads the table at the committed bitwidth).
+ * moe_ffn reads every block's b-bit LUT from an image laid out the way its
+ * kernels hold tables on chip, so that a workgroup loads its part with plain
+ * copies. kind 0: a gate_up block (N = 2I rows: 0..I-1 gate, I..2I-1 up;
+ * N % 128 == 0); kind 1: a down block (N = H rows; N % 64 == 0); N <= 131072;
+ * b in 3..8.
+ * mpb_table_image_bytes returns ceil(N/128) * 256 * 2^b, or MPB_E_ARG (bad
+ * kind), MPB_E_RANGE (b) or MPB_E_SHAPE (N). mpb_pack_table reads the canonical
+ * [N][2^b] fp16 LUT lut_dev and writes the image to image_dev (that many
+ * bytes, device), enqueued on stream; same errors plus MPB_E_ARG for a null
+ * pointer and MPB_E_HIP. The layout inside an image is private to this
+ * library. Neither needs mpb_init.
+ */
+int64_t mpb_table_image_bytes(int kind, int N, int b);
+int mpb_pack_table(int kind, const uint16_t* lut_dev, int N, int b, uint16_t* image_dev, void* stream);
+
+/*
  * Router (§2.1: "the router assigns routing weights to E experts and selects
  * the top K experts for each token"). X_dev: [T][H] activations of x_dtype
  * (MPB_F16 or MPB_BF16); W_router_dev: [E][H] fp32; bias_dev: [E] fp32 added
@@ -130,7 +148,8 @@ size_t moe_ffn_workspace_bytes(int T);
  *               plane page p of block i (written by mpb_pack_block). Only pages
  *               p < q_i are dereferenced.
  *   luts_dev    device array of 2*(E+S)*6 device pointers: entry i*6 + (b-3) is
- *               block i's canonical [N][2^b] fp16 LUT. Only b == q_i is read.
+ *               block i's b-bit table image (mpb_pack_table; kind 0 for even
+ *               i, kind 1 for odd i). Only b == q_i is read.
  *   q_dev       the page table bound by mpb_init (MPB_E_ARG for any other);
  *               values 3..8
  *   out_dev     [T][H] fp32, overwritten

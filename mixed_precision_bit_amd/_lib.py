@@ -49,6 +49,8 @@ def lib() -> ctypes.CDLL:
             "mpb_committed_bytes": (ctypes.c_int64, [_P]),
             "mpb_get_committed_bits": (_I, [_I]),
             "mpb_dequant_block": (_I, [_P, _P, _I, _I, _I, _P, _P]),
+            "mpb_table_image_bytes": (ctypes.c_int64, [_I, _I, _I]),
+            "mpb_pack_table": (_I, [_I, _P, _I, _I, _P, _P]),
             "mpb_set_resident_planes": (_I, [_I, _I]),
             "mpb_last_error": (ctypes.c_char_p, []),
             "mpb_set_kernel_events": (_I, [_P, _I]),
@@ -135,6 +137,14 @@ def mpb_committed_bytes(touched=None) -> int:
 
 def mpb_get_committed_bits(i) -> int:
     return _check("mpb_get_committed_bits", lib().mpb_get_committed_bits(i))
+
+
+def mpb_table_image_bytes(kind, N, b) -> int:
+    return _check("mpb_table_image_bytes", lib().mpb_table_image_bytes(kind, N, b))
+
+
+def mpb_pack_table(kind, lut, N, b, image, stream=None):
+    return _check("mpb_pack_table", lib().mpb_pack_table(kind, _ptr(lut), N, b, _ptr(image), _stream(stream)))
 
 
 def mpb_dequant_block(pages, lut, N, Kd, b, out, stream=None):

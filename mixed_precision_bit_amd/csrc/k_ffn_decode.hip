@@ -49,6 +49,23 @@ __device__ __forceinline__ rsrc_t tile_rsrc(const void* page, size_t tile_off, u
   return __builtin_amdgcn_make_buffer_rsrc((void*)(((uint64_t)hi << 32) | lo), (short)0, n, 0x00020000);
 }
 
+// Copy a tile's table image (256 << Q bytes) into LDS at byte 0 with direct
+// global-to-LDS loads: wave w moves 1 KiB pieces w, w + 4, ... (no registers,
+// no LDS store instructions). The caller waits for vector memory and
+// synchronises the workgroup before the first lookup.
+typedef __attribute__((address_space(3))) void lds_void;
+
+template <int Q>
+__device__ __forceinline__ void load_table_image(const uint16_t* img, int w, int lane) {
+  const char* src = (const char*)img + 16 * lane;
+#pragma unroll
+  for (int c = 0; c < (1 << Q) / 4; c += 4)
+    if (c + w < (1 << Q) / 4)
+      __builtin_amdgcn_global_load_lds(src + 1024 * (c + w), (lds_void*)(uintptr_t)(1024u * (c + w)), 16, 0, 0);
+}
+
+__device__ __forceinline__ void wait_vmem_all() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
 template <int Q>
 __device__ __forceinline__ void load_chunk(uint4 (&P)[Q], const rsrc_t (&rs)[Q], int s, int lane) {
 #pragma unroll
@@ -74,7 +91,7 @@ __device__ __forceinline__ void word_mfma(const uint4 (&P4)[Q], int j, const uin
 #pragma unroll
   for (int m = 0; m < 4; ++m) b[m] = *(const f16x8*)(stage + stage_off(r, bpiece0 + m));
 #pragma unroll
-  for (int m = 0; m < 4; ++m) acc = mfma32(lookup8(lds, O[2 * m], O[2 * m + 1], slot), b[m], acc);
+  for (int m = 0; m < 4; ++m) acc = mfma32(lookup8(O[2 * m], O[2 * m + 1], slot), b[m], acc);
 }
 
 // ---------------------------------------------------------------- gate_up
@@ -146,12 +163,13 @@ __device__ __forceinline__ void gate_up_body(const FfnParams& p, int e, int it, 
 #pragma unroll
   for (int q = 0; q < Q; ++q) rs[q] = tile_rsrc(p.planes[blk * 8 + q], (size_t)(row0 >> 5) * NC * 512, NC * 512);
 
-  LutPieces<Q> lut;
+  // prologue: tables, the first activation window and the first planes in one
+  // memory round trip; the next two steps' planes are issued after the wait
   uint4 PA[Q], PB[Q], PC[Q], xr[4];
-  load_luts<Q>(lut, p.luts[blk * 6 + (Q - 3)], row0, lane);
+  load_table_image<Q>(p.luts[blk * 6 + (Q - 3)] + (size_t)it * (128u << Q), w, lane);
   load_window(xr, sp, 0, H);
   load_chunk<Q>(PA, rs, 0, lane);
-  store_luts<Q>(lds, lut, lane, w);
+  wait_vmem_all();
   zero_dead_rows(stage, sp);
   store_window(stage, xr, sp, 0, H);
   load_chunk<Q>(PB, rs, 1, lane);
@@ -208,11 +226,12 @@ __device__ __forceinline__ void gate_up_body(const FfnParams& p, int e, int it, 
 // Work item of a decode launch: workgroup id = item * ntile + tile, so the
 // consecutive workgroups that the dispatcher spreads over the chip carry the
 // tiles of one item and every workgroup below n_items * ntile has tokens.
-__device__ __forceinline__ bool decode_item(const FfnParams& p, int ntile, int& e, int& tile, int& t0, int& nt) {
+__device__ __forceinline__ bool decode_item(const FfnParams& p, const int32_t* items, int ntile, int& e, int& tile,
+                                            int& t0, int& nt) {
   const int item = blockIdx.x / ntile;
   tile = blockIdx.x - item * ntile;
   if (item >= p.n_items[0]) return false;
-  const int v = p.items[item];
+  const int v = items[item];
   e = v >> 16;
   t0 = (v & 0xffff) * kTok;
   nt = min(p.counts[e] - t0, kTok);
@@ -220,8 +239,8 @@ __device__ __forceinline__ bool decode_item(const FfnParams& p, int ntile, int& 
 }
 
 // A block whose committed bitwidth is outside 3..qmax (the table region of
-// this launch was sized for qmax) produces NaN instead of a silently wrong
-// value.
+// this launch was sized for qmax), or a table region not at LDS byte 0,
+// produces NaN instead of a silently wrong value.
 __device__ __forceinline__ void poison(float* dst, size_t ld, int rows, int cols) {
   for (int i = threadIdx.x; i < rows * cols; i += blockDim.x) dst[(size_t)(i / cols) * ld + i % cols] = __builtin_nanf("");
 }
@@ -229,10 +248,10 @@ __device__ __forceinline__ void poison(float* dst, size_t ld, int rows, int cols
 __global__ __launch_bounds__(256) void k_gate_up_decode(FfnParams p, int qmax) {
   extern __shared__ __attribute__((aligned(256))) uint16_t lds[];
   int e, it, t0, nt;
-  if (!decode_item(p, p.I >> 6, e, it, t0, nt)) return;
+  if (!decode_item(p, p.items, p.I >> 6, e, it, t0, nt)) return;
   const int q = p.q[2 * e];
   const uint32_t lut_bytes = 256u << qmax;
-  switch (q < 3 || q > qmax ? 0 : q) {
+  switch (q < 3 || q > qmax || !tables_at_zero(lds) ? 0 : q) {
     case 3: gate_up_body<3>(p, e, it, t0, nt, lds, lut_bytes); break;
     case 4: gate_up_body<4>(p, e, it, t0, nt, lds, lut_bytes); break;
     case 5: gate_up_body<5>(p, e, it, t0, nt, lds, lut_bytes); break;
@@ -291,12 +310,11 @@ __device__ __forceinline__ void down_body(const FfnParams& p, int e, int it, int
 
   // ha holds the next round-0 window, hb the next round-1 window; each is
   // loaded one step before it is staged
-  LutPieces<Q> lut;
   uint4 PA[Q], PB[Q], PC[Q], ha[4], hb[4];
-  if (active) load_luts<Q>(lut, p.luts[blk * 6 + (Q - 3)], n0, lane);
+  load_table_image<Q>(p.luts[blk * 6 + (Q - 3)] + (size_t)it * (128u << Q), w, lane);
   load_window(ha, sp, win(0, 0), I);
   load_chunk<Q>(PA, rs, 0, lane);
-  if (active) store_luts<Q>(lds, lut, lane, w);
+  wait_vmem_all();
   zero_dead_rows(stage, sp);
   store_window(stage, ha, sp, win(0, 0), I);
   load_window(hb, sp, win(0, 1), I);
@@ -317,7 +335,7 @@ __device__ __forceinline__ void down_body(const FfnParams& p, int e, int it, int
       for (int m = 0; m < 4; ++m) {
         const f16x8 bh = *(const f16x8*)(stage + stage_off(r, 8 * g + 4 * jj + m));
         const f16x8 bl = *(const f16x8*)(stage + stage_off(r, 16 + 8 * g + 4 * jj + m));
-        const f16x8 a = lookup8(lds, O[2 * m], O[2 * m + 1], slot);
+        const f16x8 a = lookup8(O[2 * m], O[2 * m + 1], slot);
         acc = mfma32(a, bh, acc);
         acc = mfma32(a, bl, acc);
       }
@@ -359,10 +377,10 @@ __device__ __forceinline__ void down_body(const FfnParams& p, int e, int it, int
 __global__ __launch_bounds__(256) void k_down_decode(FfnParams p, int qmax) {
   extern __shared__ __attribute__((aligned(256))) uint16_t lds[];
   int e, it, t0, nt;
-  if (!decode_item(p, (p.H + 127) >> 7, e, it, t0, nt)) return;
+  if (!decode_item(p, p.items_dn, (p.H + 127) >> 7, e, it, t0, nt)) return;
   const int q = p.q[2 * e + 1];
   const uint32_t lut_bytes = 256u << qmax;
-  switch (q < 3 || q > qmax ? 0 : q) {
+  switch (q < 3 || q > qmax || !tables_at_zero(lds) ? 0 : q) {
     case 3: down_body<3>(p, e, it, t0, nt, lds, lut_bytes); break;
     case 4: down_body<4>(p, e, it, t0, nt, lds, lut_bytes); break;
     case 5: down_body<5>(p, e, it, t0, nt, lds, lut_bytes); break;

@@ -50,6 +50,36 @@ hipError_t launch_pack(const uint32_t* canon, int N, int Kd, uint32_t* const* pa
   return hipGetLastError();
 }
 
+// Table images. The FFN kernels hold, per workgroup, the b-bit tables of 128
+// rows (four waves of 32) with entry u of row r of wave w at byte
+// u * 256 + lut_slot(r, w), u the bit-reversed index. An image is that LDS
+// content for every workgroup tile, tile after tile (256 << b bytes each), so a
+// workgroup fills its table region with plain 16-byte copies. Wave w of tile t
+// holds rows
+//   kind 0 (gate_up, N = 2I): (w / 2) * N/2 + 64 t + 32 (w % 2) + r
+//   kind 1 (down,    N = H ): 128 t + 32 w + r   (zero past N)
+// One thread per image fp16.
+__global__ __launch_bounds__(256) void k_pack_table(const uint16_t* __restrict__ lut, int kind, int N, int b,
+                                                    uint16_t* __restrict__ img, size_t total) {
+  const size_t i = (size_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= total) return;
+  const int j = (int)(i & 127);                 // fp16 slot inside a 256-byte entry line
+  const size_t tu = i >> 7;
+  const int u = (int)(tu & ((1u << b) - 1));     // bit-reversed index
+  const int t = (int)(tu >> b);                  // tile
+  const int wh = j >> 6, rem = j & 63, r = rem >> 1, wl = rem & 1, w = 2 * wh + wl;
+  const int row = kind == 0 ? wh * (N / 2) + 64 * t + 32 * wl + r : 128 * t + 32 * w + r;
+  const uint32_t c = __builtin_bitreverse32((uint32_t)u) >> (32 - b);
+  img[i] = row < N ? lut[(size_t)row * (1u << b) + c] : (uint16_t)0;
+}
+
+hipError_t launch_pack_table(const uint16_t* lut, int kind, int N, int b, uint16_t* img, hipStream_t s) {
+  const size_t total = (size_t)((N + 127) / 128) * ((size_t)128 << b);
+  hipLaunchKernelGGL(k_pack_table, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, s, lut, kind, N, b, img,
+                     total);
+  return hipGetLastError();
+}
+
 // One wave per 32-row tile: stage the tile's Q-bit tables in LDS, then run the
 // FFN kernels' assemble + lookup over every word and write fp16 weights in
 // canonical element order.
@@ -78,7 +108,7 @@ __device__ void dequant_tile(const CPagePtrs& pages, const uint16_t* __restrict_
       assemble<Q>(P, O);
       uint16_t* dst = out + (size_t)(row0 + r) * Kd + word * 32;
 #pragma unroll
-      for (int m = 0; m < 4; ++m) *(f16x8*)(dst + 8 * m) = lookup8(lds, O[2 * m], O[2 * m + 1], slot);
+      for (int m = 0; m < 4; ++m) *(f16x8*)(dst + 8 * m) = lookup8(O[2 * m], O[2 * m + 1], slot);
     }
   }
 }
@@ -86,14 +116,15 @@ __device__ void dequant_tile(const CPagePtrs& pages, const uint16_t* __restrict_
 __global__ __launch_bounds__(64) void k_dequant(CPagePtrs pages, const uint16_t* __restrict__ lut, int W, int b,
                                                 uint16_t* __restrict__ out) {
   __shared__ __attribute__((aligned(256))) uint16_t lds[32768];
-  switch (b) {
+  switch (tables_at_zero(lds) ? b : 0) {
     case 3: dequant_tile<3>(pages, lut, W, out, lds); break;
     case 4: dequant_tile<4>(pages, lut, W, out, lds); break;
     case 5: dequant_tile<5>(pages, lut, W, out, lds); break;
     case 6: dequant_tile<6>(pages, lut, W, out, lds); break;
     case 7: dequant_tile<7>(pages, lut, W, out, lds); break;
     case 8: dequant_tile<8>(pages, lut, W, out, lds); break;
-    default: break;
+    default:  // table region misplaced: NaN rows
+      for (int i = threadIdx.x; i < 32 * W * 32; i += 64) out[(size_t)blockIdx.x * 32 * W * 32 + i] = 0x7e00;
   }
 }
 

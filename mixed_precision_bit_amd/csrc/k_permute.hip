@@ -9,8 +9,10 @@
 // ballot-ordered scan, so the grouping is identical on every run.
 //
 // The same pass lists the work items of the decode FFN kernels: one per
-// 32-token split of every group with tokens, in group order, so that those
-// kernels launch no workgroup without work in front of busy ones.
+// 32-token split of every group with tokens. Each kernel gets its own list,
+// ordered by that kernel's committed bitwidth of the group, highest first
+// (then by group): workgroup time grows with the bitwidth, and starting the
+// longest ones first keeps the end of the launch short.
 #include "mpb_device.h"
 #include "mpb_internal.h"
 
@@ -20,7 +22,7 @@ constexpr int kMaxGroups = 512 + 64;
 
 __global__ __launch_bounds__(256) void k_group(FfnParams p) {
   __shared__ int hist[kMaxGroups];
-  __shared__ int s_off, s_ioff;
+  __shared__ int red[3][4];
   __shared__ int wtot[4];
   const int e = blockIdx.x, tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int T = p.T, K = p.K, S = p.S, E = p.E, KS = K + S, TK = T * K;
@@ -31,29 +33,44 @@ __global__ __launch_bounds__(256) void k_group(FfnParams p) {
     if (x >= 0 && x < E) atomicAdd(&hist[x], 1);
   }
   __syncthreads();
+  // position of this group's entries (group order) and of its items in both
+  // bitwidth-ordered lists: sums over the other groups, one per thread, reduced
+  const int mine = e < E ? hist[e] : T;
+  const int ni = (mine + kDecodeTokensPerWG - 1) / kDecodeTokensPerWG;
+  const int qg = p.q[2 * e], qd = p.q[2 * e + 1];
+  int a_off = 0, a_gu = 0, a_dn = 0;
+  for (int j = tid; j < p.NB; j += 256) {
+    const int c = j < E ? hist[j] : T;
+    const int n = (c + kDecodeTokensPerWG - 1) / kDecodeTokensPerWG;
+    const int qj = p.q[2 * j], qjd = p.q[2 * j + 1];
+    if (j < e) a_off += c;
+    if (qj > qg || (qj == qg && j < e)) a_gu += n;
+    if (qjd > qd || (qjd == qd && j < e)) a_dn += n;
+  }
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) {
+    a_off += __shfl_xor(a_off, o);
+    a_gu += __shfl_xor(a_gu, o);
+    a_dn += __shfl_xor(a_dn, o);
+  }
+  if (lane == 0) { red[0][w] = a_off; red[1][w] = a_gu; red[2][w] = a_dn; }
+  __syncthreads();
+  const int off = red[0][0] + red[0][1] + red[0][2] + red[0][3];
+  const int igu = red[1][0] + red[1][1] + red[1][2] + red[1][3];
+  const int idn = red[2][0] + red[2][1] + red[2][2] + red[2][3];
   if (tid == 0) {
-    int off = 0, ioff = 0;
-    for (int j = 0; j < e; ++j) {
-      const int c = j < E ? hist[j] : T;
-      off += c;
-      ioff += (c + kDecodeTokensPerWG - 1) / kDecodeTokensPerWG;
-    }
-    const int mine = e < E ? hist[e] : T;
-    s_off = off;
-    s_ioff = ioff;
     p.offsets[e] = off;
     p.counts[e] = mine;
-    if (e == p.NB - 1) {
-      p.offsets[p.NB] = off + mine;
-      p.n_items[0] = ioff + (mine + kDecodeTokensPerWG - 1) / kDecodeTokensPerWG;
-    }
+    if (e == p.NB - 1) p.offsets[p.NB] = off + mine;
   }
-  __syncthreads();
-  const int off = s_off;
-  {
-    const int mine = e < E ? hist[e] : T;
-    const int ni = (mine + kDecodeTokensPerWG - 1) / kDecodeTokensPerWG;
-    for (int sp = tid; sp < ni; sp += 256) p.items[s_ioff + sp] = (e << 16) | sp;
+  if (e == 0 && tid == 0) {
+    int tot = 0;
+    for (int j = 0; j < p.NB; ++j) tot += ((j < E ? hist[j] : T) + kDecodeTokensPerWG - 1) / kDecodeTokensPerWG;
+    p.n_items[0] = tot;
+  }
+  for (int sp = tid; sp < ni; sp += 256) {
+    p.items[igu + sp] = (e << 16) | sp;
+    p.items_dn[idn + sp] = (e << 16) | sp;
   }
   if (e < E) {
     int run = 0;

@@ -74,6 +74,7 @@ WsLayout ws_layout(int T, int H, int I, int E, int S, int K, bool bf16) {
   L.inv = off;     off += align256(P * 4);
   L.max_items = max_decode_items(T, E, S, K);
   L.items = off;   off += align256((size_t)L.max_items * 4);
+  L.items_dn = off; off += align256((size_t)L.max_items * 4);
   L.n_items = off; off += 256;
   L.hhi = off;     off += align256(P * (size_t)I * 2);
   L.hlo = off;     off += align256(P * (size_t)I * 2);
@@ -130,6 +131,25 @@ int mpb_pack_block(const uint32_t* canon_dev, int N, int Kd, uint32_t* const* pl
   return MPB_OK;
 } catch (...) {
   return fail(MPB_E_HIP, "mpb_pack_block: unexpected exception");
+}
+
+int64_t mpb_table_image_bytes(int kind, int N, int b) {
+  if (kind != 0 && kind != 1) return fail(MPB_E_ARG, "mpb_table_image_bytes: kind must be 0 or 1");
+  if (b < 3 || b > 8) return fail(MPB_E_RANGE, "mpb_table_image_bytes: b outside 3..8");
+  if (N <= 0 || N % (kind == 0 ? 128 : 64) || N > 131072)
+    return fail(MPB_E_SHAPE, "mpb_table_image_bytes: N must be a multiple of 128 (gate_up) or 64 (down)");
+  return (int64_t)((N + 127) / 128) * (256 << b);
+}
+
+int mpb_pack_table(int kind, const uint16_t* lut_dev, int N, int b, uint16_t* image_dev, void* stream) try {
+  const int64_t n = mpb_table_image_bytes(kind, N, b);
+  if (n < 0) return (int)n;
+  if (!lut_dev || !image_dev) return fail(MPB_E_ARG, "mpb_pack_table: null pointer");
+  hipError_t e = mpb::launch_pack_table(lut_dev, kind, N, b, image_dev, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "mpb_pack_table");
+  return MPB_OK;
+} catch (...) {
+  return fail(MPB_E_HIP, "mpb_pack_table: unexpected exception");
 }
 
 int mpb_dequant_block(const uint32_t* const* pages_host, const uint16_t* lut_b_dev, int N, int Kd, int b,
@@ -198,6 +218,7 @@ int moe_ffn(const void* X_dev, int x_dtype, int T, const int32_t* topk_idx_dev, 
   p.pw = (float*)(ws + L.pw);
   p.inv = (int32_t*)(ws + L.inv);
   p.items = (int32_t*)(ws + L.items);
+  p.items_dn = (int32_t*)(ws + L.items_dn);
   p.n_items = (int32_t*)(ws + L.n_items);
   p.max_items = L.max_items;
   p.hhi = (uint16_t*)(ws + L.hhi);

@@ -46,38 +46,25 @@ __host__ __device__ constexpr uint32_t rotl_c(uint32_t x, int r) {
   return (r & 31) ? (x << (r & 31)) | (x >> (32 - (r & 31))) : x;
 }
 
-// (a & m) | c and (a & m) | (c & ~m) as single instructions (v_and_or_b32,
-// v_bfi_b32); left to itself the compiler splits these chains into and + or3.
-__device__ __forceinline__ uint32_t and_or(uint32_t a, uint32_t m, uint32_t c) {
-  uint32_t d;
-  asm("v_and_or_b32 %0, %1, %2, %3" : "=v"(d) : "v"(a), "s"(m), "v"(c));
-  return d;
-}
-__device__ __forceinline__ uint32_t bfi(uint32_t m, uint32_t a, uint32_t c) {
-  uint32_t d;
-  asm("v_bfi_b32 %0, %1, %2, %3" : "=v"(d) : "s"(m), "v"(a), "v"(c));
-  return d;
-}
+// (a & m) | (c & ~m): one v_bfi_b32 (the compiler matches this form).
+__device__ __forceinline__ uint32_t bfi(uint32_t m, uint32_t a, uint32_t c) { return (a & m) | (c & ~m); }
 
 // Index assembly. P[p] = plane-p word (p < Q) of one (row, word). On return
 // byte b of O[s] is u = sum_p bit_p(e=4s+b) << p, the Q-bit index with its bit
 // order reversed (plane 0, the code MSB, lands in bit 0). Tables are staged in
 // the same reversed order, so no per-weight reversal is needed. Cost per four
-// elements: Q and-or (bit-field-insert for Q = 8) plus one rotate.
+// elements: one and, Q-1 bit-field inserts and one rotate.
 template <int Q>
 __device__ __forceinline__ void assemble(const uint32_t (&P)[Q], uint32_t (&O)[8]) {
 #pragma unroll
   for (int s = 0; s < 8; ++s) {
-    uint32_t c;
-    if constexpr (Q == 8) {
-      // the eight masks of one s partition the word: a bit-field-insert chain
-      c = P[7];
+    // the masks of one s are disjoint, so each plane merges with a
+    // bit-field insert that leaves the bits gathered so far in place
+    uint32_t c = P[0] & rotl_c(0x01010101u, s);
 #pragma unroll
-      for (int p = 6; p >= 0; --p) c = bfi(rotl_c(0x01010101u, s + p), P[p], c);
-    } else {
-      c = P[0] & rotl_c(0x01010101u, s);
-#pragma unroll
-      for (int p = 1; p < Q; ++p) c = and_or(P[p], rotl_c(0x01010101u, s + p), c);
+    for (int p = 1; p < Q; ++p) {
+      c = (P[p] & rotl_c(0x01010101u, s + p)) | c;
+      asm("" : "+v"(c));  // keeps the chain as one and-or per plane (no and + or3 split)
     }
     O[s] = s ? __builtin_amdgcn_alignbit(c, c, s) : c;
   }
@@ -155,18 +142,26 @@ __device__ __forceinline__ uint32_t lut_addr(uint32_t O, uint32_t slot, int b) {
   return __builtin_amdgcn_perm(O, slot, 0x0c0c0000u | ((4u + (uint32_t)b) << 8));
 }
 
-__device__ __forceinline__ _Float16 lut_read(const uint16_t* lds, uint32_t addr) {
-  return __builtin_bit_cast(_Float16, *(const uint16_t*)((const char*)lds + addr));
+// Table reads address LDS directly by byte offset: the table region must start
+// at LDS byte 0 (the kernels that use it hold no other LDS object in front of
+// it; tables_at_zero checks this). Going through the shared array's generic
+// pointer instead costs one add per lookup.
+typedef const __attribute__((address_space(3))) uint16_t lds_u16;
+
+__device__ __forceinline__ bool tables_at_zero(const void* lds) { return (uint32_t)(uintptr_t)lds == 0u; }
+
+__device__ __forceinline__ _Float16 lut_read(uint32_t addr) {
+  return __builtin_bit_cast(_Float16, *(lds_u16*)(uintptr_t)addr);
 }
 
 // Eight dequantised weights, elements 8m..8m+7 of the word (O0 = O[2m],
 // O1 = O[2m+1]), as an MFMA A-operand.
-__device__ __forceinline__ f16x8 lookup8(const uint16_t* lds, uint32_t O0, uint32_t O1, uint32_t slot) {
+__device__ __forceinline__ f16x8 lookup8(uint32_t O0, uint32_t O1, uint32_t slot) {
   f16x8 a;
 #pragma unroll
-  for (int b = 0; b < 4; ++b) a[b] = lut_read(lds, lut_addr(O0, slot, b));
+  for (int b = 0; b < 4; ++b) a[b] = lut_read(lut_addr(O0, slot, b));
 #pragma unroll
-  for (int b = 0; b < 4; ++b) a[4 + b] = lut_read(lds, lut_addr(O1, slot, b));
+  for (int b = 0; b < 4; ++b) a[4 + b] = lut_read(lut_addr(O1, slot, b));
   return a;
 }
 

@@ -17,7 +17,7 @@ struct FfnParams {
   const int32_t* topk_idx;    // [T][K]
   const float* topk_w;        // [T][K]
   const uint32_t* const* planes;  // [2*NB][8]
-  const uint16_t* const* luts;    // [2*NB][6]
+  const uint16_t* const* luts;    // [2*NB][6] table images (k_pack_table layout)
   const int32_t* q;           // [2*NB]
   // workspace
   int32_t* counts;            // [NB]
@@ -25,7 +25,8 @@ struct FfnParams {
   int32_t* ptok;              // [P] token of each grouped entry
   float* pw;                  // [P] routing weight of each entry
   int32_t* inv;               // [T][K+S] entry position of (t, slot)
-  int32_t* items;             // [max_items] decode work items: (group << 16) | token split
+  int32_t* items;             // [max_items] gate_up work items: (group << 16) | token split
+  int32_t* items_dn;          // [max_items] down work items, same encoding
   int32_t* n_items;           // [1] number of valid items
   int max_items;              // capacity of items (host bound)
   uint16_t* hhi;              // [P][I] fp16 high part of h = SiLU(gate) * up
@@ -35,7 +36,7 @@ struct FfnParams {
 };
 
 struct WsLayout {
-  size_t counts, offsets, ptok, pw, inv, items, n_items, hhi, hlo, y, xh, total;
+  size_t counts, offsets, ptok, pw, inv, items, items_dn, n_items, hhi, hlo, y, xh, total;
   int max_items;
 };
 // Upper bound on decode work items (one per 32-token split of a group with
@@ -47,6 +48,7 @@ inline int max_decode_items(int T, int E, int S, int K) {
 WsLayout ws_layout(int T, int H, int I, int E, int S, int K, bool bf16);
 
 hipError_t launch_pack(const uint32_t* canon, int N, int Kd, uint32_t* const* pages, hipStream_t s);
+hipError_t launch_pack_table(const uint16_t* lut, int kind, int N, int b, uint16_t* img, hipStream_t s);
 hipError_t launch_dequant(const uint32_t* const* pages, const uint16_t* lut, int N, int Kd, int b,
                           uint16_t* out, hipStream_t s);
 hipError_t launch_route(const uint16_t* X, int xdt, const float* W, const float* bias, int T, int H,

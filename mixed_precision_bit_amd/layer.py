@@ -24,7 +24,7 @@ def _dev(a: np.ndarray, device) -> torch.Tensor:
 
 
 class DeviceLayer:
-    """Packed pages, centroid tables and pointer tables of one MoE layer.
+    """Packed pages, table images and pointer tables of one MoE layer.
 
     blocks: {i: (planes [8][N][Kd/32] uint32 canonical, luts list of 6
     [N][2**b] uint16)} for every i in 0..2(E+S)-1.
@@ -49,11 +49,18 @@ class DeviceLayer:
             pg = [torch.empty(nwords, dtype=torch.int32, device=device) for _ in range(8)]
             M.mpb_pack_block(canon, N, Kd, pg)
             del canon
-            lt = [_dev(l, device) for l in luts]
+            kind = i % 2  # 0: gate_up, 1: down
+            imgs = []
+            for b in range(3, 9):
+                lut = _dev(luts[b - 3], device)
+                img = torch.empty(M.mpb_table_image_bytes(kind, N, b) // 2, dtype=torch.int16, device=device)
+                M.mpb_pack_table(kind, lut, N, b, img)
+                imgs.append(img)
+                del lut
             self.pages.append(pg)
-            self.luts.append(lt)
+            self.luts.append(imgs)
             plane_ptrs += [p.data_ptr() for p in pg]
-            lut_ptrs += [t.data_ptr() for t in lt]
+            lut_ptrs += [t.data_ptr() for t in imgs]
         self.planes_table = torch.tensor(plane_ptrs, dtype=torch.int64, device=device)
         self.luts_table = torch.tensor(lut_ptrs, dtype=torch.int64, device=device)
         if q_dev is None:

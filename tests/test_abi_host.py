@@ -28,7 +28,8 @@ def L():
 def test_header_declares_the_calls():
     names = declared_functions()
     for n in ("moe_route", "moe_ffn", "set_committed_bits", "mpb_init", "mpb_pack_block",
-              "mpb_committed_bytes", "mpb_dequant_block", "mpb_last_error"):
+              "mpb_committed_bytes", "mpb_dequant_block", "mpb_last_error", "mpb_table_image_bytes",
+              "mpb_pack_table"):
         assert n in names
 
 
@@ -57,3 +58,11 @@ def test_host_validation_without_device(L):
     assert L.mpb_pack_block(one, 48, 128, (ctypes.c_void_p * 8)(*[1] * 8), None) == -2
     assert L.mpb_dequant_block((ctypes.c_void_p * 8)(*[1] * 8), one, 64, 128, 9, one, None) == -3
     assert L.mpb_plane_page_bytes(64, 128) == 64 * 128 // 8
+    # table images: ceil(N/128) tiles of 256 * 2^b bytes
+    assert M.mpb_table_image_bytes(0, 2816, 5) == 22 * 256 * 32
+    assert M.mpb_table_image_bytes(1, 2048, 8) == 16 * 256 * 256
+    assert M.mpb_table_image_bytes(1, 192, 3) == 2 * 256 * 8     # last tile half full
+    assert L.mpb_table_image_bytes(0, 192, 3) == -2               # gate_up needs N % 128
+    assert L.mpb_table_image_bytes(2, 256, 3) == -1               # kind
+    assert L.mpb_table_image_bytes(1, 256, 9) == -3               # b
+    assert L.mpb_pack_table(1, None, 256, 4, one, None) == -1
