@@ -116,20 +116,24 @@ int64_t mpb_table_image_bytes(int kind, int N, int b);
 int mpb_pack_table(int kind, const uint16_t* lut_dev, int N, int b, uint16_t* image_dev, void* stream);
 
 /*
- * Router (§2.1: "the router assigns routing weights to E experts and selects
- * the top K experts for each token"). X_dev: [T][H] activations of x_dtype
- * (MPB_F16 or MPB_BF16); W_router_dev: [E][H] fp32; bias_dev: [E] fp32 added
- * to the logits, or NULL. Logits are accumulated in fp64 (every product of an
- * activation and a router weight is exact in fp64). Writes topk_idx_dev [T][K]
- * int32 (descending logit, ties to the lower expert index) and topk_w_dev
- * [T][K] fp32 = softmax over all E experts restricted to the K winners and
- * renormalised (equal to a softmax over the K winning logits). Needs
- * 1 <= K <= min(E, 16), E <= 512, H a multiple of 64 up to 4096; T == 0 is a
- * no-op.
+ * Router (§2.1: a learned gate scores all E experts per token; the K best are
+ * run and weighted). X_dev: [T][H] activations of x_dtype (MPB_F16 or
+ * MPB_BF16); W_router_dev: [E][H] fp32; bias_dev: [E] fp32 added to the
+ * logits, or NULL. Logits are accumulated in fp64 (every product of an
+ * activation and a router weight is exact in fp64) in a fixed order. Writes
+ * topk_idx_dev [T][K] int32 (descending logit, ties to the lower expert index)
+ * and topk_w_dev [T][K] fp32 = softmax over all E experts restricted to the K
+ * winners and renormalised (equal to a softmax over the K winning logits).
+ * ws_dev: device workspace of ws_bytes >= moe_route_workspace_bytes(T, E)
+ * (the [T][E] fp64 logits; contents not preserved). Needs
+ * 1 <= K <= min(E, 16), E <= 512, H a multiple of 64 up to 65536, T <= 2^20;
+ * T == 0 is a no-op. Errors: MPB_E_ARG, MPB_E_SHAPE, MPB_E_WS, MPB_E_HIP.
  * Does not need mpb_init.
  */
+size_t moe_route_workspace_bytes(int T, int E);
 int moe_route(const void* X_dev, int x_dtype, const float* W_router_dev, const float* bias_dev,
-              int T, int H, int E, int K, int32_t* topk_idx_dev, float* topk_w_dev, void* stream);
+              int T, int H, int E, int K, int32_t* topk_idx_dev, float* topk_w_dev, void* ws_dev,
+              size_t ws_bytes, void* stream);
 
 /* Workspace bytes moe_ffn needs for T tokens of the bound layer (0 if unbound). */
 size_t moe_ffn_workspace_bytes(int T);

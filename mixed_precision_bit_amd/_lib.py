@@ -28,6 +28,7 @@ class LayerDesc(ctypes.Structure):
 _lib = None
 _P = ctypes.c_void_p
 _I = ctypes.c_int
+_SZ = ctypes.c_size_t
 
 
 def lib() -> ctypes.CDLL:
@@ -42,7 +43,8 @@ def lib() -> ctypes.CDLL:
             "mpb_init": (_I, [ctypes.POINTER(LayerDesc), _P, _P, _P]),
             "mpb_plane_page_bytes": (ctypes.c_size_t, [_I, _I]),
             "mpb_pack_block": (_I, [_P, _I, _I, _P, _P]),
-            "moe_route": (_I, [_P, _I, _P, _P, _I, _I, _I, _I, _P, _P, _P]),
+            "moe_route": (_I, [_P, _I, _P, _P, _I, _I, _I, _I, _P, _P, _P, _SZ, _P]),
+            "moe_route_workspace_bytes": (_SZ, [_I, _I]),
             "moe_ffn_workspace_bytes": (ctypes.c_size_t, [_I]),
             "moe_ffn": (_I, [_P, _I, _I, _P, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P]),
             "set_committed_bits": (_I, [_I, _I]),
@@ -104,11 +106,16 @@ def mpb_pack_block(canon: torch.Tensor, N, Kd, pages, stream=None):
     return _check("mpb_pack_block", lib().mpb_pack_block(_ptr(canon), N, Kd, arr, _stream(stream)))
 
 
-def moe_route(X, x_dtype, W_router, bias, K, topk_idx, topk_w, stream=None):
+def moe_route_workspace_bytes(T, E) -> int:
+    return lib().moe_route_workspace_bytes(T, E)
+
+
+def moe_route(X, x_dtype, W_router, bias, K, topk_idx, topk_w, ws, stream=None):
     T, H = X.shape
     E = W_router.shape[0]
+    nbytes = ws.numel() * ws.element_size()
     return _check("moe_route", lib().moe_route(_ptr(X), x_dtype, _ptr(W_router), _ptr(bias), T, H, E, K,
-                                               _ptr(topk_idx), _ptr(topk_w), _stream(stream)))
+                                               _ptr(topk_idx), _ptr(topk_w), _ptr(ws), nbytes, _stream(stream)))
 
 
 def moe_ffn_workspace_bytes(T) -> int:

@@ -1,28 +1,30 @@
-// Router: logits, top-K and routing weights.
+// Router: logits, top-K and routing weights (two launches).
 //
 // "PagedWeight", §2.1: the router assigns routing weights to the E experts and
 // selects the top K for each token. Logits are accumulated in fp64: an fp16 or
 // bf16 activation times an fp32 router weight is exact in fp64, and every
 // logit is summed in one fixed order (per-lane partials over a fixed set of
-// hidden indices, then a butterfly reduction whose pairwise adds are
-// commutative), so two identical router rows give bit-identical logits and the
-// lower expert index wins the tie. The routing weights are the softmax over
-// all experts restricted to the K winners and renormalised, which equals a
-// softmax over the K winning logits.
+// hidden indices, then the 64 lane partials in lane order), so two identical
+// router rows give bit-identical logits and the lower expert index wins the
+// tie. The routing weights are the softmax over all experts restricted to the
+// K winners and renormalised, which equals a softmax over the K winning logits.
 //
-// Mapping: one workgroup (8 waves) per token. Wave w scores experts w, w+8,
-// ..., EB at a time so that the router-row loads of EB experts are in flight
-// together; lane l owns hidden indices 4l + 256i + {0..3}, holds the token's
-// activations for them (exact in fp32, widened to fp64 per product) and reads
-// the matching float4 pieces of each router row (one coalesced 1 KiB access
-// per wave per piece).
+// k_route_logits: one wave per (8-token tile, EW-expert group). Lane l owns
+// hidden indices 4l + 256i + {0..3}; per piece i it reads one float4 of each
+// of the group's router rows and one ushort4 of each of the tile's tokens
+// (coalesced 1 KiB / 512 B accesses per wave) and keeps 8 x EW fp64 partial
+// sums. The partials are transposed through LDS and each (token, expert) sum
+// is finished by one lane. Logits go to the workspace ([T][E] fp64).
+//
+// k_route_topk: one wave per token. Expert e is selected at position
+// rank(e) = #{experts that beat it} when rank(e) < K.
 #include "mpb_device.h"
 #include "mpb_internal.h"
 
 namespace mpb {
 
-constexpr int kEMax = 512;   // experts supported by the LDS logit row
-constexpr int kRouteWaves = 8;
+constexpr int kTT = 8;        // tokens per logits wave
+constexpr int kEMaxTopk = 512;
 
 template <int XDT>
 __device__ __forceinline__ float x_to_f32(uint16_t v) {
@@ -30,113 +32,137 @@ __device__ __forceinline__ float x_to_f32(uint16_t v) {
   else return __builtin_bit_cast(float, (uint32_t)v << 16);
 }
 
-__device__ __forceinline__ bool better(double v, int i, double bv, int bi) {
-  return v > bv || (v == bv && i < bi);
-}
-
-template <int XDT, int NPC, int EB>
-__global__ __launch_bounds__(64 * kRouteWaves) void k_route(const uint16_t* __restrict__ X,
-                                                            const float* __restrict__ W,
-                                                            const float* __restrict__ bias, int T, int H,
-                                                            int E, int K, int32_t* __restrict__ idx_out,
-                                                            float* __restrict__ w_out) {
-  __shared__ double lg[kEMax];
-  const int t = blockIdx.x, tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-  const uint16_t* xr = X + (size_t)t * H;
-  float4 x[NPC];
+template <int XDT, int EW, int NPC>
+__global__ __launch_bounds__(256) void k_route_logits(const uint16_t* __restrict__ X, const float* __restrict__ W,
+                                                      const float* __restrict__ bias, int T, int H, int E,
+                                                      double* __restrict__ logits) {
+  __shared__ double part[4][kTT * EW][65];  // +1 column: the summing lanes read rows without bank conflicts
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int ntt = (T + kTT - 1) / kTT, neg = (E + EW - 1) / EW;
+  const int u = blockIdx.x * 4 + w;
+  const bool live = u < ntt * neg;
+  const int tt = live ? u % ntt : 0, eg = live ? u / ntt : 0;
+  const int t0 = tt * kTT, e0 = eg * EW;
+  double a[kTT][EW];
 #pragma unroll
-  for (int i = 0; i < NPC; ++i) {
-    const int h = 4 * lane + 256 * i;
-    const ushort4 v = h < H ? *(const ushort4*)(xr + h) : make_ushort4(0, 0, 0, 0);
-    x[i] = make_float4(x_to_f32<XDT>(v.x), x_to_f32<XDT>(v.y), x_to_f32<XDT>(v.z), x_to_f32<XDT>(v.w));
-  }
-  for (int e0 = w; e0 < E; e0 += kRouteWaves * EB) {
-    float4 wv[EB][NPC];
+  for (int k = 0; k < kTT; ++k)
 #pragma unroll
-    for (int b = 0; b < EB; ++b) {
-      const int e = e0 + kRouteWaves * b;
-      const float* wr = W + (size_t)(e < E ? e : 0) * H;
+    for (int j = 0; j < EW; ++j) a[k][j] = 0.0;
+  if (live) {
+    // NPC pieces per pass, all loads of a pass in flight together
+    const int npc = (H + 255) / 256;
+    for (int i0 = 0; i0 < npc; i0 += NPC)
 #pragma unroll
-      for (int i = 0; i < NPC; ++i) {
-        const int h = 4 * lane + 256 * i;
-        wv[b][i] = (e < E && h < H) ? *(const float4*)(wr + h) : make_float4(0.f, 0.f, 0.f, 0.f);
+    for (int i = i0; i < i0 + NPC; ++i) {
+      const int h = 4 * lane + 256 * i;
+      const bool hin = h < H;  // also false for pieces past npc
+      const int hc = hin ? h : 0;
+      float4 wv[EW];
+#pragma unroll
+      for (int j = 0; j < EW; ++j) {
+        const int e = e0 + j < E ? e0 + j : E - 1;
+        wv[j] = *(const float4*)(W + (size_t)e * H + hc);
+      }
+      ushort4 xv[kTT];
+#pragma unroll
+      for (int k = 0; k < kTT; ++k) {
+        const int t = t0 + k < T ? t0 + k : T - 1;
+        xv[k] = *(const ushort4*)(X + (size_t)t * H + hc);
+      }
+#pragma unroll
+      for (int k = 0; k < kTT; ++k) {
+        const double x0 = hin ? (double)x_to_f32<XDT>(xv[k].x) : 0.0;
+        const double x1 = hin ? (double)x_to_f32<XDT>(xv[k].y) : 0.0;
+        const double x2 = hin ? (double)x_to_f32<XDT>(xv[k].z) : 0.0;
+        const double x3 = hin ? (double)x_to_f32<XDT>(xv[k].w) : 0.0;
+#pragma unroll
+        for (int j = 0; j < EW; ++j) {
+          a[k][j] = fma(x0, (double)wv[j].x, a[k][j]);
+          a[k][j] = fma(x1, (double)wv[j].y, a[k][j]);
+          a[k][j] = fma(x2, (double)wv[j].z, a[k][j]);
+          a[k][j] = fma(x3, (double)wv[j].w, a[k][j]);
+        }
       }
     }
+  }
 #pragma unroll
-    for (int b = 0; b < EB; ++b) {
-      const int e = e0 + kRouteWaves * b;
-      double a = 0.0;
+  for (int k = 0; k < kTT; ++k)
 #pragma unroll
-      for (int i = 0; i < NPC; ++i) {
-        a = fma((double)x[i].x, (double)wv[b][i].x, a);
-        a = fma((double)x[i].y, (double)wv[b][i].y, a);
-        a = fma((double)x[i].z, (double)wv[b][i].z, a);
-        a = fma((double)x[i].w, (double)wv[b][i].w, a);
+    for (int j = 0; j < EW; ++j) part[w][k * EW + j][lane] = a[k][j];
+  __syncthreads();
+  if (live && lane < kTT * EW) {
+    const int k = lane / EW, j = lane % EW, t = t0 + k, e = e0 + j;
+    double s = 0.0;
+#pragma unroll 16
+    for (int l = 0; l < 64; ++l) s += part[w][lane][l];
+    if (t < T && e < E) logits[(size_t)t * E + e] = s + (bias ? (double)bias[e] : 0.0);
+  }
+}
+
+__global__ __launch_bounds__(256) void k_route_topk(const double* __restrict__ logits, int T, int E, int K,
+                                                    int32_t* __restrict__ idx_out, float* __restrict__ w_out) {
+  __shared__ double lg[4][kEMaxTopk];
+  __shared__ double sel_v[4][16];
+  __shared__ int sel_i[4][16];
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int t = blockIdx.x * 4 + w;
+  const bool live = t < T;
+  if (live)
+    for (int e = lane; e < E; e += 64) lg[w][e] = logits[(size_t)t * E + e];
+  __syncthreads();
+  if (live) {
+    for (int e = lane; e < E; e += 64) {
+      const double v = lg[w][e];
+      int rank = 0;
+#pragma unroll 4
+      for (int j = 0; j < E; ++j) {
+        const double x = lg[w][j];
+        rank += (x > v || (x == v && j < e)) ? 1 : 0;
       }
-#pragma unroll
-      for (int off = 32; off >= 1; off >>= 1) a += __shfl_xor(a, off);
-      if (lane == 0 && e < E) lg[e] = a + (bias ? (double)bias[e] : 0.0);
+      if (rank < K) {
+        sel_v[w][rank] = v;
+        sel_i[w][rank] = e;
+      }
     }
   }
   __syncthreads();
-  if (w != 0) return;
-  // top-K on wave 0; lane holds experts lane + 64i
-  uint32_t taken = 0;
-  double tv[16];
-  int ti[16];
-  for (int k = 0; k < K; ++k) {
-    double bv = -__builtin_inf();
-    int bi = 0x7fffffff;
-    for (int i = 0; i < kEMax / 64; ++i) {
-      const int e = lane + 64 * i;
-      if (e < E && !((taken >> i) & 1u)) {
-        const double v = lg[e];
-        if (better(v, e, bv, bi)) { bv = v; bi = e; }
-      }
-    }
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) {
-      const double ov = __shfl_xor(bv, off);
-      const int oi = __shfl_xor(bi, off);
-      if (better(ov, oi, bv, bi)) { bv = ov; bi = oi; }
-    }
-    if (bi < E && (bi & 63) == lane) taken |= 1u << (bi >> 6);
-#pragma unroll
-    for (int kk = 0; kk < 16; ++kk)
-      if (kk == k) { tv[kk] = bv; ti[kk] = bi; }
-  }
-  if (lane < K) {
+  if (live && lane < K) {
+    // softmax over the K winners, summed in rank order
     double sum = 0.0, mine = 0.0;
-    int myi = 0;
-#pragma unroll
-    for (int kk = 0; kk < 16; ++kk) {
-      if (kk < K) {
-        const double ex = exp(tv[kk] - tv[0]);
-        sum += ex;
-        if (kk == lane) { mine = ex; myi = ti[kk]; }
-      }
+    for (int kk = 0; kk < K; ++kk) {
+      const double ex = exp(sel_v[w][kk] - sel_v[w][0]);
+      sum += ex;
+      if (kk == lane) mine = ex;
     }
-    idx_out[(size_t)t * K + lane] = myi;
+    idx_out[(size_t)t * K + lane] = sel_i[w][lane];
     w_out[(size_t)t * K + lane] = (float)(mine / sum);
   }
 }
 
+size_t route_workspace_bytes(int T, int E) { return ((size_t)T * E * 8 + 255) / 256 * 256; }
+
 template <int XDT>
-static void launch_route_x(const uint16_t* X, const float* W, const float* bias, int T, int H, int E, int K,
-                           int32_t* idx, float* w, hipStream_t s) {
-  const int npc = (H + 255) / 256;
-  const dim3 grid(T), block(64 * kRouteWaves);
-  // EB * NPC float4 pieces of router rows in flight per lane (about 64 VGPRs)
-  if (npc <= 4) hipLaunchKernelGGL((k_route<XDT, 4, 4>), grid, block, 0, s, X, W, bias, T, H, E, K, idx, w);
-  else if (npc <= 8) hipLaunchKernelGGL((k_route<XDT, 8, 2>), grid, block, 0, s, X, W, bias, T, H, E, K, idx, w);
-  else if (npc <= 12) hipLaunchKernelGGL((k_route<XDT, 12, 1>), grid, block, 0, s, X, W, bias, T, H, E, K, idx, w);
-  else hipLaunchKernelGGL((k_route<XDT, 16, 1>), grid, block, 0, s, X, W, bias, T, H, E, K, idx, w);
+static void launch_logits(const uint16_t* X, const float* W, const float* bias, int T, int H, int E, double* lg,
+                          hipStream_t s) {
+  // experts per wave: grow the group (more reuse of each activation load) only
+  // while the launch keeps at least 2048 waves
+  const long long ntt = (T + kTT - 1) / kTT;
+  const int ew = ntt * ((E + 3) / 4) >= 2048 ? 4 : ntt * ((E + 1) / 2) >= 2048 ? 2 : 1;
+  const long long units = ntt * ((E + ew - 1) / ew);
+  const dim3 grid((unsigned)((units + 3) / 4)), block(256);
+  // pieces per pass: all of H when it fits the registers (EW = 1: 8, EW = 2: 4, EW = 4: 2)
+  if (ew == 4) hipLaunchKernelGGL((k_route_logits<XDT, 4, 2>), grid, block, 0, s, X, W, bias, T, H, E, lg);
+  else if (ew == 2) hipLaunchKernelGGL((k_route_logits<XDT, 2, 4>), grid, block, 0, s, X, W, bias, T, H, E, lg);
+  else hipLaunchKernelGGL((k_route_logits<XDT, 1, 8>), grid, block, 0, s, X, W, bias, T, H, E, lg);
 }
 
 hipError_t launch_route(const uint16_t* X, int xdt, const float* W, const float* bias, int T, int H, int E,
-                        int K, int32_t* idx, float* w, hipStream_t s) {
-  if (xdt == 0) launch_route_x<0>(X, W, bias, T, H, E, K, idx, w, s);
-  else launch_route_x<1>(X, W, bias, T, H, E, K, idx, w, s);
+                        int K, int32_t* idx, float* w, double* lg, hipStream_t s) {
+  if (xdt == 0) launch_logits<0>(X, W, bias, T, H, E, lg, s);
+  else launch_logits<1>(X, W, bias, T, H, E, lg, s);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(k_route_topk, dim3((unsigned)((T + 3) / 4)), dim3(256), 0, s, lg, T, E, K, idx, w);
   return hipGetLastError();
 }
 

@@ -167,17 +167,28 @@ int mpb_dequant_block(const uint32_t* const* pages_host, const uint16_t* lut_b_d
   return fail(MPB_E_HIP, "mpb_dequant_block: unexpected exception");
 }
 
+size_t moe_route_workspace_bytes(int T, int E) {
+  if (T < 0 || E < 1 || E > 512) return 0;
+  return mpb::route_workspace_bytes(T, E);
+}
+
 int moe_route(const void* X_dev, int x_dtype, const float* W_router_dev, const float* bias_dev, int T, int H,
-              int E, int K, int32_t* topk_idx_dev, float* topk_w_dev, void* stream) try {
+              int E, int K, int32_t* topk_idx_dev, float* topk_w_dev, void* ws_dev, size_t ws_bytes,
+              void* stream) try {
   if (x_dtype != MPB_F16 && x_dtype != MPB_BF16) return fail(MPB_E_ARG, "moe_route: bad x_dtype");
   if (T < 0) return fail(MPB_E_ARG, "moe_route: T < 0");
-  if (H <= 0 || H % 64 || H > 4096) return fail(MPB_E_SHAPE, "moe_route: H must be a multiple of 64 in 64..4096");
+  if (T > (1 << 20)) return fail(MPB_E_SHAPE, "moe_route: T above 2^20");
+  if (H <= 0 || H % 64 || H > 65536) return fail(MPB_E_SHAPE, "moe_route: H must be a multiple of 64 in 64..65536");
   if (E < 1 || E > 512) return fail(MPB_E_SHAPE, "moe_route: E must be in 1..512");
   if (K < 1 || K > 16 || K > E) return fail(MPB_E_SHAPE, "moe_route: K must be in 1..min(E,16)");
   if (T == 0) return MPB_OK;
-  if (!X_dev || !W_router_dev || !topk_idx_dev || !topk_w_dev) return fail(MPB_E_ARG, "moe_route: null pointer");
+  if (!X_dev || !W_router_dev || !topk_idx_dev || !topk_w_dev || !ws_dev)
+    return fail(MPB_E_ARG, "moe_route: null pointer");
+  const size_t need = mpb::route_workspace_bytes(T, E);
+  if (ws_bytes < need)
+    return fail(MPB_E_WS, "moe_route: workspace " + std::to_string(ws_bytes) + " < " + std::to_string(need));
   hipError_t e = mpb::launch_route((const uint16_t*)X_dev, x_dtype, W_router_dev, bias_dev, T, H, E, K,
-                                   topk_idx_dev, topk_w_dev, (hipStream_t)stream);
+                                   topk_idx_dev, topk_w_dev, (double*)ws_dev, (hipStream_t)stream);
   if (e != hipSuccess) return hip_fail(e, "moe_route");
   return MPB_OK;
 } catch (...) {

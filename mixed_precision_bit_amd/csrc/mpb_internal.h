@@ -51,8 +51,9 @@ hipError_t launch_pack(const uint32_t* canon, int N, int Kd, uint32_t* const* pa
 hipError_t launch_pack_table(const uint16_t* lut, int kind, int N, int b, uint16_t* img, hipStream_t s);
 hipError_t launch_dequant(const uint32_t* const* pages, const uint16_t* lut, int N, int Kd, int b,
                           uint16_t* out, hipStream_t s);
+size_t route_workspace_bytes(int T, int E);
 hipError_t launch_route(const uint16_t* X, int xdt, const float* W, const float* bias, int T, int H,
-                        int E, int K, int32_t* idx, float* w, hipStream_t s);
+                        int E, int K, int32_t* idx, float* w, double* logits, hipStream_t s);
 hipError_t launch_permute(const FfnParams& p, hipStream_t s);
 hipError_t launch_x_to_f16(const uint16_t* x, uint16_t* y, size_t n, hipStream_t s);
 // qmax: highest committed bitwidth among the launch's blocks (sizes the LDS

@@ -68,6 +68,7 @@ class DeviceLayer:
             if bind:
                 M.mpb_init(H, I, E, S, K, q_dev, np.asarray(q, np.int32))
         self.q_dev = q_dev
+        self.route_ws = None  # router logits scratch, sized by alloc_route
         torch.cuda.synchronize()
 
     @classmethod
@@ -81,8 +82,12 @@ class DeviceLayer:
 
     # ---------------------------------------------------------------- calls
     def alloc_route(self, T):
+        """Router outputs for T tokens; also sizes the router workspace for T."""
         idx = torch.empty((T, self.K), dtype=torch.int32, device=self.device)
         w = torch.empty((T, self.K), dtype=torch.float32, device=self.device)
+        need = max(1, M.moe_route_workspace_bytes(T, self.E))
+        if self.route_ws is None or self.route_ws.numel() < need:
+            self.route_ws = torch.empty(need, dtype=torch.uint8, device=self.device)
         return idx, w
 
     def alloc_ffn(self, T):
@@ -91,7 +96,7 @@ class DeviceLayer:
         return out, ws
 
     def route(self, X, xdtype, idx, w, stream=None):
-        M.moe_route(X, XDTYPE[xdtype], self.W_r, self.bias, self.K, idx, w, stream)
+        M.moe_route(X, XDTYPE[xdtype], self.W_r, self.bias, self.K, idx, w, self.route_ws, stream)
 
     def ffn(self, X, xdtype, idx, w, out, ws, stream=None):
         M.moe_ffn(X, XDTYPE[xdtype], idx, w, self.planes_table, self.luts_table, self.q_dev, out, ws, stream)

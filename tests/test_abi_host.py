@@ -27,7 +27,7 @@ def L():
 
 def test_header_declares_the_calls():
     names = declared_functions()
-    for n in ("moe_route", "moe_ffn", "set_committed_bits", "mpb_init", "mpb_pack_block",
+    for n in ("moe_route", "moe_route_workspace_bytes", "moe_ffn", "set_committed_bits", "mpb_init", "mpb_pack_block",
               "mpb_committed_bytes", "mpb_dequant_block", "mpb_last_error", "mpb_table_image_bytes",
               "mpb_pack_table"):
         assert n in names
@@ -51,10 +51,13 @@ def test_host_validation_without_device(L):
     assert L.mpb_init(ctypes.byref(d), ctypes.c_void_p(1), ctypes.c_void_p(1), None) == -2
     assert L.mpb_init(None, None, None, None) == -1
     one = ctypes.c_void_p(1)
-    assert L.moe_route(one, 2, one, None, 4, 256, 8, 2, one, one, None) == -1      # dtype
-    assert L.moe_route(one, 0, one, None, 4, 250, 8, 2, one, one, None) == -2      # H % 64
-    assert L.moe_route(one, 0, one, None, 4, 256, 8, 17, one, one, None) == -2     # K
-    assert L.moe_route(one, 0, one, None, 0, 256, 8, 2, one, one, None) == 0       # T = 0
+    assert L.moe_route(one, 2, one, None, 4, 256, 8, 2, one, one, one, 1 << 20, None) == -1   # dtype
+    assert L.moe_route(one, 0, one, None, 4, 250, 8, 2, one, one, one, 1 << 20, None) == -2   # H % 64
+    assert L.moe_route(one, 0, one, None, 4, 256, 8, 17, one, one, one, 1 << 20, None) == -2  # K
+    assert L.moe_route(one, 0, one, None, 0, 256, 8, 2, one, one, one, 0, None) == 0          # T = 0
+    assert L.moe_route_workspace_bytes(4, 8) == 256                                            # [4][8] fp64
+    assert L.moe_route(one, 0, one, None, 4, 256, 8, 2, one, one, one, 255, None) == -5       # workspace
+    assert L.moe_route(one, 0, one, None, 4, 256, 8, 2, one, one, None, 1 << 20, None) == -1  # null ws
     assert L.mpb_pack_block(one, 48, 128, (ctypes.c_void_p * 8)(*[1] * 8), None) == -2
     assert L.mpb_dequant_block((ctypes.c_void_p * 8)(*[1] * 8), one, 64, 128, 9, one, None) == -3
     assert L.mpb_plane_page_bytes(64, 128) == 64 * 128 // 8

@@ -96,6 +96,10 @@ def test_pack_round_trip_integer_table():
 
 
 # ---------------------------------------------------------------- routing
+def route_ws(T, E):
+    return torch.empty(max(1, M().moe_route_workspace_bytes(T, E)), dtype=torch.uint8, device="cuda")
+
+
 @pytest.mark.parametrize("cfg", [0, 1, 2, 3, 4, 10, 11])
 def test_route_bit_exact(cfg):
     c = S.layer_config(cfg)
@@ -108,7 +112,8 @@ def test_route_bit_exact(cfg):
     T = Xb.shape[0]
     idx = torch.empty((T, L.K), dtype=torch.int32, device="cuda")
     w = torch.empty((T, L.K), dtype=torch.float32, device="cuda")
-    M().moe_route(to_dev_x(Xb), 0 if c["xdtype"] == "f16" else 1, W, bias, L.K, idx, w)
+    ws = route_ws(T, L.E)
+    M().moe_route(to_dev_x(Xb), 0 if c["xdtype"] == "f16" else 1, W, bias, L.K, idx, w, ws)
     torch.cuda.synchronize()
     gi = idx.cpu().numpy()
     assert np.array_equal(gi, z), f"{np.count_nonzero((gi != z).any(1))} tokens differ"
@@ -128,7 +133,7 @@ def test_route_ties_lowest_index():
         z, r, _ = O.route(X, Wt, None, K)
         idx = torch.empty((T, K), dtype=torch.int32, device="cuda")
         w = torch.empty((T, K), dtype=torch.float32, device="cuda")
-        M().moe_route(to_dev_x(Xb), 0, torch.from_numpy(Wt).cuda(), None, K, idx, w)
+        M().moe_route(to_dev_x(Xb), 0, torch.from_numpy(Wt).cuda(), None, K, idx, w, route_ws(T, E))
         torch.cuda.synchronize()
         assert np.array_equal(idx.cpu().numpy(), z)
         assert_close(w.cpu().numpy(), r, "tie topk_w")
