@@ -237,7 +237,7 @@ def main():
         "hbm_frac": round(step_gbs / HBM_PEAK_GBS, 4),
         "phase_ms": {"group": round(float(phase[:, 0].mean()), 5), "gate_up": round(gu_ms, 5),
                      "down": round(float(phase[:, 2].mean()), 5), "combine": round(float(phase[:, 3].mean()), 5)},
-        "roofline": {"kernel": "k_gate_up_decode", "bound": "hbm", "achieved": round(gu_gbs, 1),
+        "roofline": {"kernel": "k_gate_up", "bound": "hbm", "achieved": round(gu_gbs, 1),
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(gu_gbs / HBM_PEAK_GBS, 4),
                      "traffic": traffic, "algorithmic_bytes_per_launch": int(gu_bytes)},
     }

@@ -31,14 +31,18 @@
 
 namespace mpb {
 
-constexpr int kTok = kDecodeTokensPerWG;  // 32
+constexpr int kTok = kChunkTokens;  // 32 tokens per MFMA column block
 constexpr int kWaves = 8;
 constexpr int kThreads = 64 * kWaves;
-constexpr int kStageBytes = 2 * kTok * 256;
 
+// Stage: [K half][token of the item (32 TC)][16 pieces of 16 bytes]; piece p
+// of token t sits at p ^ (t % 16).
+template <int TC>
 __device__ __forceinline__ uint32_t stage_off(int kh, int t, int piece) {
-  return (uint32_t)kh * (kTok * 256u) + t * 256u + ((piece ^ (t & 15)) << 4);
+  return (uint32_t)kh * (TC * kTok * 256u) + t * 256u + ((piece ^ (t & 15)) << 4);
 }
+template <int TC>
+constexpr int stage_bytes() { return 2 * TC * kTok * 256; }
 
 // Plane loads go through buffer descriptors, one per plane page, based at the
 // wave's 32-row tile and spanning its NC chunks; an offset past the tile
@@ -88,39 +92,47 @@ __device__ __forceinline__ void word_of(const uint2 (&P2)[Q], int j, uint32_t (&
   for (int q = 0; q < Q; ++q) P[q] = j == 0 ? P2[q].x : P2[q].y;
 }
 
-// Activation pieces staged per thread and step (or round): pc = tid + 512 i
-// is piece p = tid % 16 of token t = tid / 16 of K half i.
+// Activation pieces staged per thread and step (or round): thread tid stages
+// piece p = tid % 16 of token 32 c + tid / 16 of both K halves, c < TC.
+template <int TC>
 struct StagePlan {
-  const uint16_t* row[2];  // source row start (token slots >= nt load nothing)
-  uint32_t dst[2];         // stage byte offsets
-  bool live;               // token slot < nt
+  const uint16_t* row[TC];  // source row start (token slots >= nt load nothing)
+  uint32_t dst[2][TC];      // stage byte offsets per K half
+  bool live[TC];            // token slot < nt
 };
 
-__device__ __forceinline__ void load_window(uint4 (&v)[2], const StagePlan& sp, const int (&k)[2], int len) {
+template <int TC>
+__device__ __forceinline__ void load_window(uint4 (&v)[2][TC], const StagePlan<TC>& sp, const int (&k)[2], int len) {
 #pragma unroll
   for (int i = 0; i < 2; ++i)
-    if (sp.live && k[i] < len) v[i] = *(const uint4*)(sp.row[i] + k[i]);
+#pragma unroll
+    for (int c = 0; c < TC; ++c)
+      if (sp.live[c] && k[i] < len) v[i][c] = *(const uint4*)(sp.row[c] + k[i]);
 }
 
-__device__ __forceinline__ void store_window(char* stage, const uint4 (&v)[2], const StagePlan& sp, const int (&k)[2],
-                                             int len) {
+template <int TC>
+__device__ __forceinline__ void store_window(char* stage, const uint4 (&v)[2][TC], const StagePlan<TC>& sp,
+                                             const int (&k)[2], int len) {
 #pragma unroll
   for (int i = 0; i < 2; ++i)
-    if (sp.live) *(uint4*)(stage + sp.dst[i]) = k[i] < len ? v[i] : make_uint4(0u, 0u, 0u, 0u);
+#pragma unroll
+    for (int c = 0; c < TC; ++c)
+      if (sp.live[c]) *(uint4*)(stage + sp.dst[i][c]) = k[i] < len ? v[i][c] : make_uint4(0u, 0u, 0u, 0u);
 }
 
-// Work item of a decode launch: workgroup id = item * ntile + tile, so the
+// Work item of a launch: workgroup id = item * ntile + tile, so the
 // consecutive workgroups that the dispatcher spreads over the chip carry the
 // tiles of one item and every workgroup below n_items * ntile has tokens.
-__device__ __forceinline__ bool decode_item(const FfnParams& p, const int32_t* items, int ntile, int& e, int& tile,
-                                            int& t0, int& nt) {
+__device__ __forceinline__ bool decode_item(const FfnParams& p, bool gu, int ntile, int& e, int& tile, int& t0,
+                                            int& nt) {
   const int item = blockIdx.x / ntile;
   tile = blockIdx.x - item * ntile;
-  if (item >= p.n_items[0]) return false;
-  const int v = items[item];
+  if (item >= p.n_items[gu ? 0 : 1]) return false;
+  const int v = (gu ? p.items : p.items_dn)[item];
+  const int tpi = gu ? p.tpi : p.tpi_dn;
   e = v >> 16;
-  t0 = (v & 0xffff) * kTok;
-  nt = min(p.counts[e] - t0, kTok);
+  t0 = (v & 0xffff) * tpi;
+  nt = min(p.counts[e] - t0, tpi);
   return true;
 }
 
@@ -133,17 +145,19 @@ struct KSplit {
 
 // ---------------------------------------------------------------- gate_up
 // Waves 0/1 take gate rows c0..c0+31 / c0+32..c0+63, waves 2/3 the matching up
-// rows, waves 4..7 the same rows over the second K half. After the K loop the
-// other waves hand their accumulators to waves 0/1 through LDS, which add the
-// halves, apply SiLU(gate) * up and store h as an fp16 (hi, lo) pair (hi + lo
-// carries ~22 significant bits of the fp32 value into the down projection).
+// rows, waves 4..7 the same rows over the second K half. Each dequantised
+// A operand feeds TC MFMAs, one per 32-token chunk of the item. After the K
+// loop the other waves hand their accumulators to waves 0/1 through LDS, which
+// add the halves, apply SiLU(gate) * up and store h as an fp16 (hi, lo) pair
+// (hi + lo carries ~22 significant bits of the fp32 value into the down
+// projection).
 //
 // Issue order per step s (vector memory completes in issue order, so a wait
 // for one load also waits for every older one): compute on the planes of step
 // s, barrier, write the activations of step s+1 (loaded one step earlier) to
 // the stage, load the activations of step s+2, load the planes of step s+3,
 // barrier.
-template <int Q>
+template <int Q, int TC>
 __device__ __forceinline__ void gate_up_body(const FfnParams& p, int e, int it, int t0, int nt, uint16_t* lds,
                                              uint32_t lut_bytes) {
   const int tid = threadIdx.x, lane = tid & 63, r = lane & 31, g = lane >> 5;
@@ -158,41 +172,50 @@ __device__ __forceinline__ void gate_up_body(const FfnParams& p, int e, int it, 
   const int blk = 2 * e;
   char* stage = (char*)lds + lut_bytes;
 
-  // staging: thread tid stages piece p = tid % 16 of token tid / 16 for both halves;
-  // piece p = 8 g' + 4 j + m holds elements 32 j + 8 m .. + 7 of half-chunk 2 s + g'
-  StagePlan sp;
+  // staging: piece p = 8 g' + 4 j + m of a token holds elements 32 j + 8 m .. + 7
+  // of half-chunk 2 s + g' of the K half
+  StagePlan<TC> sp;
   const int st = tid >> 4, spc = tid & 15;
-  sp.live = st < nt;
-  sp.row[0] = sp.row[1] = p.xh + (size_t)p.ptok[base + (sp.live ? st : 0)] * H;
-  sp.dst[0] = stage_off(0, st, spc);
-  sp.dst[1] = stage_off(1, st, spc);
+#pragma unroll
+  for (int c = 0; c < TC; ++c) {
+    const int t = kTok * c + st;
+    sp.live[c] = t < nt;
+    sp.row[c] = p.xh + (size_t)p.ptok[base + (sp.live[c] ? t : 0)] * H;
+    sp.dst[0][c] = stage_off<TC>(0, t, spc);
+    sp.dst[1][c] = stage_off<TC>(1, t, spc);
+  }
   auto kwin = [&](int s, int (&k)[2]) {
 #pragma unroll
     for (int i = 0; i < 2; ++i) k[i] = (i * ks.HH + 2 * s + (spc >> 3)) * 64 + 8 * (spc & 7);
   };
 
+  // the descriptor of K half 0 ends where half 1 begins, so the prefetches
+  // past the half read zeros instead of half 1's pages
+  const int cb = kh * (ks.HH >> 1);  // first chunk of the wave's K half
+  const int ce = kh ? NC : ks.HH >> 1;
   rsrc_t rs[Q];
 #pragma unroll
-  for (int q = 0; q < Q; ++q) rs[q] = tile_rsrc(p.planes[blk * 8 + q], (size_t)(row0 >> 5) * NC * 512, NC * 512);
-  const int cb = kh * (ks.HH >> 1);  // first chunk of the wave's K half
+  for (int q = 0; q < Q; ++q) rs[q] = tile_rsrc(p.planes[blk * 8 + q], (size_t)(row0 >> 5) * NC * 512, ce * 512);
   const int voff = 16 * r + 8 * g;
 
   uint2 PA[Q], PB[Q], PC[Q];
-  uint4 xr[2];
+  uint4 xr[2][TC];
   int kk[2];
   load_table_image<Q>(p.luts[blk * 6 + (Q - 3)] + (size_t)it * (128u << Q), w, lane);
   kwin(0, kk);
-  load_window(xr, sp, kk, H);
+  load_window<TC>(xr, sp, kk, H);
   load_planes<Q>(PA, rs, cb, 0, voff);
   wait_vmem_all();
-  store_window(stage, xr, sp, kk, H);
+  store_window<TC>(stage, xr, sp, kk, H);
   load_planes<Q>(PB, rs, cb, 1, voff);
   kwin(1, kk);
-  load_window(xr, sp, kk, H);
+  load_window<TC>(xr, sp, kk, H);
   load_planes<Q>(PC, rs, cb, 2, voff);
   __syncthreads();
 
-  f32x16 acc = (f32x16){};
+  f32x16 acc[TC];
+#pragma unroll
+  for (int c = 0; c < TC; ++c) acc[c] = (f32x16){};
   auto step = [&](int s, uint2 (&P)[Q]) {
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
@@ -201,17 +224,21 @@ __device__ __forceinline__ void gate_up_body(const FfnParams& p, int e, int it, 
       assemble<Q>(Pw, O);
 #pragma unroll
       for (int m = 0; m < 4; ++m) {
-        const f16x8 b = *(const f16x8*)(stage + stage_off(kh, r, 8 * g + 4 * j + m));
-        acc = mfma32(lookup8(O[2 * m], O[2 * m + 1], slot), b, acc);
+        const f16x8 a = lookup8(O[2 * m], O[2 * m + 1], slot);
+#pragma unroll
+        for (int c = 0; c < TC; ++c) {
+          const f16x8 b = *(const f16x8*)(stage + stage_off<TC>(kh, kTok * c + r, 8 * g + 4 * j + m));
+          acc[c] = mfma32(a, b, acc[c]);
+        }
       }
     }
     __syncthreads();
     if (s + 1 < ks.NSW) {
       kwin(s + 1, kk);
-      store_window(stage, xr, sp, kk, H);
+      store_window<TC>(stage, xr, sp, kk, H);
     }
     kwin(s + 2, kk);
-    load_window(xr, sp, kk, H);
+    load_window<TC>(xr, sp, kk, H);
     load_planes<Q>(P, rs, cb, s + 3, voff);
     __syncthreads();
   };
@@ -226,31 +253,38 @@ __device__ __forceinline__ void gate_up_body(const FfnParams& p, int e, int it, 
   if (s < ks.NSW) step(s, PA);
   if (s + 1 < ks.NSW) step(s + 1, PB);
 
-  // hand the accumulators to waves 0/1; layout [wave][v][lane]
+  // hand the accumulators to waves 0/1, one token chunk at a time; layout
+  // [wave][v][lane]; gate = own + wave w+4, up = waves w+2 and w+6, each sum in
+  // that order
   float* xb = (float*)lds;
-  if (w >= 2) {
 #pragma unroll
-    for (int v = 0; v < 16; ++v) xb[(w * 16 + v) * 64 + lane] = acc[v];
-  }
-  __syncthreads();
-  if (w >= 2 || r >= nt) return;
-  // acc[v] is row 8*(v/4) + 4*g + v%4 of the wave's 32 rows, token slot r;
-  // gate = own + wave w+4, up = waves w+2 and w+6, each sum in that order
-  const size_t o = (size_t)(base + r) * I + c0 + 4 * g;
+  for (int c = 0; c < TC; ++c) {
+    if (c) __syncthreads();  // waves 0/1 are done reading the previous chunk
+    if (w >= 2) {
 #pragma unroll
-  for (int v4 = 0; v4 < 4; ++v4) {
-    uint16_t hv[4], lv[4];
-#pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      const int v = 4 * v4 + k;
-      const float gate = acc[v] + xb[((w + 4) * 16 + v) * 64 + lane];
-      const float up = xb[((w + 2) * 16 + v) * 64 + lane] + xb[((w + 6) * 16 + v) * 64 + lane];
-      const split16 sp2 = split_hi_lo(silu(gate) * up);
-      hv[k] = __builtin_bit_cast(uint16_t, sp2.hi);
-      lv[k] = __builtin_bit_cast(uint16_t, sp2.lo);
+      for (int v = 0; v < 16; ++v) xb[(w * 16 + v) * 64 + lane] = acc[c][v];
     }
-    *(ushort4*)(p.hhi + o + 8 * v4) = make_ushort4(hv[0], hv[1], hv[2], hv[3]);
-    *(ushort4*)(p.hlo + o + 8 * v4) = make_ushort4(lv[0], lv[1], lv[2], lv[3]);
+    __syncthreads();
+    const int t = kTok * c + r;
+    if (w < 2 && t < nt) {
+      // acc[c][v] is row 8*(v/4) + 4*g + v%4 of the wave's 32 rows, token t
+      const size_t o = (size_t)(base + t) * I + c0 + 4 * g;
+#pragma unroll
+      for (int v4 = 0; v4 < 4; ++v4) {
+        uint16_t hv[4], lv[4];
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          const int v = 4 * v4 + k;
+          const float gate = acc[c][v] + xb[((w + 4) * 16 + v) * 64 + lane];
+          const float up = xb[((w + 2) * 16 + v) * 64 + lane] + xb[((w + 6) * 16 + v) * 64 + lane];
+          const split16 sp2 = split_hi_lo(silu(gate) * up);
+          hv[k] = __builtin_bit_cast(uint16_t, sp2.hi);
+          lv[k] = __builtin_bit_cast(uint16_t, sp2.lo);
+        }
+        *(ushort4*)(p.hhi + o + 8 * v4) = make_ushort4(hv[0], hv[1], hv[2], hv[3]);
+        *(ushort4*)(p.hlo + o + 8 * v4) = make_ushort4(lv[0], lv[1], lv[2], lv[3]);
+      }
+    }
   }
 }
 
@@ -261,19 +295,20 @@ __device__ __forceinline__ void poison(float* dst, size_t ld, int rows, int cols
   for (int i = threadIdx.x; i < rows * cols; i += blockDim.x) dst[(size_t)(i / cols) * ld + i % cols] = __builtin_nanf("");
 }
 
-__global__ __launch_bounds__(kThreads) void k_gate_up_decode(FfnParams p, int qmax) {
+template <int TC>
+__global__ __launch_bounds__(kThreads) void k_gate_up(FfnParams p, int qmax) {
   extern __shared__ __attribute__((aligned(256))) uint16_t lds[];
   int e, it, t0, nt;
-  if (!decode_item(p, p.items, p.I >> 6, e, it, t0, nt)) return;
+  if (!decode_item(p, true, p.I >> 6, e, it, t0, nt)) return;
   const int q = p.q[2 * e];
   const uint32_t lut_bytes = 256u << qmax;
   switch (q < 3 || q > qmax || !tables_at_zero(lds) ? 0 : q) {
-    case 3: gate_up_body<3>(p, e, it, t0, nt, lds, lut_bytes); break;
-    case 4: gate_up_body<4>(p, e, it, t0, nt, lds, lut_bytes); break;
-    case 5: gate_up_body<5>(p, e, it, t0, nt, lds, lut_bytes); break;
-    case 6: gate_up_body<6>(p, e, it, t0, nt, lds, lut_bytes); break;
-    case 7: gate_up_body<7>(p, e, it, t0, nt, lds, lut_bytes); break;
-    case 8: gate_up_body<8>(p, e, it, t0, nt, lds, lut_bytes); break;
+    case 3: gate_up_body<3, TC>(p, e, it, t0, nt, lds, lut_bytes); break;
+    case 4: gate_up_body<4, TC>(p, e, it, t0, nt, lds, lut_bytes); break;
+    case 5: gate_up_body<5, TC>(p, e, it, t0, nt, lds, lut_bytes); break;
+    case 6: gate_up_body<6, TC>(p, e, it, t0, nt, lds, lut_bytes); break;
+    case 7: gate_up_body<7, TC>(p, e, it, t0, nt, lds, lut_bytes); break;
+    case 8: gate_up_body<8, TC>(p, e, it, t0, nt, lds, lut_bytes); break;
     default: {
       const size_t o = (size_t)(p.offsets[e] + t0) * p.I + it * 64;
       for (int i = threadIdx.x; i < nt * 64; i += blockDim.x) {
@@ -286,13 +321,13 @@ __global__ __launch_bounds__(kThreads) void k_gate_up_decode(FfnParams p, int qm
 
 // ---------------------------------------------------------------- down
 // Waves w and w+4 take output rows n0 + 32 (w % 4) .. +31 over the two K
-// halves. B operand = h as its fp16 hi and lo parts, two MFMAs per word into
-// the same fp32 accumulator. A step is staged in two rounds, one per word of
-// the half-chunk; piece p = 8 hl + 4 g' + m of a token holds elements 32 j +
-// 8 m .. + 7 of half-chunk 2 s + g', hi (hl = 0) or lo (hl = 1), for round j.
-// Each window is loaded one step before it is staged, ahead of the plane load
-// that follows it.
-template <int Q>
+// halves. B operand = h as its fp16 hi and lo parts, two MFMAs per word and
+// token chunk into the same fp32 accumulator. A step is staged in two rounds,
+// one per word of the half-chunk; piece p = 8 hl + 4 g' + m of a token holds
+// elements 32 j + 8 m .. + 7 of half-chunk 2 s + g', hi (hl = 0) or lo
+// (hl = 1), for round j. Each window is loaded one step before it is staged,
+// ahead of the plane load that follows it.
+template <int Q, int TC>
 __device__ __forceinline__ void down_body(const FfnParams& p, int e, int it, int t0, int nt, uint16_t* lds,
                                           uint32_t lut_bytes) {
   const int tid = threadIdx.x, lane = tid & 63, r = lane & 31, g = lane >> 5;
@@ -307,71 +342,81 @@ __device__ __forceinline__ void down_body(const FfnParams& p, int e, int it, int
   const int blk = 2 * e + 1;
   char* stage = (char*)lds + lut_bytes;
 
-  StagePlan sp;
+  StagePlan<TC> sp;
   const int st = tid >> 4, spc = tid & 15, hl = spc >> 3;
-  sp.live = st < nt;
-  sp.row[0] = sp.row[1] = (hl ? p.hlo : p.hhi) + (size_t)(base + (sp.live ? st : 0)) * I;
-  sp.dst[0] = stage_off(0, st, spc);
-  sp.dst[1] = stage_off(1, st, spc);
+#pragma unroll
+  for (int c = 0; c < TC; ++c) {
+    const int t = kTok * c + st;
+    sp.live[c] = t < nt;
+    sp.row[c] = (hl ? p.hlo : p.hhi) + (size_t)(base + (sp.live[c] ? t : 0)) * I;
+    sp.dst[0][c] = stage_off<TC>(0, t, spc);
+    sp.dst[1][c] = stage_off<TC>(1, t, spc);
+  }
   // window (s, j): for K half i, element 64 (i HH + 2 s + g') + 32 j + 8 m
   auto kwin = [&](int s, int j, int (&k)[2]) {
 #pragma unroll
     for (int i = 0; i < 2; ++i) k[i] = (i * ks.HH + 2 * s + ((spc >> 2) & 1)) * 64 + 32 * j + 8 * (spc & 3);
   };
 
+  const int cb = kh * (ks.HH >> 1);
+  const int ce = kh ? NC : ks.HH >> 1;
   rsrc_t rs[Q];
 #pragma unroll
   for (int q = 0; q < Q; ++q)
-    rs[q] = tile_rsrc(p.planes[blk * 8 + q], active ? (size_t)(n0 >> 5) * NC * 512 : 0, active ? NC * 512 : 0);
-  const int cb = kh * (ks.HH >> 1);
+    rs[q] = tile_rsrc(p.planes[blk * 8 + q], active ? (size_t)(n0 >> 5) * NC * 512 : 0, active ? ce * 512 : 0);
   const int voff = 16 * r + 8 * g;
 
   uint2 PA[Q], PB[Q], PC[Q];
-  uint4 ha[2], hb[2];
+  uint4 ha[2][TC], hb[2][TC];
   int ka[2], kb[2];
   load_table_image<Q>(p.luts[blk * 6 + (Q - 3)] + (size_t)it * (128u << Q), w, lane);
   kwin(0, 0, ka);
-  load_window(ha, sp, ka, I);
+  load_window<TC>(ha, sp, ka, I);
   load_planes<Q>(PA, rs, cb, 0, voff);
   wait_vmem_all();
-  store_window(stage, ha, sp, ka, I);
+  store_window<TC>(stage, ha, sp, ka, I);
   kwin(0, 1, kb);
-  load_window(hb, sp, kb, I);
+  load_window<TC>(hb, sp, kb, I);
   kwin(1, 0, ka);
-  load_window(ha, sp, ka, I);
+  load_window<TC>(ha, sp, ka, I);
   load_planes<Q>(PB, rs, cb, 1, voff);
   load_planes<Q>(PC, rs, cb, 2, voff);
   __syncthreads();
 
-  f32x16 acc = (f32x16){};
+  f32x16 acc[TC];
+#pragma unroll
+  for (int c = 0; c < TC; ++c) acc[c] = (f32x16){};
   auto round = [&](int j, const uint2 (&P)[Q]) {
     uint32_t Pw[Q], O[8];
     word_of<Q>(P, j, Pw);
     assemble<Q>(Pw, O);
 #pragma unroll
     for (int m = 0; m < 4; ++m) {
-      const f16x8 bh = *(const f16x8*)(stage + stage_off(kh, r, 4 * g + m));
-      const f16x8 bl = *(const f16x8*)(stage + stage_off(kh, r, 8 + 4 * g + m));
       const f16x8 a = lookup8(O[2 * m], O[2 * m + 1], slot);
-      acc = mfma32(a, bh, acc);
-      acc = mfma32(a, bl, acc);
+#pragma unroll
+      for (int c = 0; c < TC; ++c) {
+        const f16x8 bh = *(const f16x8*)(stage + stage_off<TC>(kh, kTok * c + r, 4 * g + m));
+        const f16x8 bl = *(const f16x8*)(stage + stage_off<TC>(kh, kTok * c + r, 8 + 4 * g + m));
+        acc[c] = mfma32(a, bh, acc[c]);
+        acc[c] = mfma32(a, bl, acc[c]);
+      }
     }
     __syncthreads();
   };
   auto step = [&](int s, uint2 (&P)[Q]) {
     round(0, P);
     kwin(s, 1, kb);
-    store_window(stage, hb, sp, kb, I);
+    store_window<TC>(stage, hb, sp, kb, I);
     kwin(s + 1, 1, kb);
-    load_window(hb, sp, kb, I);
+    load_window<TC>(hb, sp, kb, I);
     __syncthreads();
     round(1, P);
     if (s + 1 < ks.NSW) {
       kwin(s + 1, 0, ka);
-      store_window(stage, ha, sp, ka, I);
+      store_window<TC>(stage, ha, sp, ka, I);
     }
     kwin(s + 2, 0, ka);
-    load_window(ha, sp, ka, I);
+    load_window<TC>(ha, sp, ka, I);
     load_planes<Q>(P, rs, cb, s + 3, voff);
     __syncthreads();
   };
@@ -384,37 +429,45 @@ __device__ __forceinline__ void down_body(const FfnParams& p, int e, int it, int
   if (s < ks.NSW) step(s, PA);
   if (s + 1 < ks.NSW) step(s + 1, PB);
 
-  // second K half -> first through LDS, layout [row group][v][lane]
+  // second K half -> first through LDS, one token chunk at a time; layout
+  // [row group][v][lane]
   float* xb = (float*)lds;
-  if (kh == 1) {
 #pragma unroll
-    for (int v = 0; v < 16; ++v) xb[(rg * 16 + v) * 64 + lane] = acc[v];
-  }
-  __syncthreads();
-  if (kh == 1 || !active || r >= nt) return;
-  float* yrow = p.y + (size_t)(base + r) * H + n0 + 4 * g;
+  for (int c = 0; c < TC; ++c) {
+    if (c) __syncthreads();
+    if (kh == 1) {
 #pragma unroll
-  for (int v4 = 0; v4 < 4; ++v4) {
-    f32x4 o;
+      for (int v = 0; v < 16; ++v) xb[(rg * 16 + v) * 64 + lane] = acc[c][v];
+    }
+    __syncthreads();
+    const int t = kTok * c + r;
+    if (kh == 0 && active && t < nt) {
+      float* yrow = p.y + (size_t)(base + t) * H + n0 + 4 * g;
 #pragma unroll
-    for (int k = 0; k < 4; ++k) o[k] = acc[4 * v4 + k] + xb[(rg * 16 + 4 * v4 + k) * 64 + lane];
-    *(f32x4*)(yrow + 8 * v4) = o;
+      for (int v4 = 0; v4 < 4; ++v4) {
+        f32x4 o;
+#pragma unroll
+        for (int k = 0; k < 4; ++k) o[k] = acc[c][4 * v4 + k] + xb[(rg * 16 + 4 * v4 + k) * 64 + lane];
+        *(f32x4*)(yrow + 8 * v4) = o;
+      }
+    }
   }
 }
 
-__global__ __launch_bounds__(kThreads) void k_down_decode(FfnParams p, int qmax) {
+template <int TC>
+__global__ __launch_bounds__(kThreads) void k_down(FfnParams p, int qmax) {
   extern __shared__ __attribute__((aligned(256))) uint16_t lds[];
   int e, it, t0, nt;
-  if (!decode_item(p, p.items_dn, (p.H + 127) >> 7, e, it, t0, nt)) return;
+  if (!decode_item(p, false, (p.H + 127) >> 7, e, it, t0, nt)) return;
   const int q = p.q[2 * e + 1];
   const uint32_t lut_bytes = 256u << qmax;
   switch (q < 3 || q > qmax || !tables_at_zero(lds) ? 0 : q) {
-    case 3: down_body<3>(p, e, it, t0, nt, lds, lut_bytes); break;
-    case 4: down_body<4>(p, e, it, t0, nt, lds, lut_bytes); break;
-    case 5: down_body<5>(p, e, it, t0, nt, lds, lut_bytes); break;
-    case 6: down_body<6>(p, e, it, t0, nt, lds, lut_bytes); break;
-    case 7: down_body<7>(p, e, it, t0, nt, lds, lut_bytes); break;
-    case 8: down_body<8>(p, e, it, t0, nt, lds, lut_bytes); break;
+    case 3: down_body<3, TC>(p, e, it, t0, nt, lds, lut_bytes); break;
+    case 4: down_body<4, TC>(p, e, it, t0, nt, lds, lut_bytes); break;
+    case 5: down_body<5, TC>(p, e, it, t0, nt, lds, lut_bytes); break;
+    case 6: down_body<6, TC>(p, e, it, t0, nt, lds, lut_bytes); break;
+    case 7: down_body<7, TC>(p, e, it, t0, nt, lds, lut_bytes); break;
+    case 8: down_body<8, TC>(p, e, it, t0, nt, lds, lut_bytes); break;
     default: {
       const int n0 = it * 128;
       poison(p.y + (size_t)(p.offsets[e] + t0) * p.H + n0, p.H, nt, min(128, p.H - n0));
@@ -458,34 +511,41 @@ hipError_t launch_x_to_f16(const uint16_t* x, uint16_t* y, size_t n, hipStream_t
   return hipGetLastError();
 }
 
-static bool lds_attr_set = false;
-
-static hipError_t set_lds_attr() {
-  if (lds_attr_set) return hipSuccess;
-  const int maxb = (256 << 8) + kStageBytes;
-  hipError_t e = hipFuncSetAttribute((const void*)k_gate_up_decode, hipFuncAttributeMaxDynamicSharedMemorySize, maxb);
-  if (e != hipSuccess) return e;
-  e = hipFuncSetAttribute((const void*)k_down_decode, hipFuncAttributeMaxDynamicSharedMemorySize, maxb);
-  if (e == hipSuccess) lds_attr_set = true;
-  return e;
+// LDS per launch: the table region for the highest committed bitwidth plus the
+// stage, and at least the epilogue's exchange area (8 waves x 16 x 64 floats).
+template <int TC>
+static size_t ffn_lds_bytes(int qmax) {
+  return std::max<size_t>((256u << qmax) + stage_bytes<TC>(), kWaves * 16 * 64 * 4);
 }
 
-hipError_t launch_gate_up(const FfnParams& p, int qmax, hipStream_t s) {
-  hipError_t e = set_lds_attr();
-  if (e != hipSuccess) return e;
-  // at least the epilogue's exchange area: 8 waves x 16 x 64 floats
-  const size_t shmem = std::max<size_t>((256u << qmax) + kStageBytes, kWaves * 16 * 64 * 4);
-  hipLaunchKernelGGL(k_gate_up_decode, dim3(p.max_items * (p.I >> 6)), dim3(kThreads), shmem, s, p, qmax);
+template <int TC, bool GU>
+static hipError_t launch_tc(const FfnParams& p, int qmax, hipStream_t s) {
+  static bool attr_set = false;  // raise the dynamic LDS limit once per kernel
+  const void* fn;
+  if constexpr (GU) fn = (const void*)k_gate_up<TC>;
+  else fn = (const void*)k_down<TC>;
+  if (!attr_set) {
+    hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)ffn_lds_bytes<TC>(8));
+    if (e != hipSuccess) return e;
+    attr_set = true;
+  }
+  const size_t shmem = ffn_lds_bytes<TC>(qmax);
+  if constexpr (GU)
+    hipLaunchKernelGGL(k_gate_up<TC>, dim3(p.max_items * (p.I >> 6)), dim3(kThreads), shmem, s, p, qmax);
+  else
+    hipLaunchKernelGGL(k_down<TC>, dim3(p.max_items * ((p.H + 127) >> 7)), dim3(kThreads), shmem, s, p, qmax);
   return hipGetLastError();
 }
 
-hipError_t launch_down(const FfnParams& p, int qmax, hipStream_t s) {
-  hipError_t e = set_lds_attr();
-  if (e != hipSuccess) return e;
-  const size_t shmem = (256u << qmax) + kStageBytes;
-  hipLaunchKernelGGL(k_down_decode, dim3(p.max_items * ((p.H + 127) >> 7)), dim3(kThreads), shmem, s, p, qmax);
-  return hipGetLastError();
+hipError_t launch_gate_up(const FfnParams& p, int qmax, int tc, hipStream_t s) {
+  switch (tc) {
+    case 1: return launch_tc<1, true>(p, qmax, s);
+    case 4: return launch_tc<4, true>(p, qmax, s);
+    default: return hipErrorInvalidValue;
+  }
 }
+
+hipError_t launch_down(const FfnParams& p, int qmax, hipStream_t s) { return launch_tc<1, false>(p, qmax, s); }
 
 hipError_t launch_combine(const FfnParams& p, hipStream_t s) {
   const size_t n = (size_t)p.T * (p.H >> 2);

@@ -8,8 +8,8 @@
 // order-free), takes its own offset from it, then places its entries with a
 // ballot-ordered scan, so the grouping is identical on every run.
 //
-// The same pass lists the work items of the decode FFN kernels: one per
-// 32-token split of every group with tokens. Each kernel gets its own list,
+// The same pass lists the work items of the FFN kernels: one per tpi-token
+// (gate_up) or tpi_dn-token (down) split of every group with tokens. Each kernel gets its own list,
 // ordered by that kernel's committed bitwidth of the group, highest first
 // (then by group): workgroup time grows with the bitwidth, and starting the
 // longest ones first keeps the end of the launch short.
@@ -36,16 +36,16 @@ __global__ __launch_bounds__(256) void k_group(FfnParams p) {
   // position of this group's entries (group order) and of its items in both
   // bitwidth-ordered lists: sums over the other groups, one per thread, reduced
   const int mine = e < E ? hist[e] : T;
-  const int ni = (mine + kDecodeTokensPerWG - 1) / kDecodeTokensPerWG;
+  const int ni = (mine + p.tpi - 1) / p.tpi, ni_dn = (mine + p.tpi_dn - 1) / p.tpi_dn;
   const int qg = p.q[2 * e], qd = p.q[2 * e + 1];
   int a_off = 0, a_gu = 0, a_dn = 0;
   for (int j = tid; j < p.NB; j += 256) {
     const int c = j < E ? hist[j] : T;
-    const int n = (c + kDecodeTokensPerWG - 1) / kDecodeTokensPerWG;
+    const int n = (c + p.tpi - 1) / p.tpi, n_dn = (c + p.tpi_dn - 1) / p.tpi_dn;
     const int qj = p.q[2 * j], qjd = p.q[2 * j + 1];
     if (j < e) a_off += c;
     if (qj > qg || (qj == qg && j < e)) a_gu += n;
-    if (qjd > qd || (qjd == qd && j < e)) a_dn += n;
+    if (qjd > qd || (qjd == qd && j < e)) a_dn += n_dn;
   }
 #pragma unroll
   for (int o = 32; o >= 1; o >>= 1) {
@@ -64,14 +64,17 @@ __global__ __launch_bounds__(256) void k_group(FfnParams p) {
     if (e == p.NB - 1) p.offsets[p.NB] = off + mine;
   }
   if (e == 0 && tid == 0) {
-    int tot = 0;
-    for (int j = 0; j < p.NB; ++j) tot += ((j < E ? hist[j] : T) + kDecodeTokensPerWG - 1) / kDecodeTokensPerWG;
+    int tot = 0, tot_dn = 0;
+    for (int j = 0; j < p.NB; ++j) {
+      const int c = j < E ? hist[j] : T;
+      tot += (c + p.tpi - 1) / p.tpi;
+      tot_dn += (c + p.tpi_dn - 1) / p.tpi_dn;
+    }
     p.n_items[0] = tot;
+    p.n_items[1] = tot_dn;
   }
-  for (int sp = tid; sp < ni; sp += 256) {
-    p.items[igu + sp] = (e << 16) | sp;
-    p.items_dn[idn + sp] = (e << 16) | sp;
-  }
+  for (int sp = tid; sp < ni; sp += 256) p.items[igu + sp] = (e << 16) | sp;
+  for (int sp = tid; sp < ni_dn; sp += 256) p.items_dn[idn + sp] = (e << 16) | sp;
   if (e < E) {
     int run = 0;
     for (int b0 = 0; b0 < TK; b0 += 256) {

@@ -75,7 +75,7 @@ WsLayout ws_layout(int T, int H, int I, int E, int S, int K, bool bf16) {
   L.max_items = max_decode_items(T, E, S, K);
   L.items = off;   off += align256((size_t)L.max_items * 4);
   L.items_dn = off; off += align256((size_t)L.max_items * 4);
-  L.n_items = off; off += 256;
+  L.n_items = off; off += 256;  // [2]
   L.hhi = off;     off += align256(P * (size_t)I * 2);
   L.hlo = off;     off += align256(P * (size_t)I * 2);
   L.y = off;       off += align256(P * (size_t)H * 4);
@@ -232,6 +232,9 @@ int moe_ffn(const void* X_dev, int x_dtype, int T, const int32_t* topk_idx_dev, 
   p.items_dn = (int32_t*)(ws + L.items_dn);
   p.n_items = (int32_t*)(ws + L.n_items);
   p.max_items = L.max_items;
+  const int tc = mpb::ffn_token_chunks(T, g.E, g.K);
+  p.tpi = mpb::kChunkTokens * tc;
+  p.tpi_dn = mpb::kChunkTokens;
   p.hhi = (uint16_t*)(ws + L.hhi);
   p.hlo = (uint16_t*)(ws + L.hlo);
   p.y = (float*)(ws + L.y);
@@ -251,7 +254,7 @@ int moe_ffn(const void* X_dev, int x_dtype, int T, const int32_t* topk_idx_dev, 
     qmax_gu = std::max(qmax_gu, g.q[i]);
     qmax_dn = std::max(qmax_dn, g.q[i + 1]);
   }
-  e = mpb::launch_gate_up(p, qmax_gu, s);
+  e = mpb::launch_gate_up(p, qmax_gu, tc, s);
   if (e != hipSuccess) return hip_fail(e, "moe_ffn: gate_up");
   mark(2, s);
   e = mpb::launch_down(p, qmax_dn, s);

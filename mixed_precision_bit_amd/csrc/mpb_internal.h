@@ -7,9 +7,20 @@
 
 namespace mpb {
 
-// Tokens of one expert held per workgroup by the decode FFN kernels (the N
-// dimension of one 32x32 MFMA tile).
-constexpr int kDecodeTokensPerWG = 32;
+// Tokens per MFMA tile column block: a work item of the FFN kernels holds
+// TC chunks of kChunkTokens tokens of one group.
+constexpr int kChunkTokens = 32;
+
+// Token chunks per work item of the gate_up kernel: one dequantised weight
+// operand feeds TC MFMAs, so large groups (prefill) take four chunks and
+// decode-size groups one. The down kernel always takes one (with its two
+// MFMAs per word, h hi and lo, more chunks cost more in registers and LDS
+// reads than the shared dequantisation saves). Decided from the shapes only
+// (the workspace layout depends on it).
+inline int ffn_token_chunks(int T, int E, int K) {
+  const long long avg = (long long)T * K / E;  // tokens per routed group on average
+  return avg >= 96 ? 4 : 1;
+}
 
 struct FfnParams {
   const uint16_t* xh;         // [T][H] fp16 activations (converted copy for bf16 input)
@@ -27,8 +38,10 @@ struct FfnParams {
   int32_t* inv;               // [T][K+S] entry position of (t, slot)
   int32_t* items;             // [max_items] gate_up work items: (group << 16) | token split
   int32_t* items_dn;          // [max_items] down work items, same encoding
-  int32_t* n_items;           // [1] number of valid items
+  int32_t* n_items;           // [2] number of valid items: gate_up, down
   int max_items;              // capacity of items (host bound)
+  int tpi;                    // gate_up tokens per item: kChunkTokens * TC
+  int tpi_dn;                 // down tokens per item: kChunkTokens
   uint16_t* hhi;              // [P][I] fp16 high part of h = SiLU(gate) * up
   uint16_t* hlo;              // [P][I] fp16 remainder h - hi
   float* y;                   // [P][H] per-entry down projection
@@ -39,11 +52,12 @@ struct WsLayout {
   size_t counts, offsets, ptok, pw, inv, items, items_dn, n_items, hhi, hlo, y, xh, total;
   int max_items;
 };
-// Upper bound on decode work items (one per 32-token split of a group with
-// tokens): sum_g ceil(cnt_g / 32) <= min(NB, P) + P / 32 for P grouped entries.
+// Upper bound on work items (one per tpi-token split of a group with tokens):
+// sum_g ceil(cnt_g / tpi) <= min(NB, P) + P / tpi for P grouped entries; the
+// down list (tpi = kChunkTokens) is the longer one.
 inline int max_decode_items(int T, int E, int S, int K) {
   const long long P = (long long)T * (K + S), NB = (long long)E + S;
-  return (int)((P < NB ? P : NB) + P / kDecodeTokensPerWG);
+  return (int)((P < NB ? P : NB) + P / kChunkTokens);
 }
 WsLayout ws_layout(int T, int H, int I, int E, int S, int K, bool bf16);
 
@@ -58,7 +72,7 @@ hipError_t launch_permute(const FfnParams& p, hipStream_t s);
 hipError_t launch_x_to_f16(const uint16_t* x, uint16_t* y, size_t n, hipStream_t s);
 // qmax: highest committed bitwidth among the launch's blocks (sizes the LDS
 // table region; a block above it yields NaN)
-hipError_t launch_gate_up(const FfnParams& p, int qmax, hipStream_t s);
+hipError_t launch_gate_up(const FfnParams& p, int qmax, int tc, hipStream_t s);
 hipError_t launch_down(const FfnParams& p, int qmax, hipStream_t s);
 hipError_t launch_combine(const FfnParams& p, hipStream_t s);
 hipError_t launch_set_q(int32_t* q, int i, int b, hipStream_t s);
