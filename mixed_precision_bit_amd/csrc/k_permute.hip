@@ -20,66 +20,90 @@ namespace mpb {
 
 constexpr int kMaxGroups = 512 + 64;
 
+constexpr int kIdxCache = 8;  // topk ids kept in registers per thread between the two passes
+
 __global__ __launch_bounds__(256) void k_group(FfnParams p) {
   __shared__ int hist[kMaxGroups];
-  __shared__ int red[3][4];
+  __shared__ int red[5][4];
   __shared__ int wtot[4];
   const int e = blockIdx.x, tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int T = p.T, K = p.K, S = p.S, E = p.E, KS = K + S, TK = T * K;
+  // every global read the pass needs is issued up front (one memory round trip)
+  int xid[kIdxCache];
+#pragma unroll
+  for (int c = 0; c < kIdxCache; ++c) {
+    const int j = tid + 256 * c;
+    xid[c] = j < TK ? p.topk_idx[j] : -1;
+  }
+  int qjg[3], qjd[3];
+#pragma unroll
+  for (int c = 0; c < 3; ++c) {
+    const int j = tid + 256 * c;  // NB <= 576 < 3 * 256
+    qjg[c] = j < p.NB ? p.q[2 * j] : 0;
+    qjd[c] = j < p.NB ? p.q[2 * j + 1] : 0;
+  }
+  const int qg = p.q[2 * e], qd = p.q[2 * e + 1];
   for (int i = tid; i < E; i += 256) hist[i] = 0;
   __syncthreads();
-  for (int j = tid; j < TK; j += 256) {
+#pragma unroll
+  for (int c = 0; c < kIdxCache; ++c)
+    if (xid[c] >= 0 && xid[c] < E) atomicAdd(&hist[xid[c]], 1);
+  for (int j = tid + 256 * kIdxCache; j < TK; j += 256) {
     const int x = p.topk_idx[j];
     if (x >= 0 && x < E) atomicAdd(&hist[x], 1);
   }
   __syncthreads();
-  // position of this group's entries (group order) and of its items in both
-  // bitwidth-ordered lists: sums over the other groups, one per thread, reduced
+  // position of this group's entries (group order), of its items in both
+  // bitwidth-ordered lists, and the item totals: sums over the groups, one per
+  // thread, reduced
   const int mine = e < E ? hist[e] : T;
   const int ni = (mine + p.tpi - 1) / p.tpi, ni_dn = (mine + p.tpi_dn - 1) / p.tpi_dn;
-  const int qg = p.q[2 * e], qd = p.q[2 * e + 1];
-  int a_off = 0, a_gu = 0, a_dn = 0;
-  for (int j = tid; j < p.NB; j += 256) {
-    const int c = j < E ? hist[j] : T;
-    const int n = (c + p.tpi - 1) / p.tpi, n_dn = (c + p.tpi_dn - 1) / p.tpi_dn;
-    const int qj = p.q[2 * j], qjd = p.q[2 * j + 1];
-    if (j < e) a_off += c;
-    if (qj > qg || (qj == qg && j < e)) a_gu += n;
-    if (qjd > qd || (qjd == qd && j < e)) a_dn += n_dn;
+  int a[5] = {0, 0, 0, 0, 0};  // offset, gate_up position, down position, gate_up total, down total
+#pragma unroll
+  for (int c = 0; c < 3; ++c) {
+    const int j = tid + 256 * c;
+    if (j < p.NB) {
+      const int cnt = j < E ? hist[j] : T;
+      const int n = (cnt + p.tpi - 1) / p.tpi, n_dn = (cnt + p.tpi_dn - 1) / p.tpi_dn;
+      if (j < e) a[0] += cnt;
+      if (qjg[c] > qg || (qjg[c] == qg && j < e)) a[1] += n;
+      if (qjd[c] > qd || (qjd[c] == qd && j < e)) a[2] += n_dn;
+      a[3] += n;
+      a[4] += n_dn;
+    }
   }
 #pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) {
-    a_off += __shfl_xor(a_off, o);
-    a_gu += __shfl_xor(a_gu, o);
-    a_dn += __shfl_xor(a_dn, o);
+  for (int i = 0; i < 5; ++i) {
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) a[i] += __shfl_xor(a[i], o);
+    if (lane == 0) red[i][w] = a[i];
   }
-  if (lane == 0) { red[0][w] = a_off; red[1][w] = a_gu; red[2][w] = a_dn; }
   __syncthreads();
-  const int off = red[0][0] + red[0][1] + red[0][2] + red[0][3];
-  const int igu = red[1][0] + red[1][1] + red[1][2] + red[1][3];
-  const int idn = red[2][0] + red[2][1] + red[2][2] + red[2][3];
+  int r[5];
+#pragma unroll
+  for (int i = 0; i < 5; ++i) r[i] = red[i][0] + red[i][1] + red[i][2] + red[i][3];
+  const int off = r[0], igu = r[1], idn = r[2];
   if (tid == 0) {
     p.offsets[e] = off;
     p.counts[e] = mine;
     if (e == p.NB - 1) p.offsets[p.NB] = off + mine;
-  }
-  if (e == 0 && tid == 0) {
-    int tot = 0, tot_dn = 0;
-    for (int j = 0; j < p.NB; ++j) {
-      const int c = j < E ? hist[j] : T;
-      tot += (c + p.tpi - 1) / p.tpi;
-      tot_dn += (c + p.tpi_dn - 1) / p.tpi_dn;
+    if (e == 0) {
+      p.n_items[0] = r[3];
+      p.n_items[1] = r[4];
     }
-    p.n_items[0] = tot;
-    p.n_items[1] = tot_dn;
   }
   for (int sp = tid; sp < ni; sp += 256) p.items[igu + sp] = (e << 16) | sp;
   for (int sp = tid; sp < ni_dn; sp += 256) p.items_dn[idn + sp] = (e << 16) | sp;
   if (e < E) {
     int run = 0;
-    for (int b0 = 0; b0 < TK; b0 += 256) {
+    for (int b0 = 0, c = 0; b0 < TK; b0 += 256, ++c) {
       const int j = b0 + tid;
-      const bool m = j < TK && p.topk_idx[j] == e;
+      int x = -1;
+#pragma unroll
+      for (int cc = 0; cc < kIdxCache; ++cc)
+        if (cc == c) x = xid[cc];
+      if (c >= kIdxCache && j < TK) x = p.topk_idx[j];
+      const bool m = x == e;
       const unsigned long long bal = __ballot(m);
       const int lp = __popcll(bal & ((1ull << lane) - 1ull));
       if (lane == 0) wtot[w] = __popcll(bal);
