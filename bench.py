@@ -87,6 +87,56 @@ def cpu_baseline(L, Xbits, n_tokens):
                       f"with dequantisation of every touched block), fp64 numpy, {dt:.1f} s"}
 
 
+def page_movement(torch, M, L, D, replay, stream, ms_still, r=4):
+    """Replays the captured steps again while a copy stream keeps offloading
+    and reloading the pages above r (plane pages and the tables of bitwidths
+    above r) of every block committed at <= r bits (PagedWeight §3.3,
+    Figure 4: page I/O runs beside serving; no launch at q_i <= r reads those
+    pages), and reports the step time with the copies running, against the
+    same replay without them, and the copy rate."""
+    blocks = [i for i in range(L.n_blocks) if L.q[i] <= r]
+
+    def pinned(t):
+        return torch.empty(t.shape, dtype=t.dtype, pin_memory=True)
+
+    hp, ht, nbytes = {}, {}, {}
+    for i in blocks:
+        hp[i] = [None] * r + [pinned(D.pages[i][p]) for p in range(r, 8)]
+        ht[i] = [None] * (r - 2) + [pinned(D.luts[i][t]) for t in range(r - 2, 6)]
+        nbytes[i] = sum(D.pages[i][p].numel() * 4 + D.luts[i][p - 2].numel() * 2 for p in range(r, 8))
+    cs = torch.cuda.Stream()
+    c0, c1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    s0, s1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    moved, n_xfer = 0, 0
+    c0.record(cs)
+    s0.record(stream)
+    replay()
+    s1.record(stream)
+    while not s1.query():
+        for i in blocks:
+            st = M.mpb_page_state(i, r)
+            if st == M.MPB_PAGE_GPU:
+                M.mpb_offload_pages(i, r, hp[i], D.pages[i], ht[i], D.luts[i], cs)
+            elif st == M.MPB_PAGE_CPU:
+                M.mpb_reload_pages(i, 8, hp[i], D.pages[i], ht[i], D.luts[i], cs)
+            else:
+                continue
+            moved += nbytes[i]
+            n_xfer += 1
+    c1.record(cs)
+    torch.cuda.synchronize()
+    for i in blocks:             # leave every block resident again
+        if M.mpb_page_state(i, r) == M.MPB_PAGE_CPU:
+            M.mpb_reload_pages(i, 8, hp[i], D.pages[i], ht[i], D.luts[i], cs)
+    cs.synchronize()
+    ms_moving = s0.elapsed_time(s1) / replay.steps
+    return {"blocks_moving": len(blocks), "pages_per_transfer": 8 - r, "transfers": n_xfer,
+            "bytes_moved": int(moved), "copy_gbs": round(moved / (c0.elapsed_time(c1) * 1e-3) / 1e9, 1),
+            "ms_per_step_still": round(ms_still, 5), "ms_per_step_moving": round(ms_moving, 5),
+            "slowdown": round(ms_moving / ms_still - 1.0, 4)}
+
+
 def copy_calibration(torch, nbytes, steps):
     """Time a plain copy kernel (torch's device copy) of known size: the
     reference rocprofv3's FETCH_SIZE / WRITE_SIZE are scaled by, and the
@@ -120,6 +170,9 @@ def main():
                     help="only time a plain device-to-device copy of this many bytes (counter calibration)")
     ap.add_argument("--no-graph", dest="graph", action="store_false",
                     help="launch the timed steps eagerly instead of replaying them as one HIP graph")
+    ap.add_argument("--page-movement", action="store_true",
+                    help="also replay the steps while cold blocks' upper planes are offloaded and reloaded "
+                         "on a copy stream, and report the slowdown")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (got --gpus {args.gpus}); this layer is measured at N=1.",
@@ -261,6 +314,11 @@ def main():
                       "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(gu_gbs / HBM_PEAK_GBS, 4),
                       "traffic": traffic, "algorithmic_bytes_per_launch": int(gu_bytes)}),
     }
+    if args.page_movement and args.graph:
+        def replay():
+            graph.replay()
+        replay.steps = args.steps
+        res["page_movement"] = page_movement(torch, M, L, D0, replay, stream, ms)
     if rank == 0 and not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(L, Xbits, args.cpu_tokens)
     if rank == 0:

@@ -54,8 +54,11 @@ enum {
     MPB_E_NOT_RESIDENT = -4, /* bitwidth above the block's resident planes */
     MPB_E_WS = -5,           /* workspace too small */
     MPB_E_HIP = -6,          /* a HIP launch or API call failed */
-    MPB_E_UNINIT = -7        /* mpb_init has not bound a layer */
+    MPB_E_UNINIT = -7,       /* mpb_init has not bound a layer */
+    MPB_E_BUSY = -8          /* a page transfer of the block is still in flight */
 };
+
+enum { MPB_PAGE_GPU = 0, MPB_PAGE_CPU = 1, MPB_PAGE_IN_TRANSFER = 2 }; /* page states */
 
 enum { MPB_F16 = 0, MPB_BF16 = 1 }; /* activation dtypes */
 
@@ -135,6 +138,18 @@ int moe_route(const void* X_dev, int x_dtype, const float* W_router_dev, const f
               int T, int H, int E, int K, int32_t* topk_idx_dev, float* topk_w_dev, void* ws_dev,
               size_t ws_bytes, void* stream);
 
+/*
+ * Routing mass of a batch (§2.1, Eq. 1; the statistic the planner's hot and
+ * cold buckets are built from, §3.2): mass_dev[e] = sum of topk_w over the
+ * entries routed to expert e / sum of topk_w over all entries, for e < E, in
+ * fp64 with a fixed summation order (deterministic). topk_idx_dev/topk_w_dev
+ * are [T][K] as written by moe_route; ids outside [0, E) are ignored; an
+ * empty batch gives zeros. Needs E <= 512, K <= min(E, 16), T <= 2^20.
+ * Errors: MPB_E_ARG, MPB_E_SHAPE, MPB_E_HIP. Does not need mpb_init.
+ */
+int moe_routing_mass(const int32_t* topk_idx_dev, const float* topk_w_dev, int T, int E, int K,
+                     double* mass_dev, void* stream);
+
 /* Workspace bytes moe_ffn needs for T tokens of the bound layer (0 if unbound). */
 size_t moe_ffn_workspace_bytes(int T);
 
@@ -173,10 +188,12 @@ int moe_ffn(const void* X_dev, int x_dtype, int T, const int32_t* topk_idx_dev,
 /*
  * Commit bitwidth b for linear-block i (§3.1 and §3.3: the planner lowers or
  * raises q_i at a safe boundary; a reload raises q_i only once its pages are
- * GPU-resident). Validates 0 <= i < 2*(E+S), b in 3..8 and b <= the block's
- * resident plane count, updates the host mirror and enqueues the device write
- * of q_dev[i] on the bound stream: FFN launches enqueued before it read the old
- * value, later ones the new value. Errors: MPB_E_UNINIT, MPB_E_RANGE,
+ * GPU-resident). Validates 0 <= i < 2*(E+S), b in 3..8 and that planes 0..b-1
+ * of the block are GPU-resident (a reload whose copies have not completed
+ * leaves its pages in transfer, and the commit is refused until they have:
+ * MPB_E_NOT_RESIDENT). Then updates the host mirror and enqueues the device
+ * write of q_dev[i] on the bound stream: FFN launches enqueued before it read
+ * the old value, later ones the new value. Errors: MPB_E_UNINIT, MPB_E_RANGE,
  * MPB_E_NOT_RESIDENT, MPB_E_HIP.
  */
 int set_committed_bits(int i, int b);
@@ -204,11 +221,66 @@ int mpb_dequant_block(const uint32_t* const* pages_host, const uint16_t* lut_b_d
                       int b, uint16_t* out_f16_dev, void* stream);
 
 /*
- * Test hook: set how many of block i's planes are GPU-resident (3..8), to
- * model an offloaded or in-transfer page; set_committed_bits then refuses
- * b > r (§3.1: q_i is raised only when the page state is GPU-resident).
- * Lowering r below the committed q_i is refused with MPB_E_NOT_RESIDENT
- * (offload lowers q_i first). MPB_E_UNINIT / MPB_E_RANGE.
+ * Page movement (§3.1 after Eq. 3, §3.3 "Asynchronous Page Movement",
+ * Figure 4: an offload first lowers q_i, then moves the pages above it to CPU
+ * memory; a reload first moves the pages back and raises q_i only once they
+ * are GPU-resident). A weight page is one bit-plane with its table state
+ * (§3.1): page p (0..7) of block i is plane page p and, for p >= 2, the table
+ * image of bitwidth p + 1 (the table a block reads once it uses p + 1 planes),
+ * so a block with r resident pages can run at any q_i <= r. Each page is in
+ * one state: MPB_PAGE_GPU (p below the block's resident count),
+ * MPB_PAGE_IN_TRANSFER (a copy is enqueued and not known to have completed)
+ * or MPB_PAGE_CPU. The library only enqueues copies and tracks states; the
+ * caller owns every buffer.
+ *
+ * mpb_offload_pages(i, r, ...): needs q_i <= r (else MPB_E_NOT_RESIDENT:
+ * lower q_i with set_committed_bits first). Enqueues on copy_stream the
+ * copies of the resident pages p = r..7 to host memory: plane page p
+ * (mpb_plane_page_bytes(N, Kd) bytes) from dev_planes[p] to host_planes[p],
+ * table image p + 1 (mpb_table_image_bytes(i % 2, N, p + 1) bytes) from
+ * dev_tables[p - 2] to host_tables[p - 2]. The copies start after every
+ * launch enqueued on the bound stream before the last lowering of q_i (the
+ * only launches that may read those pages). The pages are IN_TRANSFER at once
+ * (commits above r are refused from now on) and CPU when the copies have
+ * completed; from then on no FFN launch reads them and the caller may reuse
+ * their device memory. No-op if no page above r is resident.
+ * mpb_reload_pages(i, r, ...): enqueues on copy_stream the copies of the
+ * non-resident pages p < r from host memory into the caller's device buffers
+ * dev_planes[p] / dev_tables[p - 2] (if these moved, the caller also writes
+ * their addresses into the pointer arrays it passes to moe_ffn). They are
+ * IN_TRANSFER until the copies have completed, then GPU, and only then may
+ * q_i be raised to r. No-op if pages 0..r-1 are already resident.
+ * dev_planes / host_planes: host arrays of 8 pointers (entry p: plane page
+ * p); dev_tables / host_tables: host arrays of 6 pointers (entry b - 3: the
+ * table image of bitwidth b). Only the entries of the pages that move are
+ * read and must be non-NULL. Host buffers should be pinned (hipHostMalloc)
+ * for the copies to be asynchronous. copy_stream: a hipStream_t other than
+ * the bound one, so the copies overlap the layer's kernels. A block has at
+ * most one transfer in flight: MPB_E_BUSY otherwise. States are refreshed by
+ * polling the transfer's completion (never blocking) in every call that
+ * reads them.
+ * Errors: MPB_E_UNINIT, MPB_E_RANGE (i, or r outside 3..8), MPB_E_ARG (a
+ * needed pointer is NULL), MPB_E_NOT_RESIDENT, MPB_E_BUSY, MPB_E_HIP.
+ */
+int mpb_offload_pages(int i, int r, void* const* host_planes, const uint32_t* const* dev_planes,
+                      void* const* host_tables, const uint16_t* const* dev_tables, void* copy_stream);
+int mpb_reload_pages(int i, int r, const void* const* host_planes, uint32_t* const* dev_planes,
+                     const void* const* host_tables, uint16_t* const* dev_tables, void* copy_stream);
+
+/* State of page p (0..7) of block i: MPB_PAGE_*, or MPB_E_UNINIT /
+ * MPB_E_RANGE / MPB_E_HIP (the transfer's copy stream reported a failure). */
+int mpb_page_state(int i, int p);
+
+/* Number of GPU-resident pages of block i (3..8; pages 0..n-1 are resident),
+ * or MPB_E_UNINIT / MPB_E_RANGE. */
+int mpb_get_resident_planes(int i);
+
+/*
+ * Test hook: declare how many of block i's planes are GPU-resident (3..8)
+ * without moving anything; set_committed_bits then refuses b > r. Lowering r
+ * below the committed q_i is refused with MPB_E_NOT_RESIDENT (offload lowers
+ * q_i first), and any change while a transfer is in flight with MPB_E_BUSY.
+ * MPB_E_UNINIT / MPB_E_RANGE.
  */
 int mpb_set_resident_planes(int i, int r);
 

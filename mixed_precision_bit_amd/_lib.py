@@ -11,7 +11,8 @@ LIB_PATH = os.path.join(_HERE, "libmpb.so")
 
 MPB_F16, MPB_BF16 = 0, 1
 ERRORS = {-1: "MPB_E_ARG", -2: "MPB_E_SHAPE", -3: "MPB_E_RANGE", -4: "MPB_E_NOT_RESIDENT",
-          -5: "MPB_E_WS", -6: "MPB_E_HIP", -7: "MPB_E_UNINIT"}
+          -5: "MPB_E_WS", -6: "MPB_E_HIP", -7: "MPB_E_UNINIT", -8: "MPB_E_BUSY"}
+MPB_PAGE_GPU, MPB_PAGE_CPU, MPB_PAGE_IN_TRANSFER = 0, 1, 2
 
 
 class MpbError(RuntimeError):
@@ -45,6 +46,7 @@ def lib() -> ctypes.CDLL:
             "mpb_pack_block": (_I, [_P, _I, _I, _P, _P]),
             "moe_route": (_I, [_P, _I, _P, _P, _I, _I, _I, _I, _P, _P, _P, _SZ, _P]),
             "moe_route_workspace_bytes": (_SZ, [_I, _I]),
+            "moe_routing_mass": (_I, [_P, _P, _I, _I, _I, _P, _P]),
             "moe_ffn_workspace_bytes": (ctypes.c_size_t, [_I]),
             "moe_ffn": (_I, [_P, _I, _I, _P, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P]),
             "set_committed_bits": (_I, [_I, _I]),
@@ -54,6 +56,10 @@ def lib() -> ctypes.CDLL:
             "mpb_table_image_bytes": (ctypes.c_int64, [_I, _I, _I]),
             "mpb_pack_table": (_I, [_I, _P, _I, _I, _P, _P]),
             "mpb_set_resident_planes": (_I, [_I, _I]),
+            "mpb_get_resident_planes": (_I, [_I]),
+            "mpb_offload_pages": (_I, [_I, _I, _P, _P, _P, _P, _P]),
+            "mpb_reload_pages": (_I, [_I, _I, _P, _P, _P, _P, _P]),
+            "mpb_page_state": (_I, [_I, _I]),
             "mpb_last_error": (ctypes.c_char_p, []),
             "mpb_set_kernel_events": (_I, [_P, _I]),
         }
@@ -118,6 +124,12 @@ def moe_route(X, x_dtype, W_router, bias, K, topk_idx, topk_w, ws, stream=None):
                                                _ptr(topk_idx), _ptr(topk_w), _ptr(ws), nbytes, _stream(stream)))
 
 
+def moe_routing_mass(topk_idx, topk_w, E, mass, stream=None):
+    T, K = topk_idx.shape
+    return _check("moe_routing_mass", lib().moe_routing_mass(_ptr(topk_idx), _ptr(topk_w), T, E, K, _ptr(mass),
+                                                             _stream(stream)))
+
+
 def moe_ffn_workspace_bytes(T) -> int:
     return lib().moe_ffn_workspace_bytes(T)
 
@@ -169,3 +181,34 @@ def mpb_set_kernel_events(events):
 
 def mpb_set_resident_planes(i, r):
     return _check("mpb_set_resident_planes", lib().mpb_set_resident_planes(i, r))
+
+
+def mpb_get_resident_planes(i) -> int:
+    return _check("mpb_get_resident_planes", lib().mpb_get_resident_planes(i))
+
+
+def _ptr_array(ts, n):
+    """n pointers (0 where the entry is None or missing) from a list of tensors."""
+    ptrs = [0] * n
+    for k, t in enumerate(ts):
+        if t is not None:
+            ptrs[k] = t.data_ptr()
+    return _host_ptrs(ptrs)
+
+
+def mpb_offload_pages(i, r, host_planes, dev_planes, host_tables, dev_tables, copy_stream):
+    """planes: lists of 8 tensors (plane pages 0..7), tables: lists of 6
+    (table images of bitwidths 3..8); None where a page does not move."""
+    return _check("mpb_offload_pages", lib().mpb_offload_pages(
+        i, r, _ptr_array(host_planes, 8), _ptr_array(dev_planes, 8), _ptr_array(host_tables, 6),
+        _ptr_array(dev_tables, 6), _stream(copy_stream)))
+
+
+def mpb_reload_pages(i, r, host_planes, dev_planes, host_tables, dev_tables, copy_stream):
+    return _check("mpb_reload_pages", lib().mpb_reload_pages(
+        i, r, _ptr_array(host_planes, 8), _ptr_array(dev_planes, 8), _ptr_array(host_tables, 6),
+        _ptr_array(dev_tables, 6), _stream(copy_stream)))
+
+
+def mpb_page_state(i, p) -> int:
+    return _check("mpb_page_state", lib().mpb_page_state(i, p))

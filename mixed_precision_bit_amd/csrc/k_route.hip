@@ -139,6 +139,48 @@ __global__ __launch_bounds__(256) void k_route_topk(const double* __restrict__ l
   }
 }
 
+// Routing mass of one batch ("PagedWeight", §2.1, Eq. 1): m_e = the routing
+// weight routed experts' entries carry, summed over tokens and top-K slots,
+// over the weight of all entries. One workgroup per expert; each thread sums a
+// fixed strided subset of the entries in fp64, and the partials are reduced in
+// a fixed tree, so the result is the same on every run. Entries whose expert id
+// is out of range count in neither sum.
+__global__ __launch_bounds__(256) void k_routing_mass(const int32_t* __restrict__ idx, const float* __restrict__ w,
+                                                      int TK, int E, double* __restrict__ mass) {
+  __shared__ double red[2][4];
+  const int e = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  double num = 0.0, den = 0.0;
+  for (int j = tid; j < TK; j += 256) {
+    const int x = idx[j];
+    const double r = (double)w[j];
+    if (x >= 0 && x < E) {
+      den += r;
+      if (x == e) num += r;
+    }
+  }
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) {
+    num += __shfl_xor(num, o);
+    den += __shfl_xor(den, o);
+  }
+  if (lane == 0) {
+    red[0][wv] = num;
+    red[1][wv] = den;
+  }
+  __syncthreads();
+  if (tid == 0) {
+    const double n = (red[0][0] + red[0][1]) + (red[0][2] + red[0][3]);
+    const double d = (red[1][0] + red[1][1]) + (red[1][2] + red[1][3]);
+    mass[e] = d > 0.0 ? n / d : 0.0;
+  }
+}
+
+hipError_t launch_routing_mass(const int32_t* idx, const float* w, int T, int E, int K, double* mass,
+                               hipStream_t s) {
+  hipLaunchKernelGGL(k_routing_mass, dim3(E), dim3(256), 0, s, idx, w, T * K, E, mass);
+  return hipGetLastError();
+}
+
 size_t route_workspace_bytes(int T, int E) { return ((size_t)T * E * 8 + 255) / 256 * 256; }
 
 template <int XDT>

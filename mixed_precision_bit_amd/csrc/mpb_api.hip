@@ -11,12 +11,24 @@
 
 namespace {
 
+// One page transfer of a block: planes lo..hi-1 move to the GPU (dir 1) or to
+// the CPU (dir 2); done once ev, recorded on the copy stream after the copies,
+// has completed.
+struct Xfer {
+  hipEvent_t ev = nullptr;
+  int dir = 0, lo = 0, hi = 0;
+};
+
 struct State {
   bool init = false;
   int H = 0, I = 0, E = 0, S = 0, K = 0;
   int32_t* q_dev = nullptr;
   std::vector<int> q;         // host mirror of committed bitwidths
-  std::vector<int> resident;  // GPU-resident planes per block
+  std::vector<int> resident;  // planes 0..resident-1 of each block are GPU-resident
+  std::vector<Xfer> xfer;     // the block's page transfer, if one has been enqueued
+  // recorded on the bound stream each time q_i is lowered: every launch that
+  // may read a plane above the new q_i was enqueued before it
+  std::vector<hipEvent_t> lower_ev;
   hipStream_t stream = nullptr;
   int nb() const { return 2 * (E + S); }
 };
@@ -55,6 +67,57 @@ void block_shape(int i, int* N, int* Kd) {
 
 int64_t block_bytes(int N, int Kd, int b) {
   return (int64_t)N * Kd * b / 8 + (int64_t)N * (1 << b) * 2;
+}
+
+// Moves a finished transfer's pages to their new state. Returns MPB_OK, or
+// MPB_E_HIP if the copy stream reported an error.
+int refresh_xfer(int i) {
+  Xfer& x = g.xfer[i];
+  if (!x.dir) return MPB_OK;
+  const hipError_t e = hipEventQuery(x.ev);
+  if (e == hipErrorNotReady) return MPB_OK;
+  if (e != hipSuccess) return hip_fail(e, "page transfer");
+  if (x.dir == 1) g.resident[i] = x.hi;
+  x.dir = 0;
+  return MPB_OK;
+}
+
+// Enqueues the copies of pages lo..hi-1 of block i: page p is plane page p
+// and, from p = 2 on, the table image of bitwidth p + 1 (the table a block
+// needs once it reads p + 1 planes).
+int copy_pages(int i, int lo, int hi, void* const* host_planes, uint32_t* const* dev_planes,
+               void* const* host_tables, uint16_t* const* dev_tables, bool to_gpu, hipStream_t cs) {
+  int N, Kd;
+  block_shape(i, &N, &Kd);
+  const size_t pbytes = (size_t)N * mpb::page_chunks(Kd) * 16;
+  Xfer& x = g.xfer[i];
+  hipError_t e = hipSuccess;
+  if (!x.ev) e = hipEventCreateWithFlags(&x.ev, hipEventDisableTiming);
+  for (int p = lo; e == hipSuccess && p < hi; ++p) {
+    e = to_gpu ? hipMemcpyAsync(dev_planes[p], host_planes[p], pbytes, hipMemcpyHostToDevice, cs)
+               : hipMemcpyAsync(host_planes[p], dev_planes[p], pbytes, hipMemcpyDeviceToHost, cs);
+    const int t = p - 2;  // table image of bitwidth p + 1, entry (p + 1) - 3
+    if (e == hipSuccess && t >= 0) {
+      const size_t tbytes = (size_t)((N + 127) / 128) * (256u << (p + 1));
+      e = to_gpu ? hipMemcpyAsync(dev_tables[t], host_tables[t], tbytes, hipMemcpyHostToDevice, cs)
+                 : hipMemcpyAsync(host_tables[t], dev_tables[t], tbytes, hipMemcpyDeviceToHost, cs);
+    }
+  }
+  if (e == hipSuccess) e = hipEventRecord(x.ev, cs);
+  if (e != hipSuccess) return hip_fail(e, to_gpu ? "mpb_reload_pages" : "mpb_offload_pages");
+  x.dir = to_gpu ? 1 : 2;
+  x.lo = lo;
+  x.hi = hi;
+  return MPB_OK;
+}
+
+// Checks the pointers of pages lo..hi-1 (plane p, and table p - 2 from p = 3 on).
+bool page_ptrs_ok(int lo, int hi, const void* const* hp, const void* const* dp, const void* const* ht,
+                  const void* const* dt) {
+  if (!hp || !dp || !ht || !dt) return false;
+  for (int p = lo; p < hi; ++p)
+    if (!hp[p] || !dp[p] || !ht[p - 2] || !dt[p - 2]) return false;
+  return true;
 }
 
 }  // namespace
@@ -108,6 +171,12 @@ int mpb_init(const mpb_layer_desc* d, int32_t* q_dev, const int32_t* q_init_host
   g.q_dev = q_dev;
   g.q.assign(q_init_host, q_init_host + nb);
   g.resident.assign(nb, 8);
+  for (const Xfer& x : g.xfer)
+    if (x.ev) (void)hipEventDestroy(x.ev);
+  g.xfer.assign(nb, Xfer{});
+  for (hipEvent_t ev : g.lower_ev)
+    if (ev) (void)hipEventDestroy(ev);
+  g.lower_ev.assign(nb, nullptr);
   g.stream = s;
   return MPB_OK;
 } catch (...) {
@@ -165,6 +234,19 @@ int mpb_dequant_block(const uint32_t* const* pages_host, const uint16_t* lut_b_d
   return MPB_OK;
 } catch (...) {
   return fail(MPB_E_HIP, "mpb_dequant_block: unexpected exception");
+}
+
+int moe_routing_mass(const int32_t* topk_idx_dev, const float* topk_w_dev, int T, int E, int K, double* mass_dev,
+                     void* stream) try {
+  if (T < 0 || T > (1 << 20)) return fail(MPB_E_SHAPE, "moe_routing_mass: T outside 0..2^20");
+  if (E < 1 || E > 512) return fail(MPB_E_SHAPE, "moe_routing_mass: E must be in 1..512");
+  if (K < 1 || K > 16 || K > E) return fail(MPB_E_SHAPE, "moe_routing_mass: K must be in 1..min(E,16)");
+  if (!mass_dev || (T > 0 && (!topk_idx_dev || !topk_w_dev))) return fail(MPB_E_ARG, "moe_routing_mass: null pointer");
+  hipError_t e = mpb::launch_routing_mass(topk_idx_dev, topk_w_dev, T, E, K, mass_dev, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "moe_routing_mass");
+  return MPB_OK;
+} catch (...) {
+  return fail(MPB_E_HIP, "moe_routing_mass: unexpected exception");
 }
 
 size_t moe_route_workspace_bytes(int T, int E) {
@@ -272,15 +354,88 @@ int set_committed_bits(int i, int b) try {
   if (!g.init) return fail(MPB_E_UNINIT, "set_committed_bits: no layer bound");
   if (i < 0 || i >= g.nb()) return fail(MPB_E_RANGE, "set_committed_bits: block index out of range");
   if (b < 3 || b > 8) return fail(MPB_E_RANGE, "set_committed_bits: bitwidth outside 3..8");
+  const int rc = refresh_xfer(i);
+  if (rc) return rc;
   if (b > g.resident[i])
-    return fail(MPB_E_NOT_RESIDENT, "set_committed_bits: block " + std::to_string(i) + " has only " +
-                                        std::to_string(g.resident[i]) + " resident planes");
-  hipError_t e = mpb::launch_set_q(g.q_dev, i, b, g.stream);
+    return fail(MPB_E_NOT_RESIDENT, "set_committed_bits: block " + std::to_string(i) + " has " +
+                                        std::to_string(g.resident[i]) + " GPU-resident planes");
+  hipError_t e = hipSuccess;
+  if (b < g.q[i] && !g.lower_ev[i]) e = hipEventCreateWithFlags(&g.lower_ev[i], hipEventDisableTiming);
+  if (e == hipSuccess) e = mpb::launch_set_q(g.q_dev, i, b, g.stream);
+  if (e == hipSuccess && b < g.q[i]) e = hipEventRecord(g.lower_ev[i], g.stream);
   if (e != hipSuccess) return hip_fail(e, "set_committed_bits");
   g.q[i] = b;
   return MPB_OK;
 } catch (...) {
   return fail(MPB_E_HIP, "set_committed_bits: unexpected exception");
+}
+
+int mpb_offload_pages(int i, int r, void* const* host_planes, const uint32_t* const* dev_planes,
+                      void* const* host_tables, const uint16_t* const* dev_tables, void* copy_stream) try {
+  if (!g.init) return fail(MPB_E_UNINIT, "mpb_offload_pages: no layer bound");
+  if (i < 0 || i >= g.nb()) return fail(MPB_E_RANGE, "mpb_offload_pages: block index out of range");
+  if (r < 3 || r > 8) return fail(MPB_E_RANGE, "mpb_offload_pages: page count outside 3..8");
+  const int rc = refresh_xfer(i);
+  if (rc) return rc;
+  if (g.xfer[i].dir) return fail(MPB_E_BUSY, "mpb_offload_pages: a transfer of this block is in flight");
+  if (g.q[i] > r) return fail(MPB_E_NOT_RESIDENT, "mpb_offload_pages: lower q_i to r before offloading");
+  const int hi = g.resident[i];
+  if (r >= hi) return MPB_OK;  // nothing above r is resident
+  if (!page_ptrs_ok(r, hi, host_planes, (const void* const*)dev_planes, host_tables,
+                    (const void* const*)dev_tables))
+    return fail(MPB_E_ARG, "mpb_offload_pages: null pointer");
+  hipStream_t cs = (hipStream_t)copy_stream;
+  // a launch that may read a page above r was enqueued while q_i > r, i.e.
+  // before the last lowering of q_i; the copies start after all of those, so
+  // once they have completed no launch that reads these pages is left
+  if (g.lower_ev[i]) {
+    const hipError_t e = hipStreamWaitEvent(cs, g.lower_ev[i], 0);
+    if (e != hipSuccess) return hip_fail(e, "mpb_offload_pages: ordering");
+  }
+  const int c = copy_pages(i, r, hi, host_planes, const_cast<uint32_t* const*>(dev_planes), host_tables,
+                           const_cast<uint16_t* const*>(dev_tables), false, cs);
+  if (c) return c;
+  g.resident[i] = r;
+  return MPB_OK;
+} catch (...) {
+  return fail(MPB_E_HIP, "mpb_offload_pages: unexpected exception");
+}
+
+int mpb_reload_pages(int i, int r, const void* const* host_planes, uint32_t* const* dev_planes,
+                     const void* const* host_tables, uint16_t* const* dev_tables, void* copy_stream) try {
+  if (!g.init) return fail(MPB_E_UNINIT, "mpb_reload_pages: no layer bound");
+  if (i < 0 || i >= g.nb()) return fail(MPB_E_RANGE, "mpb_reload_pages: block index out of range");
+  if (r < 3 || r > 8) return fail(MPB_E_RANGE, "mpb_reload_pages: page count outside 3..8");
+  const int rc = refresh_xfer(i);
+  if (rc) return rc;
+  if (g.xfer[i].dir) return fail(MPB_E_BUSY, "mpb_reload_pages: a transfer of this block is in flight");
+  const int lo = g.resident[i];
+  if (r <= lo) return MPB_OK;  // already resident
+  if (!page_ptrs_ok(lo, r, host_planes, (const void* const*)dev_planes, host_tables,
+                    (const void* const*)dev_tables))
+    return fail(MPB_E_ARG, "mpb_reload_pages: null pointer");
+  return copy_pages(i, lo, r, const_cast<void* const*>(host_planes), dev_planes,
+                    const_cast<void* const*>(host_tables), dev_tables, true, (hipStream_t)copy_stream);
+} catch (...) {
+  return fail(MPB_E_HIP, "mpb_reload_pages: unexpected exception");
+}
+
+int mpb_page_state(int i, int p) {
+  if (!g.init) return fail(MPB_E_UNINIT, "mpb_page_state: no layer bound");
+  if (i < 0 || i >= g.nb() || p < 0 || p > 7) return fail(MPB_E_RANGE, "mpb_page_state: index out of range");
+  const int rc = refresh_xfer(i);
+  if (rc) return rc;
+  if (p < g.resident[i]) return MPB_PAGE_GPU;
+  const Xfer& x = g.xfer[i];
+  if (x.dir && p >= x.lo && p < x.hi) return MPB_PAGE_IN_TRANSFER;
+  return MPB_PAGE_CPU;
+}
+
+int mpb_get_resident_planes(int i) {
+  if (!g.init) return fail(MPB_E_UNINIT, "mpb_get_resident_planes: no layer bound");
+  if (i < 0 || i >= g.nb()) return fail(MPB_E_RANGE, "mpb_get_resident_planes: block index out of range");
+  const int rc = refresh_xfer(i);
+  return rc ? rc : g.resident[i];
 }
 
 int mpb_set_kernel_events(void* const* events_host, int n) {
@@ -316,6 +471,9 @@ int mpb_set_resident_planes(int i, int r) {
   if (!g.init) return fail(MPB_E_UNINIT, "mpb_set_resident_planes: no layer bound");
   if (i < 0 || i >= g.nb()) return fail(MPB_E_RANGE, "mpb_set_resident_planes: block index out of range");
   if (r < 3 || r > 8) return fail(MPB_E_RANGE, "mpb_set_resident_planes: plane count outside 3..8");
+  const int rc = refresh_xfer(i);
+  if (rc) return rc;
+  if (g.xfer[i].dir) return fail(MPB_E_BUSY, "mpb_set_resident_planes: a transfer of this block is in flight");
   if (r < g.q[i])
     return fail(MPB_E_NOT_RESIDENT, "mpb_set_resident_planes: lower q_i before offloading its planes");
   g.resident[i] = r;

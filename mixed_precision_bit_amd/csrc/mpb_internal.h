@@ -66,6 +66,8 @@ hipError_t launch_pack_table(const uint16_t* lut, int kind, int N, int b, uint16
 hipError_t launch_dequant(const uint32_t* const* pages, const uint16_t* lut, int N, int Kd, int b,
                           uint16_t* out, hipStream_t s);
 size_t route_workspace_bytes(int T, int E);
+hipError_t launch_routing_mass(const int32_t* idx, const float* w, int T, int E, int K, double* mass,
+                               hipStream_t s);
 hipError_t launch_route(const uint16_t* X, int xdt, const float* W, const float* bias, int T, int H,
                         int E, int K, int32_t* idx, float* w, double* logits, hipStream_t s);
 hipError_t launch_permute(const FfnParams& p, hipStream_t s);

@@ -29,7 +29,7 @@ def test_header_declares_the_calls():
     names = declared_functions()
     for n in ("moe_route", "moe_route_workspace_bytes", "moe_ffn", "set_committed_bits", "mpb_init", "mpb_pack_block",
               "mpb_committed_bytes", "mpb_dequant_block", "mpb_last_error", "mpb_table_image_bytes",
-              "mpb_pack_table"):
+              "mpb_pack_table", "moe_routing_mass", "mpb_offload_pages", "mpb_reload_pages", "mpb_page_state"):
         assert n in names
 
 
@@ -42,6 +42,10 @@ def test_host_validation_without_device(L):
     from mixed_precision_bit_amd import _lib as M
     # nothing bound yet in this process
     assert L.set_committed_bits(0, 4) == -7
+    assert L.mpb_offload_pages(0, 4, None, None, None, None, None) == -7
+    assert L.mpb_reload_pages(0, 8, None, None, None, None, None) == -7
+    assert L.mpb_page_state(0, 0) == -7
+    assert L.mpb_get_resident_planes(0) == -7
     assert L.mpb_committed_bytes(None) == -7
     assert L.moe_ffn_workspace_bytes(16) == 0
     assert "no layer bound" in M.mpb_last_error()
@@ -69,3 +73,6 @@ def test_host_validation_without_device(L):
     assert L.mpb_table_image_bytes(2, 256, 3) == -1               # kind
     assert L.mpb_table_image_bytes(1, 256, 9) == -3               # b
     assert L.mpb_pack_table(1, None, 256, 4, one, None) == -1
+    assert L.moe_routing_mass(one, one, 4, 0, 1, one, None) == -2     # E
+    assert L.moe_routing_mass(one, one, 4, 8, 9, one, None) == -2     # K > E
+    assert L.moe_routing_mass(one, one, 4, 8, 2, None, None) == -1    # null output

@@ -139,6 +139,39 @@ def test_route_ties_lowest_index():
         assert_close(w.cpu().numpy(), r, "tie topk_w")
 
 
+@pytest.mark.parametrize("cfg", [1, 3])
+def test_routing_mass_matches_eq1(cfg):
+    """moe_routing_mass on the GPU router's output vs the oracle's Eq. 1 on the
+    oracle's routing (same top-K, weights within fp32 rounding)."""
+    c = S.layer_config(cfg)
+    L = S.make_layer(cfg, blocks=[])
+    Xb = S.make_tokens(cfg)
+    T = Xb.shape[0]
+    X, z, r = oracle_route(L, Xb)
+    W = torch.from_numpy(L.W_r).cuda()
+    bias = None if L.bias is None else torch.from_numpy(L.bias).cuda()
+    idx = torch.empty((T, L.K), dtype=torch.int32, device="cuda")
+    w = torch.empty((T, L.K), dtype=torch.float32, device="cuda")
+    M().moe_route(to_dev_x(Xb), 0 if c["xdtype"] == "f16" else 1, W, bias, L.K, idx, w, route_ws(T, L.E))
+    mass = torch.empty(L.E, dtype=torch.float64, device="cuda")
+    M().moe_routing_mass(idx, w, L.E, mass)
+    m_ref = O.routing_mass(z, r, L.E)
+    m = mass.cpu().numpy()
+    assert abs(m.sum() - 1.0) < 1e-12
+    assert_close(m, m_ref, f"cfg{cfg} routing mass")
+    # out-of-range ids count in neither sum; an empty batch gives zeros
+    idx2 = idx.clone()
+    idx2[0, 0] = L.E
+    M().moe_routing_mass(idx2, w, L.E, mass)
+    keep = np.ones((T, L.K), bool)
+    keep[0, 0] = False
+    num = np.zeros(L.E)
+    np.add.at(num, z[keep], r[keep])
+    assert_close(mass.cpu().numpy(), num / r[keep].sum(), f"cfg{cfg} routing mass, one id out of range")
+    M().moe_routing_mass(idx[:0], w[:0], L.E, mass)
+    assert not mass.cpu().numpy().any()
+
+
 # ---------------------------------------------------------------- FFN, every element
 @pytest.mark.parametrize("cfg", [0, 10, 11])
 def test_ffn_small_every_element(cfg, layer_cache):
@@ -205,6 +238,120 @@ def test_set_committed_bits_is_stream_ordered(layer_cache):
     assert_close(out1.cpu().numpy(), O.moe_ffn(Xf, z, r, L), "before commit")
     assert_close(out2.cpu().numpy(), O.moe_ffn(Xf, z, r, L, q=q2), "after commit")
     assert [M().mpb_get_committed_bits(i) for i in range(L.n_blocks)] == q2.tolist()
+
+
+def _gated_stream(cycles=200_000_000):
+    """A copy stream held back by a bounded spin kernel on another stream, so
+    that work enqueued on it right now is still in flight a moment later."""
+    gate, cs = torch.cuda.Stream(), torch.cuda.Stream()
+    with torch.cuda.stream(gate):
+        torch.cuda._sleep(cycles)
+    ev = torch.cuda.Event()
+    ev.record(gate)
+    cs.wait_event(ev)
+    return cs
+
+
+def test_page_movement_offload_then_reload(layer_cache):
+    """Offload lowers q_i first, then moves the pages above it (plane pages and
+    the tables of the higher bitwidths) to the CPU; a reload brings them back
+    and q_i rises only once they are GPU-resident (PagedWeight §3.1 after
+    Eq. 3, §3.3 and Figure 4). After the offload the freed device memory is
+    overwritten and the layer still matches the oracle; the reload goes into
+    fresh device buffers."""
+    L, D = dev_layer(layer_cache, 10)
+    E_ = M().MpbError
+    GPU, CPU, XFER = M().MPB_PAGE_GPU, M().MPB_PAGE_CPU, M().MPB_PAGE_IN_TRANSFER
+    Xb = S.make_tokens(10)
+    X, z, r = oracle_route(L, Xb)
+    Xd = to_dev_x(Xb)
+    T = Xb.shape[0]
+    idx, w = D.alloc_route(T)
+    out, ws = D.alloc_ffn(T)
+    D.route(Xd, "f16", idx, w)
+    e = int(z[0, 0])
+    blocks = [2 * e, 2 * e + 1]          # both linear-blocks of a routed expert
+
+    def pinned(t):
+        return torch.empty(t.shape, dtype=t.dtype, pin_memory=True)
+
+    keep_p = {i: [t.clone() for t in D.pages[i]] for i in blocks}
+    keep_t = {i: [t.clone() for t in D.luts[i]] for i in blocks}
+    hp = {i: [pinned(t) for t in D.pages[i]] for i in blocks}
+    ht = {i: [pinned(t) for t in D.luts[i]] for i in blocks}
+    q = L.q.copy()
+    for i in blocks:
+        M().set_committed_bits(i, 8)
+        q[i] = 8
+        with pytest.raises(E_) as ei:        # q_i must be lowered first
+            M().mpb_offload_pages(i, 4, hp[i], D.pages[i], ht[i], D.luts[i], torch.cuda.Stream())
+        assert ei.value.code == -4
+    # ---- offload to 4 pages while an FFN at 8 bits is still enqueued
+    D.ffn(Xd, "f16", idx, w, out, ws)
+    for i in blocks:
+        M().set_committed_bits(i, 4)
+        q[i] = 4
+    cs = _gated_stream()
+    for i in blocks:
+        M().mpb_offload_pages(i, 4, hp[i], D.pages[i], ht[i], D.luts[i], cs)
+        assert M().mpb_get_resident_planes(i) == 4
+        assert [M().mpb_page_state(i, p) for p in range(8)] == [GPU] * 4 + [XFER] * 4
+        with pytest.raises(E_) as ei:
+            M().set_committed_bits(i, 5)
+        assert ei.value.code == -4
+        with pytest.raises(E_) as ei:
+            M().mpb_reload_pages(i, 8, hp[i], D.pages[i], ht[i], D.luts[i], cs)
+        assert ei.value.code == -8
+    cs.synchronize()
+    for i in blocks:
+        assert [M().mpb_page_state(i, p) for p in range(8)] == [GPU] * 4 + [CPU] * 4
+        for p in range(4, 8):
+            assert torch.equal(hp[i][p], keep_p[i][p].cpu()), f"offloaded plane {p} of block {i}"
+            assert torch.equal(ht[i][p - 2], keep_t[i][p - 2].cpu()), f"offloaded table {p + 1} of block {i}"
+            D.pages[i][p].fill_(0x5A5A5A5A)   # the freed memory is reused
+            D.luts[i][p - 2].fill_(0x7E00)     # (a NaN pattern, were it ever read)
+        assert torch.equal(D.luts[i][1], keep_t[i][1]), "the 4-bit table stays"
+    torch.cuda.synchronize()
+    q8 = q.copy()
+    q8[blocks] = 8
+    assert_close(out.cpu().numpy(), O.moe_ffn(X, z, r, L, q=q8), "FFN enqueued before the offload")
+    D.ffn(Xd, "f16", idx, w, out, ws)
+    torch.cuda.synchronize()
+    assert_close(out.cpu().numpy(), O.moe_ffn(X, z, r, L, q=q), "after offload, memory reused")
+    # ---- reload into fresh buffers; q_i rises only after the copies
+    fp = {i: [None] * 4 + [torch.empty_like(D.pages[i][p]) for p in range(4, 8)] for i in blocks}
+    ft = {i: [None] * 2 + [torch.empty_like(D.luts[i][t]) for t in range(2, 6)] for i in blocks}
+    ptab, ttab = D.planes_table.clone(), D.luts_table.clone()
+    for i in blocks:
+        for p in range(4, 8):
+            ptab[i * 8 + p] = fp[i][p].data_ptr()
+            ttab[i * 6 + p - 2] = ft[i][p - 2].data_ptr()
+    cs = _gated_stream()
+    for i in blocks:
+        M().mpb_reload_pages(i, 8, hp[i], fp[i], ht[i], ft[i], cs)
+        assert [M().mpb_page_state(i, p) for p in range(8)] == [GPU] * 4 + [XFER] * 4
+        with pytest.raises(E_) as ei:
+            M().set_committed_bits(i, 6)
+        assert ei.value.code == -4
+    # an FFN at the committed 4 bits runs while the copies are in flight
+    M().moe_ffn(Xd, 0, idx, w, ptab, ttab, D.q_dev, out, ws)
+    torch.cuda.synchronize()
+    assert_close(out.cpu().numpy(), O.moe_ffn(X, z, r, L, q=q), "during reload")
+    cs.synchronize()
+    for i in blocks:
+        assert [M().mpb_page_state(i, p) for p in range(8)] == [GPU] * 8
+        assert M().mpb_get_resident_planes(i) == 8
+        M().set_committed_bits(i, 8)
+    M().moe_ffn(Xd, 0, idx, w, ptab, ttab, D.q_dev, out, ws)
+    torch.cuda.synchronize()
+    assert_close(out.cpu().numpy(), O.moe_ffn(X, z, r, L, q=q8), "after reload at 8 bits")
+    # restore the cached layer's buffers (later tests reuse it)
+    for i in blocks:
+        for p in range(8):
+            D.pages[i][p].copy_(keep_p[i][p])
+        for t in range(6):
+            D.luts[i][t].copy_(keep_t[i][t])
+    torch.cuda.synchronize()
 
 
 # ---------------------------------------------------------------- full-size layers, sampled
