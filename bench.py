@@ -137,6 +137,32 @@ def page_movement(torch, M, L, D, replay, stream, ms_still, r=4):
             "slowdown": round(ms_moving / ms_still - 1.0, 4)}
 
 
+def planner_timing(torch, M, L, cfg, idx, w, steps, F_blk=20):
+    """Times the routing-mass kernel (Eq. 1) on this batch and the host
+    planner step (Algorithm 1) fed with its output, under KV pressure."""
+    import mpb_synth as S
+    mass = torch.empty(L.E, dtype=torch.float64, device="cuda")
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    M.moe_routing_mass(idx, w, L.E, mass)
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(steps):
+        M.moe_routing_mass(idx, w, L.E, mass)
+    e1.record()
+    torch.cuda.synchronize()
+    m = mass.cpu().numpy()
+    sens = S.make_sensitivity(cfg, L.n_blocks)[:, 3:9]
+    P, phi = S.make_planner_inputs(cfg, L.n_blocks, F_blk)
+    M.mpb_plan_step(L.H, L.I, L.E, L.S, L.K, L.q, None, sens, m, phi, P)
+    t = time.perf_counter()
+    for _ in range(steps):
+        plan, summ, _ = M.mpb_plan_step(L.H, L.I, L.E, L.S, L.K, L.q, None, sens, m, phi, P)
+    dt = (time.perf_counter() - t) / steps
+    return {"routing_mass_us": round(e0.elapsed_time(e1) * 1e3 / steps, 2),
+            "plan_step_us": round(dt * 1e6, 1), "plan_blocks": len(plan), "target_bytes": summ["D"],
+            "released_bytes": summ["released"], "stage": summ["stage"]}
+
+
 def copy_calibration(torch, nbytes, steps):
     """Time a plain copy kernel (torch's device copy) of known size: the
     reference rocprofv3's FETCH_SIZE / WRITE_SIZE are scaled by, and the
@@ -170,6 +196,8 @@ def main():
                     help="only time a plain device-to-device copy of this many bytes (counter calibration)")
     ap.add_argument("--no-graph", dest="graph", action="store_false",
                     help="launch the timed steps eagerly instead of replaying them as one HIP graph")
+    ap.add_argument("--plan", action="store_true",
+                    help="also time the routing-mass kernel and the host planner step on this batch")
     ap.add_argument("--page-movement", action="store_true",
                     help="also replay the steps while cold blocks' upper planes are offloaded and reloaded "
                          "on a copy stream, and report the slowdown")
@@ -314,6 +342,8 @@ def main():
                       "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(gu_gbs / HBM_PEAK_GBS, 4),
                       "traffic": traffic, "algorithmic_bytes_per_launch": int(gu_bytes)}),
     }
+    if args.plan:
+        res["planner"] = planner_timing(torch, M, L, cfg, bufs[0][0], bufs[0][1], args.steps)
     if args.page_movement and args.graph:
         def replay():
             graph.replay()

@@ -285,6 +285,97 @@ int mpb_get_resident_planes(int i);
 int mpb_set_resident_planes(int i, int r);
 
 /*
+ * Planner step (§3.2, Algorithm 1; Eqs. 3-8), host only: turns KV-cache
+ * pressure into a byte target D (Eq. 7), scores one-bit reductions of routed
+ * linear-blocks by predicted damage (Eq. 4 global damage, Eq. 5-6 prompt
+ * residual, Eq. 8 with the routing bucket's multiplier) per released byte
+ * (Eq. 3), greedily builds one candidate plan per bitwidth-floor stage, keeps
+ * the newest plan of every stage in the queue, and when pressure is triggered
+ * selects the page-movement plan {(i, q_i -> d_i, Delta_i)}.
+ * Readings of the steps the pages leave open:
+ *  - a step lowers one block by one bit; a block's steps are taken in order;
+ *    GreedySelect repeatedly takes the available step with the smallest
+ *    damage / released bytes (ties to the lower block index) until the
+ *    released bytes reach D;
+ *  - stage s allows block i down to max(stage_floor[s], floor of i's routing
+ *    bucket); relaxing the depth cap is moving to the next stage;
+ *  - SelectBestPlan: the first stage whose plan reaches D, else the plan that
+ *    releases the most bytes (the largest safe reduction), ties to the earlier
+ *    stage;
+ *  - pressure is triggered when F_blk <= T_blk; D uses F_blk - P_blk (free
+ *    blocks after the pending KV growth);
+ *  - routing buckets: experts sorted by routing mass, hottest first (ties to
+ *    the lower index); bucket k ends at rank ceil(bucket_frac[k] * E);
+ *  - candidates are routed blocks whose pages may move (movable_host[i] != 0,
+ *    or every routed block if movable_host is NULL); shared experts' blocks
+ *    never change.
+ * Floating-point evaluation order is fixed (Eq. 5 summed left to right, eta
+ * through the C library's exp, damage sums in step order), so a plan is
+ * reproducible bit for bit.
+ */
+typedef struct {
+    int32_t n_buckets;         /* 1..8 */
+    double bucket_frac[8];     /* cumulative share of experts per bucket, increasing, last 1.0 */
+    double mu[8];              /* damage multiplier per bucket, > 0 */
+    int32_t floor[8];          /* bitwidth floor per bucket, 3..8 */
+    int32_t n_stages;          /* 1..6 */
+    int32_t stage_floor[6];    /* global floor per stage, 3..8, strictly decreasing */
+    double eps;                /* damage floor of Eq. 8, > 0 */
+    double alpha;              /* strength of Eq. 6 */
+    double rho_min, rho_max;   /* clip range of Eq. 6, rho_min <= rho_max */
+    /* Eq. 5-6 heads per block type u (0 gate_up, 1 down) and one-bit
+     * transition b -> b-1, b = 4..8 at index b - 4 */
+    double head_w[2][5][3];
+    double head_a[2][5];
+    double head_c[2][5];       /* confidence */
+    int64_t T_blk;             /* free-block threshold (Eq. 7) */
+    int64_t F_blk;             /* current free KV blocks */
+    int64_t P_blk;             /* pending KV growth in blocks (0: Eq. 7 as printed) */
+    int64_t B_kv;              /* bytes of one KV block */
+} mpb_planner_params;
+
+typedef struct {
+    int32_t i;                 /* linear-block */
+    int32_t from, to;          /* q_i -> d_i */
+    int64_t delta;             /* M_i^{from} - M_i^{to} (Eq. 3) */
+    double damage;             /* sum of the predicted damage of its steps */
+} mpb_plan_entry;
+
+typedef struct {
+    int64_t D;                 /* byte target (Eq. 7) */
+    int32_t triggered;         /* 1 if pressure is triggered */
+    int32_t stage;             /* stage of the selected plan, -1 if not triggered */
+    int32_t n_plan;            /* entries written to plan_host */
+    int32_t pad;
+    int64_t released;          /* sum of delta over the selected plan */
+    double damage;             /* sum of damage over the selected plan (entry order) */
+    int64_t stage_released[6]; /* per stage plan in the queue */
+    double stage_damage[6];
+} mpb_plan_summary;
+
+/*
+ * mpb_plan_step(d, q_host, movable_host, sens_host, mass_host, phi_host, prm,
+ *               queue_host, plan_host, summary):
+ *   d            layer geometry (as for mpb_init; no layer needs to be bound)
+ *   q_host       [2(E+S)] committed bitwidths (3..8)
+ *   movable_host [2(E+S)] flags or NULL
+ *   sens_host    [2(E+S)][6] s_i^b for b = 3..8 (Eq. 4)
+ *   mass_host    [E] routing mass (Eq. 1, e.g. from moe_routing_mass)
+ *   phi_host     [2(E+S)][3] routed-input features (Eq. 5)
+ *   queue_host   out: [n_stages][2(E+S)] desired bitwidths of each stage's
+ *                plan (the refreshed plan queue); may be NULL
+ *   plan_host    out: up to 2(E+S) entries, ascending i, only when triggered
+ *   summary      out
+ * All pointers are host memory owned by the caller. Does not touch the GPU.
+ * Errors: MPB_E_ARG (null pointer, parameter out of its range),
+ * MPB_E_SHAPE (geometry), MPB_E_RANGE (a q outside 3..8).
+ */
+int mpb_plan_step(const mpb_layer_desc* d, const int32_t* q_host, const uint8_t* movable_host,
+                  const double* sens_host, const double* mass_host, const double* phi_host,
+                  const mpb_planner_params* prm, int32_t* queue_host, mpb_plan_entry* plan_host,
+                  mpb_plan_summary* summary);
+
+/*
  * Profiling hook: with n == 5, every following moe_ffn records
  * events_host[0..4] (host array of hipEvent_t handles, caller-created) on its
  * stream before the grouping kernels, before gate_up, before down, before the

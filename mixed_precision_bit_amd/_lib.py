@@ -26,6 +26,28 @@ class LayerDesc(ctypes.Structure):
                 ("S", ctypes.c_int32), ("K", ctypes.c_int32)]
 
 
+class PlannerParams(ctypes.Structure):
+    _fields_ = [("n_buckets", ctypes.c_int32), ("bucket_frac", ctypes.c_double * 8), ("mu", ctypes.c_double * 8),
+                ("floor", ctypes.c_int32 * 8), ("n_stages", ctypes.c_int32), ("stage_floor", ctypes.c_int32 * 6),
+                ("eps", ctypes.c_double), ("alpha", ctypes.c_double), ("rho_min", ctypes.c_double),
+                ("rho_max", ctypes.c_double), ("head_w", ((ctypes.c_double * 3) * 5) * 2),
+                ("head_a", (ctypes.c_double * 5) * 2), ("head_c", (ctypes.c_double * 5) * 2),
+                ("T_blk", ctypes.c_int64), ("F_blk", ctypes.c_int64), ("P_blk", ctypes.c_int64),
+                ("B_kv", ctypes.c_int64)]
+
+
+class PlanEntry(ctypes.Structure):
+    _fields_ = [("i", ctypes.c_int32), ("from_", ctypes.c_int32), ("to", ctypes.c_int32),
+                ("delta", ctypes.c_int64), ("damage", ctypes.c_double)]
+
+
+class PlanSummary(ctypes.Structure):
+    _fields_ = [("D", ctypes.c_int64), ("triggered", ctypes.c_int32), ("stage", ctypes.c_int32),
+                ("n_plan", ctypes.c_int32), ("pad", ctypes.c_int32), ("released", ctypes.c_int64),
+                ("damage", ctypes.c_double), ("stage_released", ctypes.c_int64 * 6),
+                ("stage_damage", ctypes.c_double * 6)]
+
+
 _lib = None
 _P = ctypes.c_void_p
 _I = ctypes.c_int
@@ -60,6 +82,8 @@ def lib() -> ctypes.CDLL:
             "mpb_offload_pages": (_I, [_I, _I, _P, _P, _P, _P, _P]),
             "mpb_reload_pages": (_I, [_I, _I, _P, _P, _P, _P, _P]),
             "mpb_page_state": (_I, [_I, _I]),
+            "mpb_plan_step": (_I, [ctypes.POINTER(LayerDesc), _P, _P, _P, _P, _P, ctypes.POINTER(PlannerParams),
+                                   _P, ctypes.POINTER(PlanEntry), ctypes.POINTER(PlanSummary)]),
             "mpb_last_error": (ctypes.c_char_p, []),
             "mpb_set_kernel_events": (_I, [_P, _I]),
         }
@@ -212,3 +236,56 @@ def mpb_reload_pages(i, r, host_planes, dev_planes, host_tables, dev_tables, cop
 
 def mpb_page_state(i, p) -> int:
     return _check("mpb_page_state", lib().mpb_page_state(i, p))
+
+
+def planner_params(P: dict) -> PlannerParams:
+    """Pack a dict of planner parameters (the header's field names) into the C struct."""
+    c = PlannerParams()
+    c.n_buckets = len(P["bucket_frac"])
+    for k in range(c.n_buckets):
+        c.bucket_frac[k] = P["bucket_frac"][k]
+        c.mu[k] = P["mu"][k]
+        c.floor[k] = P["floor"][k]
+    c.n_stages = len(P["stage_floor"])
+    for k in range(c.n_stages):
+        c.stage_floor[k] = P["stage_floor"][k]
+    c.eps, c.alpha, c.rho_min, c.rho_max = P["eps"], P["alpha"], P["rho_min"], P["rho_max"]
+    for u in range(2):
+        for t in range(5):
+            for j in range(3):
+                c.head_w[u][t][j] = P["head_w"][u][t][j]
+            c.head_a[u][t] = P["head_a"][u][t]
+            c.head_c[u][t] = P["head_c"][u][t]
+    c.T_blk, c.F_blk, c.P_blk, c.B_kv = P["T_blk"], P["F_blk"], P["P_blk"], P["B_kv"]
+    return c
+
+
+def mpb_plan_step(H, I, E, S, K, q, movable, sens, mass, phi, P: dict):
+    """Host planner step. q [nb] int, movable [nb] bool or None, sens [nb][6]
+    (b = 3..8), mass [E], phi [nb][3]. Returns (plan, summary, queue) with plan
+    a list of (i, from, to, delta, damage), summary a dict and queue an
+    [n_stages][nb] int32 array."""
+    import numpy as np
+    nb = 2 * (E + S)
+    d = LayerDesc(H, I, E, S, K)
+    q = np.ascontiguousarray(q, dtype=np.int32)
+    mv = None if movable is None else np.ascontiguousarray(movable, dtype=np.uint8)
+    sens = np.ascontiguousarray(sens, dtype=np.float64)
+    mass = np.ascontiguousarray(mass, dtype=np.float64)
+    phi = np.ascontiguousarray(phi, dtype=np.float64)
+    assert q.shape == (nb,) and sens.shape == (nb, 6) and mass.shape == (E,) and phi.shape == (nb, 3)
+    prm = planner_params(P)
+    queue = np.zeros((prm.n_stages, nb), dtype=np.int32)
+    plan = (PlanEntry * nb)()
+    summ = PlanSummary()
+
+    def vp(a):
+        return None if a is None else a.ctypes.data_as(ctypes.c_void_p)
+
+    _check("mpb_plan_step", lib().mpb_plan_step(ctypes.byref(d), vp(q), vp(mv), vp(sens), vp(mass), vp(phi),
+                                                ctypes.byref(prm), vp(queue), plan, ctypes.byref(summ)))
+    entries = [(plan[k].i, plan[k].from_, plan[k].to, plan[k].delta, plan[k].damage) for k in range(summ.n_plan)]
+    summary = {"D": summ.D, "triggered": bool(summ.triggered), "stage": summ.stage, "released": summ.released,
+               "damage": summ.damage, "stage_released": list(summ.stage_released)[:prm.n_stages],
+               "stage_damage": list(summ.stage_damage)[:prm.n_stages]}
+    return entries, summary, queue

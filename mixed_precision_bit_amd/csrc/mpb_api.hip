@@ -51,15 +51,6 @@ int hip_fail(hipError_t e, const char* where) {
   return fail(MPB_E_HIP, std::string(where) + ": " + hipGetErrorString(e));
 }
 
-bool geometry_ok(int H, int I, int E, int S, int K, std::string* why) {
-  if (H <= 0 || H % 64 || H > 65536) { *why = "H must be a positive multiple of 64 (<= 65536)"; return false; }
-  if (I <= 0 || I % 64 || I > 65536) { *why = "I must be a positive multiple of 64 (<= 65536)"; return false; }
-  if (E < 1 || E > 512) { *why = "E must be in 1..512"; return false; }
-  if (S < 0 || S > 64) { *why = "S must be in 0..64"; return false; }
-  if (K < 1 || K > 16 || K > E) { *why = "K must be in 1..min(E,16)"; return false; }
-  return true;
-}
-
 void block_shape(int i, int* N, int* Kd) {
   if (i % 2 == 0) { *N = 2 * g.I; *Kd = g.H; }
   else { *N = g.H; *Kd = g.I; }
@@ -124,6 +115,17 @@ bool page_ptrs_ok(int lo, int hi, const void* const* hp, const void* const* dp, 
 
 namespace mpb {
 
+int set_error(int code, const char* msg) { return fail(code, msg); }
+
+bool geometry_ok(int H, int I, int E, int S, int K, const char** why) {
+  if (H <= 0 || H % 64 || H > 65536) { *why = "H must be a positive multiple of 64 (<= 65536)"; return false; }
+  if (I <= 0 || I % 64 || I > 65536) { *why = "I must be a positive multiple of 64 (<= 65536)"; return false; }
+  if (E < 1 || E > 512) { *why = "E must be in 1..512"; return false; }
+  if (S < 0 || S > 64) { *why = "S must be in 0..64"; return false; }
+  if (K < 1 || K > 16 || K > E) { *why = "K must be in 1..min(E,16)"; return false; }
+  return true;
+}
+
 static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 WsLayout ws_layout(int T, int H, int I, int E, int S, int K, bool bf16) {
@@ -155,8 +157,9 @@ const char* mpb_last_error(void) { return g_err.c_str(); }
 
 int mpb_init(const mpb_layer_desc* d, int32_t* q_dev, const int32_t* q_init_host, void* stream) try {
   if (!d || !q_dev || !q_init_host) return fail(MPB_E_ARG, "mpb_init: null pointer");
-  std::string why;
-  if (!geometry_ok(d->H, d->I, d->E, d->S, d->K, &why)) return fail(MPB_E_SHAPE, "mpb_init: " + why);
+  const char* why = "";
+  if (!mpb::geometry_ok(d->H, d->I, d->E, d->S, d->K, &why))
+    return fail(MPB_E_SHAPE, std::string("mpb_init: ") + why);
   const int nb = 2 * (d->E + d->S);
   for (int i = 0; i < nb; ++i)
     if (q_init_host[i] < 3 || q_init_host[i] > 8)

@@ -79,4 +79,10 @@ hipError_t launch_down(const FfnParams& p, int qmax, hipStream_t s);
 hipError_t launch_combine(const FfnParams& p, hipStream_t s);
 hipError_t launch_set_q(int32_t* q, int i, int b, hipStream_t s);
 
+// Records msg as the calling thread's last error and returns code.
+int set_error(int code, const char* msg);
+// Checks a layer geometry against the ranges the library supports; on failure
+// returns false and points *why at a message.
+bool geometry_ok(int H, int I, int E, int S, int K, const char** why);
+
 }  // namespace mpb

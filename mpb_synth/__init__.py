@@ -59,7 +59,7 @@ CONFIGS = {
 LUT_STD = 0.02  # centroid draws ~ N(0, 0.02)
 
 # SeedSequence stream ids
-_S_TOKENS, _S_ROUTER, _S_BIAS, _S_Q, _S_HOT, _S_SENS = 1, 2, 3, 4, 5, 6
+_S_TOKENS, _S_ROUTER, _S_BIAS, _S_Q, _S_HOT, _S_SENS, _S_PLAN = 1, 2, 3, 4, 5, 6, 7
 _S_BLOCK = 100
 
 
@@ -228,3 +228,32 @@ def make_sensitivity(cfg_id: int, n_blocks: int, seed=None) -> np.ndarray:
     for j, b in enumerate(range(7, 2, -1)):
         s[:, b] = s[:, b + 1] + d[:, j]
     return s
+
+
+def make_planner_inputs(cfg_id: int, n_blocks: int, F_blk: int, seed=None, P_blk: int = 0):
+    """Synthetic planner observations and calibration results (stand-ins for
+    the offline tables and runtime signals of §3.2).
+
+    Returns (P, phi): P holds three routing buckets (hot 20% / next 30% / the
+    rest with damage multipliers 4 / 2 / 1 and floors 5 / 4 / 3 bits), four
+    bitwidth-floor stages 6, 5, 4, 3, prompt-residual heads with N(0, 0.3)
+    weights and offsets and U(0.5, 1) confidences, alpha = 0.5, clip range
+    [-1, 1], eps = 1e-12, a free-block threshold of 64 blocks, the given free
+    and pending block counts, and a KV block of 16 tokens (K and V, fp16, H
+    wide); phi [n_blocks][3] holds positive routed-input features (mean norm,
+    RMS norm >= mean, max norm >= RMS) around 1.
+    """
+    c = layer_config(cfg_id)
+    seed = c["token_seed"] if seed is None else seed
+    g = _rng(seed, _S_PLAN)
+    P = {"bucket_frac": [0.2, 0.5, 1.0], "mu": [4.0, 2.0, 1.0], "floor": [5, 4, 3],
+         "stage_floor": [6, 5, 4, 3], "eps": 1e-12, "alpha": 0.5, "rho_min": -1.0, "rho_max": 1.0,
+         "head_w": g.normal(0.0, 0.3, size=(2, 5, 3)).tolist(),
+         "head_a": g.normal(0.0, 0.3, size=(2, 5)).tolist(),
+         "head_c": g.uniform(0.5, 1.0, size=(2, 5)).tolist(),
+         "T_blk": 64, "F_blk": int(F_blk), "P_blk": int(P_blk), "B_kv": 16 * 2 * c["H"] * 2}
+    mean = g.uniform(0.8, 1.2, size=n_blocks)
+    rms = mean * g.uniform(1.0, 1.2, size=n_blocks)
+    mx = rms * g.uniform(1.2, 2.0, size=n_blocks)
+    phi = np.stack([mean, rms, mx], axis=1)
+    return P, phi

@@ -305,6 +305,142 @@ def greedy_reductions(layer, s: np.ndarray, frac: float, floor_hot: int = 5, eps
     return [(i, b2) for _, i, b2 in take], max(0, want - len(take))
 
 
+# ----------------------------------------------------------------- planner step (Alg. 1)
+# Readings where [PW §3.2] leaves a step open (listed in the design doc):
+# * a step is a one-bit reduction b -> b-1 of one routed linear-block; a
+#   block's steps are taken in order, so only its next step is available;
+# * GreedySelect repeatedly takes the available step with the least predicted
+#   damage per released byte (ties to the lower block index) until the
+#   released bytes reach D;
+# * the bitwidth-floor stages are global floors, highest first; a block's
+#   floor in stage s is the larger of the stage floor and its bucket's floor;
+#   relaxing the depth cap means moving to the next stage;
+# * RefreshPlanQueue keeps the newest plan of each stage; SelectBestPlan takes
+#   the first stage whose plan meets D, else the plan that releases the most
+#   bytes (the largest safe reduction), ties to the earlier stage;
+# * PressureTriggered means the current free-block count is at or below the
+#   threshold; D uses the free count after the pending KV growth;
+# * routing buckets split the experts, sorted by routing mass (descending,
+#   ties to the lower expert index), at ceil(frac * E) boundaries;
+# * only routed blocks whose pages may move are candidates; shared experts'
+#   blocks never change.
+
+
+def kv_target_bytes(T_blk: int, F_blk: int, B_kv: int) -> int:
+    """D = max{0, T_blk + 1 - F_blk} * B_KV [PW §3.2, Eq. 7]."""
+    return max(0, T_blk + 1 - F_blk) * B_kv
+
+
+def prompt_residual(w, a: float, phi) -> float:
+    """rho^ = w . phi + a, summed left to right [PW §3.2, Eq. 5]."""
+    acc = 0.0
+    for wj, pj in zip(w, phi):
+        acc = acc + wj * pj
+    return acc + a
+
+
+def residual_multiplier(rho_hat: float, alpha: float, c: float, rho_min: float, rho_max: float) -> float:
+    """eta = exp(alpha c clip(rho^, rho_min, rho_max)) [PW §3.2, Eq. 6]."""
+    clipped = min(max(rho_hat, rho_min), rho_max)
+    return math.exp(alpha * c * clipped)
+
+
+def routing_buckets(mass: np.ndarray, fracs) -> np.ndarray:
+    """Bucket of every expert [PW §3.2 'Routing statistics']: experts sorted by
+    routing mass (hottest first, ties to the lower index); bucket k holds the
+    ranks from ceil(fracs[k-1] E) up to ceil(fracs[k] E)."""
+    E = len(mass)
+    order = sorted(range(E), key=lambda e: (-mass[e], e))
+    bucket = np.zeros(E, dtype=np.int64)
+    lo = 0
+    for k, f in enumerate(fracs):
+        hi = min(E, math.ceil(f * E))
+        for rank in range(lo, hi):
+            bucket[order[rank]] = k
+        lo = max(lo, hi)
+    return bucket
+
+
+def _step_damage(P, s, phi, i, b, bucket_mu):
+    """d^ of the one-bit step (i, b -> b-1): Eq. 4, 5, 6 and 8."""
+    u = i % 2
+    t = b - 4                    # transition b -> b-1, b = 4..8
+    g = max(s[i][b - 1] - s[i][b], 0.0)                                   # Eq. 4
+    rho = prompt_residual(P["head_w"][u][t], P["head_a"][u][t], phi[i])  # Eq. 5
+    eta = residual_multiplier(rho, P["alpha"], P["head_c"][u][t], P["rho_min"], P["rho_max"])  # Eq. 6
+    return max(P["eps"], bucket_mu * g * eta)                              # Eq. 8
+
+
+def plan_step(H, I, E, S, q, movable, s, mass, phi, P):
+    """One planner step [PW §3.2, Algorithm 1] on a layer with E routed and S
+    shared experts (block 2e+u: gate_up [2I][H] for u = 0, down [H][I]).
+
+    q: committed bitwidths; movable: per block, whether its pages may move now
+    (None = all); s: [n_blocks][9] sensitivity s_i^b (columns 3..8); mass: [E]
+    routing mass (Eq. 1); phi: [n_blocks][3] routed-input features; P: the
+    planner's parameters (buckets, stages, heads, Eq. 6 and 7 constants).
+    Returns (plan, summary, queue): plan = [(i, q_i, d_i, Delta_i, damage)]
+    when pressure is triggered (else []), queue = {stage: desired bitwidths}.
+    """
+    nb = 2 * (E + S)
+
+    def shape(i):
+        return (2 * I, H) if i % 2 == 0 else (H, I)
+
+    D = kv_target_bytes(P["T_blk"], P["F_blk"] - P["P_blk"], P["B_kv"])   # line 4
+    bucket = routing_buckets(mass, P["bucket_frac"])
+    queue, stats = {}, []
+    for st, sfloor in enumerate(P["stage_floor"]):                         # lines 5-9
+        # ScoreActions: floors of this stage; every step is scored lazily below
+        cur = [int(x) for x in q]
+        floor = [None] * nb
+        for i in range(2 * E):
+            if movable is None or movable[i]:
+                floor[i] = max(sfloor, P["floor"][bucket[i // 2]])
+        released, damage = 0, 0.0
+        step_dmg = [0.0] * nb
+        while released < D:                                                # GreedySelect
+            best = None
+            for i in range(2 * E):
+                if floor[i] is None or cur[i] <= floor[i]:
+                    continue
+                N, Kd = shape(i)
+                delta = block_bytes(N, Kd, cur[i]) - block_bytes(N, Kd, cur[i] - 1)
+                d = _step_damage(P, s, phi, i, cur[i], P["mu"][bucket[i // 2]])
+                ratio = d / delta
+                if best is None or ratio < best[0]:
+                    best = (ratio, i, delta, d)
+            if best is None:
+                break
+            _, i, delta, d = best
+            cur[i] -= 1
+            released += delta
+            damage += d
+            step_dmg[i] += d
+        queue[st] = cur                                                    # RefreshPlanQueue
+        stats.append((released, damage, step_dmg))
+    triggered = P["F_blk"] <= P["T_blk"]                                   # line 10
+    pick = None
+    for st in range(len(P["stage_floor"])):                                # SelectBestPlan
+        if stats[st][0] >= D:
+            pick = st
+            break
+    if pick is None:
+        pick = max(range(len(stats)), key=lambda st: (stats[st][0], -st))
+    plan = []
+    if triggered:
+        d_bits, step_dmg = queue[pick], stats[pick][2]
+        for i in range(nb):
+            if d_bits[i] != q[i]:
+                N, Kd = shape(i)
+                plan.append((i, int(q[i]), d_bits[i], block_bytes(N, Kd, int(q[i])) - block_bytes(N, Kd, d_bits[i]),
+                             step_dmg[i]))
+    summary = {"D": D, "triggered": triggered, "stage": pick if triggered else -1,
+               "released": sum(e[3] for e in plan), "damage": sum(e[4] for e in plan),
+               "stage_released": [x[0] for x in stats], "stage_damage": [x[1] for x in stats]}
+    return plan, summary, queue
+
+
 # ----------------------------------------------------------------- scalar loops
 def unpack_index_scalar(planes, n: int, k: int, b: int) -> int:
     """O1 for one element, in plain Python integers."""

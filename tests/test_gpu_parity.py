@@ -381,6 +381,54 @@ def test_ffn_prefill_sampled(layer_cache):
 
 
 # ---------------------------------------------------------------- bitwidth sweep
+def test_planner_drives_commits_and_offloads(layer_cache):
+    """The planner step (PagedWeight §3.2, Algorithm 1) fed with the routing
+    mass the GPU computes for this batch (Eq. 1) selects a plan; applying it
+    (lower q_i, then offload the pages above it, §3.3) releases exactly the
+    planned bytes, and the layer at the planned bitwidths matches the oracle."""
+    L, D = dev_layer(layer_cache, 1)
+    Xb = S.make_tokens(1)
+    X, z, r = oracle_route(L, Xb)
+    Xd = to_dev_x(Xb)
+    T = Xb.shape[0]
+    idx, w = D.alloc_route(T)
+    out, ws = D.alloc_ffn(T)
+    D.route(Xd, "f16", idx, w)
+    mass = torch.empty(L.E, dtype=torch.float64, device="cuda")
+    M().moe_routing_mass(idx, w, L.E, mass)
+    torch.cuda.synchronize()
+    m = mass.cpu().numpy()
+    sens = S.make_sensitivity(1, L.n_blocks)
+    P, phi = S.make_planner_inputs(1, L.n_blocks, 20)
+    plan, summ, _ = M().mpb_plan_step(L.H, L.I, L.E, L.S, L.K, L.q, None, sens[:, 3:9], m, phi, P)
+    oplan, osumm, _ = O.plan_step(L.H, L.I, L.E, L.S, L.q, None, sens, m, phi, P)
+    assert plan == oplan and summ == osumm
+    assert summ["triggered"] and summ["released"] >= summ["D"] > 0 and plan
+    say(f"  plan: stage {summ['stage']}, {len(plan)} blocks, {summ['released'] / 1e6:.2f} MB "
+        f"for a target of {summ['D'] / 1e6:.2f} MB")
+    before = M().mpb_committed_bytes()
+    cs = torch.cuda.Stream()
+    host = {}
+    q = L.q.copy()
+    for i, frm, to, delta, _ in plan:
+        M().set_committed_bits(i, to)
+        q[i] = to
+        hp = [None] * to + [torch.empty(D.pages[i][p].shape, dtype=D.pages[i][p].dtype, pin_memory=True)
+                            for p in range(to, 8)]
+        ht = [None] * (to - 2) + [torch.empty(D.luts[i][t].shape, dtype=D.luts[i][t].dtype, pin_memory=True)
+                                  for t in range(to - 2, 6)]
+        host[i] = (hp, ht)
+        M().mpb_offload_pages(i, to, hp, D.pages[i], ht, D.luts[i], cs)
+    assert before - M().mpb_committed_bytes() == summ["released"]
+    D.ffn(Xd, "f16", idx, w, out, ws)
+    cs.synchronize()
+    torch.cuda.synchronize()
+    assert_close(out.cpu().numpy(), O.moe_ffn(X, z, r, L, q=q), "at the planned bitwidths")
+    for i, frm, to, delta, _ in plan:
+        assert M().mpb_get_resident_planes(i) == to
+        assert M().mpb_page_state(i, 7) == M().MPB_PAGE_CPU
+
+
 def test_bitwidth_sweep_states(layer_cache):
     L, D = dev_layer(layer_cache, 1)   # the config-4 layer is the config-1 layer
     Xb = S.make_tokens(4)

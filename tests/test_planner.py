@@ -1,0 +1,243 @@
+"""Planner step (PagedWeight §3.2, Algorithm 1, Eqs. 3-8).
+
+The oracle's planner is pinned to closed forms of the equations, to library
+routines, to the synthetic hot bucket, and to an independent formulation of
+the greedy (a global sort of all steps) on instances where the two must agree;
+then the native planner (libmpb, host code) must reproduce the oracle's plan,
+queue and summary bit for bit. No GPU is needed.
+"""
+import math
+
+import numpy as np
+import pytest
+
+import mpb_synth as S
+import oracle as O
+
+
+def params(**kw):
+    P, _ = S.make_planner_inputs(1, 4, 64)
+    P.update(kw)
+    return P
+
+
+# ---------------------------------------------------------------- equation pins
+def test_eq7_kv_target_closed_form():
+    B = 131072
+    assert O.kv_target_bytes(64, 65, B) == 0          # one block above the threshold: no pressure
+    assert O.kv_target_bytes(64, 64, B) == B          # at the threshold: one block (the +1)
+    assert O.kv_target_bytes(64, 0, B) == 65 * B
+    assert O.kv_target_bytes(0, 1000, B) == 0
+
+
+def test_eq5_eq6_against_library_and_special_cases():
+    rng = np.random.default_rng(5)
+    for _ in range(50):
+        w, phi, a = rng.normal(size=3), rng.uniform(0, 3, size=3), rng.normal()
+        assert math.isclose(O.prompt_residual(w, a, phi), float(np.dot(w, phi)) + a, rel_tol=1e-14, abs_tol=1e-14)
+    assert O.residual_multiplier(0.7, 0.0, 0.9, -1, 1) == 1.0      # alpha = 0: no correction
+    assert O.residual_multiplier(0.7, 0.5, 0.0, -1, 1) == 1.0      # zero confidence
+    assert O.residual_multiplier(5.0, 0.5, 1.0, -1, 1) == math.exp(0.5)    # clipped at rho_max
+    assert O.residual_multiplier(-5.0, 2.0, 0.5, -1, 1) == math.exp(-1.0)  # clipped at rho_min
+    assert O.residual_multiplier(0.2, 1.0, 1.0, -1, 1) > 1.0 > O.residual_multiplier(-0.2, 1.0, 1.0, -1, 1)
+
+
+def test_eq4_eq8_clamps():
+    s = np.zeros((1, 9))
+    s[0, 5], s[0, 4] = 2.0, 1.0        # non-monotone: lowering 5 -> 4 "improves" the score
+    assert O.global_damage(s, 0, 5, 4) == 0.0
+    assert O.predicted_damage(0.0, eps=1e-12) == 1e-12
+    assert O.predicted_damage(3.0, mu=2.0, eta=0.5) == 3.0
+
+
+def test_buckets_reproduce_the_synthetic_hot_set():
+    """Config 1's hot experts are the top 20% of a Zipf(1.1) mass over a seeded
+    permutation; bucketing that mass must give exactly that set."""
+    L = S.make_layer(1, blocks=[])
+    c = S.layer_config(1)
+    order = S.zipf_order(c["seed"], S._S_HOT, L.E)
+    mass = np.empty(L.E)
+    mass[order] = np.arange(1, L.E + 1, dtype=np.float64) ** -1.1
+    mass /= mass.sum()
+    b = O.routing_buckets(mass, [0.2, 1.0])
+    assert np.array_equal(b == 0, L.hot)
+    b3 = O.routing_buckets(mass, [0.2, 0.5, 1.0])
+    assert (b3 == 0).sum() == 12 and (b3 == 1).sum() == 18 and (b3 == 2).sum() == 30
+    # ties go to the lower expert index
+    assert O.routing_buckets(np.full(5, 0.2), [0.4, 1.0]).tolist() == [0, 0, 1, 1, 1]
+
+
+def _tiny(E=3, q=(8, 7, 6, 8, 5, 6), convex=True, seed=0):
+    """A tiny layer with per-step damages chosen so each block's step ratio
+    grows as it goes deeper (convex chains) when convex is set."""
+    rng = np.random.default_rng(seed)
+    nb = 2 * E
+    s = np.zeros((nb, 9))
+    for i in range(nb):
+        for b in range(8, 3, -1):
+            inc = rng.uniform(0.5, 1.5) * (10.0 ** (8 - b) if convex else rng.uniform(0.1, 10))
+            s[i, b - 1] = s[i, b] + inc
+    return np.array(q[:nb], np.int32), s
+
+
+def _sorted_steps_plan(H, I, E, q, s, floor, D):
+    """Independent formulation of the greedy for convex chains: list every
+    step of every block, sort by damage per released byte, take the shortest
+    prefix that reaches D."""
+    steps = []
+    for i in range(2 * E):
+        N, Kd = (2 * I, H) if i % 2 == 0 else (H, I)
+        for b in range(int(q[i]), floor, -1):
+            delta = O.block_bytes(N, Kd, b) - O.block_bytes(N, Kd, b - 1)
+            steps.append(((s[i, b - 1] - s[i, b]) / delta, i, b, delta))
+    steps.sort(key=lambda x: (x[0], x[1], -x[2]))
+    d = [int(x) for x in q]
+    got = 0
+    for _, i, b, delta in steps:
+        if got >= D:
+            break
+        assert d[i] == b, "a deeper step sorted before a shallower one: not a convex instance"
+        d[i] = b - 1
+        got += delta
+    return d, got
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_greedy_equals_global_sort_on_convex_chains(seed):
+    H, I, E = 64, 64, 3
+    q, s = _tiny(E, seed=seed)
+    for F in (64, 40, 10, 0):
+        P = params(bucket_frac=[1.0], mu=[1.0], floor=[3], stage_floor=[3], alpha=0.0, F_blk=F, B_kv=4096)
+        plan, summ, queue = O.plan_step(H, I, E, 0, q, None, s, np.full(E, 1.0 / E), np.ones((2 * E, 3)), P)
+        d, got = _sorted_steps_plan(H, I, E, q, s, 3, summ["D"])
+        assert queue[0] == d
+        assert summ["stage_released"][0] == got
+        assert summ["released"] == got
+
+
+def test_greedy_stops_as_soon_as_the_target_is_met():
+    H, I, E = 64, 64, 3
+    q, s = _tiny(E, convex=False, seed=3)
+    P = params(bucket_frac=[1.0], mu=[1.0], floor=[3], stage_floor=[3], alpha=0.0, F_blk=30, B_kv=4096)
+    plan, summ, queue = O.plan_step(H, I, E, 0, q, None, s, np.full(E, 1.0 / E), np.ones((2 * E, 3)), P)
+    D = summ["D"]
+    assert summ["released"] >= D
+    # the greedy takes no step once D is met: undoing its last step (the
+    # deepest step of some block) falls below D
+    drops = []
+    for i, frm, to, delta, _ in plan:
+        N, Kd = (2 * I, H) if i % 2 == 0 else (H, I)
+        drops.append(summ["released"] - (O.block_bytes(N, Kd, to + 1) - O.block_bytes(N, Kd, to)))
+    assert min(drops) < D
+
+
+def test_fallback_is_the_largest_safe_reduction():
+    """When no stage reaches D, the selected plan takes every legal step of the
+    most relaxed stage: a closed form over the blocks' floors."""
+    L = S.make_layer(1, blocks=[])
+    s = S.make_sensitivity(1, L.n_blocks)
+    mass = np.random.default_rng(1).dirichlet(np.ones(L.E))
+    P, phi = S.make_planner_inputs(1, L.n_blocks, 0, P_blk=10 ** 6)
+    plan, summ, _ = O.plan_step(L.H, L.I, L.E, L.S, L.q, None, s, mass, phi, P)
+    bucket = O.routing_buckets(mass, P["bucket_frac"])
+    expect = 0
+    for i in range(2 * L.E):
+        fl = max(P["stage_floor"][-1], P["floor"][bucket[i // 2]])
+        if L.q[i] > fl:
+            expect += O.block_bytes(*L.shape(i), int(L.q[i])) - O.block_bytes(*L.shape(i), fl)
+    assert summ["stage"] == len(P["stage_floor"]) - 1
+    assert summ["released"] == expect < summ["D"]
+    assert all(i < 2 * L.E for i, *_ in plan)          # shared experts never change
+
+
+def test_select_prefers_the_tightest_stage_that_meets_d():
+    L = S.make_layer(1, blocks=[])
+    s = S.make_sensitivity(1, L.n_blocks)
+    mass = np.random.default_rng(2).dirichlet(np.ones(L.E))
+    for F in (64, 30, 0):
+        P, phi = S.make_planner_inputs(1, L.n_blocks, F)
+        plan, summ, queue = O.plan_step(L.H, L.I, L.E, L.S, L.q, None, s, mass, phi, P)
+        st = summ["stage"]
+        assert summ["stage_released"][st] >= summ["D"]
+        assert all(r < summ["D"] for r in summ["stage_released"][:st])
+        bucket = O.routing_buckets(mass, P["bucket_frac"])
+        for i, frm, to, delta, dmg in plan:     # floors of the selected stage hold
+            assert to >= max(P["stage_floor"][st], P["floor"][bucket[i // 2]])
+            assert to == queue[st][i] and frm == L.q[i]
+
+
+def test_no_pressure_no_plan():
+    L = S.make_layer(1, blocks=[])
+    P, phi = S.make_planner_inputs(1, L.n_blocks, 65)
+    plan, summ, _ = O.plan_step(L.H, L.I, L.E, L.S, L.q, None, S.make_sensitivity(1, L.n_blocks),
+                                np.full(L.E, 1.0 / L.E), phi, P)
+    assert plan == [] and summ["D"] == 0 and not summ["triggered"] and summ["stage"] == -1
+
+
+# ---------------------------------------------------------------- native planner vs oracle
+def _cases():
+    for cfg in (0, 1, 3):
+        for F in (65, 64, 40, 0):
+            for mv in (None, "half"):
+                yield cfg, F, mv
+
+
+@pytest.mark.parametrize("cfg,F,mv", list(_cases()))
+def test_native_planner_matches_oracle(cfg, F, mv):
+    from mixed_precision_bit_amd import _lib as M
+    L = S.make_layer(cfg, blocks=[])
+    rng = np.random.default_rng(cfg * 100 + F)
+    s = S.make_sensitivity(cfg, L.n_blocks)
+    s[:, 3:9] += rng.normal(0, 0.3, size=(L.n_blocks, 6))   # non-monotone scores exercise Eq. 4's clamp
+    mass = rng.dirichlet(np.ones(L.E) * 0.5)
+    mass[: L.E // 4] = mass[L.E // 4]                      # exact ties in routing mass
+    movable = None if mv is None else (rng.uniform(size=L.n_blocks) < 0.5)
+    P, phi = S.make_planner_inputs(cfg, L.n_blocks, F, P_blk=3 if F == 40 else 0)
+    plan, summ, queue = O.plan_step(L.H, L.I, L.E, L.S, L.q, movable, s, mass, phi, P)
+    plan2, summ2, queue2 = M.mpb_plan_step(L.H, L.I, L.E, L.S, L.K, L.q, movable, s[:, 3:9], mass, phi, P)
+    assert plan2 == plan
+    assert summ2 == summ
+    assert np.array_equal(queue2, np.array([queue[k] for k in range(len(P["stage_floor"]))]))
+
+
+def test_native_planner_ties_between_identical_blocks():
+    """Blocks with identical inputs give identical ratios: ties go to the lower
+    index. With eta = 1 the gate_up blocks ([128][128], larger Delta) are the
+    cheapest per byte; one step's worth of D takes block 0, two steps' worth
+    takes blocks 0 and 2 (block 0's second step releases fewer bytes)."""
+    from mixed_precision_bit_amd import _lib as M
+    H, I, E = 128, 64, 4
+    nb = 2 * E
+    q = np.full(nb, 8, np.int32)
+    s = np.zeros((nb, 9))
+    for b in range(7, 2, -1):
+        s[:, b] = s[:, b + 1] + 1.0
+    phi = np.ones((nb, 3))
+    for F, want in ((64, [0]), (63, [0, 2])):
+        P = params(bucket_frac=[1.0], mu=[1.0], floor=[3], stage_floor=[3], alpha=0.0, F_blk=F, B_kv=20000)
+        plan, summ, queue = O.plan_step(H, I, E, 0, q, None, s, np.full(E, 0.25), phi, P)
+        plan2, summ2, queue2 = M.mpb_plan_step(H, I, E, 0, 1, q, None, s[:, 3:9], np.full(E, 0.25), phi, P)
+        assert plan2 == plan and summ2 == summ
+        assert [e[0] for e in plan] == want and all(e[2] == 7 for e in plan)
+
+
+def test_native_planner_validation():
+    from mixed_precision_bit_amd import _lib as M
+    L = S.make_layer(0, blocks=[])
+    s = S.make_sensitivity(0, L.n_blocks)[:, 3:9]
+    P, phi = S.make_planner_inputs(0, L.n_blocks, 10)
+    mass = np.full(L.E, 1.0 / L.E)
+    for bad, code in ((dict(stage_floor=[5, 6]), -1), (dict(bucket_frac=[0.5, 0.9]), -1), (dict(eps=0.0), -1),
+                      (dict(floor=[9]), -1), (dict(rho_min=1.0, rho_max=0.0), -1)):
+        P2 = dict(P)
+        P2.update(bad)
+        if "floor" in bad:
+            P2.update(bucket_frac=[1.0], mu=[1.0])
+        with pytest.raises(M.MpbError) as ei:
+            M.mpb_plan_step(L.H, L.I, L.E, L.S, L.K, L.q, None, s, mass, phi, P2)
+        assert ei.value.code == code, bad
+    q = L.q.copy()
+    q[0] = 2
+    with pytest.raises(M.MpbError) as ei:
+        M.mpb_plan_step(L.H, L.I, L.E, L.S, L.K, q, None, s, mass, phi, P)
+    assert ei.value.code == -3
