@@ -196,6 +196,8 @@ def main():
                     help="only time a plain device-to-device copy of this many bytes (counter calibration)")
     ap.add_argument("--no-graph", dest="graph", action="store_false",
                     help="launch the timed steps eagerly instead of replaying them as one HIP graph")
+    ap.add_argument("--fused", action="store_true",
+                    help="also time the same steps as one fused launch per step (moe_fused)")
     ap.add_argument("--plan", action="store_true",
                     help="also time the routing-mass kernel and the host planner step on this batch")
     ap.add_argument("--page-movement", action="store_true",
@@ -342,6 +344,36 @@ def main():
                       "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(gu_gbs / HBM_PEAK_GBS, 4),
                       "traffic": traffic, "algorithmic_bytes_per_launch": int(gu_bytes)}),
     }
+    if args.fused:
+        fb = [D.alloc_fused(T) for D in layers]
+
+        def fstep(k):
+            D = layers[k % R]
+            idx, w = bufs[k % R][0], bufs[k % R][1]
+            out, ws = fb[k % R]
+            D.fused(X, xdt, idx, w, out, ws)
+
+        for k in range(args.warmup):
+            fstep(k)
+        torch.cuda.synchronize()
+        cap = torch.cuda.Stream()
+        cap.wait_stream(stream)
+        fg = torch.cuda.CUDAGraph()
+        with torch.cuda.stream(cap):
+            with torch.cuda.graph(fg, stream=cap):
+                for k in range(args.steps):
+                    fstep(args.warmup + k)
+        stream.wait_stream(cap)
+        fg.replay()
+        torch.cuda.synchronize()
+        f0, f1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        f0.record(stream)
+        fg.replay()
+        f1.record(stream)
+        torch.cuda.synchronize()
+        fms = f0.elapsed_time(f1) / args.steps
+        res["fused"] = {"ms_per_step": round(fms, 5), "tokens_per_s": round(T / (fms * 1e-3), 1),
+                        "launches_per_step": 1, "vs_separate": round(ms / fms, 4)}
     if args.plan:
         res["planner"] = planner_timing(torch, M, L, cfg, bufs[0][0], bufs[0][1], args.steps)
     if args.page_movement and args.graph:

@@ -186,6 +186,33 @@ int moe_ffn(const void* X_dev, int x_dtype, int T, const int32_t* topk_idx_dev,
             size_t ws_bytes, void* stream);
 
 /*
+ * The whole layer in one launch (§3.3: routing, expert activation, down
+ * projection and output accumulation in one fused kernel): moe_route followed
+ * by moe_ffn, as one persistent kernel whose workgroups take units of work in
+ * a fixed order (router logits, top-K, grouping, gate_up tiles, down tiles,
+ * combine) and wait on device counters for the units they read from; a down
+ * tile starts as soon as its own group's gate_up tiles are done. Results are
+ * bit-identical to moe_route + moe_ffn on the same inputs (same arithmetic,
+ * same order). Arguments as for those two calls; topk_idx_dev / topk_w_dev
+ * receive the routing. ws_dev: at least moe_fused_workspace_bytes(T) bytes,
+ * 256-byte aligned; its first moe_fused_counter_bytes() bytes are counters
+ * that must be zero before the first call with this workspace (allocate it
+ * zero-filled); every call leaves them zero again, so the workspace can be
+ * reused, also by graph replays.
+ * Calls sharing a workspace must not overlap. Every device-side wait is
+ * bounded: a wait that runs out (only possible if the counters were not zero)
+ * makes out NaN. Gate_up takes 32-token items (the decode configuration) for
+ * every T. Errors: as moe_route and moe_ffn, plus MPB_E_ARG for a misaligned
+ * workspace.
+ */
+size_t moe_fused_counter_bytes(void);
+size_t moe_fused_workspace_bytes(int T);
+int moe_fused(const void* X_dev, int x_dtype, int T, const float* W_router_dev, const float* bias_dev,
+              int32_t* topk_idx_dev, float* topk_w_dev, const uint32_t* const* planes_dev,
+              const uint16_t* const* luts_dev, const int32_t* q_dev, float* out_dev, void* ws_dev,
+              size_t ws_bytes, void* stream);
+
+/*
  * Commit bitwidth b for linear-block i (§3.1 and §3.3: the planner lowers or
  * raises q_i at a safe boundary; a reload raises q_i only once its pages are
  * GPU-resident). Validates 0 <= i < 2*(E+S), b in 3..8 and that planes 0..b-1

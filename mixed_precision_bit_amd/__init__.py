@@ -4,7 +4,7 @@ The compute path is libmpb.so (HIP kernels for gfx950 behind the C ABI in
 include/mpb.h); this package holds its build script and a thin ctypes binding.
 """
 from . import _lib  # noqa: F401
-from ._lib import (MPB_BF16, MPB_F16, MPB_PAGE_CPU, MPB_PAGE_GPU, MPB_PAGE_IN_TRANSFER, MpbError, moe_ffn, moe_ffn_workspace_bytes, moe_route,  # noqa: F401
+from ._lib import (MPB_BF16, MPB_F16, moe_fused, moe_fused_workspace_bytes, MPB_PAGE_CPU, MPB_PAGE_GPU, MPB_PAGE_IN_TRANSFER, MpbError, moe_ffn, moe_ffn_workspace_bytes, moe_route,  # noqa: F401
                    moe_route_workspace_bytes, moe_routing_mass,
                    mpb_committed_bytes, mpb_dequant_block, mpb_get_committed_bits, mpb_init,
                    mpb_last_error, mpb_pack_block, mpb_pack_table, mpb_plane_page_bytes,

@@ -70,6 +70,9 @@ def lib() -> ctypes.CDLL:
             "moe_route_workspace_bytes": (_SZ, [_I, _I]),
             "moe_routing_mass": (_I, [_P, _P, _I, _I, _I, _P, _P]),
             "moe_ffn_workspace_bytes": (ctypes.c_size_t, [_I]),
+            "moe_fused_workspace_bytes": (ctypes.c_size_t, [_I]),
+            "moe_fused_counter_bytes": (ctypes.c_size_t, []),
+            "moe_fused": (_I, [_P, _I, _I, _P, _P, _P, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P]),
             "moe_ffn": (_I, [_P, _I, _I, _P, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P]),
             "set_committed_bits": (_I, [_I, _I]),
             "mpb_committed_bytes": (ctypes.c_int64, [_P]),
@@ -164,6 +167,22 @@ def moe_ffn(X, x_dtype, topk_idx, topk_w, planes_table, luts_table, q, out, ws, 
     return _check("moe_ffn", lib().moe_ffn(_ptr(X), x_dtype, T, _ptr(topk_idx), _ptr(topk_w),
                                            _ptr(planes_table), _ptr(luts_table), _ptr(q), _ptr(out),
                                            _ptr(ws), nbytes, _stream(stream)))
+
+
+def moe_fused_counter_bytes() -> int:
+    return lib().moe_fused_counter_bytes()
+
+
+def moe_fused_workspace_bytes(T) -> int:
+    return lib().moe_fused_workspace_bytes(T)
+
+
+def moe_fused(X, x_dtype, W_router, bias, topk_idx, topk_w, planes_table, luts_table, q, out, ws, stream=None):
+    T = X.shape[0]
+    nbytes = ws.numel() * ws.element_size()
+    return _check("moe_fused", lib().moe_fused(_ptr(X), x_dtype, T, _ptr(W_router), _ptr(bias), _ptr(topk_idx),
+                                               _ptr(topk_w), _ptr(planes_table), _ptr(luts_table), _ptr(q),
+                                               _ptr(out), _ptr(ws), nbytes, _stream(stream)))
 
 
 def set_committed_bits(i, b):

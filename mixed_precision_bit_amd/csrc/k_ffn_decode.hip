@@ -1,299 +1,10 @@
-// Decode-size expert FFN: gate_up + SwiGLU, down, and the weighted combine.
-//
-// "PagedWeight", §3.3: the fused kernel reads the weight pages directly and
-// follows the committed bitwidth of every gate_up and down block. Here each
-// workgroup reads its block's q_i once from the device page table and runs the
-// matching instantiation, so a launch mixes bitwidths freely and a change of
-// q_i between launches takes effect on the next launch.
-//
-// Mapping (MFMA 32x32x16 fp16 -> fp32): a workgroup of 8 waves handles up to
-// 32 tokens of one expert and 128 weight rows: wave w owns row group w % 4
-// (32 rows) and K half w / 4, so two waves share every row's centroid table
-// and the table region costs half as much LDS per wave. Lane l holds row l%32;
-// in step s it reads half-chunk 2s + l/32 of its K half (2 words = 64
-// elements) from each of the q plane pages: one 8-byte load per page, the 64
-// lanes of a wave covering one 512-byte chunk of 32 rows, issued three steps
-// ahead. Each word feeds four MFMAs as the A operand.
-//
-// The B operand (the tokens) is staged into LDS by the whole workgroup and read
-// with ds_read_b128: with the weights the only vector memory traffic in the
-// loop, waits on the activations never queue behind the long-latency plane
-// loads (vector-memory completions are counted in issue order).
-//
-// LDS: [centroid tables: 2^qmax * 256 bytes][stage: 2 halves x 32 tokens x
-// 256 bytes]. Piece p (16 bytes) of token t of a half sits at p ^ (t % 16), so
-// the 16 lanes of one ds_read_b128 phase, which read one piece of 16 tokens,
-// hit distinct banks.
+// Decode-size expert FFN kernels: gate_up + SwiGLU, down, and the weighted
+// combine, one launch each (the device code is in k_ffn_body.h).
 #include <algorithm>
 
-#include "mpb_device.h"
-#include "mpb_internal.h"
+#include "k_ffn_body.h"
 
 namespace mpb {
-
-constexpr int kTok = kChunkTokens;  // 32 tokens per MFMA column block
-constexpr int kWaves = 8;
-constexpr int kThreads = 64 * kWaves;
-
-// Stage: [K half][token of the item (32 TC)][16 pieces of 16 bytes]; piece p
-// of token t sits at p ^ (t % 16).
-template <int TC>
-__device__ __forceinline__ uint32_t stage_off(int kh, int t, int piece) {
-  return (uint32_t)kh * (TC * kTok * 256u) + t * 256u + ((piece ^ (t & 15)) << 4);
-}
-template <int TC>
-constexpr int stage_bytes() { return 2 * TC * kTok * 256; }
-
-// Plane loads go through buffer descriptors, one per plane page, based at the
-// wave's 32-row tile and spanning its NC chunks; an offset past the tile
-// (padding half-chunks, prefetches past the end) reads zeros without touching
-// memory.
-typedef __amdgpu_buffer_rsrc_t rsrc_t;
-
-__device__ __forceinline__ rsrc_t tile_rsrc(const void* page, size_t tile_off, uint32_t bytes) {
-  // the operands are wave-uniform; say so, or the compiler wraps every load
-  // in a loop over distinct descriptors
-  const uint64_t a = (uint64_t)((const char*)page + tile_off);
-  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)a);
-  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(a >> 32));
-  const int n = __builtin_amdgcn_readfirstlane((int)bytes);
-  return __builtin_amdgcn_make_buffer_rsrc((void*)(((uint64_t)hi << 32) | lo), (short)0, n, 0x00020000);
-}
-
-// Copy a tile's table image (256 << Q bytes) into LDS at byte 0 with direct
-// global-to-LDS loads: wave w moves 1 KiB pieces w, w + 8, ... (no registers,
-// no LDS store instructions). The caller waits for vector memory and
-// synchronises the workgroup before the first lookup.
-typedef __attribute__((address_space(3))) void lds_void;
-
-template <int Q>
-__device__ __forceinline__ void load_table_image(const uint16_t* img, int w, int lane) {
-  const char* src = (const char*)img + 16 * lane;
-#pragma unroll
-  for (int c = 0; c < (1 << Q) / 4; c += kWaves)
-    if (c + w < (1 << Q) / 4)
-      __builtin_amdgcn_global_load_lds(src + 1024 * (c + w), (lds_void*)(uintptr_t)(1024u * (c + w)), 16, 0, 0);
-}
-
-__device__ __forceinline__ void wait_vmem_all() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
-
-// Half-chunk s of the wave's K half for every plane: lane (r, g) reads the 8
-// bytes at chunk cb + s, row r, half g.
-template <int Q>
-__device__ __forceinline__ void load_planes(uint2 (&P)[Q], const rsrc_t (&rs)[Q], int cb, int s, int voff) {
-#pragma unroll
-  for (int q = 0; q < Q; ++q)
-    P[q] = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(rs[q], (cb + s) * 512 + voff, 0, 0));
-}
-
-template <int Q>
-__device__ __forceinline__ void word_of(const uint2 (&P2)[Q], int j, uint32_t (&P)[Q]) {
-#pragma unroll
-  for (int q = 0; q < Q; ++q) P[q] = j == 0 ? P2[q].x : P2[q].y;
-}
-
-// Activation pieces staged per thread and step (or round): thread tid stages
-// piece p = tid % 16 of token 32 c + tid / 16 of both K halves, c < TC.
-template <int TC>
-struct StagePlan {
-  const uint16_t* row[TC];  // source row start (token slots >= nt load nothing)
-  uint32_t dst[2][TC];      // stage byte offsets per K half
-  bool live[TC];            // token slot < nt
-};
-
-template <int TC>
-__device__ __forceinline__ void load_window(uint4 (&v)[2][TC], const StagePlan<TC>& sp, const int (&k)[2], int len) {
-#pragma unroll
-  for (int i = 0; i < 2; ++i)
-#pragma unroll
-    for (int c = 0; c < TC; ++c)
-      if (sp.live[c] && k[i] < len) v[i][c] = *(const uint4*)(sp.row[c] + k[i]);
-}
-
-template <int TC>
-__device__ __forceinline__ void store_window(char* stage, const uint4 (&v)[2][TC], const StagePlan<TC>& sp,
-                                             const int (&k)[2], int len) {
-#pragma unroll
-  for (int i = 0; i < 2; ++i)
-#pragma unroll
-    for (int c = 0; c < TC; ++c)
-      if (sp.live[c]) *(uint4*)(stage + sp.dst[i][c]) = k[i] < len ? v[i][c] : make_uint4(0u, 0u, 0u, 0u);
-}
-
-// Work item of a launch: workgroup id = item * ntile + tile, so the
-// consecutive workgroups that the dispatcher spreads over the chip carry the
-// tiles of one item and every workgroup below n_items * ntile has tokens.
-__device__ __forceinline__ bool decode_item(const FfnParams& p, bool gu, int ntile, int& e, int& tile, int& t0,
-                                            int& nt) {
-  const int item = blockIdx.x / ntile;
-  tile = blockIdx.x - item * ntile;
-  if (item >= p.n_items[gu ? 0 : 1]) return false;
-  const int v = (gu ? p.items : p.items_dn)[item];
-  const int tpi = gu ? p.tpi : p.tpi_dn;
-  e = v >> 16;
-  t0 = (v & 0xffff) * tpi;
-  nt = min(p.counts[e] - t0, tpi);
-  return true;
-}
-
-// K split: a row has HC = Kd / 64 half-chunks; half 0 takes the first HH (even,
-// >= HC / 2), half 1 the rest, both in NSW = HH / 2 steps of two half-chunks.
-struct KSplit {
-  int HC, HH, NSW;
-  __device__ KSplit(int Kd) : HC(Kd >> 6), HH((((Kd >> 6) + 1) / 2 + 1) & ~1), NSW((((Kd >> 6) + 1) / 2 + 1) / 2) {}
-};
-
-// ---------------------------------------------------------------- gate_up
-// Waves 0/1 take gate rows c0..c0+31 / c0+32..c0+63, waves 2/3 the matching up
-// rows, waves 4..7 the same rows over the second K half. Each dequantised
-// A operand feeds TC MFMAs, one per 32-token chunk of the item. After the K
-// loop the other waves hand their accumulators to waves 0/1 through LDS, which
-// add the halves, apply SiLU(gate) * up and store h as an fp16 (hi, lo) pair
-// (hi + lo carries ~22 significant bits of the fp32 value into the down
-// projection).
-//
-// Issue order per step s (vector memory completes in issue order, so a wait
-// for one load also waits for every older one): compute on the planes of step
-// s, barrier, write the activations of step s+1 (loaded one step earlier) to
-// the stage, load the activations of step s+2, load the planes of step s+3,
-// barrier.
-template <int Q, int TC>
-__device__ __forceinline__ void gate_up_body(const FfnParams& p, int e, int it, int t0, int nt, uint16_t* lds,
-                                             uint32_t lut_bytes) {
-  const int tid = threadIdx.x, lane = tid & 63, r = lane & 31, g = lane >> 5;
-  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: plane descriptors stay scalar
-  const int rg = w & 3, kh = w >> 2;
-  const int I = p.I, H = p.H, NC = (H / 32 + 3) >> 2;
-  const KSplit ks(H);
-  const int c0 = it * 64 + (rg & 1) * 32;
-  const int row0 = (rg >> 1) * I + c0;
-  const int base = p.offsets[e] + t0;
-  const uint32_t slot = lut_slot(r, rg);
-  const int blk = 2 * e;
-  char* stage = (char*)lds + lut_bytes;
-
-  // staging: piece p = 8 g' + 4 j + m of a token holds elements 32 j + 8 m .. + 7
-  // of half-chunk 2 s + g' of the K half
-  StagePlan<TC> sp;
-  const int st = tid >> 4, spc = tid & 15;
-#pragma unroll
-  for (int c = 0; c < TC; ++c) {
-    const int t = kTok * c + st;
-    sp.live[c] = t < nt;
-    sp.row[c] = p.xh + (size_t)p.ptok[base + (sp.live[c] ? t : 0)] * H;
-    sp.dst[0][c] = stage_off<TC>(0, t, spc);
-    sp.dst[1][c] = stage_off<TC>(1, t, spc);
-  }
-  auto kwin = [&](int s, int (&k)[2]) {
-#pragma unroll
-    for (int i = 0; i < 2; ++i) k[i] = (i * ks.HH + 2 * s + (spc >> 3)) * 64 + 8 * (spc & 7);
-  };
-
-  // the descriptor of K half 0 ends where half 1 begins, so the prefetches
-  // past the half read zeros instead of half 1's pages
-  const int cb = kh * (ks.HH >> 1);  // first chunk of the wave's K half
-  const int ce = kh ? NC : ks.HH >> 1;
-  rsrc_t rs[Q];
-#pragma unroll
-  for (int q = 0; q < Q; ++q) rs[q] = tile_rsrc(p.planes[blk * 8 + q], (size_t)(row0 >> 5) * NC * 512, ce * 512);
-  const int voff = 16 * r + 8 * g;
-
-  uint2 PA[Q], PB[Q], PC[Q];
-  uint4 xr[2][TC];
-  int kk[2];
-  load_table_image<Q>(p.luts[blk * 6 + (Q - 3)] + (size_t)it * (128u << Q), w, lane);
-  kwin(0, kk);
-  load_window<TC>(xr, sp, kk, H);
-  load_planes<Q>(PA, rs, cb, 0, voff);
-  wait_vmem_all();
-  store_window<TC>(stage, xr, sp, kk, H);
-  load_planes<Q>(PB, rs, cb, 1, voff);
-  kwin(1, kk);
-  load_window<TC>(xr, sp, kk, H);
-  load_planes<Q>(PC, rs, cb, 2, voff);
-  __syncthreads();
-
-  f32x16 acc[TC];
-#pragma unroll
-  for (int c = 0; c < TC; ++c) acc[c] = (f32x16){};
-  auto step = [&](int s, uint2 (&P)[Q]) {
-#pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      uint32_t Pw[Q], O[8];
-      word_of<Q>(P, j, Pw);
-      assemble<Q>(Pw, O);
-#pragma unroll
-      for (int m = 0; m < 4; ++m) {
-        const f16x8 a = lookup8(O[2 * m], O[2 * m + 1], slot);
-#pragma unroll
-        for (int c = 0; c < TC; ++c) {
-          const f16x8 b = *(const f16x8*)(stage + stage_off<TC>(kh, kTok * c + r, 8 * g + 4 * j + m));
-          acc[c] = mfma32(a, b, acc[c]);
-        }
-      }
-    }
-    __syncthreads();
-    if (s + 1 < ks.NSW) {
-      kwin(s + 1, kk);
-      store_window<TC>(stage, xr, sp, kk, H);
-    }
-    kwin(s + 2, kk);
-    load_window<TC>(xr, sp, kk, H);
-    load_planes<Q>(P, rs, cb, s + 3, voff);
-    __syncthreads();
-  };
-  // whole ring turns in the loop, the remainder after it: the loop's back edge
-  // then always follows a PC step, which keeps the wait counts exact
-  int s = 0;
-  for (; s + 3 <= ks.NSW; s += 3) {
-    step(s, PA);
-    step(s + 1, PB);
-    step(s + 2, PC);
-  }
-  if (s < ks.NSW) step(s, PA);
-  if (s + 1 < ks.NSW) step(s + 1, PB);
-
-  // hand the accumulators to waves 0/1, one token chunk at a time; layout
-  // [wave][v][lane]; gate = own + wave w+4, up = waves w+2 and w+6, each sum in
-  // that order
-  float* xb = (float*)lds;
-#pragma unroll
-  for (int c = 0; c < TC; ++c) {
-    if (c) __syncthreads();  // waves 0/1 are done reading the previous chunk
-    if (w >= 2) {
-#pragma unroll
-      for (int v = 0; v < 16; ++v) xb[(w * 16 + v) * 64 + lane] = acc[c][v];
-    }
-    __syncthreads();
-    const int t = kTok * c + r;
-    if (w < 2 && t < nt) {
-      // acc[c][v] is row 8*(v/4) + 4*g + v%4 of the wave's 32 rows, token t
-      const size_t o = (size_t)(base + t) * I + c0 + 4 * g;
-#pragma unroll
-      for (int v4 = 0; v4 < 4; ++v4) {
-        uint16_t hv[4], lv[4];
-#pragma unroll
-        for (int k = 0; k < 4; ++k) {
-          const int v = 4 * v4 + k;
-          const float gate = acc[c][v] + xb[((w + 4) * 16 + v) * 64 + lane];
-          const float up = xb[((w + 2) * 16 + v) * 64 + lane] + xb[((w + 6) * 16 + v) * 64 + lane];
-          const split16 sp2 = split_hi_lo(silu(gate) * up);
-          hv[k] = __builtin_bit_cast(uint16_t, sp2.hi);
-          lv[k] = __builtin_bit_cast(uint16_t, sp2.lo);
-        }
-        *(ushort4*)(p.hhi + o + 8 * v4) = make_ushort4(hv[0], hv[1], hv[2], hv[3]);
-        *(ushort4*)(p.hlo + o + 8 * v4) = make_ushort4(lv[0], lv[1], lv[2], lv[3]);
-      }
-    }
-  }
-}
-
-// A block whose committed bitwidth is outside 3..qmax (the table region of
-// this launch was sized for qmax), or a table region not at LDS byte 0,
-// produces NaN instead of a silently wrong value.
-__device__ __forceinline__ void poison(float* dst, size_t ld, int rows, int cols) {
-  for (int i = threadIdx.x; i < rows * cols; i += blockDim.x) dst[(size_t)(i / cols) * ld + i % cols] = __builtin_nanf("");
-}
 
 template <int TC>
 __global__ __launch_bounds__(kThreads) void k_gate_up(FfnParams p, int qmax) {
@@ -303,12 +14,12 @@ __global__ __launch_bounds__(kThreads) void k_gate_up(FfnParams p, int qmax) {
   const int q = p.q[2 * e];
   const uint32_t lut_bytes = 256u << qmax;
   switch (q < 3 || q > qmax || !tables_at_zero(lds) ? 0 : q) {
-    case 3: gate_up_body<3, TC>(p, e, it, t0, nt, lds, lut_bytes); break;
-    case 4: gate_up_body<4, TC>(p, e, it, t0, nt, lds, lut_bytes); break;
-    case 5: gate_up_body<5, TC>(p, e, it, t0, nt, lds, lut_bytes); break;
-    case 6: gate_up_body<6, TC>(p, e, it, t0, nt, lds, lut_bytes); break;
-    case 7: gate_up_body<7, TC>(p, e, it, t0, nt, lds, lut_bytes); break;
-    case 8: gate_up_body<8, TC>(p, e, it, t0, nt, lds, lut_bytes); break;
+    case 3: gate_up_body<3, TC>(p, e, it, t0, nt, lds, lut_bytes, threadIdx.x); break;
+    case 4: gate_up_body<4, TC>(p, e, it, t0, nt, lds, lut_bytes, threadIdx.x); break;
+    case 5: gate_up_body<5, TC>(p, e, it, t0, nt, lds, lut_bytes, threadIdx.x); break;
+    case 6: gate_up_body<6, TC>(p, e, it, t0, nt, lds, lut_bytes, threadIdx.x); break;
+    case 7: gate_up_body<7, TC>(p, e, it, t0, nt, lds, lut_bytes, threadIdx.x); break;
+    case 8: gate_up_body<8, TC>(p, e, it, t0, nt, lds, lut_bytes, threadIdx.x); break;
     default: {
       const size_t o = (size_t)(p.offsets[e] + t0) * p.I + it * 64;
       for (int i = threadIdx.x; i < nt * 64; i += blockDim.x) {
@@ -319,140 +30,6 @@ __global__ __launch_bounds__(kThreads) void k_gate_up(FfnParams p, int qmax) {
   }
 }
 
-// ---------------------------------------------------------------- down
-// Waves w and w+4 take output rows n0 + 32 (w % 4) .. +31 over the two K
-// halves. B operand = h as its fp16 hi and lo parts, two MFMAs per word and
-// token chunk into the same fp32 accumulator. A step is staged in two rounds,
-// one per word of the half-chunk; piece p = 8 hl + 4 g' + m of a token holds
-// elements 32 j + 8 m .. + 7 of half-chunk 2 s + g', hi (hl = 0) or lo
-// (hl = 1), for round j. Each window is loaded one step before it is staged,
-// ahead of the plane load that follows it.
-template <int Q, int TC>
-__device__ __forceinline__ void down_body(const FfnParams& p, int e, int it, int t0, int nt, uint16_t* lds,
-                                          uint32_t lut_bytes) {
-  const int tid = threadIdx.x, lane = tid & 63, r = lane & 31, g = lane >> 5;
-  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int rg = w & 3, kh = w >> 2;
-  const int I = p.I, H = p.H, NC = (I / 32 + 3) >> 2;
-  const KSplit ks(I);
-  const int n0 = it * 128 + rg * 32;
-  const bool active = n0 < H;
-  const int base = p.offsets[e] + t0;
-  const uint32_t slot = lut_slot(r, rg);
-  const int blk = 2 * e + 1;
-  char* stage = (char*)lds + lut_bytes;
-
-  StagePlan<TC> sp;
-  const int st = tid >> 4, spc = tid & 15, hl = spc >> 3;
-#pragma unroll
-  for (int c = 0; c < TC; ++c) {
-    const int t = kTok * c + st;
-    sp.live[c] = t < nt;
-    sp.row[c] = (hl ? p.hlo : p.hhi) + (size_t)(base + (sp.live[c] ? t : 0)) * I;
-    sp.dst[0][c] = stage_off<TC>(0, t, spc);
-    sp.dst[1][c] = stage_off<TC>(1, t, spc);
-  }
-  // window (s, j): for K half i, element 64 (i HH + 2 s + g') + 32 j + 8 m
-  auto kwin = [&](int s, int j, int (&k)[2]) {
-#pragma unroll
-    for (int i = 0; i < 2; ++i) k[i] = (i * ks.HH + 2 * s + ((spc >> 2) & 1)) * 64 + 32 * j + 8 * (spc & 3);
-  };
-
-  const int cb = kh * (ks.HH >> 1);
-  const int ce = kh ? NC : ks.HH >> 1;
-  rsrc_t rs[Q];
-#pragma unroll
-  for (int q = 0; q < Q; ++q)
-    rs[q] = tile_rsrc(p.planes[blk * 8 + q], active ? (size_t)(n0 >> 5) * NC * 512 : 0, active ? ce * 512 : 0);
-  const int voff = 16 * r + 8 * g;
-
-  uint2 PA[Q], PB[Q], PC[Q];
-  uint4 ha[2][TC], hb[2][TC];
-  int ka[2], kb[2];
-  load_table_image<Q>(p.luts[blk * 6 + (Q - 3)] + (size_t)it * (128u << Q), w, lane);
-  kwin(0, 0, ka);
-  load_window<TC>(ha, sp, ka, I);
-  load_planes<Q>(PA, rs, cb, 0, voff);
-  wait_vmem_all();
-  store_window<TC>(stage, ha, sp, ka, I);
-  kwin(0, 1, kb);
-  load_window<TC>(hb, sp, kb, I);
-  kwin(1, 0, ka);
-  load_window<TC>(ha, sp, ka, I);
-  load_planes<Q>(PB, rs, cb, 1, voff);
-  load_planes<Q>(PC, rs, cb, 2, voff);
-  __syncthreads();
-
-  f32x16 acc[TC];
-#pragma unroll
-  for (int c = 0; c < TC; ++c) acc[c] = (f32x16){};
-  auto round = [&](int j, const uint2 (&P)[Q]) {
-    uint32_t Pw[Q], O[8];
-    word_of<Q>(P, j, Pw);
-    assemble<Q>(Pw, O);
-#pragma unroll
-    for (int m = 0; m < 4; ++m) {
-      const f16x8 a = lookup8(O[2 * m], O[2 * m + 1], slot);
-#pragma unroll
-      for (int c = 0; c < TC; ++c) {
-        const f16x8 bh = *(const f16x8*)(stage + stage_off<TC>(kh, kTok * c + r, 4 * g + m));
-        const f16x8 bl = *(const f16x8*)(stage + stage_off<TC>(kh, kTok * c + r, 8 + 4 * g + m));
-        acc[c] = mfma32(a, bh, acc[c]);
-        acc[c] = mfma32(a, bl, acc[c]);
-      }
-    }
-    __syncthreads();
-  };
-  auto step = [&](int s, uint2 (&P)[Q]) {
-    round(0, P);
-    kwin(s, 1, kb);
-    store_window<TC>(stage, hb, sp, kb, I);
-    kwin(s + 1, 1, kb);
-    load_window<TC>(hb, sp, kb, I);
-    __syncthreads();
-    round(1, P);
-    if (s + 1 < ks.NSW) {
-      kwin(s + 1, 0, ka);
-      store_window<TC>(stage, ha, sp, ka, I);
-    }
-    kwin(s + 2, 0, ka);
-    load_window<TC>(ha, sp, ka, I);
-    load_planes<Q>(P, rs, cb, s + 3, voff);
-    __syncthreads();
-  };
-  int s = 0;
-  for (; s + 3 <= ks.NSW; s += 3) {
-    step(s, PA);
-    step(s + 1, PB);
-    step(s + 2, PC);
-  }
-  if (s < ks.NSW) step(s, PA);
-  if (s + 1 < ks.NSW) step(s + 1, PB);
-
-  // second K half -> first through LDS, one token chunk at a time; layout
-  // [row group][v][lane]
-  float* xb = (float*)lds;
-#pragma unroll
-  for (int c = 0; c < TC; ++c) {
-    if (c) __syncthreads();
-    if (kh == 1) {
-#pragma unroll
-      for (int v = 0; v < 16; ++v) xb[(rg * 16 + v) * 64 + lane] = acc[c][v];
-    }
-    __syncthreads();
-    const int t = kTok * c + r;
-    if (kh == 0 && active && t < nt) {
-      float* yrow = p.y + (size_t)(base + t) * H + n0 + 4 * g;
-#pragma unroll
-      for (int v4 = 0; v4 < 4; ++v4) {
-        f32x4 o;
-#pragma unroll
-        for (int k = 0; k < 4; ++k) o[k] = acc[c][4 * v4 + k] + xb[(rg * 16 + 4 * v4 + k) * 64 + lane];
-        *(f32x4*)(yrow + 8 * v4) = o;
-      }
-    }
-  }
-}
 
 template <int TC>
 __global__ __launch_bounds__(kThreads) void k_down(FfnParams p, int qmax) {
@@ -462,12 +39,12 @@ __global__ __launch_bounds__(kThreads) void k_down(FfnParams p, int qmax) {
   const int q = p.q[2 * e + 1];
   const uint32_t lut_bytes = 256u << qmax;
   switch (q < 3 || q > qmax || !tables_at_zero(lds) ? 0 : q) {
-    case 3: down_body<3, TC>(p, e, it, t0, nt, lds, lut_bytes); break;
-    case 4: down_body<4, TC>(p, e, it, t0, nt, lds, lut_bytes); break;
-    case 5: down_body<5, TC>(p, e, it, t0, nt, lds, lut_bytes); break;
-    case 6: down_body<6, TC>(p, e, it, t0, nt, lds, lut_bytes); break;
-    case 7: down_body<7, TC>(p, e, it, t0, nt, lds, lut_bytes); break;
-    case 8: down_body<8, TC>(p, e, it, t0, nt, lds, lut_bytes); break;
+    case 3: down_body<3, TC>(p, e, it, t0, nt, lds, lut_bytes, threadIdx.x); break;
+    case 4: down_body<4, TC>(p, e, it, t0, nt, lds, lut_bytes, threadIdx.x); break;
+    case 5: down_body<5, TC>(p, e, it, t0, nt, lds, lut_bytes, threadIdx.x); break;
+    case 6: down_body<6, TC>(p, e, it, t0, nt, lds, lut_bytes, threadIdx.x); break;
+    case 7: down_body<7, TC>(p, e, it, t0, nt, lds, lut_bytes, threadIdx.x); break;
+    case 8: down_body<8, TC>(p, e, it, t0, nt, lds, lut_bytes, threadIdx.x); break;
     default: {
       const int n0 = it * 128;
       poison(p.y + (size_t)(p.offsets[e] + t0) * p.H + n0, p.H, nt, min(128, p.H - n0));
@@ -481,21 +58,8 @@ __global__ __launch_bounds__(256) void k_combine(FfnParams p) {
   const int H4 = p.H >> 2;
   const size_t gid = (size_t)blockIdx.x * 256 + threadIdx.x;
   if (gid >= (size_t)p.T * H4) return;
-  const int t = (int)(gid / H4), n = (int)(gid - (size_t)t * H4) * 4;
-  const int KS = p.K + p.S;
-  f32x4 s = (f32x4){};
-  for (int k = 0; k < p.K; ++k) {
-    const int ex = p.topk_idx[t * p.K + k];
-    if (ex >= 0 && ex < p.E) {
-      const int pos = p.inv[t * KS + k];
-      s += p.topk_w[t * p.K + k] * *(const f32x4*)(p.y + (size_t)pos * p.H + n);
-    }
-  }
-  for (int sh = 0; sh < p.S; ++sh) {
-    const int pos = p.inv[t * KS + p.K + sh];
-    s += *(const f32x4*)(p.y + (size_t)pos * p.H + n);
-  }
-  *(f32x4*)(p.out + (size_t)t * p.H + n) = s;
+  const int t = (int)(gid / H4);
+  combine4(p, t, (int)(gid - (size_t)t * H4) * 4);
 }
 
 // bf16 activations -> fp16 once per call (exact in the fp16 normal range).

@@ -18,85 +18,22 @@
 //
 // k_route_topk: one wave per token. Expert e is selected at position
 // rank(e) = #{experts that beat it} when rank(e) < K.
-#include "mpb_device.h"
-#include "mpb_internal.h"
+#include "k_route_body.h"
 
 namespace mpb {
 
-constexpr int kTT = 8;        // tokens per logits wave
 constexpr int kEMaxTopk = 512;
-
-template <int XDT>
-__device__ __forceinline__ float x_to_f32(uint16_t v) {
-  if constexpr (XDT == 0) return (float)__builtin_bit_cast(_Float16, v);
-  else return __builtin_bit_cast(float, (uint32_t)v << 16);
-}
 
 template <int XDT, int EW, int NPC>
 __global__ __launch_bounds__(256) void k_route_logits(const uint16_t* __restrict__ X, const float* __restrict__ W,
                                                       const float* __restrict__ bias, int T, int H, int E,
                                                       double* __restrict__ logits) {
-  __shared__ double part[4][kTT * EW][65];  // +1 column: the summing lanes read rows without bank conflicts
+  __shared__ double part[4][kTT * EW * 65];  // +1 column: the summing lanes read rows without bank conflicts
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-  const int ntt = (T + kTT - 1) / kTT, neg = (E + EW - 1) / EW;
-  const int u = blockIdx.x * 4 + w;
-  const bool live = u < ntt * neg;
-  const int tt = live ? u % ntt : 0, eg = live ? u / ntt : 0;
-  const int t0 = tt * kTT, e0 = eg * EW;
-  double a[kTT][EW];
-#pragma unroll
-  for (int k = 0; k < kTT; ++k)
-#pragma unroll
-    for (int j = 0; j < EW; ++j) a[k][j] = 0.0;
-  if (live) {
-    // NPC pieces per pass, all loads of a pass in flight together
-    const int npc = (H + 255) / 256;
-    for (int i0 = 0; i0 < npc; i0 += NPC)
-#pragma unroll
-    for (int i = i0; i < i0 + NPC; ++i) {
-      const int h = 4 * lane + 256 * i;
-      const bool hin = h < H;  // also false for pieces past npc
-      const int hc = hin ? h : 0;
-      float4 wv[EW];
-#pragma unroll
-      for (int j = 0; j < EW; ++j) {
-        const int e = e0 + j < E ? e0 + j : E - 1;
-        wv[j] = *(const float4*)(W + (size_t)e * H + hc);
-      }
-      ushort4 xv[kTT];
-#pragma unroll
-      for (int k = 0; k < kTT; ++k) {
-        const int t = t0 + k < T ? t0 + k : T - 1;
-        xv[k] = *(const ushort4*)(X + (size_t)t * H + hc);
-      }
-#pragma unroll
-      for (int k = 0; k < kTT; ++k) {
-        const double x0 = hin ? (double)x_to_f32<XDT>(xv[k].x) : 0.0;
-        const double x1 = hin ? (double)x_to_f32<XDT>(xv[k].y) : 0.0;
-        const double x2 = hin ? (double)x_to_f32<XDT>(xv[k].z) : 0.0;
-        const double x3 = hin ? (double)x_to_f32<XDT>(xv[k].w) : 0.0;
-#pragma unroll
-        for (int j = 0; j < EW; ++j) {
-          a[k][j] = fma(x0, (double)wv[j].x, a[k][j]);
-          a[k][j] = fma(x1, (double)wv[j].y, a[k][j]);
-          a[k][j] = fma(x2, (double)wv[j].z, a[k][j]);
-          a[k][j] = fma(x3, (double)wv[j].w, a[k][j]);
-        }
-      }
-    }
-  }
-#pragma unroll
-  for (int k = 0; k < kTT; ++k)
-#pragma unroll
-    for (int j = 0; j < EW; ++j) part[w][k * EW + j][lane] = a[k][j];
+  const long long u = (long long)blockIdx.x * 4 + w;
+  logits_partials<XDT, EW, NPC>(X, W, T, H, E, u, lane, part[w]);
   __syncthreads();
-  if (live && lane < kTT * EW) {
-    const int k = lane / EW, j = lane % EW, t = t0 + k, e = e0 + j;
-    double s = 0.0;
-#pragma unroll 16
-    for (int l = 0; l < 64; ++l) s += part[w][lane][l];
-    if (t < T && e < E) logits[(size_t)t * E + e] = s + (bias ? (double)bias[e] : 0.0);
-  }
+  logits_sum<EW>(bias, T, E, u, lane, part[w], logits);
 }
 
 __global__ __launch_bounds__(256) void k_route_topk(const double* __restrict__ logits, int T, int E, int K,
@@ -106,37 +43,11 @@ __global__ __launch_bounds__(256) void k_route_topk(const double* __restrict__ l
   __shared__ int sel_i[4][16];
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int t = blockIdx.x * 4 + w;
-  const bool live = t < T;
-  if (live)
-    for (int e = lane; e < E; e += 64) lg[w][e] = logits[(size_t)t * E + e];
+  topk_load(logits, t, T, E, lane, lg[w]);
   __syncthreads();
-  if (live) {
-    for (int e = lane; e < E; e += 64) {
-      const double v = lg[w][e];
-      int rank = 0;
-#pragma unroll 4
-      for (int j = 0; j < E; ++j) {
-        const double x = lg[w][j];
-        rank += (x > v || (x == v && j < e)) ? 1 : 0;
-      }
-      if (rank < K) {
-        sel_v[w][rank] = v;
-        sel_i[w][rank] = e;
-      }
-    }
-  }
+  topk_rank(t, T, E, K, lane, lg[w], sel_v[w], sel_i[w]);
   __syncthreads();
-  if (live && lane < K) {
-    // softmax over the K winners, summed in rank order
-    double sum = 0.0, mine = 0.0;
-    for (int kk = 0; kk < K; ++kk) {
-      const double ex = exp(sel_v[w][kk] - sel_v[w][0]);
-      sum += ex;
-      if (kk == lane) mine = ex;
-    }
-    idx_out[(size_t)t * K + lane] = sel_i[w][lane];
-    w_out[(size_t)t * K + lane] = (float)(mine / sum);
-  }
+  topk_finish(t, T, K, lane, sel_v[w], sel_i[w], idx_out, w_out);
 }
 
 // Routing mass of one batch ("PagedWeight", §2.1, Eq. 1): m_e = the routing

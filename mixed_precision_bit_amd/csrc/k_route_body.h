@@ -1,0 +1,149 @@
+// Device code of the router (logits and top-K), shared by the per-phase
+// kernels and the fused persistent kernel. See k_route.hip for the method.
+#pragma once
+
+#include "mpb_device.h"
+#include "mpb_internal.h"
+
+namespace mpb {
+
+constexpr int kTT = 8;  // tokens per logits wave unit
+
+template <int XDT>
+__device__ __forceinline__ float x_to_f32(uint16_t v) {
+  if constexpr (XDT == 0) return (float)__builtin_bit_cast(_Float16, v);
+  else return __builtin_bit_cast(float, (uint32_t)v << 16);
+}
+
+// Logits, first half: wave unit u = (8-token tile, EW-expert group) computes
+// its 64 lanes' partial sums and writes them to part ([8 EW][65] doubles, the
+// wave's own LDS region). Units past the last one write zeros.
+template <int XDT, int EW, int NPC>
+__device__ __forceinline__ void logits_partials(const uint16_t* __restrict__ X, const float* __restrict__ W, int T,
+                                                int H, int E, long long u, int lane, double* part) {
+  const int ntt = (T + kTT - 1) / kTT, neg = (E + EW - 1) / EW;
+  const bool live = u < (long long)ntt * neg;
+  const int tt = live ? (int)(u % ntt) : 0, eg = live ? (int)(u / ntt) : 0;
+  const int t0 = tt * kTT, e0 = eg * EW;
+  double a[kTT][EW];
+#pragma unroll
+  for (int k = 0; k < kTT; ++k)
+#pragma unroll
+    for (int j = 0; j < EW; ++j) a[k][j] = 0.0;
+  if (live) {
+    // NPC pieces per pass, all loads of a pass in flight together
+    const int npc = (H + 255) / 256;
+    for (int i0 = 0; i0 < npc; i0 += NPC)
+#pragma unroll
+    for (int i = i0; i < i0 + NPC; ++i) {
+      const int h = 4 * lane + 256 * i;
+      const bool hin = h < H;  // also false for pieces past npc
+      const int hc = hin ? h : 0;
+      float4 wv[EW];
+#pragma unroll
+      for (int j = 0; j < EW; ++j) {
+        const int e = e0 + j < E ? e0 + j : E - 1;
+        wv[j] = *(const float4*)(W + (size_t)e * H + hc);
+      }
+      ushort4 xv[kTT];
+#pragma unroll
+      for (int k = 0; k < kTT; ++k) {
+        const int t = t0 + k < T ? t0 + k : T - 1;
+        xv[k] = *(const ushort4*)(X + (size_t)t * H + hc);
+      }
+#pragma unroll
+      for (int k = 0; k < kTT; ++k) {
+        const double x0 = hin ? (double)x_to_f32<XDT>(xv[k].x) : 0.0;
+        const double x1 = hin ? (double)x_to_f32<XDT>(xv[k].y) : 0.0;
+        const double x2 = hin ? (double)x_to_f32<XDT>(xv[k].z) : 0.0;
+        const double x3 = hin ? (double)x_to_f32<XDT>(xv[k].w) : 0.0;
+#pragma unroll
+        for (int j = 0; j < EW; ++j) {
+          a[k][j] = fma(x0, (double)wv[j].x, a[k][j]);
+          a[k][j] = fma(x1, (double)wv[j].y, a[k][j]);
+          a[k][j] = fma(x2, (double)wv[j].z, a[k][j]);
+          a[k][j] = fma(x3, (double)wv[j].w, a[k][j]);
+        }
+      }
+    }
+  }
+#pragma unroll
+  for (int k = 0; k < kTT; ++k)
+#pragma unroll
+    for (int j = 0; j < EW; ++j) part[(k * EW + j) * 65 + lane] = a[k][j];
+}
+
+// Logits, second half (after a barrier): lane k EW + j sums the 64 partials of
+// (token t0 + k, expert e0 + j) in lane order and adds the bias.
+template <int EW, bool CO = false>
+__device__ __forceinline__ void logits_sum(const float* __restrict__ bias, int T, int E, long long u, int lane,
+                                           const double* part, double* __restrict__ logits) {
+  const int ntt = (T + kTT - 1) / kTT, neg = (E + EW - 1) / EW;
+  if (u >= (long long)ntt * neg || lane >= kTT * EW) return;
+  const int t0 = (int)(u % ntt) * kTT, e0 = (int)(u / ntt) * EW;
+  const int k = lane / EW, j = lane % EW, t = t0 + k, e = e0 + j;
+  double s = 0.0;
+#pragma unroll 16
+  for (int l = 0; l < 64; ++l) s += part[lane * 65 + l];
+  if (t < T && e < E) {
+    const double v = s + (bias ? (double)bias[e] : 0.0);
+    if constexpr (CO) __hip_atomic_store(logits + (size_t)t * E + e, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    else logits[(size_t)t * E + e] = v;
+  }
+}
+
+// Top-K of token t by one wave, in three parts separated by barriers: load the
+// logits into lg (E doubles of LDS), rank every expert (rank(e) = #experts that
+// beat it, ties to the lower index) into sel_v / sel_i (16 entries each), then
+// the softmax of the K winners summed in rank order.
+template <bool CO = false>
+__device__ __forceinline__ void topk_load(const double* __restrict__ logits, int t, int T, int E, int lane,
+                                          double* lg) {
+  if (t < T)
+    for (int e = lane; e < E; e += 64) {
+      const double* a = logits + (size_t)t * E + e;
+      if constexpr (CO) lg[e] = __hip_atomic_load(const_cast<double*>(a), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      else lg[e] = *a;
+    }
+}
+
+__device__ __forceinline__ void topk_rank(int t, int T, int E, int K, int lane, const double* lg, double* sel_v,
+                                          int* sel_i) {
+  if (t >= T) return;
+  for (int e = lane; e < E; e += 64) {
+    const double v = lg[e];
+    int rank = 0;
+#pragma unroll 4
+    for (int j = 0; j < E; ++j) {
+      const double x = lg[j];
+      rank += (x > v || (x == v && j < e)) ? 1 : 0;
+    }
+    if (rank < K) {
+      sel_v[rank] = v;
+      sel_i[rank] = e;
+    }
+  }
+}
+
+template <bool CO = false>
+__device__ __forceinline__ void topk_finish(int t, int T, int K, int lane, const double* sel_v, const int* sel_i,
+                                            int32_t* __restrict__ idx_out, float* __restrict__ w_out) {
+  if (t >= T || lane >= K) return;
+  double sum = 0.0, mine = 0.0;
+  for (int kk = 0; kk < K; ++kk) {
+    const double ex = exp(sel_v[kk] - sel_v[0]);
+    sum += ex;
+    if (kk == lane) mine = ex;
+  }
+  const int32_t id = sel_i[lane];
+  const float wt = (float)(mine / sum);
+  if constexpr (CO) {
+    __hip_atomic_store(idx_out + (size_t)t * K + lane, id, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __hip_atomic_store(w_out + (size_t)t * K + lane, wt, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  } else {
+    idx_out[(size_t)t * K + lane] = id;
+    w_out[(size_t)t * K + lane] = wt;
+  }
+}
+
+}  // namespace mpb

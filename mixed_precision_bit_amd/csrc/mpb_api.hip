@@ -151,6 +151,44 @@ WsLayout ws_layout(int T, int H, int I, int E, int S, int K, bool bf16) {
 
 }  // namespace mpb
 
+namespace {
+
+// FFN view of a call: workspace regions of layout L inside ws, tc token chunks
+// per gate_up item.
+mpb::FfnParams ffn_params(const mpb::WsLayout& L, char* ws, const void* X_dev, int x_dtype, int T,
+                          const int32_t* topk_idx_dev, const float* topk_w_dev, const uint32_t* const* planes_dev,
+                          const uint16_t* const* luts_dev, const int32_t* q_dev, float* out_dev, int tc) {
+  mpb::FfnParams p{};
+  p.xh = x_dtype == MPB_BF16 ? (const uint16_t*)(ws + L.xh) : (const uint16_t*)X_dev;
+  p.T = T; p.H = g.H; p.I = g.I; p.E = g.E; p.S = g.S; p.K = g.K; p.NB = g.E + g.S;
+  p.topk_idx = topk_idx_dev; p.topk_w = topk_w_dev;
+  p.planes = planes_dev; p.luts = luts_dev; p.q = q_dev;
+  p.counts = (int32_t*)(ws + L.counts);
+  p.offsets = (int32_t*)(ws + L.offsets);
+  p.ptok = (int32_t*)(ws + L.ptok);
+  p.pw = (float*)(ws + L.pw);
+  p.inv = (int32_t*)(ws + L.inv);
+  p.items = (int32_t*)(ws + L.items);
+  p.items_dn = (int32_t*)(ws + L.items_dn);
+  p.n_items = (int32_t*)(ws + L.n_items);
+  p.max_items = L.max_items;
+  p.tpi = mpb::kChunkTokens * tc;
+  p.tpi_dn = mpb::kChunkTokens;
+  p.hhi = (uint16_t*)(ws + L.hhi);
+  p.hlo = (uint16_t*)(ws + L.hlo);
+  p.y = (float*)(ws + L.y);
+  p.out = out_dev;
+  return p;
+}
+
+int qmax_all() {
+  int m = 3;
+  for (int v : g.q) m = std::max(m, v);
+  return m;
+}
+
+}  // namespace
+
 extern "C" {
 
 const char* mpb_last_error(void) { return g_err.c_str(); }
@@ -303,27 +341,9 @@ int moe_ffn(const void* X_dev, int x_dtype, int T, const int32_t* topk_idx_dev, 
   if (ws_bytes < L.total)
     return fail(MPB_E_WS, "moe_ffn: workspace " + std::to_string(ws_bytes) + " < " + std::to_string(L.total));
   char* ws = (char*)ws_dev;
-  mpb::FfnParams p{};
-  p.xh = x_dtype == MPB_BF16 ? (const uint16_t*)(ws + L.xh) : (const uint16_t*)X_dev;
-  p.T = T; p.H = g.H; p.I = g.I; p.E = g.E; p.S = g.S; p.K = g.K; p.NB = g.E + g.S;
-  p.topk_idx = topk_idx_dev; p.topk_w = topk_w_dev;
-  p.planes = planes_dev; p.luts = luts_dev; p.q = q_dev;
-  p.counts = (int32_t*)(ws + L.counts);
-  p.offsets = (int32_t*)(ws + L.offsets);
-  p.ptok = (int32_t*)(ws + L.ptok);
-  p.pw = (float*)(ws + L.pw);
-  p.inv = (int32_t*)(ws + L.inv);
-  p.items = (int32_t*)(ws + L.items);
-  p.items_dn = (int32_t*)(ws + L.items_dn);
-  p.n_items = (int32_t*)(ws + L.n_items);
-  p.max_items = L.max_items;
   const int tc = mpb::ffn_token_chunks(T, g.E, g.K);
-  p.tpi = mpb::kChunkTokens * tc;
-  p.tpi_dn = mpb::kChunkTokens;
-  p.hhi = (uint16_t*)(ws + L.hhi);
-  p.hlo = (uint16_t*)(ws + L.hlo);
-  p.y = (float*)(ws + L.y);
-  p.out = out_dev;
+  const mpb::FfnParams p = ffn_params(L, ws, X_dev, x_dtype, T, topk_idx_dev, topk_w_dev, planes_dev, luts_dev, q_dev,
+                                      out_dev, tc);
   hipStream_t s = (hipStream_t)stream;
   mark(0, s);
   hipError_t e = hipSuccess;
@@ -351,6 +371,55 @@ int moe_ffn(const void* X_dev, int x_dtype, int T, const int32_t* topk_idx_dev, 
   return MPB_OK;
 } catch (...) {
   return fail(MPB_E_HIP, "moe_ffn: unexpected exception");
+}
+
+size_t moe_fused_counter_bytes(void) { return mpb::fused_counter_bytes(); }
+
+size_t moe_fused_workspace_bytes(int T) {
+  if (!g.init || T < 0) return 0;
+  return mpb::fused_counter_bytes() + mpb::route_workspace_bytes(T, g.E) +
+         mpb::ws_layout(T, g.H, g.I, g.E, g.S, g.K, true).total;
+}
+
+int moe_fused(const void* X_dev, int x_dtype, int T, const float* W_router_dev, const float* bias_dev,
+              int32_t* topk_idx_dev, float* topk_w_dev, const uint32_t* const* planes_dev,
+              const uint16_t* const* luts_dev, const int32_t* q_dev, float* out_dev, void* ws_dev, size_t ws_bytes,
+              void* stream) try {
+  if (!g.init) return fail(MPB_E_UNINIT, "moe_fused: no layer bound (mpb_init)");
+  if (x_dtype != MPB_F16 && x_dtype != MPB_BF16) return fail(MPB_E_ARG, "moe_fused: bad x_dtype");
+  if (T < 0) return fail(MPB_E_ARG, "moe_fused: T < 0");
+  if (T == 0) return MPB_OK;
+  if (T > (1 << 20)) return fail(MPB_E_SHAPE, "moe_fused: T above 2^20");
+  if (!X_dev || !W_router_dev || !topk_idx_dev || !topk_w_dev || !planes_dev || !luts_dev || !q_dev || !out_dev ||
+      !ws_dev)
+    return fail(MPB_E_ARG, "moe_fused: null pointer");
+  if ((uintptr_t)ws_dev % 256) return fail(MPB_E_ARG, "moe_fused: workspace not 256-byte aligned");
+  if (q_dev != g.q_dev) return fail(MPB_E_ARG, "moe_fused: q_dev is not the bound page table");
+  const mpb::WsLayout L = mpb::ws_layout(T, g.H, g.I, g.E, g.S, g.K, x_dtype == MPB_BF16);
+  const long long ntile = std::max(g.I / 64, (g.H + 127) / 128);
+  if ((long long)L.max_items * ntile >= (1ll << 30)) return fail(MPB_E_SHAPE, "moe_fused: T too large for this layer");
+  const size_t c_bytes = mpb::fused_counter_bytes(), r_bytes = mpb::route_workspace_bytes(T, g.E);
+  const size_t need = c_bytes + r_bytes + L.total;
+  if (ws_bytes < need)
+    return fail(MPB_E_WS, "moe_fused: workspace " + std::to_string(ws_bytes) + " < " + std::to_string(need));
+  char* ws = (char*)ws_dev;
+  mpb::FusedLaunch F{};
+  F.f = ffn_params(L, ws + c_bytes + r_bytes, X_dev, x_dtype, T, topk_idx_dev, topk_w_dev, planes_dev, luts_dev,
+                   q_dev, out_dev, 1);
+  F.x = (const uint16_t*)X_dev;
+  F.xdt = x_dtype;
+  F.W = W_router_dev;
+  F.bias = bias_dev;
+  F.logits = (double*)(ws + c_bytes);
+  F.idx_out = topk_idx_dev;
+  F.w_out = topk_w_dev;
+  F.ctr = (uint32_t*)ws;
+  F.qmax = qmax_all();
+  const hipError_t e = mpb::launch_fused(F, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "moe_fused");
+  return MPB_OK;
+} catch (...) {
+  return fail(MPB_E_HIP, "moe_fused: unexpected exception");
 }
 
 int set_committed_bits(int i, int b) try {

@@ -79,6 +79,22 @@ hipError_t launch_down(const FfnParams& p, int qmax, hipStream_t s);
 hipError_t launch_combine(const FfnParams& p, hipStream_t s);
 hipError_t launch_set_q(int32_t* q, int i, int b, hipStream_t s);
 
+// The whole layer in one persistent launch (k_fused.hip).
+struct FusedLaunch {
+  FfnParams f;          // FFN view of the call (tpi = tpi_dn = kChunkTokens)
+  const uint16_t* x;    // activations as given
+  int xdt;              // 0 fp16, 1 bf16
+  const float* W;       // router weights [E][H]
+  const float* bias;    // [E] or null
+  double* logits;       // [T][E] workspace
+  int32_t* idx_out;     // [T][K]
+  float* w_out;         // [T][K]
+  uint32_t* ctr;        // fused_counter_bytes() of counters, zero at launch
+  int qmax;             // highest committed bitwidth (sizes the table region)
+};
+size_t fused_counter_bytes();
+hipError_t launch_fused(const FusedLaunch& L, hipStream_t s);
+
 // Records msg as the calling thread's last error and returns code.
 int set_error(int code, const char* msg);
 // Checks a layer geometry against the ranges the library supports; on failure

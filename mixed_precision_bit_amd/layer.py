@@ -95,6 +95,17 @@ class DeviceLayer:
         ws = torch.empty(max(1, M.moe_ffn_workspace_bytes(T)), dtype=torch.uint8, device=self.device)
         return out, ws
 
+    def alloc_fused(self, T):
+        """Output and a zero-filled workspace for moe_fused (its counters must
+        start at zero; each call leaves them zero)."""
+        out = torch.empty((T, self.H), dtype=torch.float32, device=self.device)
+        ws = torch.zeros(max(256, M.moe_fused_workspace_bytes(T)), dtype=torch.uint8, device=self.device)
+        return out, ws
+
+    def fused(self, X, xdtype, idx, w, out, ws, stream=None):
+        M.moe_fused(X, XDTYPE[xdtype], self.W_r, self.bias, idx, w, self.planes_table, self.luts_table, self.q_dev,
+                    out, ws, stream)
+
     def route(self, X, xdtype, idx, w, stream=None):
         M.moe_route(X, XDTYPE[xdtype], self.W_r, self.bias, self.K, idx, w, self.route_ws, stream)
 

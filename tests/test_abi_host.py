@@ -48,6 +48,9 @@ def test_host_validation_without_device(L):
     assert L.mpb_get_resident_planes(0) == -7
     assert L.mpb_committed_bytes(None) == -7
     assert L.moe_ffn_workspace_bytes(16) == 0
+    assert L.moe_fused_workspace_bytes(16) == 0
+    one_ = ctypes.c_void_p(1)
+    assert L.moe_fused(one_, 0, 4, one_, None, one_, one_, one_, one_, one_, one_, one_, 1 << 20, None) == -7
     assert "no layer bound" in M.mpb_last_error()
     d = M.LayerDesc(100, 128, 8, 0, 2)   # H not a multiple of 64
     assert L.mpb_init(ctypes.byref(d), ctypes.c_void_p(1), ctypes.c_void_p(1), None) == -2

@@ -589,3 +589,83 @@ def test_graph_replay_matches_eager(layer_cache):
         got = out.cpu().numpy()
         assert np.array_equal(got.view(np.uint32), eager.view(np.uint32)), f"replay {rep} differs"
         del junk
+
+
+# ---------------------------------------------------------------- one fused launch
+def _separate_and_fused(D, Xb, xdtype):
+    X = to_dev_x(Xb)
+    T = Xb.shape[0]
+    idx, w = D.alloc_route(T)
+    out, ws = D.alloc_ffn(T)
+    D.route(X, xdtype, idx, w)
+    D.ffn(X, xdtype, idx, w, out, ws)
+    idx2, w2 = D.alloc_route(T)
+    out2, ws2 = D.alloc_fused(T)
+    D.fused(X, xdtype, idx2, w2, out2, ws2)
+    torch.cuda.synchronize()
+    return (idx.cpu().numpy(), w.cpu().numpy(), out.cpu().numpy(), idx2.cpu().numpy(), w2.cpu().numpy(),
+            out2.cpu().numpy(), ws2)
+
+
+@pytest.mark.parametrize("cfg", [0, 10, 11, 1, 2, 3])
+def test_fused_launch_equals_separate_calls(cfg, layer_cache):
+    """moe_fused (one persistent launch, PagedWeight §3.3) gives bit for bit
+    the routing and output of moe_route + moe_ffn, which the other tests hold
+    to the oracle; the small layers are also checked against the oracle here.
+    Its counters are back at zero after the call."""
+    L, D = dev_layer(layer_cache, cfg)
+    Xb = S.make_tokens(cfg)
+    xdtype = L.cfg["xdtype"]
+    say(f"fused cfg{cfg}: T={Xb.shape[0]}")
+    i1, w1, o1, i2, w2, o2, ws2 = _separate_and_fused(D, Xb, xdtype)
+    assert np.array_equal(i1, i2)
+    assert np.array_equal(w1.view(np.uint32), w2.view(np.uint32))
+    assert np.array_equal(o1.view(np.uint32), o2.view(np.uint32)), \
+        f"max |diff| {np.abs(o1.astype(np.float64) - o2).max()}"
+    assert int(ws2[:M().moe_fused_counter_bytes()].count_nonzero()) == 0, "counters not reset"
+    if cfg in (0, 10, 11):
+        X, z, r = oracle_route(L, Xb)
+        assert np.array_equal(i2, z)
+        assert_close(o2, O.moe_ffn(X, z, r, L), f"cfg{cfg} fused")
+
+
+def test_fused_launch_graph_replays_and_commits(layer_cache):
+    """Captured in a HIP graph, every replay (with eager work and
+    synchronisation in between) reproduces the eager result; after
+    set_committed_bits the next replay follows the new bitwidths."""
+    L, D = dev_layer(layer_cache, 10)
+    Xb = S.make_tokens(10)
+    X = to_dev_x(Xb)
+    T = Xb.shape[0]
+    idx, w = D.alloc_route(T)
+    out, ws = D.alloc_fused(T)
+    D.fused(X, "f16", idx, w, out, ws)
+    torch.cuda.synchronize()
+    eager = out.cpu().numpy().copy()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(s):
+        with torch.cuda.graph(g, stream=s):
+            D.fused(X, "f16", idx, w, out, ws)
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    for rep in range(4):
+        out.fill_(float("nan"))
+        junk = torch.randn(1 << 16, device="cuda").sum()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert np.array_equal(out.cpu().numpy().view(np.uint32), eager.view(np.uint32)), f"replay {rep}"
+        del junk
+    # lower every block to 3 bits except the first routed expert, raised to the
+    # highest bitwidth already committed (the captured table region's size)
+    q2 = np.full(L.n_blocks, 3, np.int32)
+    q2[0], q2[1] = int(L.q.max()), int(L.q.max())
+    for i in range(L.n_blocks):
+        M().set_committed_bits(i, int(q2[i]))
+    g.replay()
+    torch.cuda.synchronize()
+    Xf, z, r = oracle_route(L, Xb)
+    assert_close(out.cpu().numpy(), O.moe_ffn(Xf, z, r, L, q=q2), "fused replay after commits")
+    assert int(ws[:M().moe_fused_counter_bytes()].count_nonzero()) == 0
