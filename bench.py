@@ -32,7 +32,7 @@ HBM_PEAK_GBS = 8000.0
 MFMA_PEAK_TFLOPS = 2500.0  # dense fp16 MFMA
 METRIC = "MoE-layer tokens/s and achieved HBM GB/s (% of peak) at mixed bitwidths"
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_gate_up_qwen15moe_decode.md")
-KERNEL_SRCS = ["k_ffn_decode.hip", "mpb_device.h"]
+KERNEL_SRCS = ["k_ffn_decode.hip", "k_ffn_body.h", "mpb_device.h"]
 
 
 def kernel_hash():
