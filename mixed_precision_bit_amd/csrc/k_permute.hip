@@ -132,8 +132,135 @@ __global__ __launch_bounds__(256) void k_group(FfnParams p) {
   }
 }
 
-hipError_t launch_permute(const FfnParams& p, hipStream_t s) {
-  hipLaunchKernelGGL(k_group, dim3(p.NB), dim3(256), 0, s, p);
+// Chunked grouping for large batches (the same result as k_group): k_group
+// walks all T*K routed ids once per group, which costs O(groups x T K) at
+// prefill sizes. Here the ids are cut into chunks of kGroupChunk entries:
+// k_chunk_hist counts every group's entries per chunk, k_chunk_scan turns the
+// counts into per-chunk starting ranks and per-group totals, and
+// k_chunk_scatter places the entries of one (group, chunk) pair, in (t, k)
+// order, starting at the group's offset plus the chunk's starting rank.
+__global__ __launch_bounds__(256) void k_chunk_hist(FfnParams p, int32_t* ccnt) {
+  __shared__ int hist[kMaxGroups];
+  const int c = blockIdx.x, tid = threadIdx.x, E = p.E, TK = p.T * p.K;
+  for (int i = tid; i < E; i += 256) hist[i] = 0;
+  __syncthreads();
+  const int j1 = min(TK, (c + 1) * kGroupChunk);
+  for (int j = c * kGroupChunk + tid; j < j1; j += 256) {
+    const int x = p.topk_idx[j];
+    if (x >= 0 && x < E) atomicAdd(&hist[x], 1);
+  }
+  __syncthreads();
+  for (int i = tid; i < E; i += 256) ccnt[(size_t)c * E + i] = hist[i];
+}
+
+// One thread per routed group: exclusive prefix over the chunks (in place)
+// and the group's total.
+__global__ __launch_bounds__(256) void k_chunk_scan(FfnParams p, int32_t* ccnt, int nchunk) {
+  const int e = blockIdx.x * 256 + threadIdx.x;
+  if (e >= p.E) return;
+  int run = 0;
+  for (int c = 0; c < nchunk; ++c) {
+    const int v = ccnt[(size_t)c * p.E + e];
+    ccnt[(size_t)c * p.E + e] = run;
+    run += v;
+  }
+  p.counts[e] = run;
+}
+
+__global__ __launch_bounds__(256) void k_chunk_scatter(FfnParams p, const int32_t* ccnt) {
+  __shared__ int red[5][4];
+  __shared__ int wtot[4];
+  const int e = blockIdx.x, c = blockIdx.y, tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int T = p.T, K = p.K, E = p.E, KS = K + p.S, TK = T * K;
+  // group sizes (routed: totals from the scan; shared: every token), then
+  // this group's offset and item positions as in k_group
+  const int qg = p.q[2 * e], qd = p.q[2 * e + 1];
+  const int mine = e < E ? p.counts[e] : T;
+  const int ni = (mine + p.tpi - 1) / p.tpi, ni_dn = (mine + p.tpi_dn - 1) / p.tpi_dn;
+  int a[5] = {0, 0, 0, 0, 0};
+  for (int j = tid; j < p.NB; j += 256) {
+    const int cnt = j < E ? p.counts[j] : T;
+    const int n = (cnt + p.tpi - 1) / p.tpi, n_dn = (cnt + p.tpi_dn - 1) / p.tpi_dn;
+    const int qjg = p.q[2 * j], qjd = p.q[2 * j + 1];
+    if (j < e) a[0] += cnt;
+    if (qjg > qg || (qjg == qg && j < e)) a[1] += n;
+    if (qjd > qd || (qjd == qd && j < e)) a[2] += n_dn;
+    a[3] += n;
+    a[4] += n_dn;
+  }
+#pragma unroll
+  for (int i = 0; i < 5; ++i) {
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) a[i] += __shfl_xor(a[i], o);
+    if (lane == 0) red[i][w] = a[i];
+  }
+  __syncthreads();
+  int r[5];
+#pragma unroll
+  for (int i = 0; i < 5; ++i) r[i] = red[i][0] + red[i][1] + red[i][2] + red[i][3];
+  const int off = r[0];
+  if (c == 0) {
+    if (tid == 0) {
+      p.offsets[e] = off;
+      if (e >= E) p.counts[e] = mine;
+      if (e == p.NB - 1) p.offsets[p.NB] = off + mine;
+      if (e == 0) {
+        p.n_items[0] = r[3];
+        p.n_items[1] = r[4];
+      }
+    }
+    for (int sp = tid; sp < ni; sp += 256) p.items[r[1] + sp] = (e << 16) | sp;
+    for (int sp = tid; sp < ni_dn; sp += 256) p.items_dn[r[2] + sp] = (e << 16) | sp;
+  }
+  if (e < E) {
+    int run = off + ccnt[(size_t)c * E + e];
+    const int j1 = min(TK, (c + 1) * kGroupChunk);
+    for (int b0 = c * kGroupChunk; b0 < j1; b0 += 256) {
+      const int j = b0 + tid;
+      const int x = j < j1 ? p.topk_idx[j] : -1;
+      const bool m = x == e;
+      const unsigned long long bal = __ballot(m);
+      const int lp = __popcll(bal & ((1ull << lane) - 1ull));
+      if (lane == 0) wtot[w] = __popcll(bal);
+      __syncthreads();
+      int wp = 0;
+      for (int v = 0; v < w; ++v) wp += wtot[v];
+      const int tot = wtot[0] + wtot[1] + wtot[2] + wtot[3];
+      if (m) {
+        const int pos = run + wp + lp;
+        const int t = j / K, k = j - t * K;
+        p.ptok[pos] = t;
+        p.pw[pos] = p.topk_w[j];
+        p.inv[t * KS + k] = pos;
+      }
+      run += tot;
+      __syncthreads();
+    }
+  } else if (c == 0) {
+    const int sh = e - E;
+    for (int t = tid; t < T; t += 256) {
+      const int pos = off + t;
+      p.ptok[pos] = t;
+      p.pw[pos] = 1.0f;
+      p.inv[t * KS + K + sh] = pos;
+    }
+  }
+}
+
+int group_chunks(int T, int K) {
+  const long long TK = (long long)T * K;
+  return TK >= kChunkedFrom ? (int)((TK + kGroupChunk - 1) / kGroupChunk) : 0;
+}
+
+hipError_t launch_permute(const FfnParams& p, int32_t* ccnt, hipStream_t s) {
+  const int nc = group_chunks(p.T, p.K);
+  if (nc == 0) {
+    hipLaunchKernelGGL(k_group, dim3(p.NB), dim3(256), 0, s, p);
+    return hipGetLastError();
+  }
+  hipLaunchKernelGGL(k_chunk_hist, dim3(nc), dim3(256), 0, s, p, ccnt);
+  hipLaunchKernelGGL(k_chunk_scan, dim3((p.E + 255) / 256), dim3(256), 0, s, p, ccnt, nc);
+  hipLaunchKernelGGL(k_chunk_scatter, dim3(p.NB, nc), dim3(256), 0, s, p, (const int32_t*)ccnt);
   return hipGetLastError();
 }
 

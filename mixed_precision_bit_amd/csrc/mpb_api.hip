@@ -141,6 +141,7 @@ WsLayout ws_layout(int T, int H, int I, int E, int S, int K, bool bf16) {
   L.items = off;   off += align256((size_t)L.max_items * 4);
   L.items_dn = off; off += align256((size_t)L.max_items * 4);
   L.n_items = off; off += 256;  // [2]
+  L.ccnt = off;    off += align256((size_t)group_chunks(T, K) * E * 4);
   L.hhi = off;     off += align256(P * (size_t)I * 2);
   L.hlo = off;     off += align256(P * (size_t)I * 2);
   L.y = off;       off += align256(P * (size_t)H * 4);
@@ -351,7 +352,7 @@ int moe_ffn(const void* X_dev, int x_dtype, int T, const int32_t* topk_idx_dev, 
     e = mpb::launch_x_to_f16((const uint16_t*)X_dev, (uint16_t*)(ws + L.xh), (size_t)T * g.H, s);
     if (e != hipSuccess) return hip_fail(e, "moe_ffn: activation conversion");
   }
-  e = mpb::launch_permute(p, s);
+  e = mpb::launch_permute(p, (int32_t*)(ws + L.ccnt), s);
   if (e != hipSuccess) return hip_fail(e, "moe_ffn: permute");
   mark(1, s);
   int qmax_gu = 3, qmax_dn = 3;

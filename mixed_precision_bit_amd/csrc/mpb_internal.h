@@ -49,7 +49,7 @@ struct FfnParams {
 };
 
 struct WsLayout {
-  size_t counts, offsets, ptok, pw, inv, items, items_dn, n_items, hhi, hlo, y, xh, total;
+  size_t counts, offsets, ptok, pw, inv, items, items_dn, n_items, ccnt, hhi, hlo, y, xh, total;
   int max_items;
 };
 // Upper bound on work items (one per tpi-token split of a group with tokens):
@@ -70,7 +70,13 @@ hipError_t launch_routing_mass(const int32_t* idx, const float* w, int T, int E,
                                hipStream_t s);
 hipError_t launch_route(const uint16_t* X, int xdt, const float* W, const float* bias, int T, int H,
                         int E, int K, int32_t* idx, float* w, double* logits, hipStream_t s);
-hipError_t launch_permute(const FfnParams& p, hipStream_t s);
+// Grouping: one pass per group for small batches; for T*K >= kChunkedFrom the
+// routed ids are processed in chunks of kGroupChunk (group_chunks(T, K)
+// chunks, 0 below the threshold), with ccnt = [chunks][E] int32 scratch.
+constexpr int kGroupChunk = 2048;
+constexpr long long kChunkedFrom = 8192;
+int group_chunks(int T, int K);
+hipError_t launch_permute(const FfnParams& p, int32_t* ccnt, hipStream_t s);
 hipError_t launch_x_to_f16(const uint16_t* x, uint16_t* y, size_t n, hipStream_t s);
 // qmax: highest committed bitwidth among the launch's blocks (sizes the LDS
 // table region; a block above it yields NaN)

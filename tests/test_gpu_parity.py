@@ -480,6 +480,23 @@ def test_edge_token_counts(layer_cache):
     torch.cuda.synchronize()
 
 
+def test_chunked_grouping_large_batch(layer_cache):
+    """Batches with T*K at or above the chunked-grouping threshold (8192
+    routed entries, chunks of 2048) group through the chunked path; a ragged
+    last chunk and the shared experts included. Every output element is held
+    to the oracle, and the one-launch path (single-pass grouping) agrees bit
+    for bit."""
+    L, D = dev_layer(layer_cache, 10)
+    for T in (2731, 3000):     # T*K = 8193 (last chunk of 1 entry), 9000
+        Xb = S.make_tokens(10, T=T, seed=7000 + T)
+        say(f"chunked grouping: T={T}, T*K={T * L.K}")
+        i1, w1, o1, i2, w2, o2, _ = _separate_and_fused(D, Xb, "f16")
+        X, z, r = oracle_route(L, Xb)
+        assert np.array_equal(i1, z)
+        assert_close(o1, O.moe_ffn(X, z, r, L), f"T={T}")
+        assert np.array_equal(o1.view(np.uint32), o2.view(np.uint32))
+
+
 def test_edge_one_expert_takes_all_and_extreme_bitwidths(layer_cache):
     L, D = dev_layer(layer_cache, 10)
     T = 150
