@@ -58,6 +58,7 @@ struct FusedParams {
   uint32_t slot_off;    // LDS byte offset of the unit slot and the wait flag
   int n_conv, n_logit, n_topk, n_group, n_gu, n_dn, n_comb;
   int ntile_gu, ntile_dn;
+  int logit_mfma;       // logits on the fp64 matrix cores (16 x 16 tiles), as the per-phase router does
 };
 
 namespace {
@@ -291,11 +292,15 @@ template <int XDT>
 __device__ __forceinline__ void logit_unit(const FusedParams& P, int u, uint16_t* lds, int tid) {
   const FfnParams& p = P.f;
   const int lane = tid & 63, w = tid >> 6;
-  double* part = (double*)lds + w * (kTT * 65);
   const long long wu = (long long)u * 8 + w;
-  logits_partials<XDT, 1, 2>(P.x, P.W, p.T, p.H, p.E, wu, lane, part);
-  __syncthreads();
-  logits_sum<1, true>(P.bias, p.T, p.E, wu, lane, part, P.logits);
+  if (P.logit_mfma) {
+    logits_tile_mfma<XDT, true>(P.x, P.W, P.bias, p.T, p.H, p.E, wu, lane, P.logits);
+  } else {
+    double* part = (double*)lds + w * (kTT * 65);
+    logits_partials<XDT, 1, 2>(P.x, P.W, p.T, p.H, p.E, wu, lane, part);
+    __syncthreads();
+    logits_sum<1, true>(P.bias, p.T, p.E, wu, lane, part, P.logits);
+  }
   mark_done(ctr(P, C_LOGIT));
 }
 
@@ -428,7 +433,9 @@ hipError_t launch_fused(const FusedLaunch& L, hipStream_t s) {
   const FfnParams& f = L.f;
   const long long ntt = (f.T + kTT - 1) / kTT;
   P.n_conv = L.xdt == 1 ? (int)(((long long)f.T * f.H / 8 + 511) / 512) : 0;
-  P.n_logit = (int)((ntt * f.E + 7) / 8);
+  P.logit_mfma = logits_use_mfma(f.T, f.E) ? 1 : 0;
+  P.n_logit = P.logit_mfma ? (int)(((long long)((f.T + 15) / 16) * ((f.E + 15) / 16) + 7) / 8)
+                           : (int)((ntt * f.E + 7) / 8);
   P.n_topk = (f.T + 7) / 8;
   P.n_group = f.NB;
   P.ntile_gu = f.I >> 6;

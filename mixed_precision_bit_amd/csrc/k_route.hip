@@ -36,6 +36,14 @@ __global__ __launch_bounds__(256) void k_route_logits(const uint16_t* __restrict
   logits_sum<EW>(bias, T, E, u, lane, part[w], logits);
 }
 
+template <int XDT>
+__global__ __launch_bounds__(256) void k_route_logits_mfma(const uint16_t* __restrict__ X, const float* __restrict__ W,
+                                                           const float* __restrict__ bias, int T, int H, int E,
+                                                           double* __restrict__ logits) {
+  logits_tile_mfma<XDT>(X, W, bias, T, H, E, (long long)blockIdx.x * 4 + (threadIdx.x >> 6), threadIdx.x & 63,
+                        logits);
+}
+
 __global__ __launch_bounds__(256) void k_route_topk(const double* __restrict__ logits, int T, int E, int K,
                                                     int32_t* __restrict__ idx_out, float* __restrict__ w_out) {
   __shared__ double lg[4][kEMaxTopk];
@@ -97,6 +105,14 @@ size_t route_workspace_bytes(int T, int E) { return ((size_t)T * E * 8 + 255) / 
 template <int XDT>
 static void launch_logits(const uint16_t* X, const float* W, const float* bias, int T, int H, int E, double* lg,
                           hipStream_t s) {
+  // large batches: 16 x 16 tiles on the fp64 matrix cores once there are
+  // enough tiles to fill the chip
+  const long long tiles = (long long)((T + 15) / 16) * ((E + 15) / 16);
+  if (logits_use_mfma(T, E)) {
+    hipLaunchKernelGGL(k_route_logits_mfma<XDT>, dim3((unsigned)((tiles + 3) / 4)), dim3(256), 0, s, X, W, bias, T,
+                       H, E, lg);
+    return;
+  }
   // experts per wave: grow the group (more reuse of each activation load) only
   // while the launch keeps at least 2048 waves
   const long long ntt = (T + kTT - 1) / kTT;

@@ -92,6 +92,65 @@ __device__ __forceinline__ void logits_sum(const float* __restrict__ bias, int T
   }
 }
 
+// Logits of large batches on the fp64 matrix cores: wave unit u is one 16-token x
+// 16-expert tile, v_mfma_f64_16x16x4 with tokens as rows and experts as
+// columns. Lane l supplies token tile row l % 16 and expert column l % 16 for
+// hidden index h0 + 4 (l / 16) + j in MFMA j of each 16-index step, so every
+// logit is summed over h in one fixed order (identical router rows give
+// identical logits). Output: lane l, value i holds row 4 i + l / 16, column
+// l % 16 of the tile.
+typedef double f64x4 __attribute__((ext_vector_type(4)));
+
+// The matrix-core logits are used once a batch has enough 16 x 16 tiles to
+// fill the chip.
+inline bool logits_use_mfma(int T, int E) { return (long long)((T + 15) / 16) * ((E + 15) / 16) >= 1024; }
+
+template <int XDT, bool CO = false>
+__device__ __forceinline__ void logits_tile_mfma(const uint16_t* __restrict__ X, const float* __restrict__ W,
+                                                 const float* __restrict__ bias, int T, int H, int E, long long u,
+                                                 int lane, double* __restrict__ logits) {
+  const int g = lane >> 4, c = lane & 15;
+  const int ntt = (T + 15) >> 4, net = (E + 15) >> 4;
+  if (u >= (long long)ntt * net) return;
+  const int tt = (int)(u % ntt), et = (int)(u / ntt);
+  const int t = min(tt * 16 + c, T - 1), e = min(et * 16 + c, E - 1);
+  const uint16_t* xr = X + (size_t)t * H + 4 * g;
+  const float* wr = W + (size_t)e * H + 4 * g;
+  f64x4 acc = {0.0, 0.0, 0.0, 0.0};
+  constexpr int kU = 8;  // 16-index steps per pass, loads of a pass in flight together
+  for (int h0 = 0; h0 < H; h0 += 16 * kU) {
+    ushort4 xv[kU];
+    float4 wv[kU];
+#pragma unroll
+    for (int j = 0; j < kU; ++j) {
+      const int h = min(h0 + 16 * j, H - 16);  // past the end: a valid address, skipped below
+      xv[j] = *(const ushort4*)(xr + h);
+      wv[j] = *(const float4*)(wr + h);
+    }
+#pragma unroll
+    for (int j = 0; j < kU; ++j) {
+      if (h0 + 16 * j < H) {
+        acc = __builtin_amdgcn_mfma_f64_16x16x4f64((double)x_to_f32<XDT>(xv[j].x), (double)wv[j].x, acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f64_16x16x4f64((double)x_to_f32<XDT>(xv[j].y), (double)wv[j].y, acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f64_16x16x4f64((double)x_to_f32<XDT>(xv[j].z), (double)wv[j].z, acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f64_16x16x4f64((double)x_to_f32<XDT>(xv[j].w), (double)wv[j].w, acc, 0, 0, 0);
+      }
+    }
+  }
+  const int ecol = et * 16 + c;
+  const double b = (bias && ecol < E) ? (double)bias[ecol] : 0.0;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int trow = tt * 16 + 4 * i + g;
+    if (trow < T && ecol < E) {
+      if constexpr (CO)
+        __hip_atomic_store(logits + (size_t)trow * E + ecol, acc[i] + b, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      else
+        logits[(size_t)trow * E + ecol] = acc[i] + b;
+    }
+  }
+}
+
 // Top-K of token t by one wave, in three parts separated by barriers: load the
 // logits into lg (E doubles of LDS), rank every expert (rank(e) = #experts that
 // beat it, ties to the lower index) into sel_v / sel_i (16 entries each), then

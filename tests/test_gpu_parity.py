@@ -100,11 +100,15 @@ def route_ws(T, E):
     return torch.empty(max(1, M().moe_route_workspace_bytes(T, E)), dtype=torch.uint8, device="cuda")
 
 
-@pytest.mark.parametrize("cfg", [0, 1, 2, 3, 4, 10, 11])
-def test_route_bit_exact(cfg):
+@pytest.mark.parametrize("cfg,T", [(0, None), (1, None), (2, None), (3, None), (4, None), (10, None), (11, None),
+                                   (1, 4096)])
+def test_route_bit_exact(cfg, T):
+    """Top-K bit-exact, weights within tolerance. Config 3 (bf16) and config 1
+    at 4096 tokens (fp16) take the matrix-core logits (>= 1024 16x16 tiles),
+    the others the vector path."""
     c = S.layer_config(cfg)
     L = S.make_layer(cfg, blocks=[])
-    Xb = S.make_tokens(cfg)
+    Xb = S.make_tokens(cfg, T=T, seed=None if T is None else 8000 + T)
     say(f"route cfg{cfg}: T={Xb.shape[0]} H={c['H']} E={c['E']} K={c['K']}")
     X, z, r = oracle_route(L, Xb)
     W = torch.from_numpy(L.W_r).cuda()
