@@ -128,7 +128,8 @@ int mpb_pack_table(int kind, const uint16_t* lut_dev, int N, int b, uint16_t* im
  * and topk_w_dev [T][K] fp32 = softmax over all E experts restricted to the K
  * winners and renormalised (equal to a softmax over the K winning logits).
  * ws_dev: device workspace of ws_bytes >= moe_route_workspace_bytes(T, E)
- * (the [T][E] fp64 logits; contents not preserved). Needs
+ * (fp64 logits, summed in up to 8 hidden-dimension parts for small batches;
+ * contents not preserved). Needs
  * 1 <= K <= min(E, 16), E <= 512, H a multiple of 64 up to 65536, T <= 2^20;
  * T == 0 is a no-op. Errors: MPB_E_ARG, MPB_E_SHAPE, MPB_E_WS, MPB_E_HIP.
  * Does not need mpb_init.

@@ -59,6 +59,7 @@ struct FusedParams {
   int n_conv, n_logit, n_topk, n_group, n_gu, n_dn, n_comb;
   int ntile_gu, ntile_dn;
   int logit_mfma;       // logits on the fp64 matrix cores (16 x 16 tiles), as the per-phase router does
+  int ks;               // hidden parts of the vector-path logits (route_ksplit)
 };
 
 namespace {
@@ -294,12 +295,12 @@ __device__ __forceinline__ void logit_unit(const FusedParams& P, int u, uint16_t
   const int lane = tid & 63, w = tid >> 6;
   const long long wu = (long long)u * 8 + w;
   if (P.logit_mfma) {
-    logits_tile_mfma<XDT, true>(P.x, P.W, P.bias, p.T, p.H, p.E, wu, lane, P.logits);
+    logits_tile_mfma<XDT, true>(P.x, P.W, p.T, p.H, p.E, wu, lane, P.logits);
   } else {
     double* part = (double*)lds + w * (kTT * 65);
-    logits_partials<XDT, 1, 2>(P.x, P.W, p.T, p.H, p.E, wu, lane, part);
+    logits_partials<XDT, 1, 2>(P.x, P.W, p.T, p.H, p.E, P.ks, wu, lane, part);
     __syncthreads();
-    logits_sum<1, true>(P.bias, p.T, p.E, wu, lane, part, P.logits);
+    logits_sum<1, true>(p.T, p.E, P.ks, wu, lane, part, P.logits);
   }
   mark_done(ctr(P, C_LOGIT));
 }
@@ -312,7 +313,7 @@ __device__ __forceinline__ void topk_unit(const FusedParams& P, int u, uint16_t*
     double* sel_v = (double*)lds + 8 * 512 + w * 16;
     int* sel_i = (int*)((double*)lds + 8 * 512 + 8 * 16) + w * 16;
     const int t = u * 8 + w;
-    topk_load<true>(P.logits, t, p.T, p.E, lane, lg);
+    topk_load<true>(P.logits, P.bias, P.ks, t, p.T, p.E, lane, lg);
     __syncthreads();
     topk_rank(t, p.T, p.E, p.K, lane, lg, sel_v, sel_i);
     __syncthreads();
@@ -434,8 +435,9 @@ hipError_t launch_fused(const FusedLaunch& L, hipStream_t s) {
   const long long ntt = (f.T + kTT - 1) / kTT;
   P.n_conv = L.xdt == 1 ? (int)(((long long)f.T * f.H / 8 + 511) / 512) : 0;
   P.logit_mfma = logits_use_mfma(f.T, f.E) ? 1 : 0;
+  P.ks = route_ksplit(f.T, f.H, f.E);
   P.n_logit = P.logit_mfma ? (int)(((long long)((f.T + 15) / 16) * ((f.E + 15) / 16) + 7) / 8)
-                           : (int)((ntt * f.E + 7) / 8);
+                           : (int)((ntt * f.E * P.ks + 7) / 8);
   P.n_topk = (f.T + 7) / 8;
   P.n_group = f.NB;
   P.ntile_gu = f.I >> 6;

@@ -26,32 +26,30 @@ constexpr int kEMaxTopk = 512;
 
 template <int XDT, int EW, int NPC>
 __global__ __launch_bounds__(256) void k_route_logits(const uint16_t* __restrict__ X, const float* __restrict__ W,
-                                                      const float* __restrict__ bias, int T, int H, int E,
-                                                      double* __restrict__ logits) {
+                                                      int T, int H, int E, int ks, double* __restrict__ logits) {
   __shared__ double part[4][kTT * EW * 65];  // +1 column: the summing lanes read rows without bank conflicts
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const long long u = (long long)blockIdx.x * 4 + w;
-  logits_partials<XDT, EW, NPC>(X, W, T, H, E, u, lane, part[w]);
+  logits_partials<XDT, EW, NPC>(X, W, T, H, E, ks, u, lane, part[w]);
   __syncthreads();
-  logits_sum<EW>(bias, T, E, u, lane, part[w], logits);
+  logits_sum<EW>(T, E, ks, u, lane, part[w], logits);
 }
 
 template <int XDT>
 __global__ __launch_bounds__(256) void k_route_logits_mfma(const uint16_t* __restrict__ X, const float* __restrict__ W,
-                                                           const float* __restrict__ bias, int T, int H, int E,
-                                                           double* __restrict__ logits) {
-  logits_tile_mfma<XDT>(X, W, bias, T, H, E, (long long)blockIdx.x * 4 + (threadIdx.x >> 6), threadIdx.x & 63,
-                        logits);
+                                                           int T, int H, int E, double* __restrict__ logits) {
+  logits_tile_mfma<XDT>(X, W, T, H, E, (long long)blockIdx.x * 4 + (threadIdx.x >> 6), threadIdx.x & 63, logits);
 }
 
-__global__ __launch_bounds__(256) void k_route_topk(const double* __restrict__ logits, int T, int E, int K,
-                                                    int32_t* __restrict__ idx_out, float* __restrict__ w_out) {
+__global__ __launch_bounds__(256) void k_route_topk(const double* __restrict__ logits, const float* __restrict__ bias,
+                                                    int ks, int T, int E, int K, int32_t* __restrict__ idx_out,
+                                                    float* __restrict__ w_out) {
   __shared__ double lg[4][kEMaxTopk];
   __shared__ double sel_v[4][16];
   __shared__ int sel_i[4][16];
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int t = blockIdx.x * 4 + w;
-  topk_load(logits, t, T, E, lane, lg[w]);
+  topk_load(logits, bias, ks, t, T, E, lane, lg[w]);
   __syncthreads();
   topk_rank(t, T, E, K, lane, lg[w], sel_v[w], sel_i[w]);
   __syncthreads();
@@ -100,38 +98,46 @@ hipError_t launch_routing_mass(const int32_t* idx, const float* w, int T, int E,
   return hipGetLastError();
 }
 
-size_t route_workspace_bytes(int T, int E) { return ((size_t)T * E * 8 + 255) / 256 * 256; }
+// [ks][T][E] fp64 logit parts; ks <= 8 on the vector path (it depends on H,
+// which the size query does not take), 1 on the matrix-core path
+size_t route_workspace_bytes(int T, int E) {
+  return ((size_t)(logits_use_mfma(T, E) ? 1 : 8) * T * E * 8 + 255) / 256 * 256;
+}
 
 template <int XDT>
-static void launch_logits(const uint16_t* X, const float* W, const float* bias, int T, int H, int E, double* lg,
-                          hipStream_t s) {
+static void launch_logits(const uint16_t* X, const float* W, int T, int H, int E, int ks, double* lg, hipStream_t s) {
   // large batches: 16 x 16 tiles on the fp64 matrix cores once there are
   // enough tiles to fill the chip
   const long long tiles = (long long)((T + 15) / 16) * ((E + 15) / 16);
   if (logits_use_mfma(T, E)) {
-    hipLaunchKernelGGL(k_route_logits_mfma<XDT>, dim3((unsigned)((tiles + 3) / 4)), dim3(256), 0, s, X, W, bias, T,
-                       H, E, lg);
+    hipLaunchKernelGGL(k_route_logits_mfma<XDT>, dim3((unsigned)((tiles + 3) / 4)), dim3(256), 0, s, X, W, T, H, E,
+                       lg);
     return;
   }
   // experts per wave: grow the group (more reuse of each activation load) only
   // while the launch keeps at least 2048 waves
   const long long ntt = (T + kTT - 1) / kTT;
-  const int ew = ntt * ((E + 3) / 4) >= 2048 ? 4 : ntt * ((E + 1) / 2) >= 2048 ? 2 : 1;
-  const long long units = ntt * ((E + ew - 1) / ew);
+  const int ew = ntt * ks * ((E + 3) / 4) >= 2048 ? 4 : ntt * ks * ((E + 1) / 2) >= 2048 ? 2 : 1;
+  const long long units = ntt * ((E + ew - 1) / ew) * ks;
   const dim3 grid((unsigned)((units + 3) / 4)), block(256);
-  // pieces per pass: all of H when it fits the registers (EW = 1: 8, EW = 2: 4, EW = 4: 2)
-  if (ew == 4) hipLaunchKernelGGL((k_route_logits<XDT, 4, 2>), grid, block, 0, s, X, W, bias, T, H, E, lg);
-  else if (ew == 2) hipLaunchKernelGGL((k_route_logits<XDT, 2, 4>), grid, block, 0, s, X, W, bias, T, H, E, lg);
-  else hipLaunchKernelGGL((k_route_logits<XDT, 1, 8>), grid, block, 0, s, X, W, bias, T, H, E, lg);
+  // pieces per pass: all of a part when it fits the registers (EW = 1: 8, EW = 2: 4, EW = 4: 2); a
+  // pass never loads more pieces than a part has
+  const int ppk = ((H + 255) / 256 + ks - 1) / ks;
+  if (ew == 4) hipLaunchKernelGGL((k_route_logits<XDT, 4, 2>), grid, block, 0, s, X, W, T, H, E, ks, lg);
+  else if (ew == 2) hipLaunchKernelGGL((k_route_logits<XDT, 2, 4>), grid, block, 0, s, X, W, T, H, E, ks, lg);
+  else if (ppk <= 2) hipLaunchKernelGGL((k_route_logits<XDT, 1, 2>), grid, block, 0, s, X, W, T, H, E, ks, lg);
+  else if (ppk <= 4) hipLaunchKernelGGL((k_route_logits<XDT, 1, 4>), grid, block, 0, s, X, W, T, H, E, ks, lg);
+  else hipLaunchKernelGGL((k_route_logits<XDT, 1, 8>), grid, block, 0, s, X, W, T, H, E, ks, lg);
 }
 
 hipError_t launch_route(const uint16_t* X, int xdt, const float* W, const float* bias, int T, int H, int E,
                         int K, int32_t* idx, float* w, double* lg, hipStream_t s) {
-  if (xdt == 0) launch_logits<0>(X, W, bias, T, H, E, lg, s);
-  else launch_logits<1>(X, W, bias, T, H, E, lg, s);
+  const int ks = route_ksplit(T, H, E);
+  if (xdt == 0) launch_logits<0>(X, W, T, H, E, ks, lg, s);
+  else launch_logits<1>(X, W, T, H, E, ks, lg, s);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(k_route_topk, dim3((unsigned)((T + 3) / 4)), dim3(256), 0, s, lg, T, E, K, idx, w);
+  hipLaunchKernelGGL(k_route_topk, dim3((unsigned)((T + 3) / 4)), dim3(256), 0, s, lg, bias, ks, T, E, K, idx, w);
   return hipGetLastError();
 }
 
