@@ -498,12 +498,30 @@ def test_chunked_grouping_large_batch(layer_cache):
         X, z, r = oracle_route(L, Xb)
         assert np.array_equal(i1, z)
         assert_close(o1, O.moe_ffn(X, z, r, L), f"T={T}")
+        assert_close(o2, O.moe_ffn(X, z, r, L), f"T={T} fused")
         assert np.array_equal(o1.view(np.uint32), o2.view(np.uint32))
 
 
-def test_edge_one_expert_takes_all_and_extreme_bitwidths(layer_cache):
+@pytest.mark.parametrize("cfg,T", [(0, 400), (0, 1000), (11, 4000)])
+def test_prefill_items_every_element(cfg, T, layer_cache):
+    """Batches large enough for 128-token gate_up work items: every output
+    element against the oracle, with group sizes ragged against 128 and
+    hidden sizes 256 and 192 (even and uneven K halves)."""
+    L, D = dev_layer(layer_cache, cfg)
+    assert _prefill_items(L, T)
+    Xb = S.make_tokens(cfg, T=T, seed=8000 + T)
+    say(f"prefill items cfg{cfg}: T={T}")
+    gi, _, gout = run_layer(D, Xb, L.cfg["xdtype"])
+    X, z, r = oracle_route(L, Xb)
+    assert np.array_equal(gi, z)
+    assert_close(gout, O.moe_ffn(X, z, r, L), f"cfg{cfg} T={T}")
+
+
+@pytest.mark.parametrize("T", [150, 600])
+def test_edge_one_expert_takes_all_and_extreme_bitwidths(T, layer_cache):
+    """One group of T tokens per routed expert (zero logits tie); T = 600
+    takes 128-token gate_up items (4 full items and a ragged one)."""
     L, D = dev_layer(layer_cache, 10)
-    T = 150
     Xb = S.make_tokens(10, T=T, seed=99)
     X = S.f16_bits_to_f64(Xb)
     # every token picks experts 0..K-1 (zero logits tie), one group of 150 tokens
@@ -626,6 +644,13 @@ def _separate_and_fused(D, Xb, xdtype):
     torch.cuda.synchronize()
     return (idx.cpu().numpy(), w.cpu().numpy(), out.cpu().numpy(), idx2.cpu().numpy(), w2.cpu().numpy(),
             out2.cpu().numpy(), ws2)
+
+
+def _prefill_items(L, T):
+    """moe_ffn takes 128-token gate_up work items (four 32-token chunks per
+    dequantised weight operand) once a routed group holds 96 tokens on
+    average."""
+    return T * L.K // L.E >= 96
 
 
 @pytest.mark.parametrize("cfg", [0, 10, 11, 1, 2, 3])
