@@ -84,15 +84,12 @@ static size_t ffn_lds_bytes(int qmax) {
 
 template <int TC, bool GU>
 static hipError_t launch_tc(const FfnParams& p, int qmax, hipStream_t s) {
-  static bool attr_set = false;  // raise the dynamic LDS limit once per kernel
+  static unsigned long long lds_raised = 0;  // devices on which this kernel's LDS limit is raised
   const void* fn;
   if constexpr (GU) fn = (const void*)k_gate_up<TC>;
   else fn = (const void*)k_down<TC>;
-  if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)ffn_lds_bytes<TC>(8));
-    if (e != hipSuccess) return e;
-    attr_set = true;
-  }
+  const hipError_t e = raise_lds_limit(fn, (int)ffn_lds_bytes<TC>(8), lds_raised);
+  if (e != hipSuccess) return e;
   const size_t shmem = ffn_lds_bytes<TC>(qmax);
   if constexpr (GU)
     hipLaunchKernelGGL(k_gate_up<TC>, dim3(p.max_items * (p.I >> 6)), dim3(kThreads), shmem, s, p, qmax);

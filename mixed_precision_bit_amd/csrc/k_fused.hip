@@ -450,14 +450,11 @@ hipError_t launch_fused(const FusedLaunch& L, hipStream_t s) {
   P.slot_off = 0;
   const size_t shmem = fused_lds_bytes(L.qmax);
   const void* fn = L.xdt == 1 ? (const void*)k_fused<1> : (const void*)k_fused<0>;
-  static bool attr_set[2] = {false, false};
-  if (!attr_set[L.xdt]) {
-    hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)fused_lds_bytes(8));
-    if (e != hipSuccess) return e;
-    attr_set[L.xdt] = true;
-  }
+  static unsigned long long lds_raised[2] = {0, 0};  // per activation dtype: devices done
+  hipError_t e = raise_lds_limit(fn, (int)fused_lds_bytes(8), lds_raised[L.xdt]);
+  if (e != hipSuccess) return e;
   int per_cu = 0, dev = 0, cus = 0;
-  hipError_t e = hipGetDevice(&dev);
+  e = hipGetDevice(&dev);
   if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
   if (e == hipSuccess) e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, fn, kThreads, shmem);
   if (e != hipSuccess) return e;

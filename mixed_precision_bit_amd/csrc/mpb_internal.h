@@ -61,6 +61,20 @@ inline int max_decode_items(int T, int E, int S, int K) {
 }
 WsLayout ws_layout(int T, int H, int I, int E, int S, int K, bool bf16);
 
+// Raise a kernel's dynamic LDS limit to `bytes` on the current device, once
+// per device (bit d of `done` records device d; the library is driven from
+// one host thread).
+inline hipError_t raise_lds_limit(const void* fn, int bytes, unsigned long long& done) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  const unsigned long long bit = dev < 64 ? 1ull << dev : 0ull;
+  if (done & bit) return hipSuccess;
+  e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
+  if (e == hipSuccess) done |= bit;
+  return e;
+}
+
 hipError_t launch_pack(const uint32_t* canon, int N, int Kd, uint32_t* const* pages, hipStream_t s);
 hipError_t launch_pack_table(const uint16_t* lut, int kind, int N, int b, uint16_t* img, hipStream_t s);
 hipError_t launch_dequant(const uint32_t* const* pages, const uint16_t* lut, int N, int Kd, int b,

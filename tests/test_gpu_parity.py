@@ -502,6 +502,24 @@ def test_chunked_grouping_large_batch(layer_cache):
         assert np.array_equal(o1.view(np.uint32), o2.view(np.uint32))
 
 
+def test_largest_batch_sampled(layer_cache):
+    """A batch of 65536 tokens on the small layer: 131072 routed entries in 64
+    grouping chunks, 128-token gate_up items, 4096-item down lists. Routing
+    is compared for every token, outputs on a sample of tokens (the first,
+    the last and every 1021st); the one-launch path agrees bit for bit."""
+    L, D = dev_layer(layer_cache, 0)
+    T = 65536
+    Xb = S.make_tokens(0, T=T, seed=9000)
+    say(f"largest batch: cfg0 T={T}")
+    i1, w1, o1, i2, w2, o2, _ = _separate_and_fused(D, Xb, "f16")
+    X, z, r = oracle_route(L, Xb)
+    assert np.array_equal(i1, z)
+    toks = np.unique(np.concatenate([np.arange(0, T, 1021), [T - 1]]))
+    assert_close(o1[toks], O.moe_ffn(X[toks], z[toks], r[toks], L), f"T={T} sampled")
+    assert np.array_equal(i1, i2)
+    assert np.array_equal(o1.view(np.uint32), o2.view(np.uint32))
+
+
 @pytest.mark.parametrize("cfg,T", [(0, 400), (0, 1000), (11, 4000)])
 def test_prefill_items_every_element(cfg, T, layer_cache):
     """Batches large enough for 128-token gate_up work items: every output
