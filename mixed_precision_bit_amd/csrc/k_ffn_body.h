@@ -82,12 +82,18 @@ __device__ __forceinline__ void load_table_image(const uint16_t* img, int w, int
 __device__ __forceinline__ void wait_vmem_all() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
 // Half-chunk s of the wave's K half for every plane: lane (r, g) reads the 8
-// bytes at chunk cb + s, row r, half g.
-template <int Q>
+// bytes at chunk cb + s, row r, half g. NT: the loads carry the non-temporal
+// hint (cache policy bit 1), for launches that read each plane byte about
+// once (decode-size batches: one item per group); the weight stream then does
+// not displace activations and tables in the caches (measured: gate_up -4 %,
+// down -5 % at the qwen15moe decode size). Where the several items of a group
+// re-read its planes (prefill-size batches) the hint costs 5-12 %.
+template <int Q, bool NT>
 __device__ __forceinline__ void load_planes(uint2 (&P)[Q], const rsrc_t (&rs)[Q], int cb, int s, int voff) {
+  constexpr int kPolicy = NT ? 2 : 0;
 #pragma unroll
   for (int q = 0; q < Q; ++q)
-    P[q] = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(rs[q], (cb + s) * 512 + voff, 0, 0));
+    P[q] = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(rs[q], (cb + s) * 512 + voff, 0, kPolicy));
 }
 
 template <int Q>
@@ -154,13 +160,9 @@ __device__ __forceinline__ void store_window(char* stage, const uint4 (&v)[2][TC
       if (sp.live[c]) *(uint4*)(stage + sp.dst[i][c]) = k[i] < len ? v[i][c] : make_uint4(0u, 0u, 0u, 0u);
 }
 
-// Work item of a launch: workgroup id = item * ntile + tile, so the
-// consecutive workgroups that the dispatcher spreads over the chip carry the
-// tiles of one item and every workgroup below n_items * ntile has tokens.
-__device__ __forceinline__ bool decode_item(const FfnParams& p, bool gu, int ntile, int& e, int& tile, int& t0,
-                                            int& nt) {
-  const int item = blockIdx.x / ntile;
-  tile = blockIdx.x - item * ntile;
+// Item `item` of the gate_up (gu) or down list: its group e, first token t0
+// and token count nt; false past the end of the list.
+__device__ __forceinline__ bool item_of(const FfnParams& p, bool gu, int item, int& e, int& t0, int& nt) {
   if (item >= p.n_items[gu ? 0 : 1]) return false;
   const int v = (gu ? p.items : p.items_dn)[item];
   const int tpi = gu ? p.tpi : p.tpi_dn;
@@ -168,6 +170,30 @@ __device__ __forceinline__ bool decode_item(const FfnParams& p, bool gu, int nti
   t0 = (v & 0xffff) * tpi;
   nt = min(p.counts[e] - t0, tpi);
   return true;
+}
+
+// Work item of a launch: workgroup id = item * ntile + tile, so the
+// consecutive workgroups that the dispatcher spreads over the chip carry the
+// tiles of one item and every workgroup below n_items * ntile has tokens.
+__device__ __forceinline__ bool decode_item(const FfnParams& p, bool gu, int ntile, int& e, int& tile, int& t0,
+                                            int& nt) {
+  const int item = blockIdx.x / ntile;
+  tile = blockIdx.x - item * ntile;
+  return item_of(p, gu, item, e, t0, nt);
+}
+
+// The same items for launches that stream activations from L2 (128-token
+// items): the dispatcher hands workgroup b to XCD b % 8, and workgroup b takes
+// tile k % ntile of item 8 (k / ntile) + b % 8, k = b / 8. All tiles of an
+// item then run on one XCD, one after another, so its L2 serves the item's
+// activations to every tile; items are dealt to the XCDs in turn, which keeps
+// the bitwidth mix (the list is ordered by bitwidth) the same on every XCD.
+// Needs a grid of 8 * ceil(max_items / 8) * ntile workgroups.
+__device__ __forceinline__ bool decode_item_xcd(const FfnParams& p, bool gu, int ntile, int& e, int& tile, int& t0,
+                                                int& nt) {
+  const int k = blockIdx.x >> 3, li = k / ntile;
+  tile = k - li * ntile;
+  return item_of(p, gu, 8 * li + (blockIdx.x & 7), e, t0, nt);
 }
 
 // K split: a row has HC = Kd / 64 half-chunks; half 0 takes the first HH (even,
@@ -191,7 +217,7 @@ struct KSplit {
 // s, barrier, write the activations of step s+1 (loaded one step earlier) to
 // the stage, load the activations of step s+2, load the planes of step s+3,
 // barrier.
-template <int Q, int TC, bool CO = false>
+template <int Q, int TC, bool CO = false, bool NT = (TC == 1)>
 __device__ __forceinline__ void gate_up_body(const FfnParams& p, int e, int it, int t0, int nt, uint16_t* lds,
                                              uint32_t lut_bytes, int tid) {
   const int lane = tid & 63, r = lane & 31, g = lane >> 5;
@@ -238,13 +264,13 @@ __device__ __forceinline__ void gate_up_body(const FfnParams& p, int e, int it, 
   load_table_image<Q>(p.luts[blk * 6 + (Q - 3)] + (size_t)it * (128u << Q), w, lane);
   kwin(0, kk);
   load_window<TC>(xr, sp, kk, H);
-  load_planes<Q>(PA, rs, cb, 0, voff);
+  load_planes<Q, NT>(PA, rs, cb, 0, voff);
   wait_vmem_all();
   store_window<TC>(stage, xr, sp, kk, H);
-  load_planes<Q>(PB, rs, cb, 1, voff);
+  load_planes<Q, NT>(PB, rs, cb, 1, voff);
   kwin(1, kk);
   load_window<TC>(xr, sp, kk, H);
-  load_planes<Q>(PC, rs, cb, 2, voff);
+  load_planes<Q, NT>(PC, rs, cb, 2, voff);
   __syncthreads();
 
   f32x16 acc[TC];
@@ -273,7 +299,7 @@ __device__ __forceinline__ void gate_up_body(const FfnParams& p, int e, int it, 
     }
     kwin(s + 2, kk);
     load_window<TC>(xr, sp, kk, H);
-    load_planes<Q>(P, rs, cb, s + 3, voff);
+    load_planes<Q, NT>(P, rs, cb, s + 3, voff);
     __syncthreads();
   };
   // whole ring turns in the loop, the remainder after it: the loop's back edge
@@ -337,7 +363,7 @@ __device__ __forceinline__ void poison(float* dst, size_t ld, int rows, int cols
 // elements 32 j + 8 m .. + 7 of half-chunk 2 s + g', hi (hl = 0) or lo
 // (hl = 1), for round j. Each window is loaded one step before it is staged,
 // ahead of the plane load that follows it.
-template <int Q, int TC, bool CO = false>
+template <int Q, int TC, bool CO = false, bool NT = true>
 __device__ __forceinline__ void down_body(const FfnParams& p, int e, int it, int t0, int nt, uint16_t* lds,
                                           uint32_t lut_bytes, int tid) {
   const int lane = tid & 63, r = lane & 31, g = lane >> 5;
@@ -382,15 +408,15 @@ __device__ __forceinline__ void down_body(const FfnParams& p, int e, int it, int
   load_table_image<Q>(p.luts[blk * 6 + (Q - 3)] + (size_t)it * (128u << Q), w, lane);
   kwin(0, 0, ka);
   load_window<TC>(ha, sp, ka, I);
-  load_planes<Q>(PA, rs, cb, 0, voff);
+  load_planes<Q, NT>(PA, rs, cb, 0, voff);
   wait_vmem_all();
   store_window<TC>(stage, ha, sp, ka, I);
   kwin(0, 1, kb);
   load_window<TC>(hb, sp, kb, I);
   kwin(1, 0, ka);
   load_window<TC>(ha, sp, ka, I);
-  load_planes<Q>(PB, rs, cb, 1, voff);
-  load_planes<Q>(PC, rs, cb, 2, voff);
+  load_planes<Q, NT>(PB, rs, cb, 1, voff);
+  load_planes<Q, NT>(PC, rs, cb, 2, voff);
   __syncthreads();
 
   f32x16 acc[TC];
@@ -427,7 +453,7 @@ __device__ __forceinline__ void down_body(const FfnParams& p, int e, int it, int
     }
     kwin(s + 2, 0, ka);
     load_window<TC>(ha, sp, ka, I);
-    load_planes<Q>(P, rs, cb, s + 3, voff);
+    load_planes<Q, NT>(P, rs, cb, s + 3, voff);
     __syncthreads();
   };
   int s = 0;

@@ -10,7 +10,8 @@ template <int TC>
 __global__ __launch_bounds__(kThreads) void k_gate_up(FfnParams p, int qmax) {
   extern __shared__ __attribute__((aligned(256))) uint16_t lds[];
   int e, it, t0, nt;
-  if (!decode_item(p, true, p.I >> 6, e, it, t0, nt)) return;
+  if (!(TC == 4 ? decode_item_xcd(p, true, p.I >> 6, e, it, t0, nt) : decode_item(p, true, p.I >> 6, e, it, t0, nt)))
+    return;
   const int q = p.q[2 * e];
   const uint32_t lut_bytes = 256u << qmax;
   switch (q < 3 || q > qmax || !tables_at_zero(lds) ? 0 : q) {
@@ -31,7 +32,8 @@ __global__ __launch_bounds__(kThreads) void k_gate_up(FfnParams p, int qmax) {
 }
 
 
-template <int TC>
+// NT: non-temporal plane loads (decode-size batches, see load_planes)
+template <int TC, bool NT>
 __global__ __launch_bounds__(kThreads) void k_down(FfnParams p, int qmax) {
   extern __shared__ __attribute__((aligned(256))) uint16_t lds[];
   int e, it, t0, nt;
@@ -39,12 +41,12 @@ __global__ __launch_bounds__(kThreads) void k_down(FfnParams p, int qmax) {
   const int q = p.q[2 * e + 1];
   const uint32_t lut_bytes = 256u << qmax;
   switch (q < 3 || q > qmax || !tables_at_zero(lds) ? 0 : q) {
-    case 3: down_body<3, TC>(p, e, it, t0, nt, lds, lut_bytes, threadIdx.x); break;
-    case 4: down_body<4, TC>(p, e, it, t0, nt, lds, lut_bytes, threadIdx.x); break;
-    case 5: down_body<5, TC>(p, e, it, t0, nt, lds, lut_bytes, threadIdx.x); break;
-    case 6: down_body<6, TC>(p, e, it, t0, nt, lds, lut_bytes, threadIdx.x); break;
-    case 7: down_body<7, TC>(p, e, it, t0, nt, lds, lut_bytes, threadIdx.x); break;
-    case 8: down_body<8, TC>(p, e, it, t0, nt, lds, lut_bytes, threadIdx.x); break;
+    case 3: down_body<3, TC, false, NT>(p, e, it, t0, nt, lds, lut_bytes, threadIdx.x); break;
+    case 4: down_body<4, TC, false, NT>(p, e, it, t0, nt, lds, lut_bytes, threadIdx.x); break;
+    case 5: down_body<5, TC, false, NT>(p, e, it, t0, nt, lds, lut_bytes, threadIdx.x); break;
+    case 6: down_body<6, TC, false, NT>(p, e, it, t0, nt, lds, lut_bytes, threadIdx.x); break;
+    case 7: down_body<7, TC, false, NT>(p, e, it, t0, nt, lds, lut_bytes, threadIdx.x); break;
+    case 8: down_body<8, TC, false, NT>(p, e, it, t0, nt, lds, lut_bytes, threadIdx.x); break;
     default: {
       const int n0 = it * 128;
       poison(p.y + (size_t)(p.offsets[e] + t0) * p.H + n0, p.H, nt, min(128, p.H - n0));
@@ -82,19 +84,21 @@ static size_t ffn_lds_bytes(int qmax) {
   return std::max<size_t>((256u << qmax) + stage_bytes<TC>(), kWaves * 16 * 64 * 4);
 }
 
-template <int TC, bool GU>
+template <int TC, bool GU, bool NT = true>
 static hipError_t launch_tc(const FfnParams& p, int qmax, hipStream_t s) {
   static unsigned long long lds_raised = 0;  // devices on which this kernel's LDS limit is raised
   const void* fn;
   if constexpr (GU) fn = (const void*)k_gate_up<TC>;
-  else fn = (const void*)k_down<TC>;
+  else fn = (const void*)k_down<TC, NT>;
   const hipError_t e = raise_lds_limit(fn, (int)ffn_lds_bytes<TC>(8), lds_raised);
   if (e != hipSuccess) return e;
   const size_t shmem = ffn_lds_bytes<TC>(qmax);
+  // 128-token items take the XCD-interleaved order (decode_item_xcd)
+  const int items = TC == 4 ? (p.max_items + 7) / 8 * 8 : p.max_items;
   if constexpr (GU)
-    hipLaunchKernelGGL(k_gate_up<TC>, dim3(p.max_items * (p.I >> 6)), dim3(kThreads), shmem, s, p, qmax);
+    hipLaunchKernelGGL(k_gate_up<TC>, dim3(items * (p.I >> 6)), dim3(kThreads), shmem, s, p, qmax);
   else
-    hipLaunchKernelGGL(k_down<TC>, dim3(p.max_items * ((p.H + 127) >> 7)), dim3(kThreads), shmem, s, p, qmax);
+    hipLaunchKernelGGL((k_down<TC, NT>), dim3(p.max_items * ((p.H + 127) >> 7)), dim3(kThreads), shmem, s, p, qmax);
   return hipGetLastError();
 }
 
@@ -106,7 +110,9 @@ hipError_t launch_gate_up(const FfnParams& p, int qmax, int tc, hipStream_t s) {
   }
 }
 
-hipError_t launch_down(const FfnParams& p, int qmax, hipStream_t s) { return launch_tc<1, false>(p, qmax, s); }
+hipError_t launch_down(const FfnParams& p, int qmax, bool nt, hipStream_t s) {
+  return nt ? launch_tc<1, false, true>(p, qmax, s) : launch_tc<1, false, false>(p, qmax, s);
+}
 
 hipError_t launch_combine(const FfnParams& p, hipStream_t s) {
   const size_t n = (size_t)p.T * (p.H >> 2);

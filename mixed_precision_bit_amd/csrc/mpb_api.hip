@@ -338,7 +338,7 @@ int moe_ffn(const void* X_dev, int x_dtype, int T, const int32_t* topk_idx_dev, 
   if (q_dev != g.q_dev) return fail(MPB_E_ARG, "moe_ffn: q_dev is not the bound page table");
   const mpb::WsLayout L = mpb::ws_layout(T, g.H, g.I, g.E, g.S, g.K, x_dtype == MPB_BF16);
   const long long ntile = std::max(g.I / 64, (g.H + 127) / 128);
-  if ((long long)L.max_items * ntile >= (1ll << 31)) return fail(MPB_E_SHAPE, "moe_ffn: T too large for this layer");
+  if (((long long)L.max_items + 7) / 8 * 8 * ntile >= (1ll << 31)) return fail(MPB_E_SHAPE, "moe_ffn: T too large for this layer");
   if (ws_bytes < L.total)
     return fail(MPB_E_WS, "moe_ffn: workspace " + std::to_string(ws_bytes) + " < " + std::to_string(L.total));
   char* ws = (char*)ws_dev;
@@ -363,7 +363,7 @@ int moe_ffn(const void* X_dev, int x_dtype, int T, const int32_t* topk_idx_dev, 
   e = mpb::launch_gate_up(p, qmax_gu, tc, s);
   if (e != hipSuccess) return hip_fail(e, "moe_ffn: gate_up");
   mark(2, s);
-  e = mpb::launch_down(p, qmax_dn, s);
+  e = mpb::launch_down(p, qmax_dn, tc == 1, s);
   if (e != hipSuccess) return hip_fail(e, "moe_ffn: down");
   mark(3, s);
   e = mpb::launch_combine(p, s);

@@ -95,7 +95,8 @@ hipError_t launch_x_to_f16(const uint16_t* x, uint16_t* y, size_t n, hipStream_t
 // qmax: highest committed bitwidth among the launch's blocks (sizes the LDS
 // table region; a block above it yields NaN)
 hipError_t launch_gate_up(const FfnParams& p, int qmax, int tc, hipStream_t s);
-hipError_t launch_down(const FfnParams& p, int qmax, hipStream_t s);
+// nt: non-temporal plane loads (decode-size batches, one item per group)
+hipError_t launch_down(const FfnParams& p, int qmax, bool nt, hipStream_t s);
 hipError_t launch_combine(const FfnParams& p, hipStream_t s);
 hipError_t launch_set_q(int32_t* q, int i, int b, hipStream_t s);
 
