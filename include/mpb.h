@@ -178,7 +178,8 @@ size_t moe_ffn_workspace_bytes(int T);
  * bitwidth in the host mirror; a graph captured from this call must be
  * captured again after a block is raised above that bitwidth (its outputs
  * would otherwise be NaN, never silently wrong).
- * Results are deterministic for T <= 256 (no order-dependent atomics).
+ * Results are deterministic for every T: the grouping counts with integer
+ * atomics only, and every floating-point sum runs in a fixed order.
  * Errors: MPB_E_UNINIT, MPB_E_ARG, MPB_E_WS, MPB_E_HIP.
  */
 int moe_ffn(const void* X_dev, int x_dtype, int T, const int32_t* topk_idx_dev,
