@@ -9,23 +9,24 @@
 // q_i between launches takes effect on the next launch.
 //
 // Mapping (MFMA 32x32x16 fp16 -> fp32): a workgroup of 8 waves handles up to
-// 32 tokens of one expert and 128 weight rows: wave w owns row group w % 4
-// (32 rows) and K half w / 4, so two waves share every row's centroid table
-// and the table region costs half as much LDS per wave. Lane l holds row l%32;
-// in step s it reads half-chunk 2s + l/32 of its K half (2 words = 64
-// elements) from each of the q plane pages: one 8-byte load per page, the 64
-// lanes of a wave covering one 512-byte chunk of 32 rows, issued three steps
-// ahead. Each word feeds four MFMAs as the A operand.
+// TC x 32 tokens of one expert (TC = 1 at decode sizes, 4 for prefill-size
+// groups) and 128 weight rows: wave w owns row group w % 4 (32 rows) and K
+// half w / 4, so two waves share every row's centroid table and the table
+// region costs half as much LDS per wave. Lane l holds row l%32; in step s it
+// reads half-chunk 2s + l/32 of its K half (2 words = 64 elements) from each
+// of the q plane pages: one 8-byte load per page, the 64 lanes of a wave
+// covering one 512-byte chunk of 32 rows, issued three steps ahead. Each
+// dequantised A operand feeds TC MFMAs, one per 32-token chunk.
 //
-// The B operand (the tokens) is staged into LDS by the whole workgroup and read
-// with ds_read_b128: with the weights the only vector memory traffic in the
-// loop, waits on the activations never queue behind the long-latency plane
-// loads (vector-memory completions are counted in issue order).
+// The B operand (the tokens) is staged into LDS by the whole workgroup between
+// the two barriers of a step and read with ds_read_b128, so the waits of the
+// multiply part of a step are on plane loads only (vector-memory completions
+// are counted in issue order).
 //
-// LDS: [centroid tables: 2^qmax * 256 bytes][stage: 2 halves x 32 tokens x
-// 256 bytes]. Piece p (16 bytes) of token t of a half sits at p ^ (t % 16), so
-// the 16 lanes of one ds_read_b128 phase, which read one piece of 16 tokens,
-// hit distinct banks.
+// LDS: [centroid tables: 2^qmax * 256 bytes][stage: 2 halves x TC x 32 tokens
+// x 256 bytes]. Piece p (16 bytes) of token t of a half sits at p ^ (t % 16),
+// so the 16 lanes of one ds_read_b128 phase, which read one piece of 16
+// tokens, hit distinct banks.
 #pragma once
 
 #include <algorithm>

@@ -1,5 +1,7 @@
-// Decode-size expert FFN kernels: gate_up + SwiGLU, down, and the weighted
-// combine, one launch each (the device code is in k_ffn_body.h).
+// Expert FFN kernels: gate_up + SwiGLU, down, and the weighted combine, one
+// launch each (the device code is in k_ffn_body.h). Items of 32 tokens at
+// decode sizes; gate_up takes 128-token items (TC = 4), in the XCD-interleaved
+// order, once groups hold 96 tokens on average.
 #include <algorithm>
 
 #include "k_ffn_body.h"
