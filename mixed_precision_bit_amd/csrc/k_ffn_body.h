@@ -497,16 +497,38 @@ template <bool CO = false>
 __device__ __forceinline__ void combine4(const FfnParams& p, int t, int n) {
   const int KS = p.K + p.S;
   f32x4 s = (f32x4){};
-  for (int k = 0; k < p.K; ++k) {
-    const int ex = ld_co<CO>(p.topk_idx + t * p.K + k);
-    if (ex >= 0 && ex < p.E) {
-      const int pos = ld_co<CO>(p.inv + t * KS + k);
-      s += ld_co<CO>(p.topk_w + t * p.K + k) * *(const f32x4*)(p.y + (size_t)pos * p.H + n);
+  // entries are taken 8 at a time: their ids, positions and weights are loaded
+  // together, then their rows of y, then summed in entry order (the loads
+  // overlap; the sum is the same)
+  for (int k0 = 0; k0 < KS; k0 += 8) {
+    int pos[8];
+    float w[8];
+    bool live[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int k = k0 + j;
+      live[j] = false;
+      w[j] = 1.0f;
+      pos[j] = 0;
+      if (k < p.K) {
+        const int ex = ld_co<CO>(p.topk_idx + t * p.K + k);
+        live[j] = ex >= 0 && ex < p.E;
+        w[j] = ld_co<CO>(p.topk_w + t * p.K + k);
+        pos[j] = ld_co<CO>(p.inv + t * KS + k);
+      } else if (k < KS) {
+        live[j] = true;
+        pos[j] = ld_co<CO>(p.inv + t * KS + k);
+      }
     }
-  }
-  for (int sh = 0; sh < p.S; ++sh) {
-    const int pos = ld_co<CO>(p.inv + t * KS + p.K + sh);
-    s += *(const f32x4*)(p.y + (size_t)pos * p.H + n);
+    f32x4 y[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) y[j] = live[j] ? *(const f32x4*)(p.y + (size_t)pos[j] * p.H + n) : (f32x4){};
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      if (!live[j]) continue;
+      if (k0 + j < p.K) s += w[j] * y[j];
+      else s += y[j];
+    }
   }
   *(f32x4*)(p.out + (size_t)t * p.H + n) = s;
 }
