@@ -387,10 +387,10 @@ def plan_step(H, I, E, S, q, movable, s, mass, phi, P):
     def shape(i):
         return (2 * I, H) if i % 2 == 0 else (H, I)
 
-    D = kv_target_bytes(P["T_blk"], P["F_blk"] - P["P_blk"], P["B_kv"])   # line 4
+    D = kv_target_bytes(P["T_blk"], P["F_blk"] - P["P_blk"], P["B_kv"])   # bytes to release (Eq. 7)
     bucket = routing_buckets(mass, P["bucket_frac"])
     queue, stats = {}, []
-    for st, sfloor in enumerate(P["stage_floor"]):                         # lines 5-9
+    for st, sfloor in enumerate(P["stage_floor"]):                         # one candidate plan per stage
         # ScoreActions: floors of this stage; every step is scored lazily below
         cur = [int(x) for x in q]
         floor = [None] * nb
@@ -419,7 +419,7 @@ def plan_step(H, I, E, S, q, movable, s, mass, phi, P):
             step_dmg[i] += d
         queue[st] = cur                                                    # RefreshPlanQueue
         stats.append((released, damage, step_dmg))
-    triggered = P["F_blk"] <= P["T_blk"]                                   # line 10
+    triggered = P["F_blk"] <= P["T_blk"]                                   # memory pressure
     pick = None
     for st in range(len(P["stage_floor"])):                                # SelectBestPlan
         if stats[st][0] >= D:
