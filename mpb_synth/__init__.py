@@ -54,6 +54,17 @@ CONFIGS = {
              q_mode="uniform", bias=False, seed=1010),
     11: dict(name="sparse_bf16", H=192, I=192, E=40, S=0, K=1, T=9, xdtype="bf16",
              q_mode="uniform", bias=True, seed=1011, zipf=1.1),
+    # parity-only extremes: the smallest dimensions (one half-chunk of K, one
+    # row tile) with a single expert; more shared than routed experts; the
+    # largest top-K; the largest expert count with one token
+    12: dict(name="minimal", H=64, I=64, E=1, S=0, K=1, T=5, xdtype="f16",
+             q_mode="uniform", bias=False, seed=1012),
+    13: dict(name="shared_heavy", H=128, I=192, E=2, S=3, K=2, T=40, xdtype="bf16",
+             q_mode="uniform", bias=True, seed=1013, zipf=1.1),
+    14: dict(name="top16", H=320, I=128, E=64, S=0, K=16, T=33, xdtype="f16",
+             q_mode="uniform", bias=False, seed=1014),
+    15: dict(name="e512_one_token", H=64, I=64, E=512, S=0, K=8, T=1, xdtype="f16",
+             q_mode="uniform", bias=False, seed=1015),
 }
 
 LUT_STD = 0.02  # centroid draws ~ N(0, 0.02)

@@ -520,6 +520,26 @@ def test_largest_batch_sampled(layer_cache):
     assert np.array_equal(o1.view(np.uint32), o2.view(np.uint32))
 
 
+@pytest.mark.parametrize("cfg", [12, 13, 14, 15])
+def test_edge_shapes_every_element(cfg, layer_cache):
+    """Extreme layer shapes, every element against the oracle on both paths:
+    one expert with H = I = 64 (a single K half-chunk and row tile), more
+    shared than routed experts with bf16 input and a router bias, top-16 of
+    64 experts, and 512 experts for a single token. The one-launch path
+    agrees bit for bit."""
+    L, D = dev_layer(layer_cache, cfg)
+    Xb = S.make_tokens(cfg)
+    xdtype = L.cfg["xdtype"]
+    say(f"edge shape cfg{cfg} ({L.cfg['name']}): H={L.H} I={L.I} E={L.E} S={L.S} K={L.K} T={Xb.shape[0]}")
+    i1, w1, o1, i2, w2, o2, _ = _separate_and_fused(D, Xb, xdtype)
+    X, z, r = oracle_route(L, Xb)
+    assert np.array_equal(i1, z)
+    assert_close(w1, r, f"cfg{cfg} routing weights")
+    assert_close(o1, O.moe_ffn(X, z, r, L), f"cfg{cfg} output")
+    assert np.array_equal(i1, i2)
+    assert np.array_equal(o1.view(np.uint32), o2.view(np.uint32))
+
+
 @pytest.mark.parametrize("cfg,T", [(0, 400), (0, 1000), (11, 4000)])
 def test_prefill_items_every_element(cfg, T, layer_cache):
     """Batches large enough for 128-token gate_up work items: every output
