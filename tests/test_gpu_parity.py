@@ -520,6 +520,23 @@ def test_largest_batch_sampled(layer_cache):
     assert np.array_equal(o1.view(np.uint32), o2.view(np.uint32))
 
 
+def test_activation_beyond_fp16_range_is_not_silently_wrong(layer_cache):
+    """bf16 activations are converted to fp16 for the matrix cores, whose
+    range ends at 65504: a token with entries beyond it comes out non-finite
+    (never a finite wrong value), and every other token is unaffected and
+    held to the oracle."""
+    L, D = dev_layer(layer_cache, 11)
+    Xb = S.make_tokens(11).copy()
+    bad = 4
+    Xb[bad] = S.f32_to_bf16_bits((S.bf16_bits_to_f64(Xb[bad]) * 1e6).astype(np.float32))
+    gi, _, gout = run_layer(D, Xb, "bf16")
+    X, z, r = oracle_route(L, Xb)
+    assert np.array_equal(gi, z)
+    assert not np.isfinite(gout[bad]).all()
+    ok = np.arange(Xb.shape[0]) != bad
+    assert_close(gout[ok], O.moe_ffn(X[ok], z[ok], r[ok], L), "other tokens")
+
+
 @pytest.mark.parametrize("cfg", [12, 13, 14, 15])
 def test_edge_shapes_every_element(cfg, layer_cache):
     """Extreme layer shapes, every element against the oracle on both paths:
