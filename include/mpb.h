@@ -129,7 +129,8 @@ int mpb_pack_table(int kind, const uint16_t* lut_dev, int N, int b, uint16_t* im
  * winners and renormalised (equal to a softmax over the K winning logits).
  * ws_dev: device workspace of ws_bytes >= moe_route_workspace_bytes(T, E)
  * (fp64 logits, summed in up to 8 hidden-dimension parts for small batches;
- * contents not preserved). Needs
+ * unused for batches of up to 128 tokens with E * H <= 16384, whose logits
+ * stay on chip; contents not preserved). Needs
  * 1 <= K <= min(E, 16), E <= 512, H a multiple of 64 up to 65536, T <= 2^20;
  * T == 0 is a no-op. Errors: MPB_E_ARG, MPB_E_SHAPE, MPB_E_WS, MPB_E_HIP.
  * Does not need mpb_init.
@@ -195,7 +196,10 @@ int moe_ffn(const void* X_dev, int x_dtype, int T, const int32_t* topk_idx_dev,
  * combine) and wait on device counters for the units they read from; a down
  * tile starts as soon as its own group's gate_up tiles are done. Results are
  * bit-identical to moe_route + moe_ffn on the same inputs (same arithmetic,
- * same order). Arguments as for those two calls; topk_idx_dev / topk_w_dev
+ * same order), except that for batches of up to 128 tokens with at most 16384
+ * router weights moe_route sums each fp64 logit in another fixed order, which
+ * can change an fp32 routing weight only if the fp64 value lies within an ulp
+ * of an fp32 rounding boundary. Arguments as for those two calls; topk_idx_dev / topk_w_dev
  * receive the routing. ws_dev: at least moe_fused_workspace_bytes(T) bytes,
  * 256-byte aligned; its first moe_fused_counter_bytes() bytes are counters
  * that must be zero before the first call with this workspace (allocate it
