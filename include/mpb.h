@@ -198,8 +198,9 @@ int moe_ffn(const void* X_dev, int x_dtype, int T, const int32_t* topk_idx_dev,
  * bit-identical to moe_route + moe_ffn on the same inputs (same arithmetic,
  * same order), except that for batches of up to 128 tokens with at most 16384
  * router weights moe_route sums each fp64 logit in another fixed order, which
- * can change an fp32 routing weight only if the fp64 value lies within an ulp
- * of an fp32 rounding boundary. Arguments as for those two calls; topk_idx_dev / topk_w_dev
+ * can change the routing only where two logits lie within an fp64 ulp of a
+ * tie or a weight within one of an fp32 rounding boundary. Arguments as for
+ * those two calls; topk_idx_dev / topk_w_dev
  * receive the routing. ws_dev: at least moe_fused_workspace_bytes(T) bytes,
  * 256-byte aligned; its first moe_fused_counter_bytes() bytes are counters
  * that must be zero before the first call with this workspace (allocate it
