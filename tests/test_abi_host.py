@@ -80,3 +80,15 @@ def test_host_validation_without_device(L):
     assert L.moe_routing_mass(one, one, 4, 0, 1, one, None) == -2     # E
     assert L.moe_routing_mass(one, one, 4, 8, 9, one, None) == -2     # K > E
     assert L.moe_routing_mass(one, one, 4, 8, 2, None, None) == -1    # null output
+
+
+def test_bench_refuses_more_than_one_gpu():
+    """bench.py measures one GPU; asked for more it exits with status 2 and a
+    message, before touching any device."""
+    import subprocess
+    import sys
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    r = subprocess.run([sys.executable, os.path.join(root, "bench.py"), "--gpus", "2"], capture_output=True,
+                       text=True, timeout=300)
+    assert r.returncode == 2
+    assert "one GPU only" in (r.stdout + r.stderr)
