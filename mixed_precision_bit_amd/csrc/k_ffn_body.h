@@ -49,6 +49,17 @@ __device__ __forceinline__ uint32_t stage_off(int kh, int t, int piece) {
 template <int TC>
 constexpr int stage_bytes() { return 2 * TC * kTok * 256; }
 
+// Items of at most 16 tokens (TC = 1) split the same region into two stage
+// buffers of [K half][16 tokens][16 pieces]; step s reads buffer s % 2 while
+// the activations of step s + 1 are written to the other one, so a step needs
+// one workgroup barrier instead of two. MFMA columns 16..31 read tokens 0..15
+// again; those output columns are never stored.
+constexpr int kDbTok = 16;
+__device__ __forceinline__ uint32_t stage_off_db(int s, int kh, int t, int piece) {
+  return (uint32_t)(s & 1) * (2 * kDbTok * 256u) + (uint32_t)kh * (kDbTok * 256u) + t * 256u +
+         ((piece ^ (t & 15)) << 4);
+}
+
 // Plane loads go through buffer descriptors, one per plane page, based at the
 // wave's 32-row tile and spanning its NC chunks; an offset past the tile
 // (padding half-chunks, prefetches past the end) reads zeros without touching
@@ -217,8 +228,9 @@ struct KSplit {
 // for one load also waits for every older one): compute on the planes of step
 // s, barrier, write the activations of step s+1 (loaded one step earlier) to
 // the stage, load the activations of step s+2, load the planes of step s+3,
-// barrier.
-template <int Q, int TC, bool CO = false, bool NT = (TC == 1)>
+// barrier. DB (items of <= 16 tokens, TC = 1): the stage is double-buffered
+// and the first of the two barriers is dropped.
+template <int Q, int TC, bool CO = false, bool NT = (TC == 1), bool DB = false>
 __device__ __forceinline__ void gate_up_body(const FfnParams& p, int e, int it, int t0, int nt, uint16_t* lds,
                                              uint32_t lut_bytes, int tid) {
   const int lane = tid & 63, r = lane & 31, g = lane >> 5;
@@ -242,9 +254,10 @@ __device__ __forceinline__ void gate_up_body(const FfnParams& p, int e, int it, 
     const int t = kTok * c + st;
     sp.live[c] = t < nt;
     sp.row[c] = p.xh + (size_t)ld_co<CO>(p.ptok + base + (sp.live[c] ? t : 0)) * H;
-    sp.dst[0][c] = stage_off<TC>(0, t, spc);
-    sp.dst[1][c] = stage_off<TC>(1, t, spc);
+    sp.dst[0][c] = DB ? stage_off_db(0, 0, t & 15, spc) : stage_off<TC>(0, t, spc);
+    sp.dst[1][c] = DB ? stage_off_db(0, 1, t & 15, spc) : stage_off<TC>(1, t, spc);
   }
+  static_assert(!DB || TC == 1, "double-buffered stage: one token chunk");
   auto kwin = [&](int s, int (&k)[2]) {
 #pragma unroll
     for (int i = 0; i < 2; ++i) k[i] = (i * ks.HH + 2 * s + (spc >> 3)) * 64 + 8 * (spc & 7);
@@ -277,7 +290,9 @@ __device__ __forceinline__ void gate_up_body(const FfnParams& p, int e, int it, 
   f32x16 acc[TC];
 #pragma unroll
   for (int c = 0; c < TC; ++c) acc[c] = (f32x16){};
-  auto step = [&](int s, uint2 (&P)[Q]) {
+  // par = s % 2 (the stage buffer of step s when DB), passed as a constant so
+  // that the buffer offset folds into the LDS instructions' offset field
+  auto step = [&](int s, uint2 (&P)[Q], int par) {
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
       uint32_t Pw[Q], O[8];
@@ -288,15 +303,17 @@ __device__ __forceinline__ void gate_up_body(const FfnParams& p, int e, int it, 
         const f16x8 a = lookup8(O[2 * m], O[2 * m + 1], slot);
 #pragma unroll
         for (int c = 0; c < TC; ++c) {
-          const f16x8 b = *(const f16x8*)(stage + stage_off<TC>(kh, kTok * c + r, 8 * g + 4 * j + m));
+          const uint32_t bo = DB ? stage_off_db(par, kh, r & 15, 8 * g + 4 * j + m)
+                                 : stage_off<TC>(kh, kTok * c + r, 8 * g + 4 * j + m);
+          const f16x8 b = *(const f16x8*)(stage + bo);
           acc[c] = mfma32(a, b, acc[c]);
         }
       }
     }
-    __syncthreads();
+    if (!DB) __syncthreads();
     if (s + 1 < ks.NSW) {
       kwin(s + 1, kk);
-      store_window<TC>(stage, xr, sp, kk, H);
+      store_window<TC>(stage + (DB ? stage_off_db(par ^ 1, 0, 0, 0) : 0u), xr, sp, kk, H);
     }
     kwin(s + 2, kk);
     load_window<TC>(xr, sp, kk, H);
@@ -305,14 +322,31 @@ __device__ __forceinline__ void gate_up_body(const FfnParams& p, int e, int it, 
   };
   // whole ring turns in the loop, the remainder after it: the loop's back edge
   // then always follows a PC step, which keeps the wait counts exact
+  // (DB: six steps per turn, so that the buffer parity is fixed per position)
   int s = 0;
-  for (; s + 3 <= ks.NSW; s += 3) {
-    step(s, PA);
-    step(s + 1, PB);
-    step(s + 2, PC);
+  if constexpr (DB) {
+    for (; s + 6 <= ks.NSW; s += 6) {
+      step(s, PA, 0);
+      step(s + 1, PB, 1);
+      step(s + 2, PC, 0);
+      step(s + 3, PA, 1);
+      step(s + 4, PB, 0);
+      step(s + 5, PC, 1);
+    }
+    if (s < ks.NSW) step(s, PA, 0);
+    if (s + 1 < ks.NSW) step(s + 1, PB, 1);
+    if (s + 2 < ks.NSW) step(s + 2, PC, 0);
+    if (s + 3 < ks.NSW) step(s + 3, PA, 1);
+    if (s + 4 < ks.NSW) step(s + 4, PB, 0);
+  } else {
+    for (; s + 3 <= ks.NSW; s += 3) {
+      step(s, PA, 0);
+      step(s + 1, PB, 0);
+      step(s + 2, PC, 0);
+    }
+    if (s < ks.NSW) step(s, PA, 0);
+    if (s + 1 < ks.NSW) step(s + 1, PB, 0);
   }
-  if (s < ks.NSW) step(s, PA);
-  if (s + 1 < ks.NSW) step(s + 1, PB);
 
   // hand the accumulators to waves 0/1, one token chunk at a time; layout
   // [wave][v][lane]; gate = own + wave w+4, up = waves w+2 and w+6, each sum in
@@ -363,8 +397,10 @@ __device__ __forceinline__ void poison(float* dst, size_t ld, int rows, int cols
 // one per word of the half-chunk; piece p = 8 hl + 4 g' + m of a token holds
 // elements 32 j + 8 m .. + 7 of half-chunk 2 s + g', hi (hl = 0) or lo
 // (hl = 1), for round j. Each window is loaded one step before it is staged,
-// ahead of the plane load that follows it.
-template <int Q, int TC, bool CO = false, bool NT = true>
+// ahead of the plane load that follows it. DB (items of <= 16 tokens, TC = 1):
+// round j reads stage buffer j while the next round's window is written to
+// the other one, two barriers per step instead of four.
+template <int Q, int TC, bool CO = false, bool NT = true, bool DB = false>
 __device__ __forceinline__ void down_body(const FfnParams& p, int e, int it, int t0, int nt, uint16_t* lds,
                                           uint32_t lut_bytes, int tid) {
   const int lane = tid & 63, r = lane & 31, g = lane >> 5;
@@ -386,9 +422,12 @@ __device__ __forceinline__ void down_body(const FfnParams& p, int e, int it, int
     const int t = kTok * c + st;
     sp.live[c] = t < nt;
     sp.row[c] = (hl ? p.hlo : p.hhi) + (size_t)(base + (sp.live[c] ? t : 0)) * I;
-    sp.dst[0][c] = stage_off<TC>(0, t, spc);
-    sp.dst[1][c] = stage_off<TC>(1, t, spc);
+    sp.dst[0][c] = DB ? stage_off_db(0, 0, t & 15, spc) : stage_off<TC>(0, t, spc);
+    sp.dst[1][c] = DB ? stage_off_db(0, 1, t & 15, spc) : stage_off<TC>(1, t, spc);
   }
+  static_assert(!DB || TC == 1, "double-buffered stage: one token chunk");
+  // stage buffer of round j (DB)
+  auto rbuf = [&](int j) -> uint32_t { return DB ? stage_off_db(j, 0, 0, 0) : 0u; };
   // window (s, j): for K half i, element 64 (i HH + 2 s + g') + 32 j + 8 m
   auto kwin = [&](int s, int j, int (&k)[2]) {
 #pragma unroll
@@ -432,25 +471,28 @@ __device__ __forceinline__ void down_body(const FfnParams& p, int e, int it, int
       const f16x8 a = lookup8(O[2 * m], O[2 * m + 1], slot);
 #pragma unroll
       for (int c = 0; c < TC; ++c) {
-        const f16x8 bh = *(const f16x8*)(stage + stage_off<TC>(kh, kTok * c + r, 4 * g + m));
-        const f16x8 bl = *(const f16x8*)(stage + stage_off<TC>(kh, kTok * c + r, 8 + 4 * g + m));
+        const uint32_t oh = DB ? stage_off_db(j, kh, r & 15, 4 * g + m) : stage_off<TC>(kh, kTok * c + r, 4 * g + m);
+        const uint32_t ol =
+            DB ? stage_off_db(j, kh, r & 15, 8 + 4 * g + m) : stage_off<TC>(kh, kTok * c + r, 8 + 4 * g + m);
+        const f16x8 bh = *(const f16x8*)(stage + oh);
+        const f16x8 bl = *(const f16x8*)(stage + ol);
         acc[c] = mfma32(a, bh, acc[c]);
         acc[c] = mfma32(a, bl, acc[c]);
       }
     }
-    __syncthreads();
+    if (!DB) __syncthreads();
   };
   auto step = [&](int s, uint2 (&P)[Q]) {
     round(0, P);
     kwin(s, 1, kb);
-    store_window<TC>(stage, hb, sp, kb, I);
+    store_window<TC>(stage + rbuf(1), hb, sp, kb, I);
     kwin(s + 1, 1, kb);
     load_window<TC>(hb, sp, kb, I);
     __syncthreads();
     round(1, P);
     if (s + 1 < ks.NSW) {
       kwin(s + 1, 0, ka);
-      store_window<TC>(stage, ha, sp, ka, I);
+      store_window<TC>(stage + rbuf(0), ha, sp, ka, I);
     }
     kwin(s + 2, 0, ka);
     load_window<TC>(ha, sp, ka, I);

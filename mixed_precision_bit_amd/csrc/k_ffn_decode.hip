@@ -16,13 +16,21 @@ __global__ __launch_bounds__(kThreads) void k_gate_up(FfnParams p, int qmax) {
     return;
   const int q = p.q[2 * e];
   const uint32_t lut_bytes = 256u << qmax;
+  // items of <= 16 tokens take the double-buffered stage (one barrier per step)
+  const bool db = TC == 1 && nt <= kDbTok;
+#define MPB_GU(Q)                                                                         \
+  case Q:                                                                                 \
+    if (db) gate_up_body<Q, TC, false, TC == 1, TC == 1>(p, e, it, t0, nt, lds, lut_bytes, threadIdx.x); \
+    else gate_up_body<Q, TC>(p, e, it, t0, nt, lds, lut_bytes, threadIdx.x);            \
+    break;
   switch (q < 3 || q > qmax || !tables_at_zero(lds) ? 0 : q) {
-    case 3: gate_up_body<3, TC>(p, e, it, t0, nt, lds, lut_bytes, threadIdx.x); break;
-    case 4: gate_up_body<4, TC>(p, e, it, t0, nt, lds, lut_bytes, threadIdx.x); break;
-    case 5: gate_up_body<5, TC>(p, e, it, t0, nt, lds, lut_bytes, threadIdx.x); break;
-    case 6: gate_up_body<6, TC>(p, e, it, t0, nt, lds, lut_bytes, threadIdx.x); break;
-    case 7: gate_up_body<7, TC>(p, e, it, t0, nt, lds, lut_bytes, threadIdx.x); break;
-    case 8: gate_up_body<8, TC>(p, e, it, t0, nt, lds, lut_bytes, threadIdx.x); break;
+    MPB_GU(3)
+    MPB_GU(4)
+    MPB_GU(5)
+    MPB_GU(6)
+    MPB_GU(7)
+    MPB_GU(8)
+#undef MPB_GU
     default: {
       const size_t o = (size_t)(p.offsets[e] + t0) * p.I + it * 64;
       for (int i = threadIdx.x; i < nt * 64; i += blockDim.x) {
@@ -42,13 +50,20 @@ __global__ __launch_bounds__(kThreads) void k_down(FfnParams p, int qmax) {
   if (!decode_item(p, false, (p.H + 127) >> 7, e, it, t0, nt)) return;
   const int q = p.q[2 * e + 1];
   const uint32_t lut_bytes = 256u << qmax;
+  const bool db = TC == 1 && nt <= kDbTok;
+#define MPB_DN(Q)                                                                                       \
+  case Q:                                                                                               \
+    if (db) down_body<Q, TC, false, NT, TC == 1>(p, e, it, t0, nt, lds, lut_bytes, threadIdx.x);        \
+    else down_body<Q, TC, false, NT>(p, e, it, t0, nt, lds, lut_bytes, threadIdx.x);                   \
+    break;
   switch (q < 3 || q > qmax || !tables_at_zero(lds) ? 0 : q) {
-    case 3: down_body<3, TC, false, NT>(p, e, it, t0, nt, lds, lut_bytes, threadIdx.x); break;
-    case 4: down_body<4, TC, false, NT>(p, e, it, t0, nt, lds, lut_bytes, threadIdx.x); break;
-    case 5: down_body<5, TC, false, NT>(p, e, it, t0, nt, lds, lut_bytes, threadIdx.x); break;
-    case 6: down_body<6, TC, false, NT>(p, e, it, t0, nt, lds, lut_bytes, threadIdx.x); break;
-    case 7: down_body<7, TC, false, NT>(p, e, it, t0, nt, lds, lut_bytes, threadIdx.x); break;
-    case 8: down_body<8, TC, false, NT>(p, e, it, t0, nt, lds, lut_bytes, threadIdx.x); break;
+    MPB_DN(3)
+    MPB_DN(4)
+    MPB_DN(5)
+    MPB_DN(6)
+    MPB_DN(7)
+    MPB_DN(8)
+#undef MPB_DN
     default: {
       const int n0 = it * 128;
       poison(p.y + (size_t)(p.offsets[e] + t0) * p.H + n0, p.H, nt, min(128, p.H - n0));

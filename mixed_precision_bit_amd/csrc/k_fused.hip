@@ -239,12 +239,30 @@ __device__ __forceinline__ void gate_up_unit(const FusedParams& P, int u, uint16
   const int q = p.q[2 * e];
   const uint32_t lut_bytes = 256u << P.qmax;
   switch (q < 3 || q > P.qmax || !tables_at_zero(lds) ? 0 : q) {
-    case 3: gate_up_body<3, 1, true>(p, e, it, t0, nt, lds, lut_bytes, tid); break;
-    case 4: gate_up_body<4, 1, true>(p, e, it, t0, nt, lds, lut_bytes, tid); break;
-    case 5: gate_up_body<5, 1, true>(p, e, it, t0, nt, lds, lut_bytes, tid); break;
-    case 6: gate_up_body<6, 1, true>(p, e, it, t0, nt, lds, lut_bytes, tid); break;
-    case 7: gate_up_body<7, 1, true>(p, e, it, t0, nt, lds, lut_bytes, tid); break;
-    case 8: gate_up_body<8, 1, true>(p, e, it, t0, nt, lds, lut_bytes, tid); break;
+    case 3:
+      if (nt <= kDbTok) gate_up_body<3, 1, true, true, true>(p, e, it, t0, nt, lds, lut_bytes, tid);
+      else gate_up_body<3, 1, true>(p, e, it, t0, nt, lds, lut_bytes, tid);
+      break;
+    case 4:
+      if (nt <= kDbTok) gate_up_body<4, 1, true, true, true>(p, e, it, t0, nt, lds, lut_bytes, tid);
+      else gate_up_body<4, 1, true>(p, e, it, t0, nt, lds, lut_bytes, tid);
+      break;
+    case 5:
+      if (nt <= kDbTok) gate_up_body<5, 1, true, true, true>(p, e, it, t0, nt, lds, lut_bytes, tid);
+      else gate_up_body<5, 1, true>(p, e, it, t0, nt, lds, lut_bytes, tid);
+      break;
+    case 6:
+      if (nt <= kDbTok) gate_up_body<6, 1, true, true, true>(p, e, it, t0, nt, lds, lut_bytes, tid);
+      else gate_up_body<6, 1, true>(p, e, it, t0, nt, lds, lut_bytes, tid);
+      break;
+    case 7:
+      if (nt <= kDbTok) gate_up_body<7, 1, true, true, true>(p, e, it, t0, nt, lds, lut_bytes, tid);
+      else gate_up_body<7, 1, true>(p, e, it, t0, nt, lds, lut_bytes, tid);
+      break;
+    case 8:
+      if (nt <= kDbTok) gate_up_body<8, 1, true, true, true>(p, e, it, t0, nt, lds, lut_bytes, tid);
+      else gate_up_body<8, 1, true>(p, e, it, t0, nt, lds, lut_bytes, tid);
+      break;
     default: {
       const size_t o = (size_t)(p.offsets[e] + t0) * p.I + it * 64;
       for (int i = tid; i < nt * 64; i += kThreads) {
@@ -268,12 +286,30 @@ __device__ __forceinline__ void down_unit(const FusedParams& P, int u, uint16_t*
   const int q = p.q[2 * e + 1];
   const uint32_t lut_bytes = 256u << P.qmax;
   switch (q < 3 || q > P.qmax || !tables_at_zero(lds) ? 0 : q) {
-    case 3: down_body<3, 1, true>(p, e, it, t0, nt, lds, lut_bytes, tid); break;
-    case 4: down_body<4, 1, true>(p, e, it, t0, nt, lds, lut_bytes, tid); break;
-    case 5: down_body<5, 1, true>(p, e, it, t0, nt, lds, lut_bytes, tid); break;
-    case 6: down_body<6, 1, true>(p, e, it, t0, nt, lds, lut_bytes, tid); break;
-    case 7: down_body<7, 1, true>(p, e, it, t0, nt, lds, lut_bytes, tid); break;
-    case 8: down_body<8, 1, true>(p, e, it, t0, nt, lds, lut_bytes, tid); break;
+    case 3:
+      if (nt <= kDbTok) down_body<3, 1, true, true, true>(p, e, it, t0, nt, lds, lut_bytes, tid);
+      else down_body<3, 1, true>(p, e, it, t0, nt, lds, lut_bytes, tid);
+      break;
+    case 4:
+      if (nt <= kDbTok) down_body<4, 1, true, true, true>(p, e, it, t0, nt, lds, lut_bytes, tid);
+      else down_body<4, 1, true>(p, e, it, t0, nt, lds, lut_bytes, tid);
+      break;
+    case 5:
+      if (nt <= kDbTok) down_body<5, 1, true, true, true>(p, e, it, t0, nt, lds, lut_bytes, tid);
+      else down_body<5, 1, true>(p, e, it, t0, nt, lds, lut_bytes, tid);
+      break;
+    case 6:
+      if (nt <= kDbTok) down_body<6, 1, true, true, true>(p, e, it, t0, nt, lds, lut_bytes, tid);
+      else down_body<6, 1, true>(p, e, it, t0, nt, lds, lut_bytes, tid);
+      break;
+    case 7:
+      if (nt <= kDbTok) down_body<7, 1, true, true, true>(p, e, it, t0, nt, lds, lut_bytes, tid);
+      else down_body<7, 1, true>(p, e, it, t0, nt, lds, lut_bytes, tid);
+      break;
+    case 8:
+      if (nt <= kDbTok) down_body<8, 1, true, true, true>(p, e, it, t0, nt, lds, lut_bytes, tid);
+      else down_body<8, 1, true>(p, e, it, t0, nt, lds, lut_bytes, tid);
+      break;
     default: {
       const int n0 = it * 128;
       poison(p.y + (size_t)(p.offsets[e] + t0) * p.H + n0, p.H, nt, min(128, p.H - n0));
