@@ -593,6 +593,36 @@ def test_edge_one_expert_takes_all_and_extreme_bitwidths(T, layer_cache):
         assert_close(out.cpu().numpy(), O.moe_ffn(X, z, r, L, q=np.full(L.n_blocks, qv)), f"all q={qv}")
 
 
+def test_edge_group_sizes_around_stage_switch(layer_cache):
+    """Groups of 1, 6, 15, 16, 17, 32 and 33 tokens and a 40-token shared
+    group: items of at most 16 tokens take the double-buffered activation
+    stage, larger ones the single stage; both at every committed bitwidth of
+    the layer, every output element against the oracle."""
+    L, D = dev_layer(layer_cache, 10)
+    T, K = 40, L.K
+    sizes = [(0, 16), (1, 17), (2, 15), (3, 33), (4, 1), (5, 32)]
+    ent = [e for e, n in sizes for _ in range(n)]
+    ent += [6] * (T * K - len(ent))
+    # entry j -> token j % T, slot j // T: a group spans < T entries, so no
+    # token names an expert twice
+    z = np.array(ent, dtype=np.int64).reshape(K, T).T.copy()
+    assert all(len(set(row)) == K for row in z)
+    rng = np.random.default_rng(123)
+    r = rng.uniform(0.1, 1.0, (T, K))
+    r /= r.sum(axis=1, keepdims=True)
+    r = r.astype(np.float32).astype(np.float64)
+    Xb = S.make_tokens(10, T=T, seed=321)
+    X = S.f16_bits_to_f64(Xb)
+    idx = torch.from_numpy(z.astype(np.int32)).cuda()
+    w = torch.from_numpy(r.astype(np.float32)).cuda()
+    out, ws = D.alloc_ffn(T)
+    D.ffn(to_dev_x(Xb), "f16", idx, w, out, ws)
+    torch.cuda.synchronize()
+    counts = np.bincount(z.ravel(), minlength=L.E)
+    assert sorted(counts[counts > 0].tolist()) == [1, 6, 15, 16, 17, 32, 33]
+    assert_close(out.cpu().numpy(), O.moe_ffn(X, z, r, L), "group sizes 1..33")
+
+
 def test_edge_out_of_range_expert_ids_contribute_nothing(layer_cache):
     L, D = dev_layer(layer_cache, 10)
     T = 20
