@@ -29,10 +29,9 @@ namespace mpb {
 // dwordx4 access.
 //
 // Inside a word, element e = 4*s + b (s = 0..7, b = 0..3) of plane p sits at
-// bit (8*b + s + p) mod 32. With that placement the q-bit indices of four
-// elements {4s..4s+3} come out of q plane words with one AND per plane and one
-// rotation: OR_p (P_p & rotl(0x01010101, s+p)), rotated right by s, holds in
-// byte b the bits of element 4s+b with plane p at bit p.
+// bit (8*b + s + p) mod 32: plane p is the word with element 4s+b at bit
+// 8b + s, rotated left by p. With that placement the q-bit indices come out
+// of q plane words with bit-field inserts alone (assemble).
 // ----------------------------------------------------------------------------
 __host__ __device__ constexpr int packed_pos(int e, int p) { return (8 * (e & 3) + (e >> 2) + p) & 31; }
 
@@ -52,22 +51,44 @@ __device__ __forceinline__ uint32_t bfi(uint32_t m, uint32_t a, uint32_t c) { re
 // Index assembly. P[p] = plane-p word (p < Q) of one (row, word). On return
 // byte b of O[s] is u = sum_p bit_p(e=4s+b) << p, the Q-bit index with its bit
 // order reversed (plane 0, the code MSB, lands in bit 0). Tables are staged in
-// the same reversed order, so no per-weight reversal is needed. Cost per four
-// elements: one and, Q-1 bit-field inserts and one rotate.
+// the same reversed order, so no per-weight reversal is needed.
+//
+// Per byte lane b this is the transpose of an 8x8 bit matrix: row p (plane
+// p) holds, at bit s, plane p of element 4s+b, and row s of the result must
+// hold, at bit p, the same bit. It runs as the usual three rounds of block
+// swaps (4x4, 2x2, 1x1 blocks), each of which moves bits k = 4, 2, 1 places
+// between rows p and p+k. Because plane p is stored rotated left by p bits
+// (packed_pos), row p+k already sits k bits to the left of row p, so each new
+// row is one bit-field insert of the two old rows under a rotated mask; no
+// shift is needed (rotating instead of shifting only moves bits into positions
+// the mask takes from the other row). Row s ends rotated by s and is rotated
+// back once. Cost per 32 elements: 24 inserts and 7 rotates for every Q (the
+// and-or gathering it replaces took 8Q + 7). Rows at and above Q are a zero
+// the compiler cannot see through: folded constants turned the inserts into
+// longer and/or sequences.
+template <int K>
+__device__ __forceinline__ void bfly_round(uint32_t (&X)[8], uint32_t M) {
+#pragma unroll
+  for (int p = 0; p < 8; ++p) {
+    if (p & K) continue;
+    const uint32_t a = X[p], c = X[p + K];
+    X[p] = bfi(rotl_c(M, p), a, c);
+    X[p + K] = bfi(rotl_c(M, p + K), a, c);
+  }
+}
+
 template <int Q>
 __device__ __forceinline__ void assemble(const uint32_t (&P)[Q], uint32_t (&O)[8]) {
+  uint32_t z = 0u;
+  asm("" : "+v"(z));
+  uint32_t X[8];
 #pragma unroll
-  for (int s = 0; s < 8; ++s) {
-    // the masks of one s are disjoint, so each plane merges with a
-    // bit-field insert that leaves the bits gathered so far in place
-    uint32_t c = P[0] & rotl_c(0x01010101u, s);
+  for (int p = 0; p < 8; ++p) X[p] = p < Q ? P[p] : z;
+  bfly_round<4>(X, 0x0F0F0F0Fu);
+  bfly_round<2>(X, 0x33333333u);
+  bfly_round<1>(X, 0x55555555u);
 #pragma unroll
-    for (int p = 1; p < Q; ++p) {
-      c = (P[p] & rotl_c(0x01010101u, s + p)) | c;
-      asm("" : "+v"(c));  // keeps the chain as one and-or per plane (no and + or3 split)
-    }
-    O[s] = s ? __builtin_amdgcn_alignbit(c, c, s) : c;
-  }
+  for (int s = 0; s < 8; ++s) O[s] = s ? __builtin_amdgcn_alignbit(X[s], X[s], s) : X[s];
 }
 
 template <int Q>
