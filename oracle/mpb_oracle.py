@@ -13,7 +13,7 @@ Arithmetic is float64 throughout. Every input value (fp16/bf16 activations,
 fp32 router weights, fp16 centroids) is exactly representable in float64, and
 every product of an activation with a router weight is exact in float64.
 
-Readings where the pages leave a step open (each is listed in the design doc):
+Readings where the pages leave a step open:
 * bit j of plane word w belongs to element 32*w + j; plane 0 is the code MSB;
 * the b-bit index is formed from the top b planes ([PW §2.2]: subsets of the
   bit-planes give the effective bitwidths);
@@ -306,7 +306,7 @@ def greedy_reductions(layer, s: np.ndarray, frac: float, floor_hot: int = 5, eps
 
 
 # ----------------------------------------------------------------- planner step (Alg. 1)
-# Readings where [PW §3.2] leaves a step open (listed in the design doc):
+# Readings where [PW §3.2] leaves a step open:
 # * a step is a one-bit reduction b -> b-1 of one routed linear-block; a
 #   block's steps are taken in order, so only its next step is available;
 # * GreedySelect repeatedly takes the available step with the least predicted
