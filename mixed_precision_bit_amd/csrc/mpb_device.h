@@ -187,10 +187,8 @@ __device__ __forceinline__ f16x8 lookup8(uint32_t O0, uint32_t O1, uint32_t slot
 }
 
 // ----------------------------------------------------------------------------
-// Activations as MFMA B-operands (8 consecutive elements, 16-byte aligned).
+// Activations: bf16 -> fp16 conversion of 8 consecutive elements (16-byte aligned).
 // ----------------------------------------------------------------------------
-__device__ __forceinline__ f16x8 load_x8_f16(const uint16_t* p) { return *(const f16x8*)p; }
-
 // bf16 -> fp16 (exact for |x| in the fp16 normal range; rounded below it).
 __device__ __forceinline__ f16x8 load_x8_bf16(const uint16_t* p) {
   const u16x8 v = *(const u16x8*)p;
@@ -198,12 +196,6 @@ __device__ __forceinline__ f16x8 load_x8_bf16(const uint16_t* p) {
 #pragma unroll
   for (int j = 0; j < 8; ++j) r[j] = (_Float16)__builtin_bit_cast(float, (uint32_t)v[j] << 16);
   return r;
-}
-
-template <int XDT>
-__device__ __forceinline__ f16x8 load_x8(const uint16_t* p) {
-  if constexpr (XDT == 0) return load_x8_f16(p);
-  else return load_x8_bf16(p);
 }
 
 __device__ __forceinline__ f32x16 mfma32(f16x8 a, f16x8 b, f32x16 c) {
