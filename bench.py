@@ -292,9 +292,10 @@ def main():
     ms = start.elapsed_time(end) / args.steps
 
     # Timed region 2 (per-kernel times): the same K steps launched eagerly, with
-    # moe_ffn recording HIP events on its stream before grouping, gate_up, down
-    # and combine and after the combine (event records inside a graph do not
-    # order against its kernel nodes, so kernel times come from this pass).
+    # moe_ffn recording HIP events on its stream before grouping, at the start
+    # and end of the gate_up kernel (recorded by the launch itself), before the
+    # combine and after it (event records inside a graph do not order against
+    # its kernel nodes, so kernel times come from this pass).
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
     for row in evs:              # torch creates the HIP event on first record
         for e in row:

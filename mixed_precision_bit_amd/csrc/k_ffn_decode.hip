@@ -2,6 +2,8 @@
 // launch each (the device code is in k_ffn_body.h). Items of 32 tokens at
 // decode sizes; gate_up takes 128-token items (TC = 4), in the XCD-interleaved
 // order, once groups hold 96 tokens on average.
+#include <hip/hip_ext.h>
+
 #include <algorithm>
 
 #include "k_ffn_body.h"
@@ -101,8 +103,11 @@ static size_t ffn_lds_bytes(int qmax) {
   return std::max<size_t>((256u << qmax) + stage_bytes<TC>(), kWaves * 16 * 64 * 4);
 }
 
+// ev0/ev1 (optional, gate_up): the launch itself records them at the kernel's
+// start and end (hipExtLaunchKernelGGL), for timing the kernel alone.
 template <int TC, bool GU, bool NT = true>
-static hipError_t launch_tc(const FfnParams& p, int qmax, hipStream_t s) {
+static hipError_t launch_tc(const FfnParams& p, int qmax, hipStream_t s, hipEvent_t ev0 = nullptr,
+                            hipEvent_t ev1 = nullptr) {
   static unsigned long long lds_raised = 0;  // devices on which this kernel's LDS limit is raised
   const void* fn;
   if constexpr (GU) fn = (const void*)k_gate_up<TC>;
@@ -112,17 +117,20 @@ static hipError_t launch_tc(const FfnParams& p, int qmax, hipStream_t s) {
   const size_t shmem = ffn_lds_bytes<TC>(qmax);
   // 128-token items take the XCD-interleaved order (decode_item_xcd)
   const int items = TC == 4 ? (p.max_items + 7) / 8 * 8 : p.max_items;
-  if constexpr (GU)
-    hipLaunchKernelGGL(k_gate_up<TC>, dim3(items * (p.I >> 6)), dim3(kThreads), shmem, s, p, qmax);
-  else
+  if constexpr (GU) {
+    if (ev0 && ev1)
+      hipExtLaunchKernelGGL(k_gate_up<TC>, dim3(items * (p.I >> 6)), dim3(kThreads), shmem, s, ev0, ev1, 0, p, qmax);
+    else
+      hipLaunchKernelGGL(k_gate_up<TC>, dim3(items * (p.I >> 6)), dim3(kThreads), shmem, s, p, qmax);
+  } else
     hipLaunchKernelGGL((k_down<TC, NT>), dim3(p.max_items * ((p.H + 127) >> 7)), dim3(kThreads), shmem, s, p, qmax);
   return hipGetLastError();
 }
 
-hipError_t launch_gate_up(const FfnParams& p, int qmax, int tc, hipStream_t s) {
+hipError_t launch_gate_up(const FfnParams& p, int qmax, int tc, hipStream_t s, hipEvent_t ev0, hipEvent_t ev1) {
   switch (tc) {
-    case 1: return launch_tc<1, true>(p, qmax, s);
-    case 4: return launch_tc<4, true>(p, qmax, s);
+    case 1: return launch_tc<1, true>(p, qmax, s, ev0, ev1);
+    case 4: return launch_tc<4, true>(p, qmax, s, ev0, ev1);
     default: return hipErrorInvalidValue;
   }
 }

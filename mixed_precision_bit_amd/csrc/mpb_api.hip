@@ -354,15 +354,14 @@ int moe_ffn(const void* X_dev, int x_dtype, int T, const int32_t* topk_idx_dev, 
   }
   e = mpb::launch_permute(p, (int32_t*)(ws + L.ccnt), s);
   if (e != hipSuccess) return hip_fail(e, "moe_ffn: permute");
-  mark(1, s);
   int qmax_gu = 3, qmax_dn = 3;
   for (int i = 0; i < g.nb(); i += 2) {
     qmax_gu = std::max(qmax_gu, g.q[i]);
     qmax_dn = std::max(qmax_dn, g.q[i + 1]);
   }
-  e = mpb::launch_gate_up(p, qmax_gu, tc, s);
+  // events 1 and 2 time the gate_up kernel itself: its launch records them
+  e = mpb::launch_gate_up(p, qmax_gu, tc, s, g_nev == 5 ? g_ev[1] : nullptr, g_nev == 5 ? g_ev[2] : nullptr);
   if (e != hipSuccess) return hip_fail(e, "moe_ffn: gate_up");
-  mark(2, s);
   e = mpb::launch_down(p, qmax_dn, tc == 1, s);
   if (e != hipSuccess) return hip_fail(e, "moe_ffn: down");
   mark(3, s);

@@ -94,7 +94,9 @@ hipError_t launch_permute(const FfnParams& p, int32_t* ccnt, hipStream_t s);
 hipError_t launch_x_to_f16(const uint16_t* x, uint16_t* y, size_t n, hipStream_t s);
 // qmax: highest committed bitwidth among the launch's blocks (sizes the LDS
 // table region; a block above it yields NaN)
-hipError_t launch_gate_up(const FfnParams& p, int qmax, int tc, hipStream_t s);
+// ev0/ev1: optional events the launch records at the kernel's start and end
+hipError_t launch_gate_up(const FfnParams& p, int qmax, int tc, hipStream_t s, hipEvent_t ev0 = nullptr,
+                          hipEvent_t ev1 = nullptr);
 // nt: non-temporal plane loads (decode-size batches, one item per group)
 hipError_t launch_down(const FfnParams& p, int qmax, bool nt, hipStream_t s);
 hipError_t launch_combine(const FfnParams& p, hipStream_t s);
