@@ -72,8 +72,8 @@ typedef struct {
 
 /*
  * Bind a layer: its geometry and the weight page table of committed bitwidths
- * q_i (§3.1: one table row per linear-block; q_i is "the precision currently
- * used in inference"). q_dev is a caller-owned device int32 array of
+ * q_i (§3.1: one table row per linear-block; q_i is the bitwidth the serving
+ * kernels read the block at). q_dev is a caller-owned device int32 array of
  * 2*(E+S) entries that the FFN kernels read; q_init_host (2*(E+S) values in
  * 3..8) is copied into it on `stream` and into the host mirror, and all planes
  * of every block are marked resident. `stream` becomes the stream on which
@@ -175,6 +175,13 @@ size_t moe_ffn_workspace_bytes(int T);
  *               values 3..8
  *   out_dev     [T][H] fp32, overwritten
  *   ws_dev      workspace of ws_bytes >= moe_ffn_workspace_bytes(T)
+ *   stream      the stream bound by mpb_init, where set_committed_bits
+ *               writes q_i (so every launch is ordered with every commit, and
+ *               page offloads wait for the launches that may read the pages),
+ *               or a stream under graph capture (its kernels run when the
+ *               graph is replayed; ordering replays against commits and page
+ *               offloads is then the caller's part). Any other stream:
+ *               MPB_E_ARG.
  * The kernels' on-chip table space is sized at enqueue time for the highest
  * bitwidth in the host mirror; a graph captured from this call must be
  * captured again after a block is raised above that bitwidth (its outputs
@@ -209,7 +216,7 @@ int moe_ffn(const void* X_dev, int x_dtype, int T, const int32_t* topk_idx_dev,
  * Calls sharing a workspace must not overlap. Every device-side wait is
  * bounded: a wait that runs out (only possible if the counters were not zero)
  * makes out NaN. Gate_up takes 32-token items (the decode configuration) for
- * every T. Errors: as moe_route and moe_ffn, plus MPB_E_ARG for a misaligned
+ * every T. The stream rule is moe_ffn's. Errors: as moe_route and moe_ffn, plus MPB_E_ARG for a misaligned
  * workspace.
  */
 size_t moe_fused_counter_bytes(void);

@@ -188,6 +188,16 @@ int qmax_all() {
   return m;
 }
 
+// FFN launches read q_i on the stream set_committed_bits writes it on, so the
+// two are ordered, and page offloads wait for them through lower_ev. A stream
+// under graph capture is accepted too: its kernels run when the graph is
+// replayed, and ordering replays against commits is the caller's part.
+bool stream_ok(hipStream_t s) {
+  if (s == g.stream) return true;
+  hipStreamCaptureStatus st = hipStreamCaptureStatusNone;
+  return hipStreamIsCapturing(s, &st) == hipSuccess && st == hipStreamCaptureStatusActive;
+}
+
 }  // namespace
 
 extern "C" {
@@ -336,6 +346,8 @@ int moe_ffn(const void* X_dev, int x_dtype, int T, const int32_t* topk_idx_dev, 
   if (!X_dev || !topk_idx_dev || !topk_w_dev || !planes_dev || !luts_dev || !q_dev || !out_dev || !ws_dev)
     return fail(MPB_E_ARG, "moe_ffn: null pointer");
   if (q_dev != g.q_dev) return fail(MPB_E_ARG, "moe_ffn: q_dev is not the bound page table");
+  if (!stream_ok((hipStream_t)stream))
+    return fail(MPB_E_ARG, "moe_ffn: stream is neither the bound stream nor under graph capture");
   const mpb::WsLayout L = mpb::ws_layout(T, g.H, g.I, g.E, g.S, g.K, x_dtype == MPB_BF16);
   const long long ntile = std::max(g.I / 64, (g.H + 127) / 128);
   if (((long long)L.max_items + 7) / 8 * 8 * ntile >= (1ll << 31)) return fail(MPB_E_SHAPE, "moe_ffn: T too large for this layer");
@@ -395,6 +407,8 @@ int moe_fused(const void* X_dev, int x_dtype, int T, const float* W_router_dev, 
     return fail(MPB_E_ARG, "moe_fused: null pointer");
   if ((uintptr_t)ws_dev % 256) return fail(MPB_E_ARG, "moe_fused: workspace not 256-byte aligned");
   if (q_dev != g.q_dev) return fail(MPB_E_ARG, "moe_fused: q_dev is not the bound page table");
+  if (!stream_ok((hipStream_t)stream))
+    return fail(MPB_E_ARG, "moe_fused: stream is neither the bound stream nor under graph capture");
   const mpb::WsLayout L = mpb::ws_layout(T, g.H, g.I, g.E, g.S, g.K, x_dtype == MPB_BF16);
   const long long ntile = std::max(g.I / 64, (g.H + 127) / 128);
   if ((long long)L.max_items * ntile >= (1ll << 30)) return fail(MPB_E_SHAPE, "moe_fused: T too large for this layer");

@@ -12,8 +12,8 @@ Storage format produced here (the canonical interchange format):
 * ``planes[p][n][w]`` (uint32): plane 0 holds the most significant code bit
   (bit 7), plane 7 the least significant. Bit j of word w is the bit of element
   ``k = 32*w + j`` (least significant bit first), as in the Any-Precision
-  bit-plane layout of PagedWeight §2.2 / §3.1 ("different subsets of
-  bit-planes correspond to different effective bitwidths").
+  bit-plane layout of PagedWeight §2.2 / §3.1, where a b-bit weight is read
+  from a prefix of the planes.
 * ``luts[b-3]`` (uint16, fp16 bits), shape ``[N][2**b]`` for b = 3..8: one
   centroid table per output row and bitwidth, sorted ascending.
 

@@ -24,7 +24,8 @@ Readings where the pages leave a step open:
 * shared experts are always on with weight 1;
 * M_i^b counts the b planes plus the b-bit table only ([PW §3.1], Eq. 3).
 
-Parity pins: see tests/test_oracle_pins.py. No function here is unpinned.
+Parity pins: tests/test_oracle_pins.py and tests/test_planner.py. Every
+function here is pinned by at least one check that does not re-run it.
 """
 from __future__ import annotations
 
@@ -147,10 +148,19 @@ def route(X: np.ndarray, W_r: np.ndarray, bias, K: int):
 
 
 def routing_mass(z: np.ndarray, r: np.ndarray, E: int) -> np.ndarray:
-    """Routing mass m_e of one layer [PW §2.1, Eq. 1]: sum_t sum_k r 1{z=e} / sum r."""
+    """Routing mass m_e of one layer [PW §2.1, Eq. 1]: sum_t sum_k r 1{z=e} / sum r.
+
+    Both sums run over the (t, k) entries whose expert id lies in [0, E)
+    (an id outside that range names no routed expert and carries no mass);
+    a batch with no such entry has zero mass everywhere.
+    """
+    z = np.asarray(z).ravel()
+    r = np.asarray(r, np.float64).ravel()
+    keep = (z >= 0) & (z < E)
     num = np.zeros(E)
-    np.add.at(num, z.ravel(), r.ravel())
-    return num / r.sum()
+    np.add.at(num, z[keep], r[keep])
+    den = r[keep].sum()
+    return num / den if den > 0 else num
 
 
 # ----------------------------------------------------------------- O4 FFN

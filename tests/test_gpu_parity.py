@@ -167,11 +167,9 @@ def test_routing_mass_matches_eq1(cfg):
     idx2 = idx.clone()
     idx2[0, 0] = L.E
     M().moe_routing_mass(idx2, w, L.E, mass)
-    keep = np.ones((T, L.K), bool)
-    keep[0, 0] = False
-    num = np.zeros(L.E)
-    np.add.at(num, z[keep], r[keep])
-    assert_close(mass.cpu().numpy(), num / r[keep].sum(), f"cfg{cfg} routing mass, one id out of range")
+    z2 = z.copy()
+    z2[0, 0] = L.E
+    assert_close(mass.cpu().numpy(), O.routing_mass(z2, r, L.E), f"cfg{cfg} routing mass, one id out of range")
     M().moe_routing_mass(idx[:0], w[:0], L.E, mass)
     assert not mass.cpu().numpy().any()
 
@@ -680,6 +678,17 @@ def test_abi_errors_after_init(layer_cache):
     with pytest.raises(E) as ei:
         M().moe_ffn(to_dev_x(Xb), 0, idx, w, D.planes_table, D.luts_table, other, out, ws)
     assert ei.value.code == -1
+    # a stream other than the bound one (and not under graph capture) is
+    # refused: commits on the bound stream would not be ordered with it
+    side = torch.cuda.Stream()
+    with pytest.raises(E) as ei:
+        M().moe_ffn(to_dev_x(Xb), 0, idx, w, D.planes_table, D.luts_table, D.q_dev, out, ws, side)
+    assert ei.value.code == -1
+    fo, fws = D.alloc_fused(16)
+    with pytest.raises(E) as ei:
+        M().moe_fused(to_dev_x(Xb), 0, D.W_r, D.bias, idx, w, D.planes_table, D.luts_table, D.q_dev, fo, fws, side)
+    assert ei.value.code == -1
+    torch.cuda.synchronize()
 
 
 def test_graph_replay_matches_eager(layer_cache):

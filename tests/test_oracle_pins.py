@@ -375,3 +375,135 @@ def test_bf16_rounding_is_nearest_even():
     assert got[0] == 1.0 and got[1] == 1.0 and got[2] == 1.0078125
     for v, g in zip(x, got):
         assert abs(g - v) <= abs(v) * 2 ** -8
+
+
+# ---------------------------------------------------------------- Eq. 1 closed form
+def test_routing_mass_closed_form_and_alignment():
+    # [PW §2.1, Eq. 1] worked by hand: expert 0 gets .7 + .1, expert 1 gets
+    # .4 + .9, expert 2 gets .3 + .6, over a total weight of 3
+    z = np.array([[0, 2], [2, 1], [1, 0]])
+    r = np.array([[.7, .3], [.6, .4], [.9, .1]])
+    m = O.routing_mass(z, r, 3)
+    assert np.allclose(m, [4 / 15, 13 / 30, 3 / 10], rtol=0, atol=1e-15)
+    # a z/r misalignment (weights of the transposed entry order) moves the mass
+    assert not np.allclose(O.routing_mass(z, r[:, ::-1], 3), m, rtol=0, atol=1e-6)
+    # ids outside [0, E) name no routed expert: they leave both sums
+    z2 = np.array([[0, -1], [2, 1], [1, 3]])
+    r2 = np.array([[.7, .3], [.6, .4], [.9, .1]])
+    assert np.allclose(O.routing_mass(z2, r2, 3), np.array([.7, 1.3, .6]) / 2.6, rtol=0, atol=1e-15)
+    assert (O.routing_mass(np.full((2, 2), -1), np.ones((2, 2)), 3) == 0).all()
+    assert (O.routing_mass(np.zeros((0, 2), np.int64), np.zeros((0, 2)), 3) == 0).all()
+
+
+def test_routing_mass_brute_force_per_expert(layer_cache):
+    # per-expert scalar loops over the (t, k) entries of a routed batch
+    from fractions import Fraction
+    L = layer_cache(1)
+    X = S.x_bits_to_f64(S.make_tokens(1), "f16")
+    z, r, _ = O.route(X, L.W_r, L.bias, L.K)
+    m = O.routing_mass(z, r, L.E)
+    tot = sum(Fraction(float(v)) for v in r.ravel())
+    for e in range(L.E):
+        num = sum((Fraction(float(r[t, k])) for t in range(z.shape[0]) for k in range(z.shape[1]) if z[t, k] == e),
+                  Fraction(0))
+        assert abs(m[e] - float(num / tot)) <= 1e-15
+
+
+# ---------------------------------------------------------------- sampled FFN
+@pytest.mark.parametrize("cfg", [0, 10, 13])
+def test_moe_ffn_sampled_equals_full_layer(cfg, layer_cache):
+    # the sampled evaluator is the full-size checker; hold it to moe_ffn (which
+    # the scalar loops and the closed forms above pin) at every token and a
+    # column sample that includes both ends
+    L = layer_cache(cfg)
+    Xb = S.make_tokens(cfg)
+    X = S.x_bits_to_f64(Xb, L.cfg["xdtype"])
+    z, r, _ = O.route(X, L.W_r, L.bias, L.K)
+    full = O.moe_ffn(X, z, r, L)
+    toks = np.arange(X.shape[0])
+    cols = np.unique(np.r_[0, np.arange(1, L.H, 7), L.H - 1])
+    samp = O.moe_ffn_sampled(X, z, r, L, toks, cols)
+    scale = np.abs(full).max()
+    assert np.abs(samp - full[np.ix_(toks, cols)]).max() <= 1e-12 * scale
+
+
+def test_moe_ffn_sampled_equals_scalar_loops(layer_cache):
+    L = layer_cache(0)
+    X = S.x_bits_to_f64(S.make_tokens(0), "f16")
+    z, r, _ = O.route(X, L.W_r, L.bias, L.K)
+    loops = np.array(O.moe_ffn_loops(X, z, r, L, [3]))[0]
+    cols = np.array([0, 17, 128, 255])
+    samp = O.moe_ffn_sampled(X, z, r, L, [3], cols)[0]
+    assert np.abs(samp - loops[cols]).max() <= 1e-12 * np.abs(loops).max()
+
+
+# ---------------------------------------------------------------- greedy ranking
+class _FakeLayer:
+    """A layer stub carrying only what the greedy sweep reads."""
+
+    def __init__(self, E, H, I, q, hot):
+        self.E, self.S, self.H, self.I = E, 0, H, I
+        self.q = np.array(q, np.int32)
+        self.hot = np.array(hot, bool)
+        self.n_blocks = 2 * E
+
+    def shape(self, i):
+        return (2 * self.I, self.H) if i % 2 == 0 else (self.H, self.I)
+
+
+def test_greedy_reductions_hand_ranked():
+    # [PW §3.2 "Planning objective"]: least predicted damage per released byte
+    # first. Gate_up blocks are [64][64], down blocks [64][32], so by Eq. 3
+    # M_gu^b = 512 b + 128 * 2^b and M_dn^b = 256 b + 128 * 2^b. Worked by hand:
+    #   block 0 (q 8, floor 3): damage 8 - b'; best b' = 7, 1 / (36864 - 19968)
+    #   block 1 (q 6, floor 3): damage .5/.6/10 at b' = 5/4/3; best b' = 4,
+    #           0.6 / (9728 - 3072)
+    #   block 2 (hot, q 6, floor 5): b' = 5 only, no damage: eps / 4608
+    #   block 3 (hot, q 5 = floor): no candidate
+    #   block 4 (q 4, floor 3): b' = 3, 0.2 / (4096 - 2560)
+    #   block 5 (q 3 = floor): no candidate
+    # ascending: 2 (2.2e-16), 0 (5.9e-5), 1 (9.0e-5), 4 (1.3e-4)
+    L = _FakeLayer(3, 64, 32, [8, 6, 6, 5, 4, 3], [False, True, False])
+    s = np.zeros((6, 9))
+    s[0, 3:9] = [5, 4, 3, 2, 1, 0]
+    s[1, 3:7] = [10, .6, .5, 0]
+    s[4, 3:5] = [.2, 0]
+    assert O.greedy_reductions(L, s, 0.25) == ([(2, 5), (0, 7)], 0)
+    assert O.greedy_reductions(L, s, 0.50) == ([(2, 5), (0, 7), (1, 4)], 0)
+    assert O.greedy_reductions(L, s, 0.75) == ([(2, 5), (0, 7), (1, 4), (4, 3)], 1)
+
+
+def test_greedy_reductions_equal_scores_go_to_the_lower_block():
+    L = _FakeLayer(2, 64, 32, [7, 3, 7, 3], [False, False])
+    s = np.zeros((4, 9))
+    s[0, 3:8] = [4, 3, 2, 1, 0]
+    s[2] = s[0]
+    assert O.greedy_reductions(L, s, 0.25) == ([(0, 6)], 0)
+    assert O.greedy_reductions(L, s, 0.50) == ([(0, 6), (2, 6)], 0)
+
+
+def test_greedy_reductions_against_enumeration(layer_cache):
+    # every (block, b') pair of the config-1 layer enumerated: each chosen
+    # block takes its least-score b', and no unchosen candidate scores below
+    # a chosen one (so a reversed ranking fails)
+    L = layer_cache(1)
+    s = S.make_sensitivity(4, L.n_blocks)
+    pairs = {}
+    for i in range(2 * L.E):
+        fl = 5 if L.hot[i // 2] else 3
+        N, Kd = L.shape(i)
+        for b2 in range(fl, int(L.q[i])):
+            d = max(1e-12, max(s[i, b2] - s[i, int(L.q[i])], 0.0))
+            pairs[(i, b2)] = d / (N * Kd * (int(L.q[i]) - b2) / 8 + N * (2 ** int(L.q[i]) - 2 ** b2) * 2)
+    best = {}
+    for (i, b2), sc in pairs.items():
+        if i not in best or sc < best[i][0]:
+            best[i] = (sc, b2)
+    red, short = O.greedy_reductions(L, s, 0.5)
+    chosen = {i for i, _ in red}
+    assert short == 0 and len(red) == math.ceil(0.5 * 2 * L.E)
+    for i, b2 in red:
+        assert b2 == best[i][1]
+    worst_in = max(best[i][0] for i in chosen)
+    assert all(best[i][0] >= worst_in for i in best if i not in chosen)
+    assert [i for i, _ in red] == sorted(chosen, key=lambda i: (best[i][0], i))
