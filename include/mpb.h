@@ -196,6 +196,27 @@ int moe_ffn(const void* X_dev, int x_dtype, int T, const int32_t* topk_idx_dev,
             size_t ws_bytes, void* stream);
 
 /*
+ * moe_ffn for callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): the same
+ * arguments, kernels and results as moe_ffn, with the workspace taken from a
+ * device array that the library holds, 32 MiB per GPU, for the life of the
+ * process (its address is looked up once per device, at mpb_init or at the
+ * first call on that device). Allocates nothing itself; the caller still
+ * passes inputs and outputs. Tokens whose workspace (moe_ffn_workspace_bytes
+ * for bf16, slightly less for fp16) exceeds 32 MiB are refused with
+ * MPB_E_WS: the limit is 292 tokens for a layer of H 2048, I 1408, 60 routed
+ * + 4 shared experts, top-4, and 215 tokens for H 4096, I 14336, 8 experts,
+ * top-2. Every call on one GPU shares that
+ * GPU's array and leaves its contents behind; nothing in it needs to start at
+ * zero. Calls that overlap on one GPU (on different streams, or from
+ * different threads) race on the array and must be serialised by the caller.
+ * Errors: as moe_ffn.
+ */
+int moe_ffn_static(const void* X_dev, int x_dtype, int T, const int32_t* topk_idx_dev,
+                   const float* topk_w_dev, const uint32_t* const* planes_dev,
+                   const uint16_t* const* luts_dev, const int32_t* q_dev, float* out_dev, void* stream);
+
+/*
  * The whole layer in one launch (§3.3: routing, expert activation, down
  * projection and output accumulation in one fused kernel): moe_route followed
  * by moe_ffn, as one persistent kernel whose workgroups take units of work in

@@ -74,6 +74,7 @@ def lib() -> ctypes.CDLL:
             "moe_fused_counter_bytes": (ctypes.c_size_t, []),
             "moe_fused": (_I, [_P, _I, _I, _P, _P, _P, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P]),
             "moe_ffn": (_I, [_P, _I, _I, _P, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P]),
+            "moe_ffn_static": (_I, [_P, _I, _I, _P, _P, _P, _P, _P, _P, _P]),
             "set_committed_bits": (_I, [_I, _I]),
             "mpb_committed_bytes": (ctypes.c_int64, [_P]),
             "mpb_get_committed_bits": (_I, [_I]),
@@ -167,6 +168,13 @@ def moe_ffn(X, x_dtype, topk_idx, topk_w, planes_table, luts_table, q, out, ws, 
     return _check("moe_ffn", lib().moe_ffn(_ptr(X), x_dtype, T, _ptr(topk_idx), _ptr(topk_w),
                                            _ptr(planes_table), _ptr(luts_table), _ptr(q), _ptr(out),
                                            _ptr(ws), nbytes, _stream(stream)))
+
+
+def moe_ffn_static(X, x_dtype, topk_idx, topk_w, planes_table, luts_table, q, out, stream=None):
+    T = X.shape[0]
+    return _check("moe_ffn_static", lib().moe_ffn_static(_ptr(X), x_dtype, T, _ptr(topk_idx), _ptr(topk_w),
+                                                         _ptr(planes_table), _ptr(luts_table), _ptr(q), _ptr(out),
+                                                         _stream(stream)))
 
 
 def moe_fused_counter_bytes() -> int:

@@ -9,6 +9,14 @@
 #include "mpb_device.h"
 #include "mpb_internal.h"
 
+// Workspace of moe_ffn_static, for callers that cannot allocate: a file-scope
+// device array, one copy per GPU, held until the process ends. Host code only
+// ever uses the address hipGetSymbolAddress returns for the current device,
+// never the array's name (which on the host is a stand-in, not a device
+// address).
+static constexpr size_t kScratchBytes = (size_t)32 << 20;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
 namespace {
 
 // One page transfer of a block: planes lo..hi-1 move to the GPU (dir 1) or to
@@ -35,6 +43,11 @@ struct State {
 
 State g;
 thread_local std::string g_err;
+
+// Per-device address of the scratch array (below), resolved with the device
+// current; null until then.
+constexpr int kMaxDevices = 64;
+void* g_scratch[kMaxDevices];
 hipEvent_t g_ev[5];
 int g_nev = 0;
 
@@ -49,6 +62,23 @@ int fail(int code, const std::string& msg) {
 
 int hip_fail(hipError_t e, const char* where) {
   return fail(MPB_E_HIP, std::string(where) + ": " + hipGetErrorString(e));
+}
+
+// Address of this device's scratch array, resolved once per device (with the
+// device current). Returns MPB_OK or an error code.
+int resolve_scratch(void** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "scratch: hipGetDevice");
+  if (dev < 0 || dev >= kMaxDevices) return fail(MPB_E_HIP, "scratch: device index above 63");
+  if (!g_scratch[dev]) {
+    void* ptr = nullptr;
+    e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !ptr) return hip_fail(e != hipSuccess ? e : hipErrorInvalidSymbol, "scratch: hipGetSymbolAddress");
+    g_scratch[dev] = ptr;
+  }
+  *out = g_scratch[dev];
+  return MPB_OK;
 }
 
 void block_shape(int i, int* N, int* Kd) {
@@ -218,6 +248,9 @@ int mpb_init(const mpb_layer_desc* d, int32_t* q_dev, const int32_t* q_init_host
   if (e != hipSuccess) return hip_fail(e, "mpb_init: copy of q");
   e = hipStreamSynchronize(s);
   if (e != hipSuccess) return hip_fail(e, "mpb_init: stream sync");
+  void* scr = nullptr;
+  const int rs = resolve_scratch(&scr);
+  if (rs) return rs;
   g.init = true;
   g.H = d->H; g.I = d->I; g.E = d->E; g.S = d->S; g.K = d->K;
   g.q_dev = q_dev;
@@ -335,24 +368,36 @@ size_t moe_ffn_workspace_bytes(int T) {
   return mpb::ws_layout(T, g.H, g.I, g.E, g.S, g.K, true).total;
 }
 
-int moe_ffn(const void* X_dev, int x_dtype, int T, const int32_t* topk_idx_dev, const float* topk_w_dev,
-            const uint32_t* const* planes_dev, const uint16_t* const* luts_dev, const int32_t* q_dev,
-            float* out_dev, void* ws_dev, size_t ws_bytes, void* stream) try {
-  if (!g.init) return fail(MPB_E_UNINIT, "moe_ffn: no layer bound (mpb_init)");
-  if (x_dtype != MPB_F16 && x_dtype != MPB_BF16) return fail(MPB_E_ARG, "moe_ffn: bad x_dtype");
-  if (T < 0) return fail(MPB_E_ARG, "moe_ffn: T < 0");
+}  // extern "C"
+
+namespace {
+
+// moe_ffn and moe_ffn_static: validation, workspace check and the launches.
+// static_ws: the workspace is this device's scratch array (the size check then
+// names its limit).
+int ffn_impl(const char* name, const void* X_dev, int x_dtype, int T, const int32_t* topk_idx_dev,
+             const float* topk_w_dev, const uint32_t* const* planes_dev, const uint16_t* const* luts_dev,
+             const int32_t* q_dev, float* out_dev, void* ws_dev, size_t ws_bytes, void* stream, bool static_ws) {
+  const std::string n(name);
+  if (!g.init) return fail(MPB_E_UNINIT, n + ": no layer bound (mpb_init)");
+  if (x_dtype != MPB_F16 && x_dtype != MPB_BF16) return fail(MPB_E_ARG, n + ": bad x_dtype");
+  if (T < 0) return fail(MPB_E_ARG, n + ": T < 0");
   if (T == 0) return MPB_OK;
-  if (T > (1 << 20)) return fail(MPB_E_SHAPE, "moe_ffn: T above 2^20");
+  if (T > (1 << 20)) return fail(MPB_E_SHAPE, n + ": T above 2^20");
   if (!X_dev || !topk_idx_dev || !topk_w_dev || !planes_dev || !luts_dev || !q_dev || !out_dev || !ws_dev)
-    return fail(MPB_E_ARG, "moe_ffn: null pointer");
-  if (q_dev != g.q_dev) return fail(MPB_E_ARG, "moe_ffn: q_dev is not the bound page table");
+    return fail(MPB_E_ARG, n + ": null pointer");
+  if (q_dev != g.q_dev) return fail(MPB_E_ARG, n + ": q_dev is not the bound page table");
   if (!stream_ok((hipStream_t)stream))
-    return fail(MPB_E_ARG, "moe_ffn: stream is neither the bound stream nor under graph capture");
+    return fail(MPB_E_ARG, n + ": stream is neither the bound stream nor under graph capture");
   const mpb::WsLayout L = mpb::ws_layout(T, g.H, g.I, g.E, g.S, g.K, x_dtype == MPB_BF16);
   const long long ntile = std::max(g.I / 64, (g.H + 127) / 128);
-  if (((long long)L.max_items + 7) / 8 * 8 * ntile >= (1ll << 31)) return fail(MPB_E_SHAPE, "moe_ffn: T too large for this layer");
-  if (ws_bytes < L.total)
-    return fail(MPB_E_WS, "moe_ffn: workspace " + std::to_string(ws_bytes) + " < " + std::to_string(L.total));
+  if (((long long)L.max_items + 7) / 8 * 8 * ntile >= (1ll << 31)) return fail(MPB_E_SHAPE, n + ": T too large for this layer");
+  if (ws_bytes < L.total) {
+    if (static_ws)
+      return fail(MPB_E_WS, n + ": " + std::to_string(T) + " tokens need " + std::to_string(L.total) +
+                                " workspace bytes, above the static scratch limit of " + std::to_string(ws_bytes));
+    return fail(MPB_E_WS, n + ": workspace " + std::to_string(ws_bytes) + " < " + std::to_string(L.total));
+  }
   char* ws = (char*)ws_dev;
   const int tc = mpb::ffn_token_chunks(T, g.E, g.K);
   const mpb::FfnParams p = ffn_params(L, ws, X_dev, x_dtype, T, topk_idx_dev, topk_w_dev, planes_dev, luts_dev, q_dev,
@@ -362,10 +407,10 @@ int moe_ffn(const void* X_dev, int x_dtype, int T, const int32_t* topk_idx_dev, 
   hipError_t e = hipSuccess;
   if (x_dtype == MPB_BF16) {
     e = mpb::launch_x_to_f16((const uint16_t*)X_dev, (uint16_t*)(ws + L.xh), (size_t)T * g.H, s);
-    if (e != hipSuccess) return hip_fail(e, "moe_ffn: activation conversion");
+    if (e != hipSuccess) return hip_fail(e, (n + ": activation conversion").c_str());
   }
   e = mpb::launch_permute(p, (int32_t*)(ws + L.ccnt), s);
-  if (e != hipSuccess) return hip_fail(e, "moe_ffn: permute");
+  if (e != hipSuccess) return hip_fail(e, (n + ": permute").c_str());
   int qmax_gu = 3, qmax_dn = 3;
   for (int i = 0; i < g.nb(); i += 2) {
     qmax_gu = std::max(qmax_gu, g.q[i]);
@@ -373,16 +418,40 @@ int moe_ffn(const void* X_dev, int x_dtype, int T, const int32_t* topk_idx_dev, 
   }
   // events 1 and 2 time the gate_up kernel itself: its launch records them
   e = mpb::launch_gate_up(p, qmax_gu, tc, s, g_nev == 5 ? g_ev[1] : nullptr, g_nev == 5 ? g_ev[2] : nullptr);
-  if (e != hipSuccess) return hip_fail(e, "moe_ffn: gate_up");
+  if (e != hipSuccess) return hip_fail(e, (n + ": gate_up").c_str());
   e = mpb::launch_down(p, qmax_dn, tc == 1, s);
-  if (e != hipSuccess) return hip_fail(e, "moe_ffn: down");
+  if (e != hipSuccess) return hip_fail(e, (n + ": down").c_str());
   mark(3, s);
   e = mpb::launch_combine(p, s);
-  if (e != hipSuccess) return hip_fail(e, "moe_ffn: combine");
+  if (e != hipSuccess) return hip_fail(e, (n + ": combine").c_str());
   mark(4, s);
   return MPB_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int moe_ffn(const void* X_dev, int x_dtype, int T, const int32_t* topk_idx_dev, const float* topk_w_dev,
+            const uint32_t* const* planes_dev, const uint16_t* const* luts_dev, const int32_t* q_dev,
+            float* out_dev, void* ws_dev, size_t ws_bytes, void* stream) try {
+  return ffn_impl("moe_ffn", X_dev, x_dtype, T, topk_idx_dev, topk_w_dev, planes_dev, luts_dev, q_dev, out_dev,
+                  ws_dev, ws_bytes, stream, false);
 } catch (...) {
   return fail(MPB_E_HIP, "moe_ffn: unexpected exception");
+}
+
+int moe_ffn_static(const void* X_dev, int x_dtype, int T, const int32_t* topk_idx_dev, const float* topk_w_dev,
+                   const uint32_t* const* planes_dev, const uint16_t* const* luts_dev, const int32_t* q_dev,
+                   float* out_dev, void* stream) try {
+  if (!g.init) return fail(MPB_E_UNINIT, "moe_ffn_static: no layer bound (mpb_init)");
+  void* scr = nullptr;
+  const int rs = resolve_scratch(&scr);
+  if (rs) return rs;
+  return ffn_impl("moe_ffn_static", X_dev, x_dtype, T, topk_idx_dev, topk_w_dev, planes_dev, luts_dev, q_dev,
+                  out_dev, scr, kScratchBytes, stream, true);
+} catch (...) {
+  return fail(MPB_E_HIP, "moe_ffn_static: unexpected exception");
 }
 
 size_t moe_fused_counter_bytes(void) { return mpb::fused_counter_bytes(); }
