@@ -205,7 +205,7 @@ int moe_ffn(const void* X_dev, int x_dtype, int T, const int32_t* topk_idx_dev,
  * passes inputs and outputs. Tokens whose workspace (moe_ffn_workspace_bytes
  * for bf16, slightly less for fp16) exceeds 32 MiB are refused with
  * MPB_E_WS: the limit is 292 tokens for a layer of H 2048, I 1408, 60 routed
- * + 4 shared experts, top-4, and 215 tokens for H 4096, I 14336, 8 experts,
+ * + 4 shared experts, top-4, and 151 tokens for H 4096, I 14336, 8 experts,
  * top-2. Every call on one GPU shares that
  * GPU's array and leaves its contents behind; nothing in it needs to start at
  * zero. Calls that overlap on one GPU (on different streams, or from

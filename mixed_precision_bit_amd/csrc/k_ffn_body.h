@@ -402,12 +402,16 @@ __device__ __forceinline__ void poison(float* dst, size_t ld, int rows, int cols
 // the other one, two barriers per step instead of four.
 template <int Q, int TC, bool CO = false, bool NT = true, bool DB = false>
 __device__ __forceinline__ void down_body(const FfnParams& p, int e, int it, int t0, int nt, uint16_t* lds,
-                                          uint32_t lut_bytes, int tid) {
+                                          uint32_t lut_bytes, int tid, int ksi = 0) {
   const int lane = tid & 63, r = lane & 31, g = lane >> 5;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int rg = w & 3, kh = w >> 2;
   const int I = p.I, H = p.H, NC = (I / 32 + 3) >> 2;
-  const KSplit ks(I);
+  // K range ksi: half-chunks hc0 .. hc1-1 (whole chunks; the last range ends at
+  // the row's end, whose chunk is zero-padded), split in two halves as a row
+  const int hc0 = ksi * p.dn_hcs, hc1 = min(I >> 6, hc0 + p.dn_hcs);
+  const int klen = hc1 * 64;  // activation elements at and past klen read as zero
+  const KSplit ks((hc1 - hc0) * 64);
   const int n0 = it * 128 + rg * 32;
   const bool active = n0 < H;
   const int base = ld_co<CO>(p.offsets + e) + t0;
@@ -428,14 +432,14 @@ __device__ __forceinline__ void down_body(const FfnParams& p, int e, int it, int
   static_assert(!DB || TC == 1, "double-buffered stage: one token chunk");
   // stage buffer of round j (DB)
   auto rbuf = [&](int j) -> uint32_t { return DB ? stage_off_db(j, 0, 0, 0) : 0u; };
-  // window (s, j): for K half i, element 64 (i HH + 2 s + g') + 32 j + 8 m
+  // window (s, j): for K half i, element 64 (hc0 + i HH + 2 s + g') + 32 j + 8 m
   auto kwin = [&](int s, int j, int (&k)[2]) {
 #pragma unroll
-    for (int i = 0; i < 2; ++i) k[i] = (i * ks.HH + 2 * s + ((spc >> 2) & 1)) * 64 + 32 * j + 8 * (spc & 3);
+    for (int i = 0; i < 2; ++i) k[i] = (hc0 + i * ks.HH + 2 * s + ((spc >> 2) & 1)) * 64 + 32 * j + 8 * (spc & 3);
   };
 
-  const int cb = kh * (ks.HH >> 1);
-  const int ce = kh ? NC : ks.HH >> 1;
+  const int cb = (hc0 >> 1) + kh * (ks.HH >> 1);
+  const int ce = kh ? min(NC, (hc1 + 1) >> 1) : (hc0 >> 1) + (ks.HH >> 1);
   rsrc_t rs[Q];
 #pragma unroll
   for (int q = 0; q < Q; ++q)
@@ -447,14 +451,14 @@ __device__ __forceinline__ void down_body(const FfnParams& p, int e, int it, int
   int ka[2], kb[2];
   load_table_image<Q>(p.luts[blk * 6 + (Q - 3)] + (size_t)it * (128u << Q), w, lane);
   kwin(0, 0, ka);
-  load_window<TC>(ha, sp, ka, I);
+  load_window<TC>(ha, sp, ka, klen);
   load_planes<Q, NT>(PA, rs, cb, 0, voff);
   wait_vmem_all();
-  store_window<TC>(stage, ha, sp, ka, I);
+  store_window<TC>(stage, ha, sp, ka, klen);
   kwin(0, 1, kb);
-  load_window<TC>(hb, sp, kb, I);
+  load_window<TC>(hb, sp, kb, klen);
   kwin(1, 0, ka);
-  load_window<TC>(ha, sp, ka, I);
+  load_window<TC>(ha, sp, ka, klen);
   load_planes<Q, NT>(PB, rs, cb, 1, voff);
   load_planes<Q, NT>(PC, rs, cb, 2, voff);
   __syncthreads();
@@ -485,17 +489,17 @@ __device__ __forceinline__ void down_body(const FfnParams& p, int e, int it, int
   auto step = [&](int s, uint2 (&P)[Q]) {
     round(0, P);
     kwin(s, 1, kb);
-    store_window<TC>(stage + rbuf(1), hb, sp, kb, I);
+    store_window<TC>(stage + rbuf(1), hb, sp, kb, klen);
     kwin(s + 1, 1, kb);
-    load_window<TC>(hb, sp, kb, I);
+    load_window<TC>(hb, sp, kb, klen);
     __syncthreads();
     round(1, P);
     if (s + 1 < ks.NSW) {
       kwin(s + 1, 0, ka);
-      store_window<TC>(stage + rbuf(0), ha, sp, ka, I);
+      store_window<TC>(stage + rbuf(0), ha, sp, ka, klen);
     }
     kwin(s + 2, 0, ka);
-    load_window<TC>(ha, sp, ka, I);
+    load_window<TC>(ha, sp, ka, klen);
     load_planes<Q, NT>(P, rs, cb, s + 3, voff);
     __syncthreads();
   };
@@ -521,7 +525,7 @@ __device__ __forceinline__ void down_body(const FfnParams& p, int e, int it, int
     __syncthreads();
     const int t = kTok * c + r;
     if (kh == 0 && active && t < nt) {
-      float* yrow = p.y + (size_t)(base + t) * H + n0 + 4 * g;
+      float* yrow = p.y + (size_t)ksi * p.T * (p.K + p.S) * H + (size_t)(base + t) * H + n0 + 4 * g;
 #pragma unroll
       for (int v4 = 0; v4 < 4; ++v4) {
         f32x4 o;
@@ -565,6 +569,13 @@ __device__ __forceinline__ void combine4(const FfnParams& p, int t, int n) {
     f32x4 y[8];
 #pragma unroll
     for (int j = 0; j < 8; ++j) y[j] = live[j] ? *(const f32x4*)(p.y + (size_t)pos[j] * p.H + n) : (f32x4){};
+    // partial sums of the other K ranges, added in range order
+    const size_t slice = (size_t)p.T * KS * p.H;
+    for (int r = 1; r < p.dn_split; ++r) {
+#pragma unroll
+      for (int j = 0; j < 8; ++j)
+        if (live[j]) y[j] += *(const f32x4*)(p.y + r * slice + (size_t)pos[j] * p.H + n);
+    }
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
       if (!live[j]) continue;

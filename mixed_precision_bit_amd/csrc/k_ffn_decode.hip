@@ -1,7 +1,8 @@
 // Expert FFN kernels: gate_up + SwiGLU, down, and the weighted combine, one
 // launch each (the device code is in k_ffn_body.h). Items of 32 tokens at
 // decode sizes; gate_up takes 128-token items (TC = 4), in the XCD-interleaved
-// order, once groups hold 96 tokens on average.
+// order, once groups hold 96 tokens on average. Few long down items are split
+// over K ranges (one workgroup per range, partial sums added by the combine).
 #include <hip/hip_ext.h>
 
 #include <algorithm>
@@ -48,15 +49,20 @@ __global__ __launch_bounds__(kThreads) void k_gate_up(FfnParams p, int qmax) {
 template <int TC, bool NT>
 __global__ __launch_bounds__(kThreads) void k_down(FfnParams p, int qmax) {
   extern __shared__ __attribute__((aligned(256))) uint16_t lds[];
-  int e, it, t0, nt;
-  if (!decode_item(p, false, (p.H + 127) >> 7, e, it, t0, nt)) return;
+  // workgroup b: K range b % dn_split of tile (b / dn_split) % ntile of item
+  // (b / dn_split) / ntile
+  const int ntile = (p.H + 127) >> 7;
+  const int b = blockIdx.x / p.dn_split, ksi = blockIdx.x - b * p.dn_split;
+  const int item = b / ntile, it = b - item * ntile;
+  int e, t0, nt;
+  if (!item_of(p, false, item, e, t0, nt)) return;
   const int q = p.q[2 * e + 1];
   const uint32_t lut_bytes = 256u << qmax;
   const bool db = TC == 1 && nt <= kDbTok;
 #define MPB_DN(Q)                                                                                       \
   case Q:                                                                                               \
-    if (db) down_body<Q, TC, false, NT, TC == 1>(p, e, it, t0, nt, lds, lut_bytes, threadIdx.x);        \
-    else down_body<Q, TC, false, NT>(p, e, it, t0, nt, lds, lut_bytes, threadIdx.x);                   \
+    if (db) down_body<Q, TC, false, NT, TC == 1>(p, e, it, t0, nt, lds, lut_bytes, threadIdx.x, ksi);   \
+    else down_body<Q, TC, false, NT>(p, e, it, t0, nt, lds, lut_bytes, threadIdx.x, ksi);              \
     break;
   switch (q < 3 || q > qmax || !tables_at_zero(lds) ? 0 : q) {
     MPB_DN(3)
@@ -68,7 +74,8 @@ __global__ __launch_bounds__(kThreads) void k_down(FfnParams p, int qmax) {
 #undef MPB_DN
     default: {
       const int n0 = it * 128;
-      poison(p.y + (size_t)(p.offsets[e] + t0) * p.H + n0, p.H, nt, min(128, p.H - n0));
+      poison(p.y + (size_t)ksi * p.T * (p.K + p.S) * p.H + (size_t)(p.offsets[e] + t0) * p.H + n0, p.H, nt,
+             min(128, p.H - n0));
     }
   }
 }
@@ -123,7 +130,8 @@ static hipError_t launch_tc(const FfnParams& p, int qmax, hipStream_t s, hipEven
     else
       hipLaunchKernelGGL(k_gate_up<TC>, dim3(items * (p.I >> 6)), dim3(kThreads), shmem, s, p, qmax);
   } else
-    hipLaunchKernelGGL((k_down<TC, NT>), dim3(p.max_items * ((p.H + 127) >> 7)), dim3(kThreads), shmem, s, p, qmax);
+    hipLaunchKernelGGL((k_down<TC, NT>), dim3(p.max_items * ((p.H + 127) >> 7) * p.dn_split), dim3(kThreads), shmem,
+                       s, p, qmax);
   return hipGetLastError();
 }
 

@@ -276,7 +276,9 @@ __device__ __forceinline__ void gate_up_unit(const FusedParams& P, int u, uint16
 
 __device__ __forceinline__ void down_unit(const FusedParams& P, int u, uint16_t* lds, uint32_t* slot, int tid) {
   const FfnParams& p = P.f;
-  const int item = u / P.ntile_dn, it = u - item * P.ntile_dn;
+  // unit u: K range u % dn_split of tile (u / dn_split) % ntile_dn of item (u / dn_split) / ntile_dn
+  const int b = u / p.dn_split, ksi = u - b * p.dn_split;
+  const int item = b / P.ntile_dn, it = b - item * P.ntile_dn;
   int e, t0, nt, cnt;
   if (!unit_item(p, 1, item, slot, e, t0, nt, cnt)) return;
   uint32_t* flag = slot + 1;
@@ -287,32 +289,33 @@ __device__ __forceinline__ void down_unit(const FusedParams& P, int u, uint16_t*
   const uint32_t lut_bytes = 256u << P.qmax;
   switch (q < 3 || q > P.qmax || !tables_at_zero(lds) ? 0 : q) {
     case 3:
-      if (nt <= kDbTok) down_body<3, 1, true, true, true>(p, e, it, t0, nt, lds, lut_bytes, tid);
-      else down_body<3, 1, true>(p, e, it, t0, nt, lds, lut_bytes, tid);
+      if (nt <= kDbTok) down_body<3, 1, true, true, true>(p, e, it, t0, nt, lds, lut_bytes, tid, ksi);
+      else down_body<3, 1, true>(p, e, it, t0, nt, lds, lut_bytes, tid, ksi);
       break;
     case 4:
-      if (nt <= kDbTok) down_body<4, 1, true, true, true>(p, e, it, t0, nt, lds, lut_bytes, tid);
-      else down_body<4, 1, true>(p, e, it, t0, nt, lds, lut_bytes, tid);
+      if (nt <= kDbTok) down_body<4, 1, true, true, true>(p, e, it, t0, nt, lds, lut_bytes, tid, ksi);
+      else down_body<4, 1, true>(p, e, it, t0, nt, lds, lut_bytes, tid, ksi);
       break;
     case 5:
-      if (nt <= kDbTok) down_body<5, 1, true, true, true>(p, e, it, t0, nt, lds, lut_bytes, tid);
-      else down_body<5, 1, true>(p, e, it, t0, nt, lds, lut_bytes, tid);
+      if (nt <= kDbTok) down_body<5, 1, true, true, true>(p, e, it, t0, nt, lds, lut_bytes, tid, ksi);
+      else down_body<5, 1, true>(p, e, it, t0, nt, lds, lut_bytes, tid, ksi);
       break;
     case 6:
-      if (nt <= kDbTok) down_body<6, 1, true, true, true>(p, e, it, t0, nt, lds, lut_bytes, tid);
-      else down_body<6, 1, true>(p, e, it, t0, nt, lds, lut_bytes, tid);
+      if (nt <= kDbTok) down_body<6, 1, true, true, true>(p, e, it, t0, nt, lds, lut_bytes, tid, ksi);
+      else down_body<6, 1, true>(p, e, it, t0, nt, lds, lut_bytes, tid, ksi);
       break;
     case 7:
-      if (nt <= kDbTok) down_body<7, 1, true, true, true>(p, e, it, t0, nt, lds, lut_bytes, tid);
-      else down_body<7, 1, true>(p, e, it, t0, nt, lds, lut_bytes, tid);
+      if (nt <= kDbTok) down_body<7, 1, true, true, true>(p, e, it, t0, nt, lds, lut_bytes, tid, ksi);
+      else down_body<7, 1, true>(p, e, it, t0, nt, lds, lut_bytes, tid, ksi);
       break;
     case 8:
-      if (nt <= kDbTok) down_body<8, 1, true, true, true>(p, e, it, t0, nt, lds, lut_bytes, tid);
-      else down_body<8, 1, true>(p, e, it, t0, nt, lds, lut_bytes, tid);
+      if (nt <= kDbTok) down_body<8, 1, true, true, true>(p, e, it, t0, nt, lds, lut_bytes, tid, ksi);
+      else down_body<8, 1, true>(p, e, it, t0, nt, lds, lut_bytes, tid, ksi);
       break;
     default: {
       const int n0 = it * 128;
-      poison(p.y + (size_t)(p.offsets[e] + t0) * p.H + n0, p.H, nt, min(128, p.H - n0));
+      poison(p.y + (size_t)ksi * p.T * (p.K + p.S) * p.H + (size_t)(p.offsets[e] + t0) * p.H + n0, p.H, nt,
+             min(128, p.H - n0));
     }
   }
   mark_done(ctr(P, C_DOWN));
@@ -361,7 +364,7 @@ __device__ __forceinline__ void topk_unit(const FusedParams& P, int u, uint16_t*
 __device__ __forceinline__ void comb_unit(const FusedParams& P, int u, uint32_t* flag, int tid) {
   const FfnParams& p = P.f;
   bool ok = wait_count(P, C_GROUP, P.n_group, flag);
-  if (ok) ok = wait_count(P, C_DOWN, (uint32_t)p.n_items[1] * P.ntile_dn, flag);
+  if (ok) ok = wait_count(P, C_DOWN, (uint32_t)p.n_items[1] * P.ntile_dn * p.dn_split, flag);
   const size_t H4 = p.H >> 2, gid = (size_t)u * 512 + tid;
   if (gid < (size_t)p.T * H4) {
     const int t = (int)(gid / H4), n = (int)(gid - (size_t)t * H4) * 4;
@@ -479,7 +482,7 @@ hipError_t launch_fused(const FusedLaunch& L, hipStream_t s) {
   P.ntile_gu = f.I >> 6;
   P.ntile_dn = (f.H + 127) >> 7;
   P.n_gu = f.max_items * P.ntile_gu;
-  P.n_dn = f.max_items * P.ntile_dn;
+  P.n_dn = f.max_items * P.ntile_dn * f.dn_split;
   P.n_comb = (int)(((long long)f.T * (f.H >> 2) + 511) / 512);
   // the unit slot and the wait flag sit at LDS byte 0: they are read before a
   // unit writes any LDS and rewritten only after the unit's last LDS access

@@ -174,7 +174,7 @@ WsLayout ws_layout(int T, int H, int I, int E, int S, int K, bool bf16) {
   L.ccnt = off;    off += align256((size_t)group_chunks(T, K) * E * 4);
   L.hhi = off;     off += align256(P * (size_t)I * 2);
   L.hlo = off;     off += align256(P * (size_t)I * 2);
-  L.y = off;       off += align256(P * (size_t)H * 4);
+  L.y = off;       off += align256(P * (size_t)H * 4 * dn_splits(T, H, I, E, S, K));
   L.xh = off;      off += bf16 ? align256((size_t)T * H * 2) : 0;
   L.total = off;
   return L;
@@ -209,6 +209,8 @@ mpb::FfnParams ffn_params(const mpb::WsLayout& L, char* ws, const void* X_dev, i
   p.hlo = (uint16_t*)(ws + L.hlo);
   p.y = (float*)(ws + L.y);
   p.out = out_dev;
+  p.dn_split = 1;
+  p.dn_hcs = (g.I / 64 + 1) & ~1;
   return p;
 }
 
@@ -391,7 +393,8 @@ int ffn_impl(const char* name, const void* X_dev, int x_dtype, int T, const int3
     return fail(MPB_E_ARG, n + ": stream is neither the bound stream nor under graph capture");
   const mpb::WsLayout L = mpb::ws_layout(T, g.H, g.I, g.E, g.S, g.K, x_dtype == MPB_BF16);
   const long long ntile = std::max(g.I / 64, (g.H + 127) / 128);
-  if (((long long)L.max_items + 7) / 8 * 8 * ntile >= (1ll << 31)) return fail(MPB_E_SHAPE, n + ": T too large for this layer");
+  if (((long long)L.max_items + 7) / 8 * 8 * ntile * mpb::dn_splits(T, g.H, g.I, g.E, g.S, g.K) >= (1ll << 31))
+    return fail(MPB_E_SHAPE, n + ": T too large for this layer");
   if (ws_bytes < L.total) {
     if (static_ws)
       return fail(MPB_E_WS, n + ": " + std::to_string(T) + " tokens need " + std::to_string(L.total) +
@@ -400,8 +403,10 @@ int ffn_impl(const char* name, const void* X_dev, int x_dtype, int T, const int3
   }
   char* ws = (char*)ws_dev;
   const int tc = mpb::ffn_token_chunks(T, g.E, g.K);
-  const mpb::FfnParams p = ffn_params(L, ws, X_dev, x_dtype, T, topk_idx_dev, topk_w_dev, planes_dev, luts_dev, q_dev,
-                                      out_dev, tc);
+  mpb::FfnParams p = ffn_params(L, ws, X_dev, x_dtype, T, topk_idx_dev, topk_w_dev, planes_dev, luts_dev, q_dev,
+                                out_dev, tc);
+  p.dn_split = mpb::dn_splits(T, g.H, g.I, g.E, g.S, g.K);
+  p.dn_hcs = mpb::dn_range_hcs(g.I, p.dn_split);
   hipStream_t s = (hipStream_t)stream;
   mark(0, s);
   hipError_t e = hipSuccess;
@@ -480,7 +485,8 @@ int moe_fused(const void* X_dev, int x_dtype, int T, const float* W_router_dev, 
     return fail(MPB_E_ARG, "moe_fused: stream is neither the bound stream nor under graph capture");
   const mpb::WsLayout L = mpb::ws_layout(T, g.H, g.I, g.E, g.S, g.K, x_dtype == MPB_BF16);
   const long long ntile = std::max(g.I / 64, (g.H + 127) / 128);
-  if ((long long)L.max_items * ntile >= (1ll << 30)) return fail(MPB_E_SHAPE, "moe_fused: T too large for this layer");
+  if ((long long)L.max_items * ntile * mpb::dn_splits(T, g.H, g.I, g.E, g.S, g.K) >= (1ll << 30))
+    return fail(MPB_E_SHAPE, "moe_fused: T too large for this layer");
   const size_t c_bytes = mpb::fused_counter_bytes(), r_bytes = mpb::route_workspace_bytes(T, g.E);
   const size_t need = c_bytes + r_bytes + L.total;
   if (ws_bytes < need)
@@ -489,6 +495,8 @@ int moe_fused(const void* X_dev, int x_dtype, int T, const float* W_router_dev, 
   mpb::FusedLaunch F{};
   F.f = ffn_params(L, ws + c_bytes + r_bytes, X_dev, x_dtype, T, topk_idx_dev, topk_w_dev, planes_dev, luts_dev,
                    q_dev, out_dev, 1);
+  F.f.dn_split = mpb::dn_splits(T, g.H, g.I, g.E, g.S, g.K);
+  F.f.dn_hcs = mpb::dn_range_hcs(g.I, F.f.dn_split);
   F.x = (const uint16_t*)X_dev;
   F.xdt = x_dtype;
   F.W = W_router_dev;

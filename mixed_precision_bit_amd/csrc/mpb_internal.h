@@ -12,11 +12,14 @@ namespace mpb {
 constexpr int kChunkTokens = 32;
 
 // Token chunks per work item of the gate_up kernel: one dequantised weight
-// operand feeds TC MFMAs, so large groups (prefill) take four chunks and
-// decode-size groups one. The down kernel always takes one (with its two
-// MFMAs per word, h hi and lo, more chunks cost more in registers and LDS
-// reads than the shared dequantisation saves). Decided from the shapes only
-// (the workspace layout depends on it).
+// operand feeds TC MFMAs, one per 32-token chunk, so large groups (prefill)
+// take four chunks and decode-size groups one. The down kernel always takes
+// one (with its two MFMAs per word, h hi and lo, more chunks cost more in
+// registers and LDS reads than the shared dequantisation saves). Two chunks
+// for groups of 24 to 95 tokens (one item per Mixtral-shaped decode expert)
+// were measured slower in both kernels: the second accumulator takes the
+// kernels to three waves per SIMD, which costs more than the dequantisation
+// it saves. Decided from the shapes only (the workspace layout depends on it).
 inline int ffn_token_chunks(int T, int E, int K) {
   const long long avg = (long long)T * K / E;  // tokens per routed group on average
   return avg >= 96 ? 4 : 1;
@@ -44,9 +47,33 @@ struct FfnParams {
   int tpi_dn;                 // down tokens per item: kChunkTokens
   uint16_t* hhi;              // [P][I] fp16 high part of h = SiLU(gate) * up
   uint16_t* hlo;              // [P][I] fp16 remainder h - hi
-  float* y;                   // [P][H] per-entry down projection
+  float* y;                   // [dn_split][P][H] per-entry down projection (partial sums over K ranges)
   float* out;                 // [T][H]
+  int dn_split;               // K ranges of the down projection (1: whole K per workgroup)
+  int dn_hcs;                 // half-chunks (64 elements) per K range, even
 };
+
+// Down-projection K split: a layer whose down launch would hold fewer than
+// 1024 workgroups (few, long items: Mixtral-shaped experts) splits K into
+// ranges of whole 128-element chunks, one workgroup each, with at least 16
+// half-chunks per range; the combine pass adds the partial sums in range
+// order. Decided from the shapes only (the workspace layout depends on it).
+inline int dn_splits(int T, int H, int I, int E, int S, int K) {
+  const long long P = (long long)T * (K + S), NB = (long long)E + S;
+  const long long items = (P < NB ? P : NB) + P / kChunkTokens;
+  const long long wgs = items * ((H + 127) / 128);
+  if (wgs >= 1024) return 1;
+  long long sp = (1536 + wgs - 1) / (wgs > 0 ? wgs : 1);
+  const long long most = (I / 64) / 16;
+  if (sp > most) sp = most;
+  return sp < 1 ? 1 : (int)sp;
+}
+// half-chunks per K range for n ranges of HC half-chunks (even, ranges cover HC)
+inline int dn_range_hcs(int I, int n) {
+  const int HC = I / 64;
+  const int per = (HC + n - 1) / n;
+  return (per + 1) & ~1;
+}
 
 struct WsLayout {
   size_t counts, offsets, ptok, pw, inv, items, items_dn, n_items, ccnt, hhi, hlo, y, xh, total;

@@ -65,6 +65,10 @@ CONFIGS = {
              q_mode="uniform", bias=False, seed=1014),
     15: dict(name="e512_one_token", H=64, I=64, E=512, S=0, K=8, T=1, xdtype="f16",
              q_mode="uniform", bias=False, seed=1015),
+    # parity-only: few long items, so the down projection is split over K
+    # ranges (49 half-chunks of 64 in three ranges, the last one odd)
+    16: dict(name="split_k", H=192, I=3136, E=3, S=1, K=2, T=6, xdtype="f16",
+             q_mode="uniform", bias=False, seed=1016),
 }
 
 LUT_STD = 0.02  # centroid draws ~ N(0, 0.02)

@@ -535,13 +535,14 @@ def test_activation_beyond_fp16_range_is_not_silently_wrong(layer_cache):
     assert_close(gout[ok], O.moe_ffn(X[ok], z[ok], r[ok], L), "other tokens")
 
 
-@pytest.mark.parametrize("cfg", [12, 13, 14, 15])
+@pytest.mark.parametrize("cfg", [12, 13, 14, 15, 16])
 def test_edge_shapes_every_element(cfg, layer_cache):
     """Extreme layer shapes, every element against the oracle on both paths:
     one expert with H = I = 64 (a single K half-chunk and row tile), more
     shared than routed experts with bf16 input and a router bias, top-16 of
-    64 experts, and 512 experts for a single token. The one-launch path
-    agrees bit for bit."""
+    64 experts, 512 experts for a single token, and a layer whose few long
+    down items are split over three K ranges (the last of odd length). The
+    one-launch path agrees bit for bit."""
     L, D = dev_layer(layer_cache, cfg)
     Xb = S.make_tokens(cfg)
     xdtype = L.cfg["xdtype"]
