@@ -177,6 +177,89 @@ def planner_timing(torch, M, L, cfg, idx, w, steps, F_blk=20):
             "released_bytes": summ["released"], "stage": summ["stage"]}
 
 
+def sweep_states(L, s, fracs=(0.25, 0.5, 0.75), floor_hot=5, eps=1e-12):
+    """Bitwidth states of the sweep on the config-1 layer: the initial
+    commitment; then, for each fraction f, the routed blocks with the least
+    predicted damage per released byte lowered (PagedWeight §3.2 "Planning
+    objective": damage max(eps, s_i^b' - s_i^q) of the drop q -> b' (Eq. 4, 8
+    with unit multipliers) over the bytes it releases (Eq. 3)), each block to
+    its best legal b' (floor 3 bits, 5 for hot-bucket experts), the first
+    ceil(f x #routed blocks) of that ranking (ties to the lower block), so the
+    lowered sets are nested; last, every block at 8 bits."""
+    q0 = np.asarray(L.q, np.int64)
+    best = []
+    for i in range(2 * L.E):
+        fl = floor_hot if L.hot[i // 2] else 3
+        b = int(q0[i])
+        N, Kd = L.shape(i)
+        cands = [(max(eps, s[i, b2] - s[i, b]) / (block_bytes(N, Kd, b) - block_bytes(N, Kd, b2)), b2)
+                 for b2 in range(fl, b)]
+        if cands:
+            sc, b2 = min(cands)
+            best.append((sc, i, b2))
+    best.sort()
+    states = [("initial", q0.copy())]
+    for f in fracs:
+        q = q0.copy()
+        for _, i, b2 in best[:int(np.ceil(f * 2 * L.E))]:
+            q[i] = b2
+        states.append((f"lowered {int(round(f * 100))}%", q))
+    states.append(("all 8-bit", np.full(L.n_blocks, 8, np.int64)))
+    return states
+
+
+def run_sweep(torch, M, L, idx_host, step_fn, T, steps, warmup):
+    """Times the step in every bitwidth state (eager launches, HIP events
+    around the phases as in timed region 2). Launch order: for each state,
+    warm-up steps, then `steps` timed ones."""
+    import mpb_synth as S
+    s = S.make_sensitivity(4, L.n_blocks)
+    out = []
+    prev = np.asarray(L.q, np.int64).copy()
+    stream = torch.cuda.current_stream()
+    k0 = 0
+    for name, q in sweep_states(L, s):
+        for i in np.nonzero(q != prev)[0]:
+            M.set_committed_bits(int(i), int(q[i]))
+        prev = q
+        for k in range(warmup):
+            step_fn(k0 + k)
+        k0 += warmup
+        evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(steps)]
+        for row in evs:
+            for e in row:
+                e.record(stream)
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        for k in range(steps):
+            M.mpb_set_kernel_events([e.cuda_event for e in evs[k]])
+            step_fn(k0 + k)
+        M.mpb_set_kernel_events([])
+        b.record(stream)
+        torch.cuda.synchronize()
+        k0 += steps
+        ms = a.elapsed_time(b) / steps
+        ph = np.array([[evs[k][j].elapsed_time(evs[k][j + 1]) for j in range(4)] for k in range(steps)])
+        gu, dn = float(ph[:, 1].mean()), float(ph[:, 2].mean())
+        # blocks of the experts this batch touches (routed experts with tokens, every shared one)
+        hit = np.zeros(L.E + L.S, bool)
+        hit[np.unique(idx_host[(idx_host >= 0) & (idx_host < L.E)])] = True
+        hit[L.E:] = True
+        touched = np.repeat(hit, 2).astype(np.uint8)
+        mb = int(M.mpb_committed_bytes(touched))
+        gu_b = sum(block_bytes(*L.shape(2 * e), int(q[2 * e])) for e in np.nonzero(hit)[0])
+        dn_b = mb - gu_b
+        out.append({"state": name, "committed_bytes": mb, "gate_up_block_bytes": int(gu_b),
+                    "down_block_bytes": int(dn_b), "ms_per_step": round(ms, 5),
+                    "tokens_per_s": round(T / (ms * 1e-3), 1), "gate_up_us": round(gu * 1e3, 2),
+                    "down_us": round(dn * 1e3, 2),
+                    "gate_up_gbs": round((gu_b + T * L.H * 2) / (gu * 1e-3) / 1e9, 1),
+                    "down_gbs": round(dn_b / (dn * 1e-3) / 1e9, 1),
+                    "launches": [warmup, steps]})
+    return out
+
+
 def copy_calibration(torch, nbytes, steps):
     """Time a plain copy kernel (torch's device copy) of known size: the
     reference rocprofv3's FETCH_SIZE / WRITE_SIZE are scaled by, and the
@@ -214,6 +297,9 @@ def main():
                     help="also time the same steps as one fused launch per step (moe_fused)")
     ap.add_argument("--plan", action="store_true",
                     help="also time the routing-mass kernel and the host planner step on this batch")
+    ap.add_argument("--sweep", action="store_true",
+                    help="config 4: also time the step in each bitwidth state (initial, 25/50/75%% of the routed "
+                         "blocks lowered by damage per released byte, all 8-bit)")
     ap.add_argument("--page-movement", action="store_true",
                     help="also replay the steps while cold blocks' upper planes are offloaded and reloaded "
                          "on a copy stream, and report the slowdown")
@@ -396,6 +482,11 @@ def main():
             graph.replay()
         replay.steps = args.steps
         res["page_movement"] = page_movement(torch, M, L, D0, replay, stream, ms)
+    if args.sweep:
+        if cfg != 4:
+            print("--sweep runs on config 4 (the bitwidth-change sweep)", file=sys.stderr)
+            sys.exit(2)
+        res["sweep"] = run_sweep(torch, M, L, idx_host, step, T, args.steps, max(1, args.warmup // 4))
     if rank == 0 and not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(L, Xbits, args.cpu_tokens)
     if rank == 0:

@@ -362,7 +362,10 @@ __device__ __forceinline__ void gate_up_body(const FfnParams& p, int e, int it, 
     __syncthreads();
     const int t = kTok * c + r;
     if (w < 2 && t < nt) {
-      // acc[c][v] is row 8*(v/4) + 4*g + v%4 of the wave's 32 rows, token t
+      // acc[c][v] is row 8*(v/4) + 4*g + v%4 of the wave's 32 rows, token t.
+      // A token converted scaled by 2^-sc (bf16 beyond the fp16 range) gets
+      // gate and up scaled back, and h carried as h 2^(-2 sc).
+      const int sc = p.xsc ? ld_co<CO>(p.xsc + ld_co<CO>(p.ptok + base + t)) : 0;
       const size_t o = (size_t)(base + t) * I + c0 + 4 * g;
 #pragma unroll
       for (int v4 = 0; v4 < 4; ++v4) {
@@ -370,9 +373,10 @@ __device__ __forceinline__ void gate_up_body(const FfnParams& p, int e, int it, 
 #pragma unroll
         for (int k = 0; k < 4; ++k) {
           const int v = 4 * v4 + k;
-          const float gate = acc[c][v] + xb[((w + 4) * 16 + v) * 64 + lane];
-          const float up = xb[((w + 2) * 16 + v) * 64 + lane] + xb[((w + 6) * 16 + v) * 64 + lane];
-          const split16 sp2 = split_hi_lo(silu(gate) * up);
+          const float gate = __builtin_amdgcn_ldexpf(acc[c][v] + xb[((w + 4) * 16 + v) * 64 + lane], sc);
+          const float up =
+              __builtin_amdgcn_ldexpf(xb[((w + 2) * 16 + v) * 64 + lane] + xb[((w + 6) * 16 + v) * 64 + lane], sc);
+          const split16 sp2 = split_hi_lo(__builtin_amdgcn_ldexpf(silu(gate) * up, -2 * sc));
           hv[k] = __builtin_bit_cast(uint16_t, sp2.hi);
           lv[k] = __builtin_bit_cast(uint16_t, sp2.lo);
         }
@@ -525,12 +529,15 @@ __device__ __forceinline__ void down_body(const FfnParams& p, int e, int it, int
     __syncthreads();
     const int t = kTok * c + r;
     if (kh == 0 && active && t < nt) {
+      // h of a scaled token was carried as h 2^(-2 sc)
+      const int sc = p.xsc ? ld_co<CO>(p.xsc + ld_co<CO>(p.ptok + base + t)) : 0;
       float* yrow = p.y + (size_t)ksi * p.T * (p.K + p.S) * H + (size_t)(base + t) * H + n0 + 4 * g;
 #pragma unroll
       for (int v4 = 0; v4 < 4; ++v4) {
         f32x4 o;
 #pragma unroll
-        for (int k = 0; k < 4; ++k) o[k] = acc[c][4 * v4 + k] + xb[(rg * 16 + 4 * v4 + k) * 64 + lane];
+        for (int k = 0; k < 4; ++k)
+          o[k] = __builtin_amdgcn_ldexpf(acc[c][4 * v4 + k] + xb[(rg * 16 + 4 * v4 + k) * 64 + lane], 2 * sc);
         st_co16<CO>(yrow + 8 * v4, __builtin_bit_cast(uint4, o));
       }
     }

@@ -90,16 +90,27 @@ __global__ __launch_bounds__(256) void k_combine(FfnParams p) {
   combine4(p, t, (int)(gid - (size_t)t * H4) * 4);
 }
 
-// bf16 activations -> fp16 once per call (exact in the fp16 normal range).
+// bf16 activations -> fp16 once per call, one workgroup per token: the
+// token's scale shift from its largest finite exponent, then the scaled
+// conversion (a plain conversion for tokens within the fp16 range).
 __global__ __launch_bounds__(256) void k_x_to_f16(const uint16_t* __restrict__ x, uint16_t* __restrict__ y,
-                                                  size_t n8) {
-  const size_t i = (size_t)blockIdx.x * 256 + threadIdx.x;
-  if (i < n8) *(f16x8*)(y + 8 * i) = load_x8_bf16(x + 8 * i);
+                                                  int32_t* __restrict__ sc, int H) {
+  __shared__ int red[4];
+  const int t = blockIdx.x, tid = threadIdx.x, n8 = H / 8;
+  const uint16_t* xr = x + (size_t)t * H;
+  int m = 0;
+  for (int i = tid; i < n8; i += 256) m = max(m, max_exp8_bf16(xr + 8 * i));
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) m = max(m, __shfl_xor(m, o));
+  if ((tid & 63) == 0) red[tid >> 6] = m;
+  __syncthreads();
+  const int shift = x_scale_shift(max(max(red[0], red[1]), max(red[2], red[3])));
+  if (tid == 0) sc[t] = shift;
+  for (int i = tid; i < n8; i += 256) *(f16x8*)(y + (size_t)t * H + 8 * i) = load_x8_bf16(xr + 8 * i, shift);
 }
 
-hipError_t launch_x_to_f16(const uint16_t* x, uint16_t* y, size_t n, hipStream_t s) {
-  const size_t n8 = n / 8;
-  hipLaunchKernelGGL(k_x_to_f16, dim3((unsigned)((n8 + 255) / 256)), dim3(256), 0, s, x, y, n8);
+hipError_t launch_x_to_f16(const uint16_t* x, uint16_t* y, int32_t* sc, int T, int H, hipStream_t s) {
+  hipLaunchKernelGGL(k_x_to_f16, dim3((unsigned)T), dim3(256), 0, s, x, y, sc, H);
   return hipGetLastError();
 }
 

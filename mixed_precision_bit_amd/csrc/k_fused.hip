@@ -2,7 +2,7 @@
 // expert activation, down projection and output accumulation in one fused
 // kernel that reads the weight pages at each block's committed bitwidth).
 //
-// The work is a sequence of units, in this order: [bf16 -> fp16 conversion]
+// The work is a sequence of units, in this order: [bf16 -> fp16 conversion, one per token]
 // [router logits] [top-K] [grouping, one per group] [gate_up, one per (item,
 // 128-column tile)] [down, one per (item, 128-row tile)] [combine]. Each
 // workgroup repeatedly takes the next unit from a global counter and runs it;
@@ -321,10 +321,27 @@ __device__ __forceinline__ void down_unit(const FusedParams& P, int u, uint16_t*
   mark_done(ctr(P, C_DOWN));
 }
 
-__device__ __forceinline__ void conv_unit(const FusedParams& P, int u, int tid) {
+// bf16 -> fp16 conversion of token t: its scale shift (largest finite
+// exponent, reduced through LDS bytes 64..95, clear of the unit slot), then
+// the scaled conversion, as k_x_to_f16 does.
+__device__ __forceinline__ void conv_unit(const FusedParams& P, int t, uint16_t* lds, int tid) {
   const FfnParams& p = P.f;
-  const size_t i = (size_t)u * 512 + tid, n8 = (size_t)p.T * p.H / 8;
-  if (i < n8) st_co16<true>((uint16_t*)p.xh + 8 * i, __builtin_bit_cast(uint4, load_x8_bf16(P.x + 8 * i)));
+  int* red = (int*)((char*)lds + 64);
+  const int n8 = p.H / 8;
+  const uint16_t* xr = P.x + (size_t)t * p.H;
+  int m = 0;
+  for (int i = tid; i < n8; i += kThreads) m = max(m, max_exp8_bf16(xr + 8 * i));
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) m = max(m, __shfl_xor(m, o));
+  if ((tid & 63) == 0) red[tid >> 6] = m;
+  __syncthreads();
+  int mx = red[0];
+#pragma unroll
+  for (int w = 1; w < kWaves; ++w) mx = max(mx, red[w]);
+  const int shift = x_scale_shift(mx);
+  if (tid == 0) st_co<true>(const_cast<int32_t*>(p.xsc) + t, shift);
+  for (int i = tid; i < n8; i += kThreads)
+    st_co16<true>((uint16_t*)p.xh + (size_t)t * p.H + 8 * i, __builtin_bit_cast(uint4, load_x8_bf16(xr + 8 * i, shift)));
   mark_done(ctr(P, C_CONV));
 }
 
@@ -417,7 +434,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4, 4))
   const uint32_t b_logit = P.n_conv, b_topk = b_logit + P.n_logit, b_group = b_topk + P.n_topk,
                  b_gu = b_group + P.n_group, b_dn = b_gu + P.n_gu, b_comb = b_dn + P.n_dn, b_end = b_comb + P.n_comb;
   uint32_t u = next_unit(P, slot);
-  for (; u < b_logit; u = next_unit(P, slot)) conv_unit(unit_params(), (int)u, opaque_tid());
+  for (; u < b_logit; u = next_unit(P, slot)) conv_unit(unit_params(), (int)u, lds, opaque_tid());
   for (; u < b_topk; u = next_unit(P, slot)) logit_unit<XDT>(unit_params(), (int)(u - b_logit), lds, opaque_tid());
   for (; u < b_group; u = next_unit(P, slot)) topk_unit(unit_params(), (int)(u - b_topk), lds, flag, opaque_tid());
   for (; u < b_gu; u = next_unit(P, slot)) {
@@ -472,7 +489,7 @@ hipError_t launch_fused(const FusedLaunch& L, hipStream_t s) {
   P.qmax = L.qmax;
   const FfnParams& f = L.f;
   const long long ntt = (f.T + kTT - 1) / kTT;
-  P.n_conv = L.xdt == 1 ? (int)(((long long)f.T * f.H / 8 + 511) / 512) : 0;
+  P.n_conv = L.xdt == 1 ? f.T : 0;  // one unit per token
   P.logit_mfma = logits_use_mfma(f.T, f.E) ? 1 : 0;
   P.ks = route_ksplit(f.T, f.H, f.E);
   P.n_logit = P.logit_mfma ? (int)(((long long)((f.T + 15) / 16) * ((f.E + 15) / 16) + 7) / 8)

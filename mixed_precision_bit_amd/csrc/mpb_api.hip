@@ -176,6 +176,7 @@ WsLayout ws_layout(int T, int H, int I, int E, int S, int K, bool bf16) {
   L.hlo = off;     off += align256(P * (size_t)I * 2);
   L.y = off;       off += align256(P * (size_t)H * 4 * dn_splits(T, H, I, E, S, K));
   L.xh = off;      off += bf16 ? align256((size_t)T * H * 2) : 0;
+  L.xsc = off;     off += bf16 ? align256((size_t)T * 4) : 0;
   L.total = off;
   return L;
 }
@@ -191,6 +192,7 @@ mpb::FfnParams ffn_params(const mpb::WsLayout& L, char* ws, const void* X_dev, i
                           const uint16_t* const* luts_dev, const int32_t* q_dev, float* out_dev, int tc) {
   mpb::FfnParams p{};
   p.xh = x_dtype == MPB_BF16 ? (const uint16_t*)(ws + L.xh) : (const uint16_t*)X_dev;
+  p.xsc = x_dtype == MPB_BF16 ? (const int32_t*)(ws + L.xsc) : nullptr;
   p.T = T; p.H = g.H; p.I = g.I; p.E = g.E; p.S = g.S; p.K = g.K; p.NB = g.E + g.S;
   p.topk_idx = topk_idx_dev; p.topk_w = topk_w_dev;
   p.planes = planes_dev; p.luts = luts_dev; p.q = q_dev;
@@ -411,7 +413,7 @@ int ffn_impl(const char* name, const void* X_dev, int x_dtype, int T, const int3
   mark(0, s);
   hipError_t e = hipSuccess;
   if (x_dtype == MPB_BF16) {
-    e = mpb::launch_x_to_f16((const uint16_t*)X_dev, (uint16_t*)(ws + L.xh), (size_t)T * g.H, s);
+    e = mpb::launch_x_to_f16((const uint16_t*)X_dev, (uint16_t*)(ws + L.xh), (int32_t*)(ws + L.xsc), T, g.H, s);
     if (e != hipSuccess) return hip_fail(e, (n + ": activation conversion").c_str());
   }
   e = mpb::launch_permute(p, (int32_t*)(ws + L.ccnt), s);

@@ -187,14 +187,38 @@ __device__ __forceinline__ f16x8 lookup8(uint32_t O0, uint32_t O1, uint32_t slot
 }
 
 // ----------------------------------------------------------------------------
-// Activations: bf16 -> fp16 conversion of 8 consecutive elements (16-byte aligned).
+// Activations: bf16 -> fp16 conversion of 8 consecutive elements (16-byte
+// aligned), scaled by 2^-sc. The fp16 range ends at 65504, the bf16 one near
+// 3.4e38: a token holding larger values is converted scaled down by a power
+// of two (exact) and the FFN kernels undo the scale in fp32, so it stays on
+// the fp16 matrix cores without overflowing.
 // ----------------------------------------------------------------------------
-// bf16 -> fp16 (exact for |x| in the fp16 normal range; rounded below it).
-__device__ __forceinline__ f16x8 load_x8_bf16(const uint16_t* p) {
+// Largest biased exponent among the finite bf16 values of 8 elements (0 for zeros).
+__device__ __forceinline__ int max_exp8_bf16(const uint16_t* p) {
+  const u16x8 v = *(const u16x8*)p;
+  int m = 0;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const int e = (v[j] >> 7) & 0xff;
+    m = e == 0xff ? m : max(m, e);
+  }
+  return m;
+}
+// Scale shift of a token whose largest finite |x| has biased bf16 exponent
+// emax, i.e. |x| < 2^(emax - 126): 0 when every |x| < 2^15 (the conversion is
+// exact in the fp16 normal range), else the shift that brings |x| below 2^8,
+// which also leaves room for h = SiLU(gate) * up, quadratic in x, carried at
+// 2^(-2 sc) through fp16.
+__device__ __forceinline__ int x_scale_shift(int emax) { return emax > 141 ? emax - 134 : 0; }
+
+// bf16 -> fp16 of x * 2^-sc (exact for results in the fp16 normal range;
+// rounded below it).
+__device__ __forceinline__ f16x8 load_x8_bf16(const uint16_t* p, int sc = 0) {
   const u16x8 v = *(const u16x8*)p;
   f16x8 r;
 #pragma unroll
-  for (int j = 0; j < 8; ++j) r[j] = (_Float16)__builtin_bit_cast(float, (uint32_t)v[j] << 16);
+  for (int j = 0; j < 8; ++j)
+    r[j] = (_Float16)__builtin_amdgcn_ldexpf(__builtin_bit_cast(float, (uint32_t)v[j] << 16), -sc);
   return r;
 }
 

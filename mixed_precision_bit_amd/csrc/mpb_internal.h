@@ -27,6 +27,7 @@ inline int ffn_token_chunks(int T, int E, int K) {
 
 struct FfnParams {
   const uint16_t* xh;         // [T][H] fp16 activations (converted copy for bf16 input)
+  const int32_t* xsc;         // [T] per-token scale exponent of the converted copy, or null (fp16 input)
   int T, H, I, E, S, K, NB;   // NB = E + S
   const int32_t* topk_idx;    // [T][K]
   const float* topk_w;        // [T][K]
@@ -76,7 +77,7 @@ inline int dn_range_hcs(int I, int n) {
 }
 
 struct WsLayout {
-  size_t counts, offsets, ptok, pw, inv, items, items_dn, n_items, ccnt, hhi, hlo, y, xh, total;
+  size_t counts, offsets, ptok, pw, inv, items, items_dn, n_items, ccnt, hhi, hlo, y, xh, xsc, total;
   int max_items;
 };
 // Upper bound on work items (one per tpi-token split of a group with tokens):
@@ -118,7 +119,10 @@ constexpr int kGroupChunk = 2048;
 constexpr long long kChunkedFrom = 8192;
 int group_chunks(int T, int K);
 hipError_t launch_permute(const FfnParams& p, int32_t* ccnt, hipStream_t s);
-hipError_t launch_x_to_f16(const uint16_t* x, uint16_t* y, size_t n, hipStream_t s);
+// bf16 activations [T][H] -> fp16 y = x * 2^-sc[t] per token: sc[t] = 0 (a
+// plain conversion) when every finite |x| of the token is below 2^15, else the
+// shift that brings them below 2^8
+hipError_t launch_x_to_f16(const uint16_t* x, uint16_t* y, int32_t* sc, int T, int H, hipStream_t s);
 // qmax: highest committed bitwidth among the launch's blocks (sizes the LDS
 // table region; a block above it yields NaN)
 // ev0/ev1: optional events the launch records at the kernel's start and end

@@ -212,30 +212,24 @@ def moe_ffn(X: np.ndarray, z: np.ndarray, r: np.ndarray, layer, q=None, wcache=N
 def moe_ffn_sampled(X, z, r, layer, tokens, cols, q=None) -> np.ndarray:
     """out[t][c] for t in tokens, c in cols (same definition as moe_ffn), for
     layers too large to dequantise whole: only the touched experts' gate_up
-    blocks and the sampled rows of their down blocks are expanded."""
+    blocks and the sampled rows of their down blocks are expanded, and each
+    expert runs on the sampled tokens routed to it at once."""
     X = np.asarray(X, np.float64)
     q = layer.q if q is None else q
     tokens = np.asarray(tokens)
     cols = np.asarray(cols)
     out = np.zeros((len(tokens), len(cols)))
-    I = layer.I
     for e in range(layer.E + layer.S):
-        sel = []
-        for j, t in enumerate(tokens):
-            if e >= layer.E:
-                sel.append((j, t, 1.0))
-            else:
-                hit = np.nonzero(z[t] == e)[0]
-                if len(hit):
-                    sel.append((j, t, r[t, hit[0]]))
-        if not sel:
+        if e >= layer.E:
+            js, ws = np.arange(len(tokens)), np.ones(len(tokens))
+        else:
+            js, ks = np.nonzero(z[tokens] == e)
+            ws = r[tokens[js], ks]
+        if len(js) == 0:
             continue
         Wg = dequant_block(layer, 2 * e, int(q[2 * e]))
         Wd = dequant_block(layer, 2 * e + 1, int(q[2 * e + 1]), rows=cols)
-        for j, t, w in sel:
-            a = Wg @ X[t]
-            h = silu(a[:I]) * a[I:]
-            out[j] += w * (Wd @ h)
+        out[js] += ws[:, None] * expert_ffn(X[tokens[js]], Wg, Wd)
         del Wg
     return out
 

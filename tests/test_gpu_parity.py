@@ -357,29 +357,52 @@ def test_page_movement_offload_then_reload(layer_cache):
 
 
 # ---------------------------------------------------------------- full-size layers, sampled
-def test_ffn_mixtral_decode_sampled(layer_cache):
+def _coverage(L, z, T, tpi_gu, tpi_dn):
+    """(token, expert) pairs of a batch and the FFN work items they form."""
+    cnt = np.bincount(z.ravel(), minlength=L.E)
+    cnt = np.concatenate([cnt, np.full(L.S, T)])
+    pairs = int(cnt.sum())
+    gu = int(sum((c + tpi_gu - 1) // tpi_gu for c in cnt))
+    dn = int(sum((c + tpi_dn - 1) // tpi_dn for c in cnt))
+    return pairs, gu, dn
+
+
+def test_ffn_mixtral_decode_every_element(layer_cache):
+    """The Mixtral-shaped decode layer (H 4096, I 14336, 8 experts, top-2, 128
+    tokens, gate_up 4-bit / down 3-bit) at every output element: every token's
+    two experts, every 32-token item (including the short second items of
+    experts with more than 32 tokens) and every K range of the split down
+    projection."""
     L, D = dev_layer(layer_cache, 2)
     Xb = S.make_tokens(2)
-    say(f"ffn cfg2 full: T={Xb.shape[0]} (sampled check)")
+    T = Xb.shape[0]
     gi, gw, gout = run_layer(D, Xb, "f16")
     X, z, r = oracle_route(L, Xb)
     assert np.array_equal(gi, z)
-    toks = [0, 77, 127]
-    cols = np.arange(0, L.H, 7)
-    ref = O.moe_ffn_sampled(X, z, r, L, toks, cols)
-    assert_close(gout[np.ix_(toks, cols)], ref, "cfg2 sampled out")
+    pairs, n_gu, n_dn = _coverage(L, z, T, 32, 32)
+    say(f"ffn cfg2 full: T={T}, {pairs} (token, expert) pairs, {n_gu} gate_up / {n_dn} down items, "
+        f"{T * L.H} outputs")
+    ref = O.moe_ffn(X, z, r, L)
+    assert_close(gout, ref, "cfg2 out")
 
 
-def test_ffn_prefill_sampled(layer_cache):
+def test_ffn_prefill_every_element(layer_cache):
+    """The prefill-shaped layer (H 2816, I 704, 128 + 1 experts, top-8, 4096
+    bf16 tokens, Zipf-skewed router bias) at every output element: every
+    128-token gate_up item, including each expert's last, ragged one and all
+    items of the largest group, and every 32-token down item."""
     L, D = dev_layer(layer_cache, 3)
     Xb = S.make_tokens(3)
-    say(f"ffn cfg3 full: T={Xb.shape[0]} (sampled check)")
+    T = Xb.shape[0]
     gi, gw, gout = run_layer(D, Xb, "bf16")
     X, z, r = oracle_route(L, Xb)
     assert np.array_equal(gi, z)
-    toks = np.arange(0, Xb.shape[0], 171)
-    ref = O.moe_ffn(X[toks], z[toks], r[toks], L)
-    assert_close(gout[toks], ref, "cfg3 sampled out")
+    pairs, n_gu, n_dn = _coverage(L, z, T, 128, 32)
+    cnt = np.bincount(z.ravel(), minlength=L.E)
+    say(f"ffn cfg3 full: T={T}, {pairs} (token, expert) pairs, {n_gu} gate_up / {n_dn} down items, "
+        f"largest group {cnt.max()} tokens, {int((cnt % 128 != 0).sum())} ragged last items, {T * L.H} outputs")
+    ref = O.moe_ffn(X, z, r, L)
+    assert_close(gout, ref, "cfg3 out")
 
 
 # ---------------------------------------------------------------- bitwidth sweep
@@ -518,21 +541,27 @@ def test_largest_batch_sampled(layer_cache):
     assert np.array_equal(o1.view(np.uint32), o2.view(np.uint32))
 
 
-def test_activation_beyond_fp16_range_is_not_silently_wrong(layer_cache):
-    """bf16 activations are converted to fp16 for the matrix cores, whose
-    range ends at 65504: a token with entries beyond it comes out non-finite
-    (never a finite wrong value), and every other token is unaffected and
-    held to the oracle."""
+def test_bf16_beyond_fp16_range_every_element(layer_cache):
+    """bf16 activations reach the fp16 matrix cores through a per-token
+    power-of-two scale: tokens holding values far beyond the fp16 range
+    (|x| up to ~4e6 and ~1e5) or far below its normal range (~1e-30) are held
+    to the oracle at every element, like the ordinary tokens beside them, on
+    both paths; the one-launch path agrees bit for bit."""
     L, D = dev_layer(layer_cache, 11)
     Xb = S.make_tokens(11).copy()
-    bad = 4
-    Xb[bad] = S.f32_to_bf16_bits((S.bf16_bits_to_f64(Xb[bad]) * 1e6).astype(np.float32))
-    gi, _, gout = run_layer(D, Xb, "bf16")
+    for t, f in ((4, 1e6), (6, 3e4), (7, 1e-30)):
+        Xb[t] = S.f32_to_bf16_bits((S.bf16_bits_to_f64(Xb[t]) * f).astype(np.float32))
     X, z, r = oracle_route(L, Xb)
-    assert np.array_equal(gi, z)
-    assert not np.isfinite(gout[bad]).all()
-    ok = np.arange(Xb.shape[0]) != bad
-    assert_close(gout[ok], O.moe_ffn(X[ok], z[ok], r[ok], L), "other tokens")
+    assert np.abs(X[4]).max() > 65504 and np.abs(X[6]).max() > 65504
+    i1, w1, o1, i2, w2, o2, _ = _separate_and_fused(D, Xb, "bf16")
+    assert np.array_equal(i1, z)
+    ref = O.moe_ffn(X, z, r, L)
+    say(f"  max |ref| of the large tokens: {np.abs(ref[4]).max():.3e}, {np.abs(ref[6]).max():.3e}")
+    assert_close(o1, ref, "every token")
+    for t in (4, 6, 7):
+        assert_close(o1[t], ref[t], f"token {t}", guard=None)
+    assert np.array_equal(i1, i2)
+    assert np.array_equal(o1.view(np.uint32), o2.view(np.uint32))
 
 
 @pytest.mark.parametrize("cfg", [12, 13, 14, 15, 16])

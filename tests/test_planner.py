@@ -241,3 +241,22 @@ def test_native_planner_validation():
     with pytest.raises(M.MpbError) as ei:
         M.mpb_plan_step(L.H, L.I, L.E, L.S, L.K, q, None, s, mass, phi, P)
     assert ei.value.code == -3
+
+
+def test_bench_sweep_states_follow_the_greedy_ranking(layer_cache):
+    """The bitwidth states bench.py times for the sweep on the config-1 layer
+    are the oracle's greedy reductions (PagedWeight §3.2 'Planning
+    objective') at 25/50/75 % of the routed blocks, then all 8-bit."""
+    import bench
+    L = layer_cache(1)
+    s = S.make_sensitivity(4, L.n_blocks)
+    states = bench.sweep_states(L, s)
+    assert [n for n, _ in states] == ["initial", "lowered 25%", "lowered 50%", "lowered 75%", "all 8-bit"]
+    assert np.array_equal(states[0][1], L.q)
+    for (name, q), f in zip(states[1:4], (0.25, 0.5, 0.75)):
+        red, _ = O.greedy_reductions(L, s, f)
+        ref = L.q.astype(np.int64).copy()
+        for i, b2 in red:
+            ref[i] = b2
+        assert np.array_equal(q, ref), name
+    assert (states[4][1] == 8).all()
