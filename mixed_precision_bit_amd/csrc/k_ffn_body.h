@@ -83,12 +83,13 @@ __device__ __forceinline__ rsrc_t tile_rsrc(const void* page, size_t tile_off, u
 typedef __attribute__((address_space(3))) void lds_void;
 
 template <int Q>
-__device__ __forceinline__ void load_table_image(const uint16_t* img, int w, int lane) {
+__device__ __forceinline__ void load_table_image(const uint16_t* img, int w, int lane, uint32_t dst = 0) {
   const char* src = (const char*)img + 16 * lane;
 #pragma unroll
   for (int c = 0; c < (1 << Q) / 4; c += kWaves)
     if (c + w < (1 << Q) / 4)
-      __builtin_amdgcn_global_load_lds(src + 1024 * (c + w), (lds_void*)(uintptr_t)(1024u * (c + w)), 16, 0, 0);
+      __builtin_amdgcn_global_load_lds(src + 1024 * (c + w), (lds_void*)(uintptr_t)(dst + 1024u * (c + w)), 16, 0,
+                                       0);
 }
 
 __device__ __forceinline__ void wait_vmem_all() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
@@ -172,6 +173,42 @@ __device__ __forceinline__ void store_window(char* stage, const uint4 (&v)[2][TC
       if (sp.live[c]) *(uint4*)(stage + sp.dst[i][c]) = k[i] < len ? v[i][c] : make_uint4(0u, 0u, 0u, 0u);
 }
 
+// Pair-order staging (3-bit pair tables): a piece holds elements e..e+3 and
+// e+32..e+35 of a half-chunk interleaved (one from each word per fp16 pair),
+// matching the order of lookup_pairs4. k[i] is the first element (e) of the
+// piece for K half i.
+template <int TC>
+__device__ __forceinline__ void load_window_pairs(uint4 (&v)[2][TC], const StagePlan<TC>& sp, const int (&k)[2],
+                                                  int len) {
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int c = 0; c < TC; ++c)
+      if (sp.live[c] && k[i] < len) {
+        const uint2 a = *(const uint2*)(sp.row[c] + k[i]);
+        const uint2 b = *(const uint2*)(sp.row[c] + k[i] + 32);
+        v[i][c] = make_uint4(a.x, a.y, b.x, b.y);
+      }
+}
+
+template <int TC>
+__device__ __forceinline__ void store_window_pairs(char* stage, const uint4 (&v)[2][TC], const StagePlan<TC>& sp,
+                                                  const int (&k)[2], int len) {
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int c = 0; c < TC; ++c)
+      if (sp.live[c]) {
+        uint4 o = make_uint4(0u, 0u, 0u, 0u);
+        if (k[i] < len) {  // (a0 a1 | a2 a3) and (b0 b1 | b2 b3) -> a0 b0, a1 b1, a2 b2, a3 b3
+          const uint4 x = v[i][c];
+          o = make_uint4(__builtin_amdgcn_perm(x.z, x.x, 0x05040100u), __builtin_amdgcn_perm(x.z, x.x, 0x07060302u),
+                         __builtin_amdgcn_perm(x.w, x.y, 0x05040100u), __builtin_amdgcn_perm(x.w, x.y, 0x07060302u));
+        }
+        *(uint4*)(stage + sp.dst[i][c]) = o;
+      }
+}
+
 // Item `item` of the gate_up (gu) or down list: its group e, first token t0
 // and token count nt; false past the end of the list.
 __device__ __forceinline__ bool item_of(const FfnParams& p, bool gu, int item, int& e, int& t0, int& nt) {
@@ -230,9 +267,17 @@ struct KSplit {
 // the stage, load the activations of step s+2, load the planes of step s+3,
 // barrier. DB (items of <= 16 tokens, TC = 1): the stage is double-buffered
 // and the first of the two barriers is dropped.
-template <int Q, int TC, bool CO = false, bool NT = (TC == 1), bool DB = false>
+//
+// PR (3-bit blocks): pair tables. lut_bytes is kPairTableBytes; the
+// tile's 3-bit table image is copied to the stage region, expanded into the
+// pair table before the first activations are staged, and each step runs
+// eight lookup_pairs4 groups over both words of the lane's half-chunk, with
+// the activations staged in pair order (piece 8 g' + m: elements 4m..4m+3 of
+// both words of half-chunk 2s + g').
+template <int Q, int TC, bool CO = false, bool NT = (TC == 1), bool DB = false, bool PR = false>
 __device__ __forceinline__ void gate_up_body(const FfnParams& p, int e, int it, int t0, int nt, uint16_t* lds,
                                              uint32_t lut_bytes, int tid) {
+  static_assert(!PR || Q == 3, "pair tables: 3-bit blocks");
   const int lane = tid & 63, r = lane & 31, g = lane >> 5;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: plane descriptors stay scalar
   const int rg = w & 3, kh = w >> 2;
@@ -241,12 +286,13 @@ __device__ __forceinline__ void gate_up_body(const FfnParams& p, int e, int it, 
   const int c0 = it * 64 + (rg & 1) * 32;
   const int row0 = (rg >> 1) * I + c0;
   const int base = ld_co<CO>(p.offsets + e) + t0;
-  const uint32_t slot = lut_slot(r, rg);
+  const uint32_t slot = PR ? pair_slot(r, rg) : lut_slot(r, rg);
   const int blk = 2 * e;
   char* stage = (char*)lds + lut_bytes;
 
   // staging: piece p = 8 g' + 4 j + m of a token holds elements 32 j + 8 m .. + 7
-  // of half-chunk 2 s + g' of the K half
+  // of half-chunk 2 s + g' of the K half (PR: piece 8 g' + m, elements 4 m ..
+  // 4 m + 3 of both words)
   StagePlan<TC> sp;
   const int st = tid >> 4, spc = tid & 15;
 #pragma unroll
@@ -260,7 +306,15 @@ __device__ __forceinline__ void gate_up_body(const FfnParams& p, int e, int it, 
   static_assert(!DB || TC == 1, "double-buffered stage: one token chunk");
   auto kwin = [&](int s, int (&k)[2]) {
 #pragma unroll
-    for (int i = 0; i < 2; ++i) k[i] = (i * ks.HH + 2 * s + (spc >> 3)) * 64 + 8 * (spc & 7);
+    for (int i = 0; i < 2; ++i) k[i] = (i * ks.HH + 2 * s + (spc >> 3)) * 64 + (PR ? 4 : 8) * (spc & 7);
+  };
+  auto ld_win = [&](uint4 (&v)[2][TC], const int (&k)[2]) {
+    if constexpr (PR) load_window_pairs<TC>(v, sp, k, H);
+    else load_window<TC>(v, sp, k, H);
+  };
+  auto st_win = [&](char* dst, const uint4 (&v)[2][TC], const int (&k)[2]) {
+    if constexpr (PR) store_window_pairs<TC>(dst, v, sp, k, H);
+    else store_window<TC>(dst, v, sp, k, H);
   };
 
   // the descriptor of K half 0 ends where half 1 begins, so the prefetches
@@ -275,15 +329,22 @@ __device__ __forceinline__ void gate_up_body(const FfnParams& p, int e, int it, 
   uint2 PA[Q], PB[Q], PC[Q];
   uint4 xr[2][TC];
   int kk[2];
-  load_table_image<Q>(p.luts[blk * 6 + (Q - 3)] + (size_t)it * (128u << Q), w, lane);
+  // PR: the 3-bit image goes to the stage region, which is staged only after
+  // the pair table has been built from it
+  load_table_image<Q>(p.luts[blk * 6 + (Q - 3)] + (size_t)it * (128u << Q), w, lane, PR ? lut_bytes : 0u);
   kwin(0, kk);
-  load_window<TC>(xr, sp, kk, H);
+  ld_win(xr, kk);
   load_planes<Q, NT>(PA, rs, cb, 0, voff);
   wait_vmem_all();
-  store_window<TC>(stage, xr, sp, kk, H);
+  if constexpr (PR) {
+    __syncthreads();
+    build_pair_table3(lut_bytes, tid);
+    __syncthreads();
+  }
+  st_win(stage, xr, kk);
   load_planes<Q, NT>(PB, rs, cb, 1, voff);
   kwin(1, kk);
-  load_window<TC>(xr, sp, kk, H);
+  ld_win(xr, kk);
   load_planes<Q, NT>(PC, rs, cb, 2, voff);
   __syncthreads();
 
@@ -293,30 +354,47 @@ __device__ __forceinline__ void gate_up_body(const FfnParams& p, int e, int it, 
   // par = s % 2 (the stage buffer of step s when DB), passed as a constant so
   // that the buffer offset folds into the LDS instructions' offset field
   auto step = [&](int s, uint2 (&P)[Q], int par) {
+    if constexpr (PR) {
+      uint32_t Pa[3], Pb[3], O[8];
+      word_of<3>(P, 0, Pa);
+      word_of<3>(P, 1, Pb);
+      assemble_pairs3(Pa, Pb, rg >> 1, O);
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      uint32_t Pw[Q], O[8];
-      word_of<Q>(P, j, Pw);
-      assemble<Q>(Pw, O);
-#pragma unroll
-      for (int m = 0; m < 4; ++m) {
-        const f16x8 a = lookup8(O[2 * m], O[2 * m + 1], slot);
+      for (int m = 0; m < 8; ++m) {
+        const f16x8 a = lookup_pairs4(O[m], slot);
 #pragma unroll
         for (int c = 0; c < TC; ++c) {
-          const uint32_t bo = DB ? stage_off_db(par, kh, r & 15, 8 * g + 4 * j + m)
-                                 : stage_off<TC>(kh, kTok * c + r, 8 * g + 4 * j + m);
-          const f16x8 b = *(const f16x8*)(stage + bo);
-          acc[c] = mfma32(a, b, acc[c]);
+          const uint32_t bo =
+              DB ? stage_off_db(par, kh, r & 15, 8 * g + m) : stage_off<TC>(kh, kTok * c + r, 8 * g + m);
+          acc[c] = mfma32(a, *(const f16x8*)(stage + bo), acc[c]);
+        }
+      }
+    } else {
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        uint32_t Pw[Q], O[8];
+        word_of<Q>(P, j, Pw);
+        assemble<Q>(Pw, O);
+#pragma unroll
+        for (int m = 0; m < 4; ++m) {
+          const f16x8 a = lookup8(O[2 * m], O[2 * m + 1], slot);
+#pragma unroll
+          for (int c = 0; c < TC; ++c) {
+            const uint32_t bo = DB ? stage_off_db(par, kh, r & 15, 8 * g + 4 * j + m)
+                                   : stage_off<TC>(kh, kTok * c + r, 8 * g + 4 * j + m);
+            const f16x8 b = *(const f16x8*)(stage + bo);
+            acc[c] = mfma32(a, b, acc[c]);
+          }
         }
       }
     }
     if (!DB) __syncthreads();
     if (s + 1 < ks.NSW) {
       kwin(s + 1, kk);
-      store_window<TC>(stage + (DB ? stage_off_db(par ^ 1, 0, 0, 0) : 0u), xr, sp, kk, H);
+      st_win(stage + (DB ? stage_off_db(par ^ 1, 0, 0, 0) : 0u), xr, kk);
     }
     kwin(s + 2, kk);
-    load_window<TC>(xr, sp, kk, H);
+    ld_win(xr, kk);
     load_planes<Q, NT>(P, rs, cb, s + 3, voff);
     __syncthreads();
   };
@@ -404,7 +482,7 @@ __device__ __forceinline__ void poison(float* dst, size_t ld, int rows, int cols
 // ahead of the plane load that follows it. DB (items of <= 16 tokens, TC = 1):
 // round j reads stage buffer j while the next round's window is written to
 // the other one, two barriers per step instead of four.
-template <int Q, int TC, bool CO = false, bool NT = true, bool DB = false>
+template <int Q, int TC, bool CO = false, bool NT = true, bool DB = false, bool PR = false>
 __device__ __forceinline__ void down_body(const FfnParams& p, int e, int it, int t0, int nt, uint16_t* lds,
                                           uint32_t lut_bytes, int tid, int ksi = 0) {
   const int lane = tid & 63, r = lane & 31, g = lane >> 5;
@@ -419,7 +497,8 @@ __device__ __forceinline__ void down_body(const FfnParams& p, int e, int it, int
   const int n0 = it * 128 + rg * 32;
   const bool active = n0 < H;
   const int base = ld_co<CO>(p.offsets + e) + t0;
-  const uint32_t slot = lut_slot(r, rg);
+  static_assert(!PR || Q == 3, "pair tables: 3-bit blocks");
+  const uint32_t slot = PR ? pair_slot(r, rg) : lut_slot(r, rg);
   const int blk = 2 * e + 1;
   char* stage = (char*)lds + lut_bytes;
 
@@ -437,9 +516,20 @@ __device__ __forceinline__ void down_body(const FfnParams& p, int e, int it, int
   // stage buffer of round j (DB)
   auto rbuf = [&](int j) -> uint32_t { return DB ? stage_off_db(j, 0, 0, 0) : 0u; };
   // window (s, j): for K half i, element 64 (hc0 + i HH + 2 s + g') + 32 j + 8 m
+  // (PR: round j takes pair groups 4 j .. 4 j + 3, elements 4 m .. 4 m + 3 of
+  // both words, m = 4 j + (piece & 3), staged in pair order)
   auto kwin = [&](int s, int j, int (&k)[2]) {
 #pragma unroll
-    for (int i = 0; i < 2; ++i) k[i] = (hc0 + i * ks.HH + 2 * s + ((spc >> 2) & 1)) * 64 + 32 * j + 8 * (spc & 3);
+    for (int i = 0; i < 2; ++i)
+      k[i] = (hc0 + i * ks.HH + 2 * s + ((spc >> 2) & 1)) * 64 + (PR ? 4 * (4 * j + (spc & 3)) : 32 * j + 8 * (spc & 3));
+  };
+  auto ld_win = [&](uint4 (&v)[2][TC], const int (&k)[2]) {
+    if constexpr (PR) load_window_pairs<TC>(v, sp, k, klen);
+    else load_window<TC>(v, sp, k, klen);
+  };
+  auto st_win = [&](char* dst, const uint4 (&v)[2][TC], const int (&k)[2]) {
+    if constexpr (PR) store_window_pairs<TC>(dst, v, sp, k, klen);
+    else store_window<TC>(dst, v, sp, k, klen);
   };
 
   const int cb = (hc0 >> 1) + kh * (ks.HH >> 1);
@@ -453,16 +543,21 @@ __device__ __forceinline__ void down_body(const FfnParams& p, int e, int it, int
   uint2 PA[Q], PB[Q], PC[Q];
   uint4 ha[2][TC], hb[2][TC];
   int ka[2], kb[2];
-  load_table_image<Q>(p.luts[blk * 6 + (Q - 3)] + (size_t)it * (128u << Q), w, lane);
+  load_table_image<Q>(p.luts[blk * 6 + (Q - 3)] + (size_t)it * (128u << Q), w, lane, PR ? lut_bytes : 0u);
   kwin(0, 0, ka);
-  load_window<TC>(ha, sp, ka, klen);
+  ld_win(ha, ka);
   load_planes<Q, NT>(PA, rs, cb, 0, voff);
   wait_vmem_all();
-  store_window<TC>(stage, ha, sp, ka, klen);
+  if constexpr (PR) {
+    __syncthreads();
+    build_pair_table3(lut_bytes, tid);
+    __syncthreads();
+  }
+  st_win(stage, ha, ka);
   kwin(0, 1, kb);
-  load_window<TC>(hb, sp, kb, klen);
+  ld_win(hb, kb);
   kwin(1, 0, ka);
-  load_window<TC>(ha, sp, ka, klen);
+  ld_win(ha, ka);
   load_planes<Q, NT>(PB, rs, cb, 1, voff);
   load_planes<Q, NT>(PC, rs, cb, 2, voff);
   __syncthreads();
@@ -470,13 +565,23 @@ __device__ __forceinline__ void down_body(const FfnParams& p, int e, int it, int
   f32x16 acc[TC];
 #pragma unroll
   for (int c = 0; c < TC; ++c) acc[c] = (f32x16){};
-  auto round = [&](int j, const uint2 (&P)[Q]) {
+  // O: PR, the pair words of both rounds (assembled in round 0)
+  auto round = [&](int j, const uint2 (&P)[Q], uint32_t (&Op)[8]) {
     uint32_t Pw[Q], O[8];
-    word_of<Q>(P, j, Pw);
-    assemble<Q>(Pw, O);
+    if constexpr (PR) {
+      if (j == 0) {
+        uint32_t Pa[3], Pb[3];
+        word_of<3>(P, 0, Pa);
+        word_of<3>(P, 1, Pb);
+        assemble_pairs3(Pa, Pb, rg >> 1, Op);
+      }
+    } else {
+      word_of<Q>(P, j, Pw);
+      assemble<Q>(Pw, O);
+    }
 #pragma unroll
     for (int m = 0; m < 4; ++m) {
-      const f16x8 a = lookup8(O[2 * m], O[2 * m + 1], slot);
+      const f16x8 a = PR ? lookup_pairs4(Op[4 * j + m], slot) : lookup8(O[2 * m], O[2 * m + 1], slot);
 #pragma unroll
       for (int c = 0; c < TC; ++c) {
         const uint32_t oh = DB ? stage_off_db(j, kh, r & 15, 4 * g + m) : stage_off<TC>(kh, kTok * c + r, 4 * g + m);
@@ -491,19 +596,20 @@ __device__ __forceinline__ void down_body(const FfnParams& p, int e, int it, int
     if (!DB) __syncthreads();
   };
   auto step = [&](int s, uint2 (&P)[Q]) {
-    round(0, P);
+    uint32_t Op[8];
+    round(0, P, Op);
     kwin(s, 1, kb);
-    store_window<TC>(stage + rbuf(1), hb, sp, kb, klen);
+    st_win(stage + rbuf(1), hb, kb);
     kwin(s + 1, 1, kb);
-    load_window<TC>(hb, sp, kb, klen);
+    ld_win(hb, kb);
     __syncthreads();
-    round(1, P);
+    round(1, P, Op);
     if (s + 1 < ks.NSW) {
       kwin(s + 1, 0, ka);
-      store_window<TC>(stage + rbuf(0), ha, sp, ka, klen);
+      st_win(stage + rbuf(0), ha, ka);
     }
     kwin(s + 2, 0, ka);
-    load_window<TC>(ha, sp, ka, klen);
+    ld_win(ha, ka);
     load_planes<Q, NT>(P, rs, cb, s + 3, voff);
     __syncthreads();
   };

@@ -11,8 +11,10 @@
 
 namespace mpb {
 
+// pr3: the launch holds LDS for a 3-bit pair table and the stage, so 3-bit
+// blocks take the pair-table path
 template <int TC>
-__global__ __launch_bounds__(kThreads) void k_gate_up(FfnParams p, int qmax) {
+__global__ __launch_bounds__(kThreads) void k_gate_up(FfnParams p, int qmax, int pr3) {
   extern __shared__ __attribute__((aligned(256))) uint16_t lds[];
   int e, it, t0, nt;
   if (!(TC == 4 ? decode_item_xcd(p, true, p.I >> 6, e, it, t0, nt) : decode_item(p, true, p.I >> 6, e, it, t0, nt)))
@@ -27,7 +29,15 @@ __global__ __launch_bounds__(kThreads) void k_gate_up(FfnParams p, int qmax) {
     else gate_up_body<Q, TC>(p, e, it, t0, nt, lds, lut_bytes, threadIdx.x);            \
     break;
   switch (q < 3 || q > qmax || !tables_at_zero(lds) ? 0 : q) {
-    MPB_GU(3)
+    case 3:
+      if (pr3) {
+        if (db) gate_up_body<3, TC, false, TC == 1, TC == 1, true>(p, e, it, t0, nt, lds, kPairTableBytes, threadIdx.x);
+        else gate_up_body<3, TC, false, TC == 1, false, true>(p, e, it, t0, nt, lds, kPairTableBytes, threadIdx.x);
+      } else {
+        if (db) gate_up_body<3, TC, false, TC == 1, TC == 1>(p, e, it, t0, nt, lds, lut_bytes, threadIdx.x);
+        else gate_up_body<3, TC>(p, e, it, t0, nt, lds, lut_bytes, threadIdx.x);
+      }
+      break;
     MPB_GU(4)
     MPB_GU(5)
     MPB_GU(6)
@@ -47,7 +57,7 @@ __global__ __launch_bounds__(kThreads) void k_gate_up(FfnParams p, int qmax) {
 
 // NT: non-temporal plane loads (decode-size batches, see load_planes)
 template <int TC, bool NT>
-__global__ __launch_bounds__(kThreads) void k_down(FfnParams p, int qmax) {
+__global__ __launch_bounds__(kThreads) void k_down(FfnParams p, int qmax, int pr3) {
   extern __shared__ __attribute__((aligned(256))) uint16_t lds[];
   // workgroup b: K range b % dn_split of tile (b / dn_split) % ntile of item
   // (b / dn_split) / ntile
@@ -65,7 +75,15 @@ __global__ __launch_bounds__(kThreads) void k_down(FfnParams p, int qmax) {
     else down_body<Q, TC, false, NT>(p, e, it, t0, nt, lds, lut_bytes, threadIdx.x, ksi);              \
     break;
   switch (q < 3 || q > qmax || !tables_at_zero(lds) ? 0 : q) {
-    MPB_DN(3)
+    case 3:
+      if (pr3) {
+        if (db) down_body<3, TC, false, NT, TC == 1, true>(p, e, it, t0, nt, lds, kPairTableBytes, threadIdx.x, ksi);
+        else down_body<3, TC, false, NT, false, true>(p, e, it, t0, nt, lds, kPairTableBytes, threadIdx.x, ksi);
+      } else {
+        if (db) down_body<3, TC, false, NT, TC == 1>(p, e, it, t0, nt, lds, lut_bytes, threadIdx.x, ksi);
+        else down_body<3, TC, false, NT>(p, e, it, t0, nt, lds, lut_bytes, threadIdx.x, ksi);
+      }
+      break;
     MPB_DN(4)
     MPB_DN(5)
     MPB_DN(6)
@@ -130,19 +148,27 @@ static hipError_t launch_tc(const FfnParams& p, int qmax, hipStream_t s, hipEven
   const void* fn;
   if constexpr (GU) fn = (const void*)k_gate_up<TC>;
   else fn = (const void*)k_down<TC, NT>;
-  const hipError_t e = raise_lds_limit(fn, (int)ffn_lds_bytes<TC>(8), lds_raised);
+  const hipError_t e = raise_lds_limit(fn, (int)std::max<size_t>(ffn_lds_bytes<TC>(8), kPairTableBytes + stage_bytes<TC>()),
+                                       lds_raised);
   if (e != hipSuccess) return e;
-  const size_t shmem = ffn_lds_bytes<TC>(qmax);
+  // every launch holds room for a 3-bit pair table and the stage (registers,
+  // not LDS, bound these kernels' occupancy: two workgroups per CU at one
+  // token chunk, one at four), so a block committed at 3 bits later, under a
+  // captured graph, still takes the pair path
+  constexpr size_t kPairLds = kPairTableBytes + stage_bytes<TC>();
+  const size_t shmem = std::max(ffn_lds_bytes<TC>(qmax), kPairLds);
+  const int pr3 = 1;
   // 128-token items take the XCD-interleaved order (decode_item_xcd)
   const int items = TC == 4 ? (p.max_items + 7) / 8 * 8 : p.max_items;
   if constexpr (GU) {
     if (ev0 && ev1)
-      hipExtLaunchKernelGGL(k_gate_up<TC>, dim3(items * (p.I >> 6)), dim3(kThreads), shmem, s, ev0, ev1, 0, p, qmax);
+      hipExtLaunchKernelGGL(k_gate_up<TC>, dim3(items * (p.I >> 6)), dim3(kThreads), shmem, s, ev0, ev1, 0, p, qmax,
+                            pr3);
     else
-      hipLaunchKernelGGL(k_gate_up<TC>, dim3(items * (p.I >> 6)), dim3(kThreads), shmem, s, p, qmax);
+      hipLaunchKernelGGL(k_gate_up<TC>, dim3(items * (p.I >> 6)), dim3(kThreads), shmem, s, p, qmax, pr3);
   } else
     hipLaunchKernelGGL((k_down<TC, NT>), dim3(p.max_items * ((p.H + 127) >> 7) * p.dn_split), dim3(kThreads), shmem,
-                       s, p, qmax);
+                       s, p, qmax, pr3);
   return hipGetLastError();
 }
 

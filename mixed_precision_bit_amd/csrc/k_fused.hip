@@ -239,9 +239,9 @@ __device__ __forceinline__ void gate_up_unit(const FusedParams& P, int u, uint16
   const int q = p.q[2 * e];
   const uint32_t lut_bytes = 256u << P.qmax;
   switch (q < 3 || q > P.qmax || !tables_at_zero(lds) ? 0 : q) {
-    case 3:
-      if (nt <= kDbTok) gate_up_body<3, 1, true, true, true>(p, e, it, t0, nt, lds, lut_bytes, tid);
-      else gate_up_body<3, 1, true>(p, e, it, t0, nt, lds, lut_bytes, tid);
+    case 3:  // pair tables (the launch holds their LDS, fused_lds_bytes)
+      if (nt <= kDbTok) gate_up_body<3, 1, true, true, true, true>(p, e, it, t0, nt, lds, kPairTableBytes, tid);
+      else gate_up_body<3, 1, true, true, false, true>(p, e, it, t0, nt, lds, kPairTableBytes, tid);
       break;
     case 4:
       if (nt <= kDbTok) gate_up_body<4, 1, true, true, true>(p, e, it, t0, nt, lds, lut_bytes, tid);
@@ -288,9 +288,9 @@ __device__ __forceinline__ void down_unit(const FusedParams& P, int u, uint16_t*
   const int q = p.q[2 * e + 1];
   const uint32_t lut_bytes = 256u << P.qmax;
   switch (q < 3 || q > P.qmax || !tables_at_zero(lds) ? 0 : q) {
-    case 3:
-      if (nt <= kDbTok) down_body<3, 1, true, true, true>(p, e, it, t0, nt, lds, lut_bytes, tid, ksi);
-      else down_body<3, 1, true>(p, e, it, t0, nt, lds, lut_bytes, tid, ksi);
+    case 3:  // pair tables (the launch holds their LDS, fused_lds_bytes)
+      if (nt <= kDbTok) down_body<3, 1, true, true, true, true>(p, e, it, t0, nt, lds, kPairTableBytes, tid, ksi);
+      else down_body<3, 1, true, true, false, true>(p, e, it, t0, nt, lds, kPairTableBytes, tid, ksi);
       break;
     case 4:
       if (nt <= kDbTok) down_body<4, 1, true, true, true>(p, e, it, t0, nt, lds, lut_bytes, tid, ksi);
@@ -465,7 +465,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4, 4))
 }
 
 size_t fused_lds_bytes(int qmax) {
-  const size_t ffn = std::max<size_t>((256u << qmax) + stage_bytes<1>(), kWaves * 16 * 64 * 4);
+  const size_t ffn = std::max<size_t>(std::max<size_t>((256u << qmax) + stage_bytes<1>(), kWaves * 16 * 64 * 4),
+                                      kPairTableBytes + stage_bytes<1>());
   const size_t logit = 8 * kTT * 65 * 8;
   const size_t topk = 8 * 512 * 8 + 8 * 16 * 8 + 8 * 16 * 4;
   const size_t grp = (kMaxGroupsF + 48) * 4;

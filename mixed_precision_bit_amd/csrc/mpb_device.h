@@ -91,6 +91,33 @@ __device__ __forceinline__ void assemble(const uint32_t (&P)[Q], uint32_t (&O)[8
   for (int s = 0; s < 8; ++s) O[s] = s ? __builtin_amdgcn_alignbit(X[s], X[s], s) : X[s];
 }
 
+// Pair indices of two words at 3 bits. PA/PB = planes 0..2 of word A and word
+// B of one (row, half-chunk). On return byte b of O[s] is
+//   hb + 2 (uA + 8 uB),
+// uA, uB the reversed 3-bit indices of element 4s+b of word A and word B and
+// hb = 1 when h (wave-uniform) is set: the same transpose with word A's planes
+// in rows 1..3, word B's in rows 4..6 and row 0 all ones or all zeros.
+// Rows 1..3 need their plane rotated left by one more bit than stored, rows
+// 4..6 by four more.
+__device__ __forceinline__ void assemble_pairs3(const uint32_t (&PA)[3], const uint32_t (&PB)[3], bool h,
+                                                uint32_t (&O)[8]) {
+  uint32_t z = 0u;
+  asm("" : "+v"(z));
+  uint32_t X[8];
+  X[0] = h ? ~z : z;
+#pragma unroll
+  for (int q = 0; q < 3; ++q) {
+    X[1 + q] = __builtin_amdgcn_alignbit(PA[q], PA[q], 31);  // rotl 1
+    X[4 + q] = __builtin_amdgcn_alignbit(PB[q], PB[q], 28);  // rotl 4
+  }
+  X[7] = z;
+  bfly_round<4>(X, 0x0F0F0F0Fu);
+  bfly_round<2>(X, 0x33333333u);
+  bfly_round<1>(X, 0x55555555u);
+#pragma unroll
+  for (int s = 0; s < 8; ++s) O[s] = s ? __builtin_amdgcn_alignbit(X[s], X[s], s) : X[s];
+}
+
 template <int Q>
 __device__ __forceinline__ uint32_t bitrev(uint32_t v) {
   return __builtin_bitreverse32(v) >> (32 - Q);
@@ -173,6 +200,49 @@ __device__ __forceinline__ bool tables_at_zero(const void* lds) { return (uint32
 
 __device__ __forceinline__ _Float16 lut_read(uint32_t addr) {
   return __builtin_bit_cast(_Float16, *(lds_u16*)(uintptr_t)addr);
+}
+
+// ----------------------------------------------------------------------------
+// Pair tables (3-bit blocks). A 128-row tile's 3-bit table expands in LDS into
+// a table of 64 pairs per row: entry P = uA + 8 uB of tile row R = 32 g + r
+// (row group g) is the dword at byte P * 512 + 4 R holding (LUT[uA],
+// LUT[uB]), word A's value in the low half. With hb = g >> 1 in bit 0 of the
+// assembled pair byte (assemble_pairs3) and pair_slot below, lut_addr gives
+// the entry's address, and one ds_read_b32 yields two dequantised weights
+// packed as the MFMA operand wants them (half the table reads of lookup8 and
+// no packing). Lanes r = 0..31 hit banks r.
+// ----------------------------------------------------------------------------
+constexpr uint32_t kPairTableBytes = 64u * 512u;
+
+__device__ __forceinline__ uint32_t pair_slot(int r, int g) { return 4u * r + 128u * (g & 1); }
+
+// Builds the pair table at LDS byte 0 from the tile's 3-bit table image,
+// already copied to LDS at byte `src` (image layout of lut_slot). Every
+// thread of a 512-thread workgroup writes 16 entries of one row. The caller
+// synchronises the workgroup before and after.
+__device__ __forceinline__ void build_pair_table3(uint32_t src, int tid) {
+  typedef __attribute__((address_space(3))) uint32_t lds_u32;
+  const int R = tid & 127, p0 = tid >> 7;
+  const uint32_t ss = src + lut_slot(R & 31, R >> 5);
+  uint32_t T[8];
+#pragma unroll
+  for (int u = 0; u < 8; ++u) T[u] = *(lds_u16*)(uintptr_t)(ss + 256u * u);
+  const uint32_t a0 = *(lds_u16*)(uintptr_t)(ss + 256u * p0), a1 = *(lds_u16*)(uintptr_t)(ss + 256u * (p0 + 4));
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    const int P = p0 + 4 * i;  // uA = p0 + 4 (i & 1), uB = i >> 1
+    *(lds_u32*)(uintptr_t)(P * 512u + 4u * R) = ((i & 1) ? a1 : a0) | (T[i >> 1] << 16);
+  }
+}
+
+// Eight dequantised weights from one assembled pair word: the pairs of
+// elements 4s..4s+3 of words A and B, as an MFMA A-operand (A, B alternating).
+__device__ __forceinline__ f16x8 lookup_pairs4(uint32_t O, uint32_t slot) {
+  typedef const __attribute__((address_space(3))) uint32_t lds_cu32;
+  uint32_t v[4];
+#pragma unroll
+  for (int b = 0; b < 4; ++b) v[b] = *(lds_cu32*)(uintptr_t)lut_addr(O, slot, b);
+  return __builtin_bit_cast(f16x8, v);
 }
 
 // Eight dequantised weights, elements 8m..8m+7 of the word (O0 = O[2m],
