@@ -31,7 +31,7 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBS = 8000.0
 MFMA_PEAK_TFLOPS = 2500.0  # dense fp16 MFMA
 METRIC = "MoE-layer tokens/s and achieved HBM GB/s (% of peak) at mixed bitwidths"
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_gate_up_qwen15moe_decode.md")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_ffn_qwen15moe_decode.md")
 KERNEL_SRCS = ["k_ffn_decode.hip", "k_ffn_body.h", "mpb_device.h"]
 
 
@@ -50,7 +50,8 @@ def block_bytes(N, Kd, b):
 def algorithmic_bytes(L, idx, T):
     """Bytes the method must move per step: touched blocks at q_i (planes +
     q_i-bit table), activations in, output out, router weights. Also the gate_up
-    kernel's share: touched gate_up blocks + activations."""
+    kernel's share (touched gate_up blocks + activations) and the down
+    kernel's (touched down blocks; h is an intermediate)."""
     touched = np.zeros(L.E + L.S, bool)
     touched[np.unique(idx[(idx >= 0) & (idx < L.E)])] = True
     touched[L.E:] = True
@@ -58,7 +59,7 @@ def algorithmic_bytes(L, idx, T):
     blocks_dn = sum(block_bytes(*L.shape(2 * e + 1), int(L.q[2 * e + 1])) for e in np.nonzero(touched)[0])
     x_bytes = T * L.H * 2
     step = blocks_gu + blocks_dn + x_bytes + T * L.H * 4 + L.E * L.H * 4 + (4 * L.E if L.bias is not None else 0)
-    return step, blocks_gu + x_bytes, int(touched.sum())
+    return step, blocks_gu + x_bytes, blocks_dn, int(touched.sum())
 
 
 def q_desc(c):
@@ -82,6 +83,12 @@ def cpu_baseline(L, Xbits, n_tokens, min_s=10.0, max_s=30.0):
         cores = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
     except Exception:
         cores = os.cpu_count() or 1
+    model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as fh:
+            model = next((ln.split(":", 1)[1].strip() for ln in fh if ln.startswith("model name")), model)
+    except OSError:
+        pass
     T = Xbits.shape[0]
     n = min(T, n_tokens if n_tokens > 0 else (T if T <= 256 else 64))
     X = S.x_bits_to_f64(Xbits[:n], L.cfg["xdtype"])
@@ -94,7 +101,8 @@ def cpu_baseline(L, Xbits, n_tokens, min_s=10.0, max_s=30.0):
         if dt >= min_s or dt * (passes + 1) / passes > max_s:
             break
     what = f"the whole {T}-token batch" if n == T else f"the first {n} of the {T} tokens"
-    return {"value": round(passes * n / dt, 3), "unit": "tokens/s", "cores": int(cores), "kind": "oracle",
+    return {"value": round(passes * n / dt, 3), "unit": "tokens/s", "cores": int(cores), "cpu_model": model,
+            "kind": "oracle",
             "sample": f"{what} of the same layer, {passes} pass(es) of route + FFN (every touched block "
                       f"dequantised on each pass), fp64 numpy, {dt:.1f} s"}
 
@@ -225,7 +233,7 @@ def run_sweep(torch, M, L, idx_host, step_fn, T, steps, warmup):
         for k in range(warmup):
             step_fn(k0 + k)
         k0 += warmup
-        evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(steps)]
+        evs = [[torch.cuda.Event(enable_timing=True) for _ in range(7)] for _ in range(steps)]
         for row in evs:
             for e in row:
                 e.record(stream)
@@ -240,8 +248,8 @@ def run_sweep(torch, M, L, idx_host, step_fn, T, steps, warmup):
         torch.cuda.synchronize()
         k0 += steps
         ms = a.elapsed_time(b) / steps
-        ph = np.array([[evs[k][j].elapsed_time(evs[k][j + 1]) for j in range(4)] for k in range(steps)])
-        gu, dn = float(ph[:, 1].mean()), float(ph[:, 2].mean())
+        gu = float(np.mean([evs[k][1].elapsed_time(evs[k][2]) for k in range(steps)]))
+        dn = float(np.mean([evs[k][5].elapsed_time(evs[k][6]) for k in range(steps)]))
         # blocks of the experts this batch touches (routed experts with tokens, every shared one)
         hit = np.zeros(L.E + L.S, bool)
         hit[np.unique(idx_host[(idx_host >= 0) & (idx_host < L.E)])] = True
@@ -347,7 +355,7 @@ def main():
         step(k)
     torch.cuda.synchronize()
     idx_host = bufs[0][0].cpu().numpy()
-    step_bytes, gu_bytes, n_touched = algorithmic_bytes(L, idx_host, T)
+    step_bytes, gu_bytes, dn_bytes, n_touched = algorithmic_bytes(L, idx_host, T)
 
     start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
 
@@ -379,10 +387,10 @@ def main():
 
     # Timed region 2 (per-kernel times): the same K steps launched eagerly, with
     # moe_ffn recording HIP events on its stream before grouping, at the start
-    # and end of the gate_up kernel (recorded by the launch itself), before the
-    # combine and after it (event records inside a graph do not order against
-    # its kernel nodes, so kernel times come from this pass).
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
+    # and end of the gate_up and down kernels (recorded by their launches),
+    # before the combine and after it (event records inside a graph do not
+    # order against its kernel nodes, so kernel times come from this pass).
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(7)] for _ in range(args.steps)]
     for row in evs:              # torch creates the HIP event on first record
         for e in row:
             e.record(stream)
@@ -398,6 +406,7 @@ def main():
     ms_eager = start2.elapsed_time(end2) / args.steps
     phase = np.array([[evs[k][j].elapsed_time(evs[k][j + 1]) for j in range(4)] for k in range(args.steps)])
     gu_ms = float(phase[:, 1].mean())
+    dn_ms = float(np.mean([evs[k][5].elapsed_time(evs[k][6]) for k in range(args.steps)]))
 
     tok_s = T / (ms * 1e-3)
     step_gbs = step_bytes / (ms * 1e-3) / 1e9
@@ -408,11 +417,12 @@ def main():
     n_rows = int(((idx_host >= 0) & (idx_host < L.E)).sum()) + T * L.S
     gu_flops = 2.0 * n_rows * (2 * L.I) * L.H
     prefill = T * L.K / L.E >= 96
-    traffic = None
+    traffic = dn_traffic = None
     if os.path.exists(TRAFFIC_FILE):
         tf = json.loads([ln for ln in open(TRAFFIC_FILE) if ln.strip().startswith("{")][-1])
         if tf.get("kernel_hash") == kernel_hash() and tf.get("workload") == c["name"]:
             traffic = tf.get("bytes_per_launch")
+            dn_traffic = tf.get("down_bytes_per_launch")
     res = {
         "metric": METRIC,
         "value": round(tok_s, 1),
@@ -435,7 +445,7 @@ def main():
         "hbm_gbs": round(step_gbs, 1),
         "hbm_frac": round(step_gbs / HBM_PEAK_GBS, 4),
         "phase_ms": {"group": round(float(phase[:, 0].mean()), 5), "gate_up": round(gu_ms, 5),
-                     "down": round(float(phase[:, 2].mean()), 5), "combine": round(float(phase[:, 3].mean()), 5)},
+                     "down": round(dn_ms, 5), "combine": round(float(phase[:, 3].mean()), 5)},
         "roofline": ({"kernel": "k_gate_up", "bound": "mfma", "achieved": round(gu_flops / (gu_ms * 1e-3) / 1e12, 1),
                       "peak": MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",
                       "frac": round(gu_flops / (gu_ms * 1e-3) / 1e12 / MFMA_PEAK_TFLOPS, 4),
@@ -445,6 +455,16 @@ def main():
                       "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(gu_gbs / HBM_PEAK_GBS, 4),
                       "traffic": traffic, "algorithmic_bytes_per_launch": int(gu_bytes)}),
     }
+    # the second FFN kernel, timed by its own launch events: down blocks' bytes
+    # against HBM (prefill-size layers: its useful flops against the MFMA peak)
+    dn_flops = 2.0 * n_rows * L.H * L.I
+    res["roofline"]["k_down"] = (
+        {"bound": "mfma", "achieved": round(dn_flops / (dn_ms * 1e-3) / 1e12, 1), "peak": MFMA_PEAK_TFLOPS,
+         "unit": "TFLOP/s", "frac": round(dn_flops / (dn_ms * 1e-3) / 1e12 / MFMA_PEAK_TFLOPS, 4),
+         "algorithmic_flops_per_launch": dn_flops, "us": round(dn_ms * 1e3, 2)} if prefill else
+        {"bound": "hbm", "achieved": round(dn_bytes / (dn_ms * 1e-3) / 1e9, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+         "frac": round(dn_bytes / (dn_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4), "traffic": dn_traffic,
+         "algorithmic_bytes_per_launch": int(dn_bytes), "us": round(dn_ms * 1e3, 2)})
     if args.fused:
         fb = [D.alloc_fused(T) for D in layers]
 

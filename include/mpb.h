@@ -438,14 +438,15 @@ int mpb_plan_step(const mpb_layer_desc* d, const int32_t* q_host, const uint8_t*
                   mpb_plan_summary* summary);
 
 /*
- * Profiling hook: with n == 5, every following moe_ffn records
- * events_host[0..4] (host array of hipEvent_t handles, caller-created) on its
- * stream: 0 before the grouping kernels, 1 and 2 at the start and end of the
- * gate_up kernel (recorded by its launch, so 1 -> 2 is the kernel alone and
- * 0 -> 1 includes the dispatch of gate_up), 3 before the combine and 4 after
- * it, so the caller can time each phase with hipEventElapsedTime. n == 0
- * turns recording off. The handles are borrowed until the hook is changed.
- * MPB_E_ARG for any other n or a null handle.
+ * Profiling hook: with n == 5 or 7, every following moe_ffn records
+ * events_host[0..n-1] (host array of hipEvent_t handles, caller-created) on
+ * its stream: 0 before the grouping kernels, 1 and 2 at the start and end of
+ * the gate_up kernel (recorded by its launch, so 1 -> 2 is the kernel alone
+ * and 0 -> 1 includes the dispatch of gate_up), 3 before the combine and 4
+ * after it, and with n == 7, 5 and 6 at the start and end of the down kernel
+ * (recorded by its launch), so the caller can time each phase with
+ * hipEventElapsedTime. n == 0 turns recording off. The handles are borrowed
+ * until the hook is changed. MPB_E_ARG for any other n or a null handle.
  */
 int mpb_set_kernel_events(void* const* events_host, int n);
 

@@ -227,7 +227,7 @@ def mpb_set_kernel_events(events):
     """events: list of 5 raw hipEvent_t handles (ints), or [] to turn recording off."""
     if not events:
         return _check("mpb_set_kernel_events", lib().mpb_set_kernel_events(None, 0))
-    return _check("mpb_set_kernel_events", lib().mpb_set_kernel_events(_host_ptrs(events), 5))
+    return _check("mpb_set_kernel_events", lib().mpb_set_kernel_events(_host_ptrs(events), len(events)))
 
 
 def mpb_set_resident_planes(i, r):

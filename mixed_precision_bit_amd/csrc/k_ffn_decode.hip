@@ -139,8 +139,8 @@ static size_t ffn_lds_bytes(int qmax) {
   return std::max<size_t>((256u << qmax) + stage_bytes<TC>(), kWaves * 16 * 64 * 4);
 }
 
-// ev0/ev1 (optional, gate_up): the launch itself records them at the kernel's
-// start and end (hipExtLaunchKernelGGL), for timing the kernel alone.
+// ev0/ev1 (optional): the launch itself records them at the kernel's start and
+// end (hipExtLaunchKernelGGL), for timing the kernel alone.
 template <int TC, bool GU, bool NT = true>
 static hipError_t launch_tc(const FfnParams& p, int qmax, hipStream_t s, hipEvent_t ev0 = nullptr,
                             hipEvent_t ev1 = nullptr) {
@@ -166,9 +166,13 @@ static hipError_t launch_tc(const FfnParams& p, int qmax, hipStream_t s, hipEven
                             pr3);
     else
       hipLaunchKernelGGL(k_gate_up<TC>, dim3(items * (p.I >> 6)), dim3(kThreads), shmem, s, p, qmax, pr3);
-  } else
-    hipLaunchKernelGGL((k_down<TC, NT>), dim3(p.max_items * ((p.H + 127) >> 7) * p.dn_split), dim3(kThreads), shmem,
-                       s, p, qmax, pr3);
+  } else {
+    const dim3 grid(p.max_items * ((p.H + 127) >> 7) * p.dn_split);
+    if (ev0 && ev1)
+      hipExtLaunchKernelGGL((k_down<TC, NT>), grid, dim3(kThreads), shmem, s, ev0, ev1, 0, p, qmax, pr3);
+    else
+      hipLaunchKernelGGL((k_down<TC, NT>), grid, dim3(kThreads), shmem, s, p, qmax, pr3);
+  }
   return hipGetLastError();
 }
 
@@ -180,8 +184,8 @@ hipError_t launch_gate_up(const FfnParams& p, int qmax, int tc, hipStream_t s, h
   }
 }
 
-hipError_t launch_down(const FfnParams& p, int qmax, bool nt, hipStream_t s) {
-  return nt ? launch_tc<1, false, true>(p, qmax, s) : launch_tc<1, false, false>(p, qmax, s);
+hipError_t launch_down(const FfnParams& p, int qmax, bool nt, hipStream_t s, hipEvent_t ev0, hipEvent_t ev1) {
+  return nt ? launch_tc<1, false, true>(p, qmax, s, ev0, ev1) : launch_tc<1, false, false>(p, qmax, s, ev0, ev1);
 }
 
 hipError_t launch_combine(const FfnParams& p, hipStream_t s) {

@@ -48,11 +48,11 @@ thread_local std::string g_err;
 // current; null until then.
 constexpr int kMaxDevices = 64;
 void* g_scratch[kMaxDevices];
-hipEvent_t g_ev[5];
+hipEvent_t g_ev[7];
 int g_nev = 0;
 
 void mark(int k, hipStream_t s) {
-  if (g_nev == 5) (void)hipEventRecord(g_ev[k], s);
+  if (g_nev >= 5) (void)hipEventRecord(g_ev[k], s);
 }
 
 int fail(int code, const std::string& msg) {
@@ -424,9 +424,10 @@ int ffn_impl(const char* name, const void* X_dev, int x_dtype, int T, const int3
     qmax_dn = std::max(qmax_dn, g.q[i + 1]);
   }
   // events 1 and 2 time the gate_up kernel itself: its launch records them
-  e = mpb::launch_gate_up(p, qmax_gu, tc, s, g_nev == 5 ? g_ev[1] : nullptr, g_nev == 5 ? g_ev[2] : nullptr);
+  e = mpb::launch_gate_up(p, qmax_gu, tc, s, g_nev >= 5 ? g_ev[1] : nullptr, g_nev >= 5 ? g_ev[2] : nullptr);
   if (e != hipSuccess) return hip_fail(e, (n + ": gate_up").c_str());
-  e = mpb::launch_down(p, qmax_dn, tc == 1, s);
+  // events 5 and 6 (optional) time the down kernel itself
+  e = mpb::launch_down(p, qmax_dn, tc == 1, s, g_nev == 7 ? g_ev[5] : nullptr, g_nev == 7 ? g_ev[6] : nullptr);
   if (e != hipSuccess) return hip_fail(e, (n + ": down").c_str());
   mark(3, s);
   e = mpb::launch_combine(p, s);
@@ -605,12 +606,12 @@ int mpb_get_resident_planes(int i) {
 
 int mpb_set_kernel_events(void* const* events_host, int n) {
   if (n == 0) { g_nev = 0; return MPB_OK; }
-  if (n != 5 || !events_host) return fail(MPB_E_ARG, "mpb_set_kernel_events: need 5 events or 0");
-  for (int k = 0; k < 5; ++k) {
+  if ((n != 5 && n != 7) || !events_host) return fail(MPB_E_ARG, "mpb_set_kernel_events: need 5, 7 or 0 events");
+  for (int k = 0; k < n; ++k) {
     if (!events_host[k]) return fail(MPB_E_ARG, "mpb_set_kernel_events: null event");
     g_ev[k] = (hipEvent_t)events_host[k];
   }
-  g_nev = 5;
+  g_nev = n;
   return MPB_OK;
 }
 

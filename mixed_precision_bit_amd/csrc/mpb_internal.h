@@ -129,7 +129,9 @@ hipError_t launch_x_to_f16(const uint16_t* x, uint16_t* y, int32_t* sc, int T, i
 hipError_t launch_gate_up(const FfnParams& p, int qmax, int tc, hipStream_t s, hipEvent_t ev0 = nullptr,
                           hipEvent_t ev1 = nullptr);
 // nt: non-temporal plane loads (decode-size batches, one item per group)
-hipError_t launch_down(const FfnParams& p, int qmax, bool nt, hipStream_t s);
+// ev0/ev1: optional events the launch records at the kernel's start and end
+hipError_t launch_down(const FfnParams& p, int qmax, bool nt, hipStream_t s, hipEvent_t ev0 = nullptr,
+                       hipEvent_t ev1 = nullptr);
 hipError_t launch_combine(const FfnParams& p, hipStream_t s);
 hipError_t launch_set_q(int32_t* q, int i, int b, hipStream_t s);
 
