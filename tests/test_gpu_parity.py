@@ -124,6 +124,50 @@ def test_route_bit_exact(cfg, T):
     assert_close(w.cpu().numpy(), r, f"cfg{cfg} topk_w")
 
 
+def test_route_workspace_reused_across_calls_and_replays():
+    """One router workspace serves calls of different sizes in a row and a
+    captured graph's replays, each bit-identical to the first call and to the
+    oracle's top-K."""
+    c = S.layer_config(1)
+    L = S.make_layer(1, blocks=[])
+    Xb = S.make_tokens(1)
+    T = Xb.shape[0]
+    X, z, r = oracle_route(L, Xb)
+    W = torch.from_numpy(L.W_r).cuda()
+    Xd = to_dev_x(Xb)
+    ws = route_ws(T, L.E)
+    outs = []
+    for n in (T, 37, T, 5, T):
+        idx = torch.empty((n, L.K), dtype=torch.int32, device="cuda")
+        w = torch.empty((n, L.K), dtype=torch.float32, device="cuda")
+        M().moe_route(Xd[:n].contiguous(), 0, W, None, L.K, idx, w, ws)
+        torch.cuda.synchronize()
+        say(f"route call T={n}")
+        assert np.array_equal(idx.cpu().numpy(), z[:n]), f"T={n}"
+        outs.append((idx.cpu().numpy(), w.cpu().numpy()))
+    for gi, gw in outs[1:]:
+        n = gi.shape[0]
+        assert np.array_equal(gw.view(np.uint32), outs[0][1][:n].view(np.uint32))
+    assert_close(outs[0][1], r, "topk_w")
+    idx = torch.full((T, L.K), -1, dtype=torch.int32, device="cuda")
+    w = torch.zeros((T, L.K), dtype=torch.float32, device="cuda")
+    cap = torch.cuda.Stream()
+    cap.wait_stream(torch.cuda.current_stream())
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(cap):
+        with torch.cuda.graph(g, stream=cap):
+            M().moe_route(Xd, 0, W, None, L.K, idx, w, ws, stream=cap)
+    torch.cuda.current_stream().wait_stream(cap)
+    for k in range(3):
+        idx.fill_(-1)
+        w.zero_()
+        g.replay()
+        torch.cuda.synchronize()
+        say(f"route replay {k}")
+        assert np.array_equal(idx.cpu().numpy(), z)
+        assert np.array_equal(w.cpu().numpy().view(np.uint32), outs[0][1].view(np.uint32))
+
+
 def test_route_ties_lowest_index():
     rng = np.random.default_rng(12)
     H, E, K, T = 256, 24, 6, 40
