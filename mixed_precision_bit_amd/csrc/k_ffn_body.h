@@ -256,10 +256,10 @@ struct KSplit {
 // Waves 0/1 take gate rows c0..c0+31 / c0+32..c0+63, waves 2/3 the matching up
 // rows, waves 4..7 the same rows over the second K half. Each dequantised
 // A operand feeds TC MFMAs, one per 32-token chunk of the item. After the K
-// loop the other waves hand their accumulators to waves 0/1 through LDS, which
-// add the halves, apply SiLU(gate) * up and store h as an fp16 (hi, lo) pair
-// (hi + lo carries ~22 significant bits of the fp32 value into the down
-// projection).
+// loop the waves exchange their accumulators through LDS; each then adds the
+// halves for a quarter of a row half, applies SiLU(gate) * up and stores h as
+// an fp16 (hi, lo) pair (hi + lo carries ~22 significant bits of the fp32
+// value into the down projection).
 //
 // Issue order per step s (vector memory completes in issue order, so a wait
 // for one load also waits for every older one): compute on the planes of step
@@ -426,41 +426,40 @@ __device__ __forceinline__ void gate_up_body(const FfnParams& p, int e, int it, 
     if (s + 1 < ks.NSW) step(s + 1, PB, 0);
   }
 
-  // hand the accumulators to waves 0/1, one token chunk at a time; layout
-  // [wave][v][lane]; gate = own + wave w+4, up = waves w+2 and w+6, each sum in
-  // that order
+  // SwiGLU, one token chunk at a time: every wave puts its accumulators in LDS
+  // (layout [wave][v][lane]), then wave w finishes v = 4 (w >> 1) .. + 3 of
+  // row half hr = w & 1 (columns it * 64 + 32 hr + ...), with gate = the
+  // partials of waves hr and hr + 4 and up = those of waves hr + 2 and hr + 6,
+  // each sum in that order; all eight waves share the SiLU work
   float* xb = (float*)lds;
+  const int hr = w & 1, v4 = w >> 1;
 #pragma unroll
   for (int c = 0; c < TC; ++c) {
-    if (c) __syncthreads();  // waves 0/1 are done reading the previous chunk
-    if (w >= 2) {
+    if (c) __syncthreads();  // the previous chunk's partials have been read
 #pragma unroll
-      for (int v = 0; v < 16; ++v) xb[(w * 16 + v) * 64 + lane] = acc[c][v];
-    }
+    for (int v = 0; v < 16; ++v) xb[(w * 16 + v) * 64 + lane] = acc[c][v];
     __syncthreads();
     const int t = kTok * c + r;
-    if (w < 2 && t < nt) {
-      // acc[c][v] is row 8*(v/4) + 4*g + v%4 of the wave's 32 rows, token t.
+    if (t < nt) {
+      // acc[c][v] is row 8*(v/4) + 4*g + v%4 of a wave's 32 rows, token t.
       // A token converted scaled by 2^-sc (bf16 beyond the fp16 range) gets
       // gate and up scaled back, and h carried as h 2^(-2 sc).
       const int sc = p.xsc ? ld_co<CO>(p.xsc + ld_co<CO>(p.ptok + base + t)) : 0;
-      const size_t o = (size_t)(base + t) * I + c0 + 4 * g;
+      const size_t o = (size_t)(base + t) * I + it * 64 + hr * 32 + 4 * g;
+      uint16_t hv[4], lv[4];
 #pragma unroll
-      for (int v4 = 0; v4 < 4; ++v4) {
-        uint16_t hv[4], lv[4];
-#pragma unroll
-        for (int k = 0; k < 4; ++k) {
-          const int v = 4 * v4 + k;
-          const float gate = __builtin_amdgcn_ldexpf(acc[c][v] + xb[((w + 4) * 16 + v) * 64 + lane], sc);
-          const float up =
-              __builtin_amdgcn_ldexpf(xb[((w + 2) * 16 + v) * 64 + lane] + xb[((w + 6) * 16 + v) * 64 + lane], sc);
-          const split16 sp2 = split_hi_lo(__builtin_amdgcn_ldexpf(silu(gate) * up, -2 * sc));
-          hv[k] = __builtin_bit_cast(uint16_t, sp2.hi);
-          lv[k] = __builtin_bit_cast(uint16_t, sp2.lo);
-        }
-        st_co<CO>((uint64_t*)(p.hhi + o + 8 * v4), __builtin_bit_cast(uint64_t, make_ushort4(hv[0], hv[1], hv[2], hv[3])));
-        st_co<CO>((uint64_t*)(p.hlo + o + 8 * v4), __builtin_bit_cast(uint64_t, make_ushort4(lv[0], lv[1], lv[2], lv[3])));
+      for (int k = 0; k < 4; ++k) {
+        const int v = 4 * v4 + k;
+        const float gate =
+            __builtin_amdgcn_ldexpf(xb[(hr * 16 + v) * 64 + lane] + xb[((hr + 4) * 16 + v) * 64 + lane], sc);
+        const float up =
+            __builtin_amdgcn_ldexpf(xb[((hr + 2) * 16 + v) * 64 + lane] + xb[((hr + 6) * 16 + v) * 64 + lane], sc);
+        const split16 sp2 = split_hi_lo(__builtin_amdgcn_ldexpf(silu(gate) * up, -2 * sc));
+        hv[k] = __builtin_bit_cast(uint16_t, sp2.hi);
+        lv[k] = __builtin_bit_cast(uint16_t, sp2.lo);
       }
+      st_co<CO>((uint64_t*)(p.hhi + o + 8 * v4), __builtin_bit_cast(uint64_t, make_ushort4(hv[0], hv[1], hv[2], hv[3])));
+      st_co<CO>((uint64_t*)(p.hlo + o + 8 * v4), __builtin_bit_cast(uint64_t, make_ushort4(lv[0], lv[1], lv[2], lv[3])));
     }
   }
 }
