@@ -188,7 +188,10 @@ size_t moe_ffn_workspace_bytes(int T);
  * would otherwise be NaN, never silently wrong).
  * Results are deterministic for every T: the grouping counts with integer
  * atomics only, and every floating-point sum runs in a fixed order.
- * Errors: MPB_E_UNINIT, MPB_E_ARG, MPB_E_WS, MPB_E_HIP.
+ * Errors: MPB_E_UNINIT, MPB_E_ARG, MPB_E_WS, MPB_E_HIP, and MPB_E_SHAPE when T
+ * is too large for the layer (the kernels address the activations, T*H*2
+ * bytes, and h, about 4*T*(K+S)*I bytes, with 32-bit offsets: each must stay
+ * below 4 GiB; the launch grid must stay below 2^31 workgroups).
  */
 int moe_ffn(const void* X_dev, int x_dtype, int T, const int32_t* topk_idx_dev,
             const float* topk_w_dev, const uint32_t* const* planes_dev,

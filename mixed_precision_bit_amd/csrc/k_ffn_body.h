@@ -149,28 +149,52 @@ __device__ __forceinline__ void st_co16(void* p, uint4 v) {
 // piece p = tid % 16 of token 32 c + tid / 16 of both K halves, c < TC.
 template <int TC>
 struct StagePlan {
-  const uint16_t* row[TC];  // source row start (token slots >= nt load nothing)
+  rsrc_t rs;                // the activation rows (x, or h hi and lo), one descriptor for the wave
+  uint32_t off[TC];         // byte offset of the slot's row in rs
+  int lim[TC];              // elements of the row the slot reads (0 for token slots >= nt)
   uint32_t dst[2][TC];      // stage byte offsets per K half
-  bool live[TC];            // token slot < nt
+  bool wl[TC];              // the wave holds a token slot < nt in chunk c (wave-uniform)
+  bool wr;                  // the thread's slots land in the stage (DB: slots 16..31 do not)
 };
 
+// wave-uniform: some token slot of the calling wave's chunk c is live (a wave
+// stages the four consecutive slots st & ~3 .. st | 3)
+__device__ __forceinline__ bool wave_has_tokens(int c, int st, int nt) {
+  return __builtin_amdgcn_readfirstlane(kTok * c + (st & ~3)) < nt;
+}
+
+// A window element k of slot c: its byte offset in the rows' descriptor, or
+// kNoRow, past any buffer, for elements the slot does not read (the load then
+// returns zeros without touching memory), so staging needs no branches.
 template <int TC>
-__device__ __forceinline__ void load_window(uint4 (&v)[2][TC], const StagePlan<TC>& sp, const int (&k)[2], int len) {
-#pragma unroll
-  for (int i = 0; i < 2; ++i)
-#pragma unroll
-    for (int c = 0; c < TC; ++c)
-      if (sp.live[c] && k[i] < len) v[i][c] = *(const uint4*)(sp.row[c] + k[i]);
+__device__ __forceinline__ uint32_t win_off(const StagePlan<TC>& sp, int c, int k) {
+  return k < sp.lim[c] ? sp.off[c] + 2u * (uint32_t)k : kNoRow;
+}
+
+// The descriptor over [lo, lo + bytes) for the staged rows; bytes < kNoRow
+// (rows_fit: the host refuses batches whose activation or h arrays are larger).
+__device__ __forceinline__ rsrc_t rows_rsrc(const void* lo, size_t bytes) {
+  return tile_rsrc(lo, 0, (uint32_t)bytes);
 }
 
 template <int TC>
-__device__ __forceinline__ void store_window(char* stage, const uint4 (&v)[2][TC], const StagePlan<TC>& sp,
-                                             const int (&k)[2], int len) {
+__device__ __forceinline__ void load_window(uint4 (&v)[2][TC], const StagePlan<TC>& sp, const int (&k)[2]) {
 #pragma unroll
   for (int i = 0; i < 2; ++i)
 #pragma unroll
     for (int c = 0; c < TC; ++c)
-      if (sp.live[c]) *(uint4*)(stage + sp.dst[i][c]) = k[i] < len ? v[i][c] : make_uint4(0u, 0u, 0u, 0u);
+      if (sp.wl[c])
+        v[i][c] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(sp.rs, win_off(sp, c, k[i]), 0, 0));
+}
+
+template <int TC>
+__device__ __forceinline__ void store_window(char* stage, const uint4 (&v)[2][TC], const StagePlan<TC>& sp) {
+  if (!sp.wr) return;
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int c = 0; c < TC; ++c)
+      if (sp.wl[c]) *(uint4*)(stage + sp.dst[i][c]) = v[i][c];
 }
 
 // Pair-order staging (3-bit pair tables): a piece holds elements e..e+3 and
@@ -178,35 +202,33 @@ __device__ __forceinline__ void store_window(char* stage, const uint4 (&v)[2][TC
 // matching the order of lookup_pairs4. k[i] is the first element (e) of the
 // piece for K half i.
 template <int TC>
-__device__ __forceinline__ void load_window_pairs(uint4 (&v)[2][TC], const StagePlan<TC>& sp, const int (&k)[2],
-                                                  int len) {
+__device__ __forceinline__ void load_window_pairs(uint4 (&v)[2][TC], const StagePlan<TC>& sp, const int (&k)[2]) {
 #pragma unroll
   for (int i = 0; i < 2; ++i)
 #pragma unroll
-    for (int c = 0; c < TC; ++c)
-      if (sp.live[c] && k[i] < len) {
-        const uint2 a = *(const uint2*)(sp.row[c] + k[i]);
-        const uint2 b = *(const uint2*)(sp.row[c] + k[i] + 32);
-        v[i][c] = make_uint4(a.x, a.y, b.x, b.y);
-      }
+    for (int c = 0; c < TC; ++c) {
+      if (!sp.wl[c]) continue;
+      const uint2 a = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(sp.rs, win_off(sp, c, k[i]), 0, 0));
+      const uint2 b =
+          __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(sp.rs, win_off(sp, c, k[i] + 32), 0, 0));
+      v[i][c] = make_uint4(a.x, a.y, b.x, b.y);
+    }
 }
 
 template <int TC>
-__device__ __forceinline__ void store_window_pairs(char* stage, const uint4 (&v)[2][TC], const StagePlan<TC>& sp,
-                                                  const int (&k)[2], int len) {
+__device__ __forceinline__ void store_window_pairs(char* stage, const uint4 (&v)[2][TC], const StagePlan<TC>& sp) {
+  if (!sp.wr) return;
 #pragma unroll
   for (int i = 0; i < 2; ++i)
 #pragma unroll
-    for (int c = 0; c < TC; ++c)
-      if (sp.live[c]) {
-        uint4 o = make_uint4(0u, 0u, 0u, 0u);
-        if (k[i] < len) {  // (a0 a1 | a2 a3) and (b0 b1 | b2 b3) -> a0 b0, a1 b1, a2 b2, a3 b3
-          const uint4 x = v[i][c];
-          o = make_uint4(__builtin_amdgcn_perm(x.z, x.x, 0x05040100u), __builtin_amdgcn_perm(x.z, x.x, 0x07060302u),
-                         __builtin_amdgcn_perm(x.w, x.y, 0x05040100u), __builtin_amdgcn_perm(x.w, x.y, 0x07060302u));
-        }
-        *(uint4*)(stage + sp.dst[i][c]) = o;
-      }
+    for (int c = 0; c < TC; ++c) {
+      if (!sp.wl[c]) continue;
+      // (a0 a1 | a2 a3) and (b0 b1 | b2 b3) -> a0 b0, a1 b1, a2 b2, a3 b3
+      const uint4 x = v[i][c];
+      *(uint4*)(stage + sp.dst[i][c]) =
+          make_uint4(__builtin_amdgcn_perm(x.z, x.x, 0x05040100u), __builtin_amdgcn_perm(x.z, x.x, 0x07060302u),
+                     __builtin_amdgcn_perm(x.w, x.y, 0x05040100u), __builtin_amdgcn_perm(x.w, x.y, 0x07060302u));
+    }
 }
 
 // Item `item` of the gate_up (gu) or down list: its group e, first token t0
@@ -295,11 +317,14 @@ __device__ __forceinline__ void gate_up_body(const FfnParams& p, int e, int it, 
   // 4 m + 3 of both words)
   StagePlan<TC> sp;
   const int st = tid >> 4, spc = tid & 15;
+  sp.rs = rows_rsrc(p.xh, (size_t)p.T * H * 2);
+  sp.wr = !DB || st < 16;
 #pragma unroll
   for (int c = 0; c < TC; ++c) {
     const int t = kTok * c + st;
-    sp.live[c] = t < nt;
-    sp.row[c] = p.xh + (size_t)ld_co<CO>(p.ptok + base + (sp.live[c] ? t : 0)) * H;
+    sp.wl[c] = wave_has_tokens(c, st, nt);
+    sp.lim[c] = t < nt ? H : 0;
+    sp.off[c] = t < nt ? (uint32_t)ld_co<CO>(p.ptok + base + t) * (uint32_t)H * 2u : 0u;
     sp.dst[0][c] = DB ? stage_off_db(0, 0, t & 15, spc) : stage_off<TC>(0, t, spc);
     sp.dst[1][c] = DB ? stage_off_db(0, 1, t & 15, spc) : stage_off<TC>(1, t, spc);
   }
@@ -309,12 +334,12 @@ __device__ __forceinline__ void gate_up_body(const FfnParams& p, int e, int it, 
     for (int i = 0; i < 2; ++i) k[i] = (i * ks.HH + 2 * s + (spc >> 3)) * 64 + (PR ? 4 : 8) * (spc & 7);
   };
   auto ld_win = [&](uint4 (&v)[2][TC], const int (&k)[2]) {
-    if constexpr (PR) load_window_pairs<TC>(v, sp, k, H);
-    else load_window<TC>(v, sp, k, H);
+    if constexpr (PR) load_window_pairs<TC>(v, sp, k);
+    else load_window<TC>(v, sp, k);
   };
   auto st_win = [&](char* dst, const uint4 (&v)[2][TC], const int (&k)[2]) {
-    if constexpr (PR) store_window_pairs<TC>(dst, v, sp, k, H);
-    else store_window<TC>(dst, v, sp, k, H);
+    if constexpr (PR) store_window_pairs<TC>(dst, v, sp);
+    else store_window<TC>(dst, v, sp);
   };
 
   // the descriptor of K half 0 ends where half 1 begins, so the prefetches
@@ -503,13 +528,24 @@ __device__ __forceinline__ void down_body(const FfnParams& p, int e, int it, int
 
   StagePlan<TC> sp;
   const int st = tid >> 4, spc = tid & 15, hl = spc >> 3;
+  {
+    // one descriptor over both halves of h
+    const size_t hbytes = (size_t)p.T * (p.K + p.S) * I * 2;
+    const char* a = (const char*)p.hhi;
+    const char* b = (const char*)p.hlo;
+    const char* lo = a < b ? a : b;
+    sp.rs = rows_rsrc(lo, (size_t)((a < b ? b : a) - lo) + hbytes);
+    const uint32_t half = (uint32_t)((hl ? b : a) - lo);
+    sp.wr = !DB || st < 16;
 #pragma unroll
-  for (int c = 0; c < TC; ++c) {
-    const int t = kTok * c + st;
-    sp.live[c] = t < nt;
-    sp.row[c] = (hl ? p.hlo : p.hhi) + (size_t)(base + (sp.live[c] ? t : 0)) * I;
-    sp.dst[0][c] = DB ? stage_off_db(0, 0, t & 15, spc) : stage_off<TC>(0, t, spc);
-    sp.dst[1][c] = DB ? stage_off_db(0, 1, t & 15, spc) : stage_off<TC>(1, t, spc);
+    for (int c = 0; c < TC; ++c) {
+      const int t = kTok * c + st;
+      sp.wl[c] = wave_has_tokens(c, st, nt);
+      sp.lim[c] = t < nt ? klen : 0;
+      sp.off[c] = t < nt ? half + (uint32_t)(base + t) * (uint32_t)I * 2u : 0u;
+      sp.dst[0][c] = DB ? stage_off_db(0, 0, t & 15, spc) : stage_off<TC>(0, t, spc);
+      sp.dst[1][c] = DB ? stage_off_db(0, 1, t & 15, spc) : stage_off<TC>(1, t, spc);
+    }
   }
   static_assert(!DB || TC == 1, "double-buffered stage: one token chunk");
   // stage buffer of round j (DB)
@@ -523,12 +559,12 @@ __device__ __forceinline__ void down_body(const FfnParams& p, int e, int it, int
       k[i] = (hc0 + i * ks.HH + 2 * s + ((spc >> 2) & 1)) * 64 + (PR ? 4 * (4 * j + (spc & 3)) : 32 * j + 8 * (spc & 3));
   };
   auto ld_win = [&](uint4 (&v)[2][TC], const int (&k)[2]) {
-    if constexpr (PR) load_window_pairs<TC>(v, sp, k, klen);
-    else load_window<TC>(v, sp, k, klen);
+    if constexpr (PR) load_window_pairs<TC>(v, sp, k);
+    else load_window<TC>(v, sp, k);
   };
   auto st_win = [&](char* dst, const uint4 (&v)[2][TC], const int (&k)[2]) {
-    if constexpr (PR) store_window_pairs<TC>(dst, v, sp, k, klen);
-    else store_window<TC>(dst, v, sp, k, klen);
+    if constexpr (PR) store_window_pairs<TC>(dst, v, sp);
+    else store_window<TC>(dst, v, sp);
   };
 
   const int cb = (hc0 >> 1) + kh * (ks.HH >> 1);

@@ -395,7 +395,8 @@ int ffn_impl(const char* name, const void* X_dev, int x_dtype, int T, const int3
     return fail(MPB_E_ARG, n + ": stream is neither the bound stream nor under graph capture");
   const mpb::WsLayout L = mpb::ws_layout(T, g.H, g.I, g.E, g.S, g.K, x_dtype == MPB_BF16);
   const long long ntile = std::max(g.I / 64, (g.H + 127) / 128);
-  if (((long long)L.max_items + 7) / 8 * 8 * ntile * mpb::dn_splits(T, g.H, g.I, g.E, g.S, g.K) >= (1ll << 31))
+  if (((long long)L.max_items + 7) / 8 * 8 * ntile * mpb::dn_splits(T, g.H, g.I, g.E, g.S, g.K) >= (1ll << 31) ||
+      !mpb::rows_fit(L, T, g.H, g.I, g.K, g.S))
     return fail(MPB_E_SHAPE, n + ": T too large for this layer");
   if (ws_bytes < L.total) {
     if (static_ws)
@@ -488,7 +489,8 @@ int moe_fused(const void* X_dev, int x_dtype, int T, const float* W_router_dev, 
     return fail(MPB_E_ARG, "moe_fused: stream is neither the bound stream nor under graph capture");
   const mpb::WsLayout L = mpb::ws_layout(T, g.H, g.I, g.E, g.S, g.K, x_dtype == MPB_BF16);
   const long long ntile = std::max(g.I / 64, (g.H + 127) / 128);
-  if ((long long)L.max_items * ntile * mpb::dn_splits(T, g.H, g.I, g.E, g.S, g.K) >= (1ll << 30))
+  if ((long long)L.max_items * ntile * mpb::dn_splits(T, g.H, g.I, g.E, g.S, g.K) >= (1ll << 30) ||
+      !mpb::rows_fit(L, T, g.H, g.I, g.K, g.S))
     return fail(MPB_E_SHAPE, "moe_fused: T too large for this layer");
   const size_t c_bytes = mpb::fused_counter_bytes(), r_bytes = mpb::route_workspace_bytes(T, g.E);
   const size_t need = c_bytes + r_bytes + L.total;

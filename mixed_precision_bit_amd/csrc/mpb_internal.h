@@ -89,6 +89,15 @@ inline int max_decode_items(int T, int E, int S, int K) {
 }
 WsLayout ws_layout(int T, int H, int I, int E, int S, int K, bool bf16);
 
+// The FFN kernels stage activation and h rows through buffer descriptors with
+// 32-bit byte offsets, kNoRow standing for "no row" (reads as zeros): the
+// activations ([T][H] fp16) and the span of h's two halves must stay below it.
+constexpr uint32_t kNoRow = 0xfffffff0u;
+inline bool rows_fit(const WsLayout& L, int T, int H, int I, int K, int S) {
+  const size_t P = (size_t)T * (K + S);
+  return (size_t)T * H * 2 < kNoRow && (L.hlo - L.hhi) + P * I * 2 < kNoRow;
+}
+
 // Raise a kernel's dynamic LDS limit to `bytes` on the current device, once
 // per device (bit d of `done` records device d; the library is driven from
 // one host thread).
