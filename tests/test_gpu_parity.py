@@ -242,6 +242,23 @@ def test_ffn_qwen_decode_every_element(layer_cache):
     assert_close(gout, ref, "cfg1 out")
 
 
+def test_ffn_refuses_batches_beyond_32bit_staging(layer_cache):
+    """The FFN kernels stage activation and h rows with 32-bit byte offsets:
+    a batch whose activations or h would span 4 GiB is refused on the host
+    (MPB_E_SHAPE) before anything is enqueued."""
+    L, D = dev_layer(layer_cache, 1)
+    lib = M()
+    tiny = torch.zeros(64, dtype=torch.int32, device="cuda")
+    out = torch.zeros(64, dtype=torch.float32, device="cuda")
+    T = 1 << 20   # 2^20 tokens of H = 2048: 4 GiB of fp16 activations
+    rc = lib.lib().moe_ffn(lib._ptr(tiny), 0, T, lib._ptr(tiny), lib._ptr(tiny), lib._ptr(D.planes_table),
+                           lib._ptr(D.luts_table), lib._ptr(D.q_dev), lib._ptr(out), lib._ptr(tiny), tiny.numel() * 4,
+                           lib._stream(None))
+    assert rc == -2, (rc, lib.mpb_last_error())
+    assert "too large" in lib.mpb_last_error()
+    torch.cuda.synchronize()
+
+
 def test_ffn_deterministic_and_block_independent(layer_cache):
     L, D = dev_layer(layer_cache, 10)
     Xb = S.make_tokens(10)
