@@ -48,6 +48,10 @@ __device__ __forceinline__ uint32_t stage_off(int kh, int t, int piece) {
 }
 template <int TC>
 constexpr int stage_bytes() { return 2 * TC * kTok * 256; }
+// 128-token items of blocks below 8 bits: table region (the 7-bit table, or
+// the 3-bit pair table) before two stage buffers, 160 KiB in all
+constexpr uint32_t kDbTable4 = 32768;
+static_assert(kDbTable4 + 2 * 2 * 4 * 32 * 256 <= 163840, "two 128-token stage buffers fit the LDS");
 
 // Items of at most 16 tokens (TC = 1) split the same region into two stage
 // buffers of [K half][16 tokens][16 pieces]; step s reads buffer s % 2 while
@@ -93,6 +97,13 @@ __device__ __forceinline__ void load_table_image(const uint16_t* img, int w, int
 }
 
 __device__ __forceinline__ void wait_vmem_all() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
+// wait until at most N vector memory operations of the wave are outstanding
+template <int N>
+__device__ __forceinline__ void wait_vmem_le() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
 
 // Half-chunk s of the wave's K half for every plane: lane (r, g) reads the 8
 // bytes at chunk cb + s, row r, half g. NT: the loads carry the non-temporal
@@ -287,8 +298,10 @@ struct KSplit {
 // for one load also waits for every older one): compute on the planes of step
 // s, barrier, write the activations of step s+1 (loaded one step earlier) to
 // the stage, load the activations of step s+2, load the planes of step s+3,
-// barrier. DB (items of <= 16 tokens, TC = 1): the stage is double-buffered
-// and the first of the two barriers is dropped.
+// barrier. DB: the stage is double-buffered and the first of the two barriers
+// is dropped; items of <= 16 tokens (TC = 1) split the stage region into two
+// 16-token buffers, 128-token items (TC = 4) of blocks below 8 bits take two
+// full stage buffers after a 32 KiB table region (the 8-bit table needs 64 KiB).
 //
 // PR (3-bit blocks): pair tables. lut_bytes is kPairTableBytes; the
 // tile's 3-bit table image is copied to the stage region, expanded into the
@@ -318,17 +331,21 @@ __device__ __forceinline__ void gate_up_body(const FfnParams& p, int e, int it, 
   StagePlan<TC> sp;
   const int st = tid >> 4, spc = tid & 15;
   sp.rs = rows_rsrc(p.xh, (size_t)p.T * H * 2);
-  sp.wr = !DB || st < 16;
+  sp.wr = !DB || TC > 1 || st < 16;
 #pragma unroll
   for (int c = 0; c < TC; ++c) {
     const int t = kTok * c + st;
     sp.wl[c] = wave_has_tokens(c, st, nt);
     sp.lim[c] = t < nt ? H : 0;
     sp.off[c] = t < nt ? (uint32_t)ld_co<CO>(p.ptok + base + t) * (uint32_t)H * 2u : 0u;
-    sp.dst[0][c] = DB ? stage_off_db(0, 0, t & 15, spc) : stage_off<TC>(0, t, spc);
-    sp.dst[1][c] = DB ? stage_off_db(0, 1, t & 15, spc) : stage_off<TC>(1, t, spc);
+    sp.dst[0][c] = DB && TC == 1 ? stage_off_db(0, 0, t & 15, spc) : stage_off<TC>(0, t, spc);
+    sp.dst[1][c] = DB && TC == 1 ? stage_off_db(0, 1, t & 15, spc) : stage_off<TC>(1, t, spc);
   }
-  static_assert(!DB || TC == 1, "double-buffered stage: one token chunk");
+  // stage byte offset of piece `pc` of token chunk c, row r, in buffer par
+  auto rd_off = [&](int par, int c, int pc) -> uint32_t {
+    if constexpr (DB && TC == 1) return stage_off_db(par, kh, r & 15, pc);
+    else return (DB ? (uint32_t)par * stage_bytes<TC>() : 0u) + stage_off<TC>(kh, kTok * c + r, pc);
+  };
   auto kwin = [&](int s, int (&k)[2]) {
 #pragma unroll
     for (int i = 0; i < 2; ++i) k[i] = (i * ks.HH + 2 * s + (spc >> 3)) * 64 + (PR ? 4 : 8) * (spc & 7);
@@ -340,6 +357,30 @@ __device__ __forceinline__ void gate_up_body(const FfnParams& p, int e, int it, 
   auto st_win = [&](char* dst, const uint4 (&v)[2][TC], const int (&k)[2]) {
     if constexpr (PR) store_window_pairs<TC>(dst, v, sp);
     else store_window<TC>(dst, v, sp);
+  };
+  // DMA (double-buffered stage, natural piece order): the window of step s
+  // goes from memory straight into stage buffer par with buffer-to-LDS loads
+  // (no registers, no LDS stores). One load moves 1 KiB: lane L writes slot
+  // L % 16 of token (L / 16) of the wave's four token rows, so it reads piece
+  // (L % 16) ^ (t % 16) of its token t (the stage's swizzle); rows past the
+  // item and elements past the row read as zeros.
+  constexpr bool DMA = DB && !PR;
+  const int pdma = spc ^ (st & 15);
+  auto dma_win = [&](int par, int s) {
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int k = (i * ks.HH + 2 * s + (pdma >> 3)) * 64 + 8 * (pdma & 7);
+#pragma unroll
+      for (int c = 0; c < TC; ++c) {
+        if (!sp.wl[c] || !sp.wr) continue;
+        // the wave's first token row (slot 0, before the swizzle)
+        const uint32_t row0b = TC == 1 ? (uint32_t)par * (2 * kDbTok * 256u) + (uint32_t)i * (kDbTok * 256u)
+                                       : (uint32_t)par * stage_bytes<TC>() + (uint32_t)i * (TC * kTok * 256u);
+        const uint32_t dst = lut_bytes + row0b + (uint32_t)(kTok * c + (st & ~3)) * 256u;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(sp.rs, (lds_void*)(uintptr_t)__builtin_amdgcn_readfirstlane(dst), 16,
+                                                 win_off(sp, c, k), 0, 0, 0);
+      }
+    }
   };
 
   // the descriptor of K half 0 ends where half 1 begins, so the prefetches
@@ -357,21 +398,30 @@ __device__ __forceinline__ void gate_up_body(const FfnParams& p, int e, int it, 
   // PR: the 3-bit image goes to the stage region, which is staged only after
   // the pair table has been built from it
   load_table_image<Q>(p.luts[blk * 6 + (Q - 3)] + (size_t)it * (128u << Q), w, lane, PR ? lut_bytes : 0u);
-  kwin(0, kk);
-  ld_win(xr, kk);
-  load_planes<Q, NT>(PA, rs, cb, 0, voff);
-  wait_vmem_all();
-  if constexpr (PR) {
+  if constexpr (DMA) {
+    dma_win(0, 0);
+    load_planes<Q, NT>(PA, rs, cb, 0, voff);
+    load_planes<Q, NT>(PB, rs, cb, 1, voff);
+    load_planes<Q, NT>(PC, rs, cb, 2, voff);
+    wait_vmem_le<2 * Q>();  // the table, step 0's activations and planes
     __syncthreads();
-    build_pair_table3(lut_bytes, tid);
+  } else {
+    kwin(0, kk);
+    ld_win(xr, kk);
+    load_planes<Q, NT>(PA, rs, cb, 0, voff);
+    wait_vmem_all();
+    if constexpr (PR) {
+      __syncthreads();
+      build_pair_table3(lut_bytes, tid);
+      __syncthreads();
+    }
+    st_win(stage, xr, kk);
+    load_planes<Q, NT>(PB, rs, cb, 1, voff);
+    kwin(1, kk);
+    ld_win(xr, kk);
+    load_planes<Q, NT>(PC, rs, cb, 2, voff);
     __syncthreads();
   }
-  st_win(stage, xr, kk);
-  load_planes<Q, NT>(PB, rs, cb, 1, voff);
-  kwin(1, kk);
-  ld_win(xr, kk);
-  load_planes<Q, NT>(PC, rs, cb, 2, voff);
-  __syncthreads();
 
   f32x16 acc[TC];
 #pragma unroll
@@ -379,6 +429,9 @@ __device__ __forceinline__ void gate_up_body(const FfnParams& p, int e, int it, 
   // par = s % 2 (the stage buffer of step s when DB), passed as a constant so
   // that the buffer offset folds into the LDS instructions' offset field
   auto step = [&](int s, uint2 (&P)[Q], int par) {
+    // DMA: the buffer of step s + 1 was last read in step s - 1
+    if constexpr (DMA)
+      if (s + 1 < ks.NSW) dma_win(par ^ 1, s + 1);
     if constexpr (PR) {
       uint32_t Pa[3], Pb[3], O[8];
       word_of<3>(P, 0, Pa);
@@ -389,8 +442,7 @@ __device__ __forceinline__ void gate_up_body(const FfnParams& p, int e, int it, 
         const f16x8 a = lookup_pairs4(O[m], slot);
 #pragma unroll
         for (int c = 0; c < TC; ++c) {
-          const uint32_t bo =
-              DB ? stage_off_db(par, kh, r & 15, 8 * g + m) : stage_off<TC>(kh, kTok * c + r, 8 * g + m);
+          const uint32_t bo = rd_off(par, c, 8 * g + m);
           acc[c] = mfma32(a, *(const f16x8*)(stage + bo), acc[c]);
         }
       }
@@ -405,18 +457,24 @@ __device__ __forceinline__ void gate_up_body(const FfnParams& p, int e, int it, 
           const f16x8 a = lookup8(O[2 * m], O[2 * m + 1], slot);
 #pragma unroll
           for (int c = 0; c < TC; ++c) {
-            const uint32_t bo = DB ? stage_off_db(par, kh, r & 15, 8 * g + 4 * j + m)
-                                   : stage_off<TC>(kh, kTok * c + r, 8 * g + 4 * j + m);
+            const uint32_t bo = rd_off(par, c, 8 * g + 4 * j + m);
             const f16x8 b = *(const f16x8*)(stage + bo);
             acc[c] = mfma32(a, b, acc[c]);
           }
         }
       }
     }
+    if constexpr (DMA) {
+      load_planes<Q, NT>(P, rs, cb, s + 3, voff);
+      wait_vmem_le<Q>();  // step s + 1's activations (older than these planes)
+      __syncthreads();
+      return;
+    }
     if (!DB) __syncthreads();
     if (s + 1 < ks.NSW) {
       kwin(s + 1, kk);
-      st_win(stage + (DB ? stage_off_db(par ^ 1, 0, 0, 0) : 0u), xr, kk);
+      st_win(stage + (!DB ? 0u : TC == 1 ? stage_off_db(par ^ 1, 0, 0, 0) : (uint32_t)(par ^ 1) * stage_bytes<TC>()),
+             xr, kk);
     }
     kwin(s + 2, kk);
     ld_win(xr, kk);

@@ -21,20 +21,22 @@ __global__ __launch_bounds__(kThreads) void k_gate_up(FfnParams p, int qmax, int
     return;
   const int q = p.q[2 * e];
   const uint32_t lut_bytes = 256u << qmax;
-  // items of <= 16 tokens take the double-buffered stage (one barrier per step)
-  const bool db = TC == 1 && nt <= kDbTok;
+  // double-buffered stage (one barrier per step): items of <= 16 tokens, and
+  // every 128-token item below 8 bits (its stage buffers start at kDbTable4)
+  const bool db = TC == 1 ? nt <= kDbTok : q < 8;
+  const uint32_t lb = TC == 1 ? lut_bytes : kDbTable4;
 #define MPB_GU(Q)                                                                         \
   case Q:                                                                                 \
-    if (db) gate_up_body<Q, TC, false, TC == 1, TC == 1>(p, e, it, t0, nt, lds, lut_bytes, threadIdx.x); \
+    if (db) gate_up_body<Q, TC, false, TC == 1, true>(p, e, it, t0, nt, lds, lb, threadIdx.x); \
     else gate_up_body<Q, TC>(p, e, it, t0, nt, lds, lut_bytes, threadIdx.x);            \
     break;
   switch (q < 3 || q > qmax || !tables_at_zero(lds) ? 0 : q) {
     case 3:
       if (pr3) {
-        if (db) gate_up_body<3, TC, false, TC == 1, TC == 1, true>(p, e, it, t0, nt, lds, kPairTableBytes, threadIdx.x);
+        if (db) gate_up_body<3, TC, false, TC == 1, true, true>(p, e, it, t0, nt, lds, kPairTableBytes, threadIdx.x);
         else gate_up_body<3, TC, false, TC == 1, false, true>(p, e, it, t0, nt, lds, kPairTableBytes, threadIdx.x);
       } else {
-        if (db) gate_up_body<3, TC, false, TC == 1, TC == 1>(p, e, it, t0, nt, lds, lut_bytes, threadIdx.x);
+        if (db) gate_up_body<3, TC, false, TC == 1, true>(p, e, it, t0, nt, lds, lb, threadIdx.x);
         else gate_up_body<3, TC>(p, e, it, t0, nt, lds, lut_bytes, threadIdx.x);
       }
       break;
@@ -136,7 +138,9 @@ hipError_t launch_x_to_f16(const uint16_t* x, uint16_t* y, int32_t* sc, int T, i
 // stage, and at least the epilogue's exchange area (8 waves x 16 x 64 floats).
 template <int TC>
 static size_t ffn_lds_bytes(int qmax) {
-  return std::max<size_t>((256u << qmax) + stage_bytes<TC>(), kWaves * 16 * 64 * 4);
+  const size_t single = std::max<size_t>((256u << qmax) + stage_bytes<TC>(), kWaves * 16 * 64 * 4);
+  // TC > 1: room for the double-buffered stage of blocks below 8 bits
+  return TC == 1 ? single : std::max<size_t>(single, kDbTable4 + 2 * stage_bytes<TC>());
 }
 
 // ev0/ev1 (optional): the launch itself records them at the kernel's start and
