@@ -48,8 +48,9 @@ __device__ __forceinline__ uint32_t stage_off(int kh, int t, int piece) {
 }
 template <int TC>
 constexpr int stage_bytes() { return 2 * TC * kTok * 256; }
-// 128-token items of blocks below 8 bits: table region (the 7-bit table, or
-// the 3-bit pair table) before two stage buffers, 160 KiB in all
+// Full double-buffered stages (items of more than 16 tokens, blocks below 8
+// bits): the table region (the 7-bit table, or the 3-bit pair table) is 32 KiB,
+// the two stage buffers follow it (160 KiB in all for 128-token items)
 constexpr uint32_t kDbTable4 = 32768;
 static_assert(kDbTable4 + 2 * 2 * 4 * 32 * 256 <= 163840, "two 128-token stage buffers fit the LDS");
 
@@ -309,10 +310,13 @@ struct KSplit {
 // eight lookup_pairs4 groups over both words of the lane's half-chunk, with
 // the activations staged in pair order (piece 8 g' + m: elements 4m..4m+3 of
 // both words of half-chunk 2s + g').
-template <int Q, int TC, bool CO = false, bool NT = (TC == 1), bool DB = false, bool PR = false>
+template <int Q, int TC, bool CO = false, bool NT = (TC == 1), bool DB = false, bool PR = false, bool DF = false>
 __device__ __forceinline__ void gate_up_body(const FfnParams& p, int e, int it, int t0, int nt, uint16_t* lds,
                                              uint32_t lut_bytes, int tid) {
   static_assert(!PR || Q == 3, "pair tables: 3-bit blocks");
+  // DB with one token chunk: two 16-token buffers in the 16 KiB stage region
+  // (HALF), or with DF two full 32-token buffers after a 32 KiB table region
+  constexpr bool HALF = DB && TC == 1 && !DF;
   const int lane = tid & 63, r = lane & 31, g = lane >> 5;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: plane descriptors stay scalar
   const int rg = w & 3, kh = w >> 2;
@@ -331,19 +335,19 @@ __device__ __forceinline__ void gate_up_body(const FfnParams& p, int e, int it, 
   StagePlan<TC> sp;
   const int st = tid >> 4, spc = tid & 15;
   sp.rs = rows_rsrc(p.xh, (size_t)p.T * H * 2);
-  sp.wr = !DB || TC > 1 || st < 16;
+  sp.wr = !HALF || st < 16;
 #pragma unroll
   for (int c = 0; c < TC; ++c) {
     const int t = kTok * c + st;
     sp.wl[c] = wave_has_tokens(c, st, nt);
     sp.lim[c] = t < nt ? H : 0;
     sp.off[c] = t < nt ? (uint32_t)ld_co<CO>(p.ptok + base + t) * (uint32_t)H * 2u : 0u;
-    sp.dst[0][c] = DB && TC == 1 ? stage_off_db(0, 0, t & 15, spc) : stage_off<TC>(0, t, spc);
-    sp.dst[1][c] = DB && TC == 1 ? stage_off_db(0, 1, t & 15, spc) : stage_off<TC>(1, t, spc);
+    sp.dst[0][c] = HALF ? stage_off_db(0, 0, t & 15, spc) : stage_off<TC>(0, t, spc);
+    sp.dst[1][c] = HALF ? stage_off_db(0, 1, t & 15, spc) : stage_off<TC>(1, t, spc);
   }
   // stage byte offset of piece `pc` of token chunk c, row r, in buffer par
   auto rd_off = [&](int par, int c, int pc) -> uint32_t {
-    if constexpr (DB && TC == 1) return stage_off_db(par, kh, r & 15, pc);
+    if constexpr (HALF) return stage_off_db(par, kh, r & 15, pc);
     else return (DB ? (uint32_t)par * stage_bytes<TC>() : 0u) + stage_off<TC>(kh, kTok * c + r, pc);
   };
   auto kwin = [&](int s, int (&k)[2]) {
@@ -374,8 +378,8 @@ __device__ __forceinline__ void gate_up_body(const FfnParams& p, int e, int it, 
       for (int c = 0; c < TC; ++c) {
         if (!sp.wl[c] || !sp.wr) continue;
         // the wave's first token row (slot 0, before the swizzle)
-        const uint32_t row0b = TC == 1 ? (uint32_t)par * (2 * kDbTok * 256u) + (uint32_t)i * (kDbTok * 256u)
-                                       : (uint32_t)par * stage_bytes<TC>() + (uint32_t)i * (TC * kTok * 256u);
+        const uint32_t row0b = HALF ? (uint32_t)par * (2 * kDbTok * 256u) + (uint32_t)i * (kDbTok * 256u)
+                                    : (uint32_t)par * stage_bytes<TC>() + (uint32_t)i * (TC * kTok * 256u);
         const uint32_t dst = lut_bytes + row0b + (uint32_t)(kTok * c + (st & ~3)) * 256u;
         __builtin_amdgcn_raw_ptr_buffer_load_lds(sp.rs, (lds_void*)(uintptr_t)__builtin_amdgcn_readfirstlane(dst), 16,
                                                  win_off(sp, c, k), 0, 0, 0);
@@ -473,7 +477,7 @@ __device__ __forceinline__ void gate_up_body(const FfnParams& p, int e, int it, 
     if (!DB) __syncthreads();
     if (s + 1 < ks.NSW) {
       kwin(s + 1, kk);
-      st_win(stage + (!DB ? 0u : TC == 1 ? stage_off_db(par ^ 1, 0, 0, 0) : (uint32_t)(par ^ 1) * stage_bytes<TC>()),
+      st_win(stage + (!DB ? 0u : HALF ? stage_off_db(par ^ 1, 0, 0, 0) : (uint32_t)(par ^ 1) * stage_bytes<TC>()),
              xr, kk);
     }
     kwin(s + 2, kk);
@@ -564,9 +568,12 @@ __device__ __forceinline__ void poison(float* dst, size_t ld, int rows, int cols
 // ahead of the plane load that follows it. DB (items of <= 16 tokens, TC = 1):
 // round j reads stage buffer j while the next round's window is written to
 // the other one, two barriers per step instead of four.
-template <int Q, int TC, bool CO = false, bool NT = true, bool DB = false, bool PR = false>
+template <int Q, int TC, bool CO = false, bool NT = true, bool DB = false, bool PR = false, bool DF = false>
 __device__ __forceinline__ void down_body(const FfnParams& p, int e, int it, int t0, int nt, uint16_t* lds,
                                           uint32_t lut_bytes, int tid, int ksi = 0) {
+  // DB: two 16-token round buffers in the 16 KiB stage region (HALF), or with
+  // DF two full 32-token round buffers after a 32 KiB table region
+  constexpr bool HALF = DB && !DF;
   const int lane = tid & 63, r = lane & 31, g = lane >> 5;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int rg = w & 3, kh = w >> 2;
@@ -594,20 +601,22 @@ __device__ __forceinline__ void down_body(const FfnParams& p, int e, int it, int
     const char* lo = a < b ? a : b;
     sp.rs = rows_rsrc(lo, (size_t)((a < b ? b : a) - lo) + hbytes);
     const uint32_t half = (uint32_t)((hl ? b : a) - lo);
-    sp.wr = !DB || st < 16;
+    sp.wr = !HALF || st < 16;
 #pragma unroll
     for (int c = 0; c < TC; ++c) {
       const int t = kTok * c + st;
       sp.wl[c] = wave_has_tokens(c, st, nt);
       sp.lim[c] = t < nt ? klen : 0;
       sp.off[c] = t < nt ? half + (uint32_t)(base + t) * (uint32_t)I * 2u : 0u;
-      sp.dst[0][c] = DB ? stage_off_db(0, 0, t & 15, spc) : stage_off<TC>(0, t, spc);
-      sp.dst[1][c] = DB ? stage_off_db(0, 1, t & 15, spc) : stage_off<TC>(1, t, spc);
+      sp.dst[0][c] = HALF ? stage_off_db(0, 0, t & 15, spc) : stage_off<TC>(0, t, spc);
+      sp.dst[1][c] = HALF ? stage_off_db(0, 1, t & 15, spc) : stage_off<TC>(1, t, spc);
     }
   }
   static_assert(!DB || TC == 1, "double-buffered stage: one token chunk");
   // stage buffer of round j (DB)
-  auto rbuf = [&](int j) -> uint32_t { return DB ? stage_off_db(j, 0, 0, 0) : 0u; };
+  auto rbuf = [&](int j) -> uint32_t {
+    return !DB ? 0u : HALF ? stage_off_db(j, 0, 0, 0) : (uint32_t)j * stage_bytes<TC>();
+  };
   // window (s, j): for K half i, element 64 (hc0 + i HH + 2 s + g') + 32 j + 8 m
   // (PR: round j takes pair groups 4 j .. 4 j + 3, elements 4 m .. 4 m + 3 of
   // both words, m = 4 j + (piece & 3), staged in pair order)
@@ -677,9 +686,10 @@ __device__ __forceinline__ void down_body(const FfnParams& p, int e, int it, int
       const f16x8 a = PR ? lookup_pairs4(Op[4 * j + m], slot) : lookup8(O[2 * m], O[2 * m + 1], slot);
 #pragma unroll
       for (int c = 0; c < TC; ++c) {
-        const uint32_t oh = DB ? stage_off_db(j, kh, r & 15, 4 * g + m) : stage_off<TC>(kh, kTok * c + r, 4 * g + m);
-        const uint32_t ol =
-            DB ? stage_off_db(j, kh, r & 15, 8 + 4 * g + m) : stage_off<TC>(kh, kTok * c + r, 8 + 4 * g + m);
+        const uint32_t oh = HALF ? stage_off_db(j, kh, r & 15, 4 * g + m)
+                                 : rbuf(j) + stage_off<TC>(kh, kTok * c + r, 4 * g + m);
+        const uint32_t ol = HALF ? stage_off_db(j, kh, r & 15, 8 + 4 * g + m)
+                                 : rbuf(j) + stage_off<TC>(kh, kTok * c + r, 8 + 4 * g + m);
         const f16x8 bh = *(const f16x8*)(stage + oh);
         const f16x8 bl = *(const f16x8*)(stage + ol);
         acc[c] = mfma32(a, bh, acc[c]);

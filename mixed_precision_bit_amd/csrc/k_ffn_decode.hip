@@ -1,104 +1,12 @@
 // Expert FFN kernels: gate_up + SwiGLU, down, and the weighted combine, one
-// launch each (the device code is in k_ffn_body.h). Items of 32 tokens at
-// decode sizes; gate_up takes 128-token items (TC = 4), in the XCD-interleaved
-// order, once groups hold 96 tokens on average. Few long down items are split
-// over K ranges (one workgroup per range, partial sums added by the combine).
-#include <hip/hip_ext.h>
-
-#include <algorithm>
-
-#include "k_ffn_body.h"
+// launch each (device code in k_ffn_body.h, the gate_up and down kernels and
+// their launcher in k_ffn_kernels.h). Items of 32 tokens at decode sizes;
+// gate_up takes 128-token items (TC = 4), in the XCD-interleaved order, once
+// groups hold 96 tokens on average. Few long down items are split over K
+// ranges (one workgroup per range, partial sums added by the combine).
+#include "k_ffn_kernels.h"
 
 namespace mpb {
-
-// pr3: the launch holds LDS for a 3-bit pair table and the stage, so 3-bit
-// blocks take the pair-table path
-template <int TC>
-__global__ __launch_bounds__(kThreads) void k_gate_up(FfnParams p, int qmax, int pr3) {
-  extern __shared__ __attribute__((aligned(256))) uint16_t lds[];
-  int e, it, t0, nt;
-  if (!(TC == 4 ? decode_item_xcd(p, true, p.I >> 6, e, it, t0, nt) : decode_item(p, true, p.I >> 6, e, it, t0, nt)))
-    return;
-  const int q = p.q[2 * e];
-  const uint32_t lut_bytes = 256u << qmax;
-  // double-buffered stage (one barrier per step): items of <= 16 tokens, and
-  // every 128-token item below 8 bits (its stage buffers start at kDbTable4)
-  const bool db = TC == 1 ? nt <= kDbTok : q < 8;
-  const uint32_t lb = TC == 1 ? lut_bytes : kDbTable4;
-#define MPB_GU(Q)                                                                         \
-  case Q:                                                                                 \
-    if (db) gate_up_body<Q, TC, false, TC == 1, true>(p, e, it, t0, nt, lds, lb, threadIdx.x); \
-    else gate_up_body<Q, TC>(p, e, it, t0, nt, lds, lut_bytes, threadIdx.x);            \
-    break;
-  switch (q < 3 || q > qmax || !tables_at_zero(lds) ? 0 : q) {
-    case 3:
-      if (pr3) {
-        if (db) gate_up_body<3, TC, false, TC == 1, true, true>(p, e, it, t0, nt, lds, kPairTableBytes, threadIdx.x);
-        else gate_up_body<3, TC, false, TC == 1, false, true>(p, e, it, t0, nt, lds, kPairTableBytes, threadIdx.x);
-      } else {
-        if (db) gate_up_body<3, TC, false, TC == 1, true>(p, e, it, t0, nt, lds, lb, threadIdx.x);
-        else gate_up_body<3, TC>(p, e, it, t0, nt, lds, lut_bytes, threadIdx.x);
-      }
-      break;
-    MPB_GU(4)
-    MPB_GU(5)
-    MPB_GU(6)
-    MPB_GU(7)
-    MPB_GU(8)
-#undef MPB_GU
-    default: {
-      const size_t o = (size_t)(p.offsets[e] + t0) * p.I + it * 64;
-      for (int i = threadIdx.x; i < nt * 64; i += blockDim.x) {
-        p.hhi[o + (size_t)(i >> 6) * p.I + (i & 63)] = 0x7e00;  // fp16 NaN
-        p.hlo[o + (size_t)(i >> 6) * p.I + (i & 63)] = 0;
-      }
-    }
-  }
-}
-
-
-// NT: non-temporal plane loads (decode-size batches, see load_planes)
-template <int TC, bool NT>
-__global__ __launch_bounds__(kThreads) void k_down(FfnParams p, int qmax, int pr3) {
-  extern __shared__ __attribute__((aligned(256))) uint16_t lds[];
-  // workgroup b: K range b % dn_split of tile (b / dn_split) % ntile of item
-  // (b / dn_split) / ntile
-  const int ntile = (p.H + 127) >> 7;
-  const int b = blockIdx.x / p.dn_split, ksi = blockIdx.x - b * p.dn_split;
-  const int item = b / ntile, it = b - item * ntile;
-  int e, t0, nt;
-  if (!item_of(p, false, item, e, t0, nt)) return;
-  const int q = p.q[2 * e + 1];
-  const uint32_t lut_bytes = 256u << qmax;
-  const bool db = TC == 1 && nt <= kDbTok;
-#define MPB_DN(Q)                                                                                       \
-  case Q:                                                                                               \
-    if (db) down_body<Q, TC, false, NT, TC == 1>(p, e, it, t0, nt, lds, lut_bytes, threadIdx.x, ksi);   \
-    else down_body<Q, TC, false, NT>(p, e, it, t0, nt, lds, lut_bytes, threadIdx.x, ksi);              \
-    break;
-  switch (q < 3 || q > qmax || !tables_at_zero(lds) ? 0 : q) {
-    case 3:
-      if (pr3) {
-        if (db) down_body<3, TC, false, NT, TC == 1, true>(p, e, it, t0, nt, lds, kPairTableBytes, threadIdx.x, ksi);
-        else down_body<3, TC, false, NT, false, true>(p, e, it, t0, nt, lds, kPairTableBytes, threadIdx.x, ksi);
-      } else {
-        if (db) down_body<3, TC, false, NT, TC == 1>(p, e, it, t0, nt, lds, lut_bytes, threadIdx.x, ksi);
-        else down_body<3, TC, false, NT>(p, e, it, t0, nt, lds, lut_bytes, threadIdx.x, ksi);
-      }
-      break;
-    MPB_DN(4)
-    MPB_DN(5)
-    MPB_DN(6)
-    MPB_DN(7)
-    MPB_DN(8)
-#undef MPB_DN
-    default: {
-      const int n0 = it * 128;
-      poison(p.y + (size_t)ksi * p.T * (p.K + p.S) * p.H + (size_t)(p.offsets[e] + t0) * p.H + n0, p.H, nt,
-             min(128, p.H - n0));
-    }
-  }
-}
 
 // ---------------------------------------------------------------- combine
 // out[t] = sum_k w_tk * y[entry(t,k)] + sum_s y[entry(t,K+s)], in that order.
@@ -136,60 +44,21 @@ hipError_t launch_x_to_f16(const uint16_t* x, uint16_t* y, int32_t* sc, int T, i
 
 // LDS per launch: the table region for the highest committed bitwidth plus the
 // stage, and at least the epilogue's exchange area (8 waves x 16 x 64 floats).
-template <int TC>
-static size_t ffn_lds_bytes(int qmax) {
-  const size_t single = std::max<size_t>((256u << qmax) + stage_bytes<TC>(), kWaves * 16 * 64 * 4);
-  // TC > 1: room for the double-buffered stage of blocks below 8 bits
-  return TC == 1 ? single : std::max<size_t>(single, kDbTable4 + 2 * stage_bytes<TC>());
-}
-
-// ev0/ev1 (optional): the launch itself records them at the kernel's start and
-// end (hipExtLaunchKernelGGL), for timing the kernel alone.
-template <int TC, bool GU, bool NT = true>
-static hipError_t launch_tc(const FfnParams& p, int qmax, hipStream_t s, hipEvent_t ev0 = nullptr,
-                            hipEvent_t ev1 = nullptr) {
-  static unsigned long long lds_raised = 0;  // devices on which this kernel's LDS limit is raised
-  const void* fn;
-  if constexpr (GU) fn = (const void*)k_gate_up<TC>;
-  else fn = (const void*)k_down<TC, NT>;
-  const hipError_t e = raise_lds_limit(fn, (int)std::max<size_t>(ffn_lds_bytes<TC>(8), kPairTableBytes + stage_bytes<TC>()),
-                                       lds_raised);
-  if (e != hipSuccess) return e;
-  // every launch holds room for a 3-bit pair table and the stage (registers,
-  // not LDS, bound these kernels' occupancy: two workgroups per CU at one
-  // token chunk, one at four), so a block committed at 3 bits later, under a
-  // captured graph, still takes the pair path
-  constexpr size_t kPairLds = kPairTableBytes + stage_bytes<TC>();
-  const size_t shmem = std::max(ffn_lds_bytes<TC>(qmax), kPairLds);
-  const int pr3 = 1;
-  // 128-token items take the XCD-interleaved order (decode_item_xcd)
-  const int items = TC == 4 ? (p.max_items + 7) / 8 * 8 : p.max_items;
-  if constexpr (GU) {
-    if (ev0 && ev1)
-      hipExtLaunchKernelGGL(k_gate_up<TC>, dim3(items * (p.I >> 6)), dim3(kThreads), shmem, s, ev0, ev1, 0, p, qmax,
-                            pr3);
-    else
-      hipLaunchKernelGGL(k_gate_up<TC>, dim3(items * (p.I >> 6)), dim3(kThreads), shmem, s, p, qmax, pr3);
-  } else {
-    const dim3 grid(p.max_items * ((p.H + 127) >> 7) * p.dn_split);
-    if (ev0 && ev1)
-      hipExtLaunchKernelGGL((k_down<TC, NT>), grid, dim3(kThreads), shmem, s, ev0, ev1, 0, p, qmax, pr3);
-    else
-      hipLaunchKernelGGL((k_down<TC, NT>), grid, dim3(kThreads), shmem, s, p, qmax, pr3);
-  }
-  return hipGetLastError();
-}
+// Full double-buffered stages pay off where groups hold several 32-token
+// items (8 or more tokens per routed expert on average, or 128-token items);
+// at smaller batches the larger kernel they need costs more than they save
+// (qwen15moe decode: +1 %, with no item taking them).
+static bool use_df(const FfnParams& p) { return (long long)p.T * p.K >= 8ll * p.E; }
 
 hipError_t launch_gate_up(const FfnParams& p, int qmax, int tc, hipStream_t s, hipEvent_t ev0, hipEvent_t ev1) {
-  switch (tc) {
-    case 1: return launch_tc<1, true>(p, qmax, s, ev0, ev1);
-    case 4: return launch_tc<4, true>(p, qmax, s, ev0, ev1);
-    default: return hipErrorInvalidValue;
-  }
+  if (tc == 4 || use_df(p)) return launch_gate_up_df(p, qmax, tc, s, ev0, ev1);
+  if (tc != 1) return hipErrorInvalidValue;
+  return launch_tc<1, true, true, false>(p, qmax, s, ev0, ev1);
 }
 
 hipError_t launch_down(const FfnParams& p, int qmax, bool nt, hipStream_t s, hipEvent_t ev0, hipEvent_t ev1) {
-  return nt ? launch_tc<1, false, true>(p, qmax, s, ev0, ev1) : launch_tc<1, false, false>(p, qmax, s, ev0, ev1);
+  if (!nt || use_df(p)) return launch_down_df(p, qmax, nt, s, ev0, ev1);
+  return launch_tc<1, false, true, false>(p, qmax, s, ev0, ev1);
 }
 
 hipError_t launch_combine(const FfnParams& p, hipStream_t s) {

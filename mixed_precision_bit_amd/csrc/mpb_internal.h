@@ -137,6 +137,9 @@ hipError_t launch_x_to_f16(const uint16_t* x, uint16_t* y, int32_t* sc, int T, i
 // ev0/ev1: optional events the launch records at the kernel's start and end
 hipError_t launch_gate_up(const FfnParams& p, int qmax, int tc, hipStream_t s, hipEvent_t ev0 = nullptr,
                           hipEvent_t ev1 = nullptr);
+// the variants with full double-buffered stages (their own translation unit)
+hipError_t launch_gate_up_df(const FfnParams& p, int qmax, int tc, hipStream_t s, hipEvent_t ev0, hipEvent_t ev1);
+hipError_t launch_down_df(const FfnParams& p, int qmax, bool nt, hipStream_t s, hipEvent_t ev0, hipEvent_t ev1);
 // nt: non-temporal plane loads (decode-size batches, one item per group)
 // ev0/ev1: optional events the launch records at the kernel's start and end
 hipError_t launch_down(const FfnParams& p, int qmax, bool nt, hipStream_t s, hipEvent_t ev0 = nullptr,
