@@ -32,14 +32,39 @@ HBM_PEAK_GBS = 8000.0
 MFMA_PEAK_TFLOPS = 2500.0  # dense fp16 MFMA
 METRIC = "MoE-layer tokens/s and achieved HBM GB/s (% of peak) at mixed bitwidths"
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_ffn_qwen15moe_decode.md")
-KERNEL_SRCS = ["k_ffn_decode.hip", "k_ffn_body.h", "mpb_device.h"]
+KERNEL_SRCS = ["k_ffn_decode.hip", "k_ffn_decode_df.hip", "k_ffn_kernels.h", "k_ffn_body.h", "mpb_device.h"]
+
+
+def _code_only(text):
+    """C++ source without comments and blank lines (string literals kept), so
+    that edits of comments leave the hash of the kernels' code unchanged."""
+    out, i, n = [], 0, len(text)
+    while i < n:
+        if text.startswith("//", i):
+            j = text.find("\n", i)
+            i = n if j < 0 else j
+        elif text.startswith("/*", i):
+            j = text.find("*/", i + 2)
+            i = n if j < 0 else j + 2
+        elif text[i] == '"':
+            j = i + 1
+            while j < n and text[j] != '"':
+                j += 2 if text[j] == "\\" else 1
+            out.append(text[i:j + 1])
+            i = j + 1
+        else:
+            out.append(text[i])
+            i += 1
+    return "\n".join(ln.rstrip() for ln in "".join(out).splitlines() if ln.strip())
 
 
 def kernel_hash():
+    """Hash of the FFN kernels' code (comments excluded): the traffic profile
+    read into the bench line must have been taken of this code."""
     h = hashlib.sha256()
     for f in KERNEL_SRCS:
-        with open(os.path.join(ROOT, "mixed_precision_bit_amd", "csrc", f), "rb") as fh:
-            h.update(fh.read())
+        with open(os.path.join(ROOT, "mixed_precision_bit_amd", "csrc", f), encoding="utf-8") as fh:
+            h.update(_code_only(fh.read()).encode())
     return h.hexdigest()[:16]
 
 

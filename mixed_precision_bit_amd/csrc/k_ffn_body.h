@@ -166,7 +166,7 @@ struct StagePlan {
   int lim[TC];              // elements of the row the slot reads (0 for token slots >= nt)
   uint32_t dst[2][TC];      // stage byte offsets per K half
   bool wl[TC];              // the wave holds a token slot < nt in chunk c (wave-uniform)
-  bool wr;                  // the thread's slots land in the stage (DB: slots 16..31 do not)
+  bool wr;                  // the thread's slots land in the stage (16-token buffers: slots 16..31 do not)
 };
 
 // wave-uniform: some token slot of the calling wave's chunk c is live (a wave
@@ -565,9 +565,11 @@ __device__ __forceinline__ void poison(float* dst, size_t ld, int rows, int cols
 // one per word of the half-chunk; piece p = 8 hl + 4 g' + m of a token holds
 // elements 32 j + 8 m .. + 7 of half-chunk 2 s + g', hi (hl = 0) or lo
 // (hl = 1), for round j. Each window is loaded one step before it is staged,
-// ahead of the plane load that follows it. DB (items of <= 16 tokens, TC = 1):
-// round j reads stage buffer j while the next round's window is written to
-// the other one, two barriers per step instead of four.
+// ahead of the plane load that follows it. DB (TC = 1): round j reads stage
+// buffer j while the next round's window is written to the other one, two
+// barriers per step instead of four; the buffers are 16-token halves of the
+// stage region for items of <= 16 tokens, or with DF full 32-token buffers
+// after a 32 KiB table region.
 template <int Q, int TC, bool CO = false, bool NT = true, bool DB = false, bool PR = false, bool DF = false>
 __device__ __forceinline__ void down_body(const FfnParams& p, int e, int it, int t0, int nt, uint16_t* lds,
                                           uint32_t lut_bytes, int tid, int ksi = 0) {
