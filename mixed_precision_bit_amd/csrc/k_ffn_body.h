@@ -243,26 +243,56 @@ __device__ __forceinline__ void store_window_pairs(char* stage, const uint4 (&v)
     }
 }
 
-// Item `item` of the gate_up (gu) or down list: its group e, first token t0
-// and token count nt; false past the end of the list.
-__device__ __forceinline__ bool item_of(const FfnParams& p, bool gu, int item, int& e, int& t0, int& nt) {
-  if (item >= p.n_items[gu ? 0 : 1]) return false;
-  const int v = (gu ? p.items : p.items_dn)[item];
+// A work item as the FFN bodies take it: group e, the item's first token t0
+// within the group and its token count nt, its first grouped entry base =
+// offsets[e] + t0, the block's committed bitwidth q, its plane pages and its
+// row of table-image pointers (b = 3..8; the body reads the one it needs
+// after its first plane loads are out, so that round trip overlaps them).
+struct Item {
+  int e, t0, nt, base, q;
+  const uint32_t* planes[8];
+  const uint16_t* const* luts;
+};
+
+// The group-indexed fields of an item: token count, offset, bitwidth and page
+// pointers, loaded together (one round trip).
+template <bool CO>
+__device__ __forceinline__ void item_fields(const FfnParams& p, int blk, int e, int t0, int tpi, Item& m) {
+  const int cnt = ld_co<CO>(p.counts + e);
+  const int off = ld_co<CO>(p.offsets + e);
+  m.q = p.q[blk];
+#pragma unroll
+  for (int k = 0; k < 8; ++k) m.planes[k] = p.planes[blk * 8 + k];
+  m.luts = p.luts + blk * 6;
+  m.e = e;
+  m.t0 = t0;
+  m.nt = min(cnt - t0, tpi);
+  m.base = off + t0;
+}
+
+// Item `item` of the gate_up (gu) or down list; false past the end of the
+// list. The list entry is read together with the list length (at an index
+// clamped to the list's capacity, so the read stays inside it), then the
+// group's fields.
+__device__ __forceinline__ bool item_of(const FfnParams& p, bool gu, int item, Item& m) {
+  const int n = p.n_items[gu ? 0 : 1];
+  const int v = (gu ? p.items : p.items_dn)[min(item, p.max_items - 1)];
+  // a list entry is never negative (group << 16 | split); testing it too
+  // keeps its load ahead of the test, beside the length's
+  if ((item >= n) | (v < 0)) return false;
   const int tpi = gu ? p.tpi : p.tpi_dn;
-  e = v >> 16;
-  t0 = (v & 0xffff) * tpi;
-  nt = min(p.counts[e] - t0, tpi);
+  const int e = v >> 16;
+  item_fields<false>(p, 2 * e + (gu ? 0 : 1), e, (v & 0xffff) * tpi, tpi, m);
   return true;
 }
 
 // Work item of a launch: workgroup id = item * ntile + tile, so the
 // consecutive workgroups that the dispatcher spreads over the chip carry the
 // tiles of one item and every workgroup below n_items * ntile has tokens.
-__device__ __forceinline__ bool decode_item(const FfnParams& p, bool gu, int ntile, int& e, int& tile, int& t0,
-                                            int& nt) {
+__device__ __forceinline__ bool decode_item(const FfnParams& p, bool gu, int ntile, int& tile, Item& m) {
   const int item = blockIdx.x / ntile;
   tile = blockIdx.x - item * ntile;
-  return item_of(p, gu, item, e, t0, nt);
+  return item_of(p, gu, item, m);
 }
 
 // The same items for launches that stream activations from L2 (128-token
@@ -272,11 +302,10 @@ __device__ __forceinline__ bool decode_item(const FfnParams& p, bool gu, int nti
 // activations to every tile; items are dealt to the XCDs in turn, which keeps
 // the bitwidth mix (the list is ordered by bitwidth) the same on every XCD.
 // Needs a grid of 8 * ceil(max_items / 8) * ntile workgroups.
-__device__ __forceinline__ bool decode_item_xcd(const FfnParams& p, bool gu, int ntile, int& e, int& tile, int& t0,
-                                                int& nt) {
+__device__ __forceinline__ bool decode_item_xcd(const FfnParams& p, bool gu, int ntile, int& tile, Item& m) {
   const int k = blockIdx.x >> 3, li = k / ntile;
   tile = k - li * ntile;
-  return item_of(p, gu, 8 * li + (blockIdx.x & 7), e, t0, nt);
+  return item_of(p, gu, 8 * li + (blockIdx.x & 7), m);
 }
 
 // K split: a row has HC = Kd / 64 half-chunks; half 0 takes the first HH (even,
@@ -311,7 +340,7 @@ struct KSplit {
 // the activations staged in pair order (piece 8 g' + m: elements 4m..4m+3 of
 // both words of half-chunk 2s + g').
 template <int Q, int TC, bool CO = false, bool NT = (TC == 1), bool DB = false, bool PR = false, bool DF = false>
-__device__ __forceinline__ void gate_up_body(const FfnParams& p, int e, int it, int t0, int nt, uint16_t* lds,
+__device__ __forceinline__ void gate_up_body(const FfnParams& p, const Item& m, int it, uint16_t* lds,
                                              uint32_t lut_bytes, int tid) {
   static_assert(!PR || Q == 3, "pair tables: 3-bit blocks");
   // DB with one token chunk: two 16-token buffers in the 16 KiB stage region
@@ -324,9 +353,8 @@ __device__ __forceinline__ void gate_up_body(const FfnParams& p, int e, int it, 
   const KSplit ks(H);
   const int c0 = it * 64 + (rg & 1) * 32;
   const int row0 = (rg >> 1) * I + c0;
-  const int base = ld_co<CO>(p.offsets + e) + t0;
+  const int nt = m.nt, base = m.base;
   const uint32_t slot = PR ? pair_slot(r, rg) : lut_slot(r, rg);
-  const int blk = 2 * e;
   char* stage = (char*)lds + lut_bytes;
 
   // staging: piece p = 8 g' + 4 j + m of a token holds elements 32 j + 8 m .. + 7
@@ -336,15 +364,23 @@ __device__ __forceinline__ void gate_up_body(const FfnParams& p, int e, int it, 
   const int st = tid >> 4, spc = tid & 15;
   sp.rs = rows_rsrc(p.xh, (size_t)p.T * H * 2);
   sp.wr = !HALF || st < 16;
+  // the token ids are loaded first (the entry of the item's last token stands
+  // in for slots past it) and turned into row offsets only after the table
+  // and the first planes are requested, so those loads do not wait for them
+  int tok[TC];
 #pragma unroll
   for (int c = 0; c < TC; ++c) {
     const int t = kTok * c + st;
+    tok[c] = ld_co<CO>(p.ptok + base + min(t, nt - 1));
     sp.wl[c] = wave_has_tokens(c, st, nt);
     sp.lim[c] = t < nt ? H : 0;
-    sp.off[c] = t < nt ? (uint32_t)ld_co<CO>(p.ptok + base + t) * (uint32_t)H * 2u : 0u;
     sp.dst[0][c] = HALF ? stage_off_db(0, 0, t & 15, spc) : stage_off<TC>(0, t, spc);
     sp.dst[1][c] = HALF ? stage_off_db(0, 1, t & 15, spc) : stage_off<TC>(1, t, spc);
   }
+  auto row_offsets = [&]() {
+#pragma unroll
+    for (int c = 0; c < TC; ++c) sp.off[c] = kTok * c + st < nt ? (uint32_t)tok[c] * (uint32_t)H * 2u : 0u;
+  };
   // stage byte offset of piece `pc` of token chunk c, row r, in buffer par
   auto rd_off = [&](int par, int c, int pc) -> uint32_t {
     if constexpr (HALF) return stage_off_db(par, kh, r & 15, pc);
@@ -393,7 +429,7 @@ __device__ __forceinline__ void gate_up_body(const FfnParams& p, int e, int it, 
   const int ce = kh ? NC : ks.HH >> 1;
   rsrc_t rs[Q];
 #pragma unroll
-  for (int q = 0; q < Q; ++q) rs[q] = tile_rsrc(p.planes[blk * 8 + q], (size_t)(row0 >> 5) * NC * 512, ce * 512);
+  for (int q = 0; q < Q; ++q) rs[q] = tile_rsrc(m.planes[q], (size_t)(row0 >> 5) * NC * 512, ce * 512);
   const int voff = 16 * r + 8 * g;
 
   uint2 PA[Q], PB[Q], PC[Q];
@@ -401,26 +437,28 @@ __device__ __forceinline__ void gate_up_body(const FfnParams& p, int e, int it, 
   int kk[2];
   // PR: the 3-bit image goes to the stage region, which is staged only after
   // the pair table has been built from it
-  load_table_image<Q>(p.luts[blk * 6 + (Q - 3)] + (size_t)it * (128u << Q), w, lane, PR ? lut_bytes : 0u);
+  // step 0's planes first: their pointers are known a round trip before the
+  // table's
+  load_planes<Q, NT>(PA, rs, cb, 0, voff);
+  load_table_image<Q>(m.luts[Q - 3] + (size_t)it * (128u << Q), w, lane, PR ? lut_bytes : 0u);
+  row_offsets();
   if constexpr (DMA) {
     dma_win(0, 0);
-    load_planes<Q, NT>(PA, rs, cb, 0, voff);
     load_planes<Q, NT>(PB, rs, cb, 1, voff);
     load_planes<Q, NT>(PC, rs, cb, 2, voff);
-    wait_vmem_le<2 * Q>();  // the table, step 0's activations and planes
+    wait_vmem_le<2 * Q>();  // step 0's planes, the table and step 0's activations
     __syncthreads();
   } else {
     kwin(0, kk);
     ld_win(xr, kk);
-    load_planes<Q, NT>(PA, rs, cb, 0, voff);
-    wait_vmem_all();
+    load_planes<Q, NT>(PB, rs, cb, 1, voff);
+    wait_vmem_le<Q>();  // step 0's planes, the table and step 0's activations
     if constexpr (PR) {
       __syncthreads();
       build_pair_table3(lut_bytes, tid);
       __syncthreads();
     }
     st_win(stage, xr, kk);
-    load_planes<Q, NT>(PB, rs, cb, 1, voff);
     kwin(1, kk);
     ld_win(xr, kk);
     load_planes<Q, NT>(PC, rs, cb, 2, voff);
@@ -571,7 +609,7 @@ __device__ __forceinline__ void poison(float* dst, size_t ld, int rows, int cols
 // stage region for items of <= 16 tokens, or with DF full 32-token buffers
 // after a 32 KiB table region.
 template <int Q, int TC, bool CO = false, bool NT = true, bool DB = false, bool PR = false, bool DF = false>
-__device__ __forceinline__ void down_body(const FfnParams& p, int e, int it, int t0, int nt, uint16_t* lds,
+__device__ __forceinline__ void down_body(const FfnParams& p, const Item& m, int it, uint16_t* lds,
                                           uint32_t lut_bytes, int tid, int ksi = 0) {
   // DB: two 16-token round buffers in the 16 KiB stage region (HALF), or with
   // DF two full 32-token round buffers after a 32 KiB table region
@@ -587,10 +625,9 @@ __device__ __forceinline__ void down_body(const FfnParams& p, int e, int it, int
   const KSplit ks((hc1 - hc0) * 64);
   const int n0 = it * 128 + rg * 32;
   const bool active = n0 < H;
-  const int base = ld_co<CO>(p.offsets + e) + t0;
+  const int nt = m.nt, base = m.base;
   static_assert(!PR || Q == 3, "pair tables: 3-bit blocks");
   const uint32_t slot = PR ? pair_slot(r, rg) : lut_slot(r, rg);
-  const int blk = 2 * e + 1;
   char* stage = (char*)lds + lut_bytes;
 
   StagePlan<TC> sp;
@@ -641,13 +678,15 @@ __device__ __forceinline__ void down_body(const FfnParams& p, int e, int it, int
   rsrc_t rs[Q];
 #pragma unroll
   for (int q = 0; q < Q; ++q)
-    rs[q] = tile_rsrc(p.planes[blk * 8 + q], active ? (size_t)(n0 >> 5) * NC * 512 : 0, active ? ce * 512 : 0);
+    rs[q] = tile_rsrc(m.planes[q], active ? (size_t)(n0 >> 5) * NC * 512 : 0, active ? ce * 512 : 0);
   const int voff = 16 * r + 8 * g;
 
   uint2 PA[Q], PB[Q], PC[Q];
   uint4 ha[2][TC], hb[2][TC];
   int ka[2], kb[2];
-  load_table_image<Q>(p.luts[blk * 6 + (Q - 3)] + (size_t)it * (128u << Q), w, lane, PR ? lut_bytes : 0u);
+  // (requesting steps 1 and 2's planes before this first wait as well, or
+  // step 0's planes before the table, measured 1-3 % slower)
+  load_table_image<Q>(m.luts[Q - 3] + (size_t)it * (128u << Q), w, lane, PR ? lut_bytes : 0u);
   kwin(0, 0, ka);
   ld_win(ha, ka);
   load_planes<Q, NT>(PA, rs, cb, 0, voff);
