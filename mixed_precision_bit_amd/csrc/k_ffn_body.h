@@ -340,7 +340,7 @@ struct KSplit {
 // the activations staged in pair order (piece 8 g' + m: elements 4m..4m+3 of
 // both words of half-chunk 2s + g').
 template <int Q, int TC, bool CO = false, bool NT = (TC == 1), bool DB = false, bool PR = false, bool DF = false>
-__device__ __forceinline__ void gate_up_body(const FfnParams& p, const Item& m, int it, uint16_t* lds,
+__device__ __forceinline__ void gate_up_body(const FfnParams& p, const Item& wi, int it, uint16_t* lds,
                                              uint32_t lut_bytes, int tid) {
   static_assert(!PR || Q == 3, "pair tables: 3-bit blocks");
   // DB with one token chunk: two 16-token buffers in the 16 KiB stage region
@@ -353,7 +353,7 @@ __device__ __forceinline__ void gate_up_body(const FfnParams& p, const Item& m, 
   const KSplit ks(H);
   const int c0 = it * 64 + (rg & 1) * 32;
   const int row0 = (rg >> 1) * I + c0;
-  const int nt = m.nt, base = m.base;
+  const int nt = wi.nt, base = wi.base;
   const uint32_t slot = PR ? pair_slot(r, rg) : lut_slot(r, rg);
   char* stage = (char*)lds + lut_bytes;
 
@@ -429,7 +429,7 @@ __device__ __forceinline__ void gate_up_body(const FfnParams& p, const Item& m, 
   const int ce = kh ? NC : ks.HH >> 1;
   rsrc_t rs[Q];
 #pragma unroll
-  for (int q = 0; q < Q; ++q) rs[q] = tile_rsrc(m.planes[q], (size_t)(row0 >> 5) * NC * 512, ce * 512);
+  for (int q = 0; q < Q; ++q) rs[q] = tile_rsrc(wi.planes[q], (size_t)(row0 >> 5) * NC * 512, ce * 512);
   const int voff = 16 * r + 8 * g;
 
   uint2 PA[Q], PB[Q], PC[Q];
@@ -440,7 +440,7 @@ __device__ __forceinline__ void gate_up_body(const FfnParams& p, const Item& m, 
   // step 0's planes first: their pointers are known a round trip before the
   // table's
   load_planes<Q, NT>(PA, rs, cb, 0, voff);
-  load_table_image<Q>(m.luts[Q - 3] + (size_t)it * (128u << Q), w, lane, PR ? lut_bytes : 0u);
+  load_table_image<Q>(wi.luts[Q - 3] + (size_t)it * (128u << Q), w, lane, PR ? lut_bytes : 0u);
   row_offsets();
   if constexpr (DMA) {
     dma_win(0, 0);
@@ -599,7 +599,9 @@ __device__ __forceinline__ void poison(float* dst, size_t ld, int rows, int cols
 // ---------------------------------------------------------------- down
 // Waves w and w+4 take output rows n0 + 32 (w % 4) .. +31 over the two K
 // halves. B operand = h as its fp16 hi and lo parts, two MFMAs per word and
-// token chunk into the same fp32 accumulator. A step is staged in two rounds,
+// token chunk into the same fp32 accumulator; items of <= 16 tokens put hi in
+// MFMA columns 0..15 and lo in columns 16..31 instead (one MFMA per word),
+// and each column adds its lo partner after the K loop. A step is staged in two rounds,
 // one per word of the half-chunk; piece p = 8 hl + 4 g' + m of a token holds
 // elements 32 j + 8 m .. + 7 of half-chunk 2 s + g', hi (hl = 0) or lo
 // (hl = 1), for round j. Each window is loaded one step before it is staged,
@@ -609,7 +611,7 @@ __device__ __forceinline__ void poison(float* dst, size_t ld, int rows, int cols
 // stage region for items of <= 16 tokens, or with DF full 32-token buffers
 // after a 32 KiB table region.
 template <int Q, int TC, bool CO = false, bool NT = true, bool DB = false, bool PR = false, bool DF = false>
-__device__ __forceinline__ void down_body(const FfnParams& p, const Item& m, int it, uint16_t* lds,
+__device__ __forceinline__ void down_body(const FfnParams& p, const Item& wi, int it, uint16_t* lds,
                                           uint32_t lut_bytes, int tid, int ksi = 0) {
   // DB: two 16-token round buffers in the 16 KiB stage region (HALF), or with
   // DF two full 32-token round buffers after a 32 KiB table region
@@ -625,7 +627,7 @@ __device__ __forceinline__ void down_body(const FfnParams& p, const Item& m, int
   const KSplit ks((hc1 - hc0) * 64);
   const int n0 = it * 128 + rg * 32;
   const bool active = n0 < H;
-  const int nt = m.nt, base = m.base;
+  const int nt = wi.nt, base = wi.base;
   static_assert(!PR || Q == 3, "pair tables: 3-bit blocks");
   const uint32_t slot = PR ? pair_slot(r, rg) : lut_slot(r, rg);
   char* stage = (char*)lds + lut_bytes;
@@ -678,7 +680,7 @@ __device__ __forceinline__ void down_body(const FfnParams& p, const Item& m, int
   rsrc_t rs[Q];
 #pragma unroll
   for (int q = 0; q < Q; ++q)
-    rs[q] = tile_rsrc(m.planes[q], active ? (size_t)(n0 >> 5) * NC * 512 : 0, active ? ce * 512 : 0);
+    rs[q] = tile_rsrc(wi.planes[q], active ? (size_t)(n0 >> 5) * NC * 512 : 0, active ? ce * 512 : 0);
   const int voff = 16 * r + 8 * g;
 
   uint2 PA[Q], PB[Q], PC[Q];
@@ -686,7 +688,7 @@ __device__ __forceinline__ void down_body(const FfnParams& p, const Item& m, int
   int ka[2], kb[2];
   // (requesting steps 1 and 2's planes before this first wait as well, or
   // step 0's planes before the table, measured 1-3 % slower)
-  load_table_image<Q>(m.luts[Q - 3] + (size_t)it * (128u << Q), w, lane, PR ? lut_bytes : 0u);
+  load_table_image<Q>(wi.luts[Q - 3] + (size_t)it * (128u << Q), w, lane, PR ? lut_bytes : 0u);
   kwin(0, 0, ka);
   ld_win(ha, ka);
   load_planes<Q, NT>(PA, rs, cb, 0, voff);
@@ -727,14 +729,19 @@ __device__ __forceinline__ void down_body(const FfnParams& p, const Item& m, int
       const f16x8 a = PR ? lookup_pairs4(Op[4 * j + m], slot) : lookup8(O[2 * m], O[2 * m + 1], slot);
 #pragma unroll
       for (int c = 0; c < TC; ++c) {
-        const uint32_t oh = HALF ? stage_off_db(j, kh, r & 15, 4 * g + m)
-                                 : rbuf(j) + stage_off<TC>(kh, kTok * c + r, 4 * g + m);
-        const uint32_t ol = HALF ? stage_off_db(j, kh, r & 15, 8 + 4 * g + m)
-                                 : rbuf(j) + stage_off<TC>(kh, kTok * c + r, 8 + 4 * g + m);
-        const f16x8 bh = *(const f16x8*)(stage + oh);
-        const f16x8 bl = *(const f16x8*)(stage + ol);
-        acc[c] = mfma32(a, bh, acc[c]);
-        acc[c] = mfma32(a, bl, acc[c]);
+        if constexpr (HALF) {
+          // columns 0..15: h hi of the item's tokens, 16..31: h lo of the
+          // same tokens (one MFMA and one operand read instead of two)
+          const f16x8 b = *(const f16x8*)(stage + stage_off_db(j, kh, r & 15, 8 * (r >> 4) + 4 * g + m));
+          acc[c] = mfma32(a, b, acc[c]);
+        } else {
+          const uint32_t oh = rbuf(j) + stage_off<TC>(kh, kTok * c + r, 4 * g + m);
+          const uint32_t ol = rbuf(j) + stage_off<TC>(kh, kTok * c + r, 8 + 4 * g + m);
+          const f16x8 bh = *(const f16x8*)(stage + oh);
+          const f16x8 bl = *(const f16x8*)(stage + ol);
+          acc[c] = mfma32(a, bh, acc[c]);
+          acc[c] = mfma32(a, bl, acc[c]);
+        }
       }
     }
     if (!DB) __syncthreads();
@@ -766,6 +773,12 @@ __device__ __forceinline__ void down_body(const FfnParams& p, const Item& m, int
   if (s < ks.NSW) step(s, PA);
   if (s + 1 < ks.NSW) step(s + 1, PB);
 
+  // 16-token buffers: each column c < 16 takes its h lo partner from column
+  // c + 16, so column c holds the whole sum over the wave's K half
+  if constexpr (HALF) {
+#pragma unroll
+    for (int v = 0; v < 16; ++v) acc[0][v] += __shfl_xor(acc[0][v], 16);
+  }
   // second K half -> first through LDS, one token chunk at a time; layout
   // [row group][v][lane]
   float* xb = (float*)lds;

@@ -17,37 +17,37 @@ namespace mpb {
 // chunk), 2 two full buffers after a 32 KiB table region (blocks below 8
 // bits); 1 and 2 need one barrier per step (gate_up) or round (down).
 template <int Q, int TC, bool PRV, bool DF>
-__device__ __forceinline__ void gu_modes(const FfnParams& p, const Item& m, int it, uint16_t* lds, uint32_t lb,
+__device__ __forceinline__ void gu_modes(const FfnParams& p, const Item& wi, int it, uint16_t* lds, uint32_t lb,
                                          int mode) {
   if constexpr (TC == 1) {
     if (mode == 1) {
-      gate_up_body<Q, 1, false, true, true, PRV, false>(p, m, it, lds, lb, threadIdx.x);
+      gate_up_body<Q, 1, false, true, true, PRV, false>(p, wi, it, lds, lb, threadIdx.x);
       return;
     }
   }
   if constexpr (DF && Q < 8) {
     if (mode == 2) {
-      gate_up_body<Q, TC, false, TC == 1, true, PRV, true>(p, m, it, lds, kDbTable4, threadIdx.x);
+      gate_up_body<Q, TC, false, TC == 1, true, PRV, true>(p, wi, it, lds, kDbTable4, threadIdx.x);
       return;
     }
   }
-  gate_up_body<Q, TC, false, TC == 1, false, PRV, false>(p, m, it, lds, lb, threadIdx.x);
+  gate_up_body<Q, TC, false, TC == 1, false, PRV, false>(p, wi, it, lds, lb, threadIdx.x);
 }
 
 template <int Q, int TC, bool NT, bool PRV, bool DF>
-__device__ __forceinline__ void dn_modes(const FfnParams& p, const Item& m, int it, uint16_t* lds, uint32_t lb,
+__device__ __forceinline__ void dn_modes(const FfnParams& p, const Item& wi, int it, uint16_t* lds, uint32_t lb,
                                          int mode, int ksi) {
   if (mode == 1) {
-    down_body<Q, TC, false, NT, true, PRV, false>(p, m, it, lds, lb, threadIdx.x, ksi);
+    down_body<Q, TC, false, NT, true, PRV, false>(p, wi, it, lds, lb, threadIdx.x, ksi);
     return;
   }
   if constexpr (DF && Q < 8) {
     if (mode == 2) {
-      down_body<Q, TC, false, NT, true, PRV, true>(p, m, it, lds, kDbTable4, threadIdx.x, ksi);
+      down_body<Q, TC, false, NT, true, PRV, true>(p, wi, it, lds, kDbTable4, threadIdx.x, ksi);
       return;
     }
   }
-  down_body<Q, TC, false, NT, false, PRV, false>(p, m, it, lds, lb, threadIdx.x, ksi);
+  down_body<Q, TC, false, NT, false, PRV, false>(p, wi, it, lds, lb, threadIdx.x, ksi);
 }
 
 // pr3: the launch holds LDS for a 3-bit pair table and the stage, so 3-bit
@@ -58,27 +58,27 @@ template <int TC, bool DF>
 __global__ __launch_bounds__(kThreads) void k_gate_up(FfnParams p, int qmax, int pr3) {
   extern __shared__ __attribute__((aligned(256))) uint16_t lds[];
   int it;
-  Item m;
-  if (!(TC == 4 ? decode_item_xcd(p, true, p.I >> 6, it, m) : decode_item(p, true, p.I >> 6, it, m))) return;
-  const int q = m.q;
+  Item wi;
+  if (!(TC == 4 ? decode_item_xcd(p, true, p.I >> 6, it, wi) : decode_item(p, true, p.I >> 6, it, wi))) return;
+  const int q = wi.q;
   const uint32_t lut_bytes = 256u << qmax;
   // stage: double-buffered (one barrier per step) in two 16-token buffers for
   // items of <= 16 tokens (mode 1), in two full buffers after a 32 KiB table
   // region for larger items of blocks below 8 bits (mode 2), else single
-  const int mode = TC == 1 && m.nt <= kDbTok ? 1 : DF && q < 8 ? 2 : 0;
+  const int mode = TC == 1 && wi.nt <= kDbTok ? 1 : DF && q < 8 ? 2 : 0;
   switch (q < 3 || q > qmax || !tables_at_zero(lds) ? 0 : q) {
     case 3:
-      if (pr3) gu_modes<3, TC, true, DF>(p, m, it, lds, kPairTableBytes, mode);
-      else gu_modes<3, TC, false, DF>(p, m, it, lds, lut_bytes, mode);
+      if (pr3) gu_modes<3, TC, true, DF>(p, wi, it, lds, kPairTableBytes, mode);
+      else gu_modes<3, TC, false, DF>(p, wi, it, lds, lut_bytes, mode);
       break;
-    case 4: gu_modes<4, TC, false, DF>(p, m, it, lds, lut_bytes, mode); break;
-    case 5: gu_modes<5, TC, false, DF>(p, m, it, lds, lut_bytes, mode); break;
-    case 6: gu_modes<6, TC, false, DF>(p, m, it, lds, lut_bytes, mode); break;
-    case 7: gu_modes<7, TC, false, DF>(p, m, it, lds, lut_bytes, mode); break;
-    case 8: gu_modes<8, TC, false, DF>(p, m, it, lds, lut_bytes, mode); break;
+    case 4: gu_modes<4, TC, false, DF>(p, wi, it, lds, lut_bytes, mode); break;
+    case 5: gu_modes<5, TC, false, DF>(p, wi, it, lds, lut_bytes, mode); break;
+    case 6: gu_modes<6, TC, false, DF>(p, wi, it, lds, lut_bytes, mode); break;
+    case 7: gu_modes<7, TC, false, DF>(p, wi, it, lds, lut_bytes, mode); break;
+    case 8: gu_modes<8, TC, false, DF>(p, wi, it, lds, lut_bytes, mode); break;
     default: {
-      const size_t o = (size_t)m.base * p.I + it * 64;
-      for (int i = threadIdx.x; i < m.nt * 64; i += blockDim.x) {
+      const size_t o = (size_t)wi.base * p.I + it * 64;
+      for (int i = threadIdx.x; i < wi.nt * 64; i += blockDim.x) {
         p.hhi[o + (size_t)(i >> 6) * p.I + (i & 63)] = 0x7e00;  // fp16 NaN
         p.hlo[o + (size_t)(i >> 6) * p.I + (i & 63)] = 0;
       }
@@ -96,26 +96,26 @@ __global__ __launch_bounds__(kThreads) void k_down(FfnParams p, int qmax, int pr
   const int ntile = (p.H + 127) >> 7;
   const int b = blockIdx.x / p.dn_split, ksi = blockIdx.x - b * p.dn_split;
   const int item = b / ntile, it = b - item * ntile;
-  Item m;
-  if (!item_of(p, false, item, m)) return;
-  const int q = m.q;
+  Item wi;
+  if (!item_of(p, false, item, wi)) return;
+  const int q = wi.q;
   const uint32_t lut_bytes = 256u << qmax;
   // round buffers as for gate_up: 16-token halves (mode 1), full buffers after
   // a 32 KiB table region (mode 2), or one buffer
-  const int mode = TC == 1 && m.nt <= kDbTok ? 1 : TC == 1 && DF && q < 8 ? 2 : 0;
+  const int mode = TC == 1 && wi.nt <= kDbTok ? 1 : TC == 1 && DF && q < 8 ? 2 : 0;
   switch (q < 3 || q > qmax || !tables_at_zero(lds) ? 0 : q) {
     case 3:
-      if (pr3) dn_modes<3, TC, NT, true, DF>(p, m, it, lds, kPairTableBytes, mode, ksi);
-      else dn_modes<3, TC, NT, false, DF>(p, m, it, lds, lut_bytes, mode, ksi);
+      if (pr3) dn_modes<3, TC, NT, true, DF>(p, wi, it, lds, kPairTableBytes, mode, ksi);
+      else dn_modes<3, TC, NT, false, DF>(p, wi, it, lds, lut_bytes, mode, ksi);
       break;
-    case 4: dn_modes<4, TC, NT, false, DF>(p, m, it, lds, lut_bytes, mode, ksi); break;
-    case 5: dn_modes<5, TC, NT, false, DF>(p, m, it, lds, lut_bytes, mode, ksi); break;
-    case 6: dn_modes<6, TC, NT, false, DF>(p, m, it, lds, lut_bytes, mode, ksi); break;
-    case 7: dn_modes<7, TC, NT, false, DF>(p, m, it, lds, lut_bytes, mode, ksi); break;
-    case 8: dn_modes<8, TC, NT, false, DF>(p, m, it, lds, lut_bytes, mode, ksi); break;
+    case 4: dn_modes<4, TC, NT, false, DF>(p, wi, it, lds, lut_bytes, mode, ksi); break;
+    case 5: dn_modes<5, TC, NT, false, DF>(p, wi, it, lds, lut_bytes, mode, ksi); break;
+    case 6: dn_modes<6, TC, NT, false, DF>(p, wi, it, lds, lut_bytes, mode, ksi); break;
+    case 7: dn_modes<7, TC, NT, false, DF>(p, wi, it, lds, lut_bytes, mode, ksi); break;
+    case 8: dn_modes<8, TC, NT, false, DF>(p, wi, it, lds, lut_bytes, mode, ksi); break;
     default: {
       const int n0 = it * 128;
-      poison(p.y + (size_t)ksi * p.T * (p.K + p.S) * p.H + (size_t)m.base * p.H + n0, p.H, m.nt,
+      poison(p.y + (size_t)ksi * p.T * (p.K + p.S) * p.H + (size_t)wi.base * p.H + n0, p.H, wi.nt,
              min(128, p.H - n0));
     }
   }

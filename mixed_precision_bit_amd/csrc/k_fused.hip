@@ -236,38 +236,38 @@ __device__ __forceinline__ void gate_up_unit(const FusedParams& P, int u, uint16
   const int item = u / P.ntile_gu, it = u - item * P.ntile_gu;
   int e, t0, nt, cnt;
   if (!unit_item(p, 0, item, slot, e, t0, nt, cnt)) return;
-  Item m;
-  item_fields<true>(p, 2 * e, e, t0, p.tpi, m);
-  m.nt = nt;
-  const int q = m.q;
+  Item wi;
+  item_fields<true>(p, 2 * e, e, t0, p.tpi, wi);
+  wi.nt = nt;
+  const int q = wi.q;
   const uint32_t lut_bytes = 256u << P.qmax;
   switch (q < 3 || q > P.qmax || !tables_at_zero(lds) ? 0 : q) {
     case 3:  // pair tables (the launch holds their LDS, fused_lds_bytes)
-      if (nt <= kDbTok) gate_up_body<3, 1, true, true, true, true>(p, m, it, lds, kPairTableBytes, tid);
-      else gate_up_body<3, 1, true, true, false, true>(p, m, it, lds, kPairTableBytes, tid);
+      if (nt <= kDbTok) gate_up_body<3, 1, true, true, true, true>(p, wi, it, lds, kPairTableBytes, tid);
+      else gate_up_body<3, 1, true, true, false, true>(p, wi, it, lds, kPairTableBytes, tid);
       break;
     case 4:
-      if (nt <= kDbTok) gate_up_body<4, 1, true, true, true>(p, m, it, lds, lut_bytes, tid);
-      else gate_up_body<4, 1, true>(p, m, it, lds, lut_bytes, tid);
+      if (nt <= kDbTok) gate_up_body<4, 1, true, true, true>(p, wi, it, lds, lut_bytes, tid);
+      else gate_up_body<4, 1, true>(p, wi, it, lds, lut_bytes, tid);
       break;
     case 5:
-      if (nt <= kDbTok) gate_up_body<5, 1, true, true, true>(p, m, it, lds, lut_bytes, tid);
-      else gate_up_body<5, 1, true>(p, m, it, lds, lut_bytes, tid);
+      if (nt <= kDbTok) gate_up_body<5, 1, true, true, true>(p, wi, it, lds, lut_bytes, tid);
+      else gate_up_body<5, 1, true>(p, wi, it, lds, lut_bytes, tid);
       break;
     case 6:
-      if (nt <= kDbTok) gate_up_body<6, 1, true, true, true>(p, m, it, lds, lut_bytes, tid);
-      else gate_up_body<6, 1, true>(p, m, it, lds, lut_bytes, tid);
+      if (nt <= kDbTok) gate_up_body<6, 1, true, true, true>(p, wi, it, lds, lut_bytes, tid);
+      else gate_up_body<6, 1, true>(p, wi, it, lds, lut_bytes, tid);
       break;
     case 7:
-      if (nt <= kDbTok) gate_up_body<7, 1, true, true, true>(p, m, it, lds, lut_bytes, tid);
-      else gate_up_body<7, 1, true>(p, m, it, lds, lut_bytes, tid);
+      if (nt <= kDbTok) gate_up_body<7, 1, true, true, true>(p, wi, it, lds, lut_bytes, tid);
+      else gate_up_body<7, 1, true>(p, wi, it, lds, lut_bytes, tid);
       break;
     case 8:
-      if (nt <= kDbTok) gate_up_body<8, 1, true, true, true>(p, m, it, lds, lut_bytes, tid);
-      else gate_up_body<8, 1, true>(p, m, it, lds, lut_bytes, tid);
+      if (nt <= kDbTok) gate_up_body<8, 1, true, true, true>(p, wi, it, lds, lut_bytes, tid);
+      else gate_up_body<8, 1, true>(p, wi, it, lds, lut_bytes, tid);
       break;
     default: {
-      const size_t o = (size_t)m.base * p.I + it * 64;
+      const size_t o = (size_t)wi.base * p.I + it * 64;
       for (int i = tid; i < nt * 64; i += kThreads) {
         p.hhi[o + (size_t)(i >> 6) * p.I + (i & 63)] = 0x7e00;  // fp16 NaN
         p.hlo[o + (size_t)(i >> 6) * p.I + (i & 63)] = 0;
@@ -288,39 +288,39 @@ __device__ __forceinline__ void down_unit(const FusedParams& P, int u, uint16_t*
   // h of group e is complete once all of its gate_up units are
   const uint32_t need = (uint32_t)((cnt + p.tpi - 1) / p.tpi) * P.ntile_gu;
   if (!wait_count(P, C_GU + e, need, flag)) return;
-  Item m;
-  item_fields<true>(p, 2 * e + 1, e, t0, p.tpi_dn, m);
-  m.nt = nt;
-  const int q = m.q;
+  Item wi;
+  item_fields<true>(p, 2 * e + 1, e, t0, p.tpi_dn, wi);
+  wi.nt = nt;
+  const int q = wi.q;
   const uint32_t lut_bytes = 256u << P.qmax;
   switch (q < 3 || q > P.qmax || !tables_at_zero(lds) ? 0 : q) {
     case 3:  // pair tables (the launch holds their LDS, fused_lds_bytes)
-      if (nt <= kDbTok) down_body<3, 1, true, true, true, true>(p, m, it, lds, kPairTableBytes, tid, ksi);
-      else down_body<3, 1, true, true, false, true>(p, m, it, lds, kPairTableBytes, tid, ksi);
+      if (nt <= kDbTok) down_body<3, 1, true, true, true, true>(p, wi, it, lds, kPairTableBytes, tid, ksi);
+      else down_body<3, 1, true, true, false, true>(p, wi, it, lds, kPairTableBytes, tid, ksi);
       break;
     case 4:
-      if (nt <= kDbTok) down_body<4, 1, true, true, true>(p, m, it, lds, lut_bytes, tid, ksi);
-      else down_body<4, 1, true>(p, m, it, lds, lut_bytes, tid, ksi);
+      if (nt <= kDbTok) down_body<4, 1, true, true, true>(p, wi, it, lds, lut_bytes, tid, ksi);
+      else down_body<4, 1, true>(p, wi, it, lds, lut_bytes, tid, ksi);
       break;
     case 5:
-      if (nt <= kDbTok) down_body<5, 1, true, true, true>(p, m, it, lds, lut_bytes, tid, ksi);
-      else down_body<5, 1, true>(p, m, it, lds, lut_bytes, tid, ksi);
+      if (nt <= kDbTok) down_body<5, 1, true, true, true>(p, wi, it, lds, lut_bytes, tid, ksi);
+      else down_body<5, 1, true>(p, wi, it, lds, lut_bytes, tid, ksi);
       break;
     case 6:
-      if (nt <= kDbTok) down_body<6, 1, true, true, true>(p, m, it, lds, lut_bytes, tid, ksi);
-      else down_body<6, 1, true>(p, m, it, lds, lut_bytes, tid, ksi);
+      if (nt <= kDbTok) down_body<6, 1, true, true, true>(p, wi, it, lds, lut_bytes, tid, ksi);
+      else down_body<6, 1, true>(p, wi, it, lds, lut_bytes, tid, ksi);
       break;
     case 7:
-      if (nt <= kDbTok) down_body<7, 1, true, true, true>(p, m, it, lds, lut_bytes, tid, ksi);
-      else down_body<7, 1, true>(p, m, it, lds, lut_bytes, tid, ksi);
+      if (nt <= kDbTok) down_body<7, 1, true, true, true>(p, wi, it, lds, lut_bytes, tid, ksi);
+      else down_body<7, 1, true>(p, wi, it, lds, lut_bytes, tid, ksi);
       break;
     case 8:
-      if (nt <= kDbTok) down_body<8, 1, true, true, true>(p, m, it, lds, lut_bytes, tid, ksi);
-      else down_body<8, 1, true>(p, m, it, lds, lut_bytes, tid, ksi);
+      if (nt <= kDbTok) down_body<8, 1, true, true, true>(p, wi, it, lds, lut_bytes, tid, ksi);
+      else down_body<8, 1, true>(p, wi, it, lds, lut_bytes, tid, ksi);
       break;
     default: {
       const int n0 = it * 128;
-      poison(p.y + (size_t)ksi * p.T * (p.K + p.S) * p.H + (size_t)m.base * p.H + n0, p.H, nt,
+      poison(p.y + (size_t)ksi * p.T * (p.K + p.S) * p.H + (size_t)wi.base * p.H + n0, p.H, nt,
              min(128, p.H - n0));
     }
   }
