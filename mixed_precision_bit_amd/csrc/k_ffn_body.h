@@ -30,6 +30,8 @@
 #pragma once
 
 #include <algorithm>
+#include <type_traits>
+#include <utility>
 
 #include "mpb_device.h"
 #include "mpb_internal.h"
@@ -53,6 +55,25 @@ constexpr int stage_bytes() { return 2 * TC * kTok * 256; }
 // the two stage buffers follow it (160 KiB in all for 128-token items)
 constexpr uint32_t kDbTable4 = 32768;
 static_assert(kDbTable4 + 2 * 2 * 4 * 32 * 256 <= 163840, "two 128-token stage buffers fit the LDS");
+
+// LDS bytes of a per-phase FFN launch for blocks of at most qmax bits: the
+// table region and the stage, the SwiGLU exchange, and room for a 3-bit pair
+// table and the stage in every launch (registers, not LDS, bound these
+// kernels' occupancy: two workgroups per CU at one token chunk, one at four),
+// so that a block committed at 3 bits later, under a captured graph, still
+// takes the pair path; with DF also the two full stage buffers after a 32 KiB
+// table region. The kernels read it too (the room left beside a block's own
+// table decides whether its activations stay resident).
+template <int TC, bool DF>
+__host__ __device__ constexpr uint32_t ffn_shmem(int qmax) {
+  constexpr uint32_t kSwiglu = kWaves * 16 * 64 * 4;  // the exchanged accumulators
+  uint32_t b = (256u << qmax) + (uint32_t)stage_bytes<TC>();
+  b = b > kSwiglu ? b : kSwiglu;
+  const uint32_t pr = kPairTableBytes + (uint32_t)stage_bytes<TC>();
+  b = b > pr ? b : pr;
+  const uint32_t df = kDbTable4 + 2u * (uint32_t)stage_bytes<TC>();
+  return DF && df > b ? df : b;
+}
 
 // Items of at most 16 tokens (TC = 1) split the same region into two stage
 // buffers of [K half][16 tokens][16 pieces]; step s reads buffer s % 2 while
@@ -253,16 +274,28 @@ struct Item {
   const uint32_t* planes[8];
   const uint16_t* const* luts;
 };
+// The same with the block's row of page pointers instead of the pointers (the
+// body reads the ones it needs): for the fused kernel, where eight more live
+// pointers would push its waves past their register budget.
+struct ItemRow {
+  int e, t0, nt, base, q;
+  const uint32_t* const* planes;
+  const uint16_t* const* luts;
+};
 
 // The group-indexed fields of an item: token count, offset, bitwidth and page
 // pointers, loaded together (one round trip).
-template <bool CO>
-__device__ __forceinline__ void item_fields(const FfnParams& p, int blk, int e, int t0, int tpi, Item& m) {
+template <bool CO, typename It>
+__device__ __forceinline__ void item_fields(const FfnParams& p, int blk, int e, int t0, int tpi, It& m) {
   const int cnt = ld_co<CO>(p.counts + e);
   const int off = ld_co<CO>(p.offsets + e);
   m.q = p.q[blk];
+  if constexpr (std::is_same<It, Item>::value) {
 #pragma unroll
-  for (int k = 0; k < 8; ++k) m.planes[k] = p.planes[blk * 8 + k];
+    for (int k = 0; k < 8; ++k) m.planes[k] = p.planes[blk * 8 + k];
+  } else {
+    m.planes = p.planes + blk * 8;
+  }
   m.luts = p.luts + blk * 6;
   m.e = e;
   m.t0 = t0;
@@ -315,6 +348,29 @@ struct KSplit {
   __device__ KSplit(int Kd) : HC(Kd >> 6), HH((((Kd >> 6) + 1) / 2 + 1) & ~1), NSW((((Kd >> 6) + 1) / 2 + 1) / 2) {}
 };
 
+// f(integral_constant<int, 0>) .. f(integral_constant<int, N - 1>) in order:
+// an unrolled loop whose index is a constant in every copy (so ring slots
+// stay in registers), however large the body
+template <typename F, int... I>
+__device__ __forceinline__ void each_const(F&& f, std::integer_sequence<int, I...>) {
+  (f(std::integral_constant<int, I>{}), ...);
+}
+template <int N, typename F>
+__device__ __forceinline__ void unroll_const(F&& f) {
+  each_const(f, std::make_integer_sequence<int, N>{});
+}
+
+// Steps of plane loads in flight per wave (the plane ring). Three at every
+// bitwidth: rings of about 48 VGPRs at each bitwidth (6 steps at 3 and 4
+// bits, 4 at 5 and 6) were measured no faster at the qwen15moe decode shape
+// (gate_up +1 %, down +2 %) and mixed at the Mixtral shape (4-bit gate_up
+// +6 %, 3-bit down -3 %): with three steps in flight the plane stream is not
+// what holds these kernels back.
+template <int Q, int TC>
+constexpr int plane_ring() {
+  return 3;
+}
+
 // ---------------------------------------------------------------- gate_up
 // Waves 0/1 take gate rows c0..c0+31 / c0+32..c0+63, waves 2/3 the matching up
 // rows, waves 4..7 the same rows over the second K half. Each dequantised
@@ -339,8 +395,9 @@ struct KSplit {
 // eight lookup_pairs4 groups over both words of the lane's half-chunk, with
 // the activations staged in pair order (piece 8 g' + m: elements 4m..4m+3 of
 // both words of half-chunk 2s + g').
-template <int Q, int TC, bool CO = false, bool NT = (TC == 1), bool DB = false, bool PR = false, bool DF = false>
-__device__ __forceinline__ void gate_up_body(const FfnParams& p, const Item& wi, int it, uint16_t* lds,
+template <int Q, int TC, bool CO = false, bool NT = (TC == 1), bool DB = false, bool PR = false, bool DF = false,
+          typename It = Item>
+__device__ __forceinline__ void gate_up_body(const FfnParams& p, const It& wi, int it, uint16_t* lds,
                                              uint32_t lut_bytes, int tid) {
   static_assert(!PR || Q == 3, "pair tables: 3-bit blocks");
   // DB with one token chunk: two 16-token buffers in the 16 KiB stage region
@@ -432,26 +489,27 @@ __device__ __forceinline__ void gate_up_body(const FfnParams& p, const Item& wi,
   for (int q = 0; q < Q; ++q) rs[q] = tile_rsrc(wi.planes[q], (size_t)(row0 >> 5) * NC * 512, ce * 512);
   const int voff = 16 * r + 8 * g;
 
-  uint2 PA[Q], PB[Q], PC[Q];
+  constexpr int D = plane_ring<Q, TC>();
+  uint2 P[D][Q];
   uint4 xr[2][TC];
   int kk[2];
   // PR: the 3-bit image goes to the stage region, which is staged only after
   // the pair table has been built from it
   // step 0's planes first: their pointers are known a round trip before the
   // table's
-  load_planes<Q, NT>(PA, rs, cb, 0, voff);
+  load_planes<Q, NT>(P[0], rs, cb, 0, voff);
   load_table_image<Q>(wi.luts[Q - 3] + (size_t)it * (128u << Q), w, lane, PR ? lut_bytes : 0u);
   row_offsets();
   if constexpr (DMA) {
     dma_win(0, 0);
-    load_planes<Q, NT>(PB, rs, cb, 1, voff);
-    load_planes<Q, NT>(PC, rs, cb, 2, voff);
-    wait_vmem_le<2 * Q>();  // step 0's planes, the table and step 0's activations
+#pragma unroll
+    for (int d = 1; d < D; ++d) load_planes<Q, NT>(P[d], rs, cb, d, voff);
+    wait_vmem_le<(D - 1) * Q>();  // step 0's planes, the table and step 0's activations
     __syncthreads();
   } else {
     kwin(0, kk);
     ld_win(xr, kk);
-    load_planes<Q, NT>(PB, rs, cb, 1, voff);
+    load_planes<Q, NT>(P[1], rs, cb, 1, voff);
     wait_vmem_le<Q>();  // step 0's planes, the table and step 0's activations
     if constexpr (PR) {
       __syncthreads();
@@ -461,7 +519,8 @@ __device__ __forceinline__ void gate_up_body(const FfnParams& p, const Item& wi,
     st_win(stage, xr, kk);
     kwin(1, kk);
     ld_win(xr, kk);
-    load_planes<Q, NT>(PC, rs, cb, 2, voff);
+#pragma unroll
+    for (int d = 2; d < D; ++d) load_planes<Q, NT>(P[d], rs, cb, d, voff);
     __syncthreads();
   }
 
@@ -470,14 +529,14 @@ __device__ __forceinline__ void gate_up_body(const FfnParams& p, const Item& wi,
   for (int c = 0; c < TC; ++c) acc[c] = (f32x16){};
   // par = s % 2 (the stage buffer of step s when DB), passed as a constant so
   // that the buffer offset folds into the LDS instructions' offset field
-  auto step = [&](int s, uint2 (&P)[Q], int par) {
+  auto step = [&](int s, uint2 (&Ps)[Q], int par) {
     // DMA: the buffer of step s + 1 was last read in step s - 1
     if constexpr (DMA)
       if (s + 1 < ks.NSW) dma_win(par ^ 1, s + 1);
     if constexpr (PR) {
       uint32_t Pa[3], Pb[3], O[8];
-      word_of<3>(P, 0, Pa);
-      word_of<3>(P, 1, Pb);
+      word_of<3>(Ps, 0, Pa);
+      word_of<3>(Ps, 1, Pb);
       assemble_pairs3(Pa, Pb, rg >> 1, O);
 #pragma unroll
       for (int m = 0; m < 8; ++m) {
@@ -492,7 +551,7 @@ __device__ __forceinline__ void gate_up_body(const FfnParams& p, const Item& wi,
 #pragma unroll
       for (int j = 0; j < 2; ++j) {
         uint32_t Pw[Q], O[8];
-        word_of<Q>(P, j, Pw);
+        word_of<Q>(Ps, j, Pw);
         assemble<Q>(Pw, O);
 #pragma unroll
         for (int m = 0; m < 4; ++m) {
@@ -507,7 +566,7 @@ __device__ __forceinline__ void gate_up_body(const FfnParams& p, const Item& wi,
       }
     }
     if constexpr (DMA) {
-      load_planes<Q, NT>(P, rs, cb, s + 3, voff);
+      load_planes<Q, NT>(Ps, rs, cb, s + D, voff);
       wait_vmem_le<Q>();  // step s + 1's activations (older than these planes)
       __syncthreads();
       return;
@@ -520,36 +579,20 @@ __device__ __forceinline__ void gate_up_body(const FfnParams& p, const Item& wi,
     }
     kwin(s + 2, kk);
     ld_win(xr, kk);
-    load_planes<Q, NT>(P, rs, cb, s + 3, voff);
+    load_planes<Q, NT>(Ps, rs, cb, s + D, voff);
     __syncthreads();
   };
   // whole ring turns in the loop, the remainder after it: the loop's back edge
-  // then always follows a PC step, which keeps the wait counts exact
-  // (DB: six steps per turn, so that the buffer parity is fixed per position)
+  // then always follows the ring's last step, which keeps the wait counts
+  // exact (DB with an odd ring: two turns per pass, so that the buffer parity
+  // is fixed per position)
+  constexpr int U = DB && (D & 1) ? 2 * D : D;
   int s = 0;
-  if constexpr (DB) {
-    for (; s + 6 <= ks.NSW; s += 6) {
-      step(s, PA, 0);
-      step(s + 1, PB, 1);
-      step(s + 2, PC, 0);
-      step(s + 3, PA, 1);
-      step(s + 4, PB, 0);
-      step(s + 5, PC, 1);
-    }
-    if (s < ks.NSW) step(s, PA, 0);
-    if (s + 1 < ks.NSW) step(s + 1, PB, 1);
-    if (s + 2 < ks.NSW) step(s + 2, PC, 0);
-    if (s + 3 < ks.NSW) step(s + 3, PA, 1);
-    if (s + 4 < ks.NSW) step(s + 4, PB, 0);
-  } else {
-    for (; s + 3 <= ks.NSW; s += 3) {
-      step(s, PA, 0);
-      step(s + 1, PB, 0);
-      step(s + 2, PC, 0);
-    }
-    if (s < ks.NSW) step(s, PA, 0);
-    if (s + 1 < ks.NSW) step(s + 1, PB, 0);
-  }
+  for (; s + U <= ks.NSW; s += U)
+    unroll_const<U>([&](auto u) { step(s + u, P[u % D], u & 1); });
+  unroll_const<U - 1>([&](auto u) {
+    if (s + u < ks.NSW) step(s + u, P[u % D], u & 1);
+  });
 
   // SwiGLU, one token chunk at a time: every wave puts its accumulators in LDS
   // (layout [wave][v][lane]), then wave w finishes v = 4 (w >> 1) .. + 3 of
@@ -610,8 +653,9 @@ __device__ __forceinline__ void poison(float* dst, size_t ld, int rows, int cols
 // barriers per step instead of four; the buffers are 16-token halves of the
 // stage region for items of <= 16 tokens, or with DF full 32-token buffers
 // after a 32 KiB table region.
-template <int Q, int TC, bool CO = false, bool NT = true, bool DB = false, bool PR = false, bool DF = false>
-__device__ __forceinline__ void down_body(const FfnParams& p, const Item& wi, int it, uint16_t* lds,
+template <int Q, int TC, bool CO = false, bool NT = true, bool DB = false, bool PR = false, bool DF = false,
+          typename It = Item>
+__device__ __forceinline__ void down_body(const FfnParams& p, const It& wi, int it, uint16_t* lds,
                                           uint32_t lut_bytes, int tid, int ksi = 0) {
   // DB: two 16-token round buffers in the 16 KiB stage region (HALF), or with
   // DF two full 32-token round buffers after a 32 KiB table region
@@ -683,7 +727,8 @@ __device__ __forceinline__ void down_body(const FfnParams& p, const Item& wi, in
     rs[q] = tile_rsrc(wi.planes[q], active ? (size_t)(n0 >> 5) * NC * 512 : 0, active ? ce * 512 : 0);
   const int voff = 16 * r + 8 * g;
 
-  uint2 PA[Q], PB[Q], PC[Q];
+  constexpr int D = plane_ring<Q, TC>();
+  uint2 P[D][Q];
   uint4 ha[2][TC], hb[2][TC];
   int ka[2], kb[2];
   // (requesting steps 1 and 2's planes before this first wait as well, or
@@ -691,7 +736,7 @@ __device__ __forceinline__ void down_body(const FfnParams& p, const Item& wi, in
   load_table_image<Q>(wi.luts[Q - 3] + (size_t)it * (128u << Q), w, lane, PR ? lut_bytes : 0u);
   kwin(0, 0, ka);
   ld_win(ha, ka);
-  load_planes<Q, NT>(PA, rs, cb, 0, voff);
+  load_planes<Q, NT>(P[0], rs, cb, 0, voff);
   wait_vmem_all();
   if constexpr (PR) {
     __syncthreads();
@@ -703,25 +748,25 @@ __device__ __forceinline__ void down_body(const FfnParams& p, const Item& wi, in
   ld_win(hb, kb);
   kwin(1, 0, ka);
   ld_win(ha, ka);
-  load_planes<Q, NT>(PB, rs, cb, 1, voff);
-  load_planes<Q, NT>(PC, rs, cb, 2, voff);
+#pragma unroll
+  for (int d = 1; d < D; ++d) load_planes<Q, NT>(P[d], rs, cb, d, voff);
   __syncthreads();
 
   f32x16 acc[TC];
 #pragma unroll
   for (int c = 0; c < TC; ++c) acc[c] = (f32x16){};
   // O: PR, the pair words of both rounds (assembled in round 0)
-  auto round = [&](int j, const uint2 (&P)[Q], uint32_t (&Op)[8]) {
+  auto round = [&](int j, const uint2 (&Ps)[Q], uint32_t (&Op)[8]) {
     uint32_t Pw[Q], O[8];
     if constexpr (PR) {
       if (j == 0) {
         uint32_t Pa[3], Pb[3];
-        word_of<3>(P, 0, Pa);
-        word_of<3>(P, 1, Pb);
+        word_of<3>(Ps, 0, Pa);
+        word_of<3>(Ps, 1, Pb);
         assemble_pairs3(Pa, Pb, rg >> 1, Op);
       }
     } else {
-      word_of<Q>(P, j, Pw);
+      word_of<Q>(Ps, j, Pw);
       assemble<Q>(Pw, O);
     }
 #pragma unroll
@@ -746,32 +791,30 @@ __device__ __forceinline__ void down_body(const FfnParams& p, const Item& wi, in
     }
     if (!DB) __syncthreads();
   };
-  auto step = [&](int s, uint2 (&P)[Q]) {
+  auto step = [&](int s, uint2 (&Ps)[Q]) {
     uint32_t Op[8];
-    round(0, P, Op);
+    round(0, Ps, Op);
     kwin(s, 1, kb);
     st_win(stage + rbuf(1), hb, kb);
     kwin(s + 1, 1, kb);
     ld_win(hb, kb);
     __syncthreads();
-    round(1, P, Op);
+    round(1, Ps, Op);
     if (s + 1 < ks.NSW) {
       kwin(s + 1, 0, ka);
       st_win(stage + rbuf(0), ha, ka);
     }
     kwin(s + 2, 0, ka);
     ld_win(ha, ka);
-    load_planes<Q, NT>(P, rs, cb, s + 3, voff);
+    load_planes<Q, NT>(Ps, rs, cb, s + D, voff);
     __syncthreads();
   };
+  // whole ring turns in the loop, the remainder after it (exact wait counts)
   int s = 0;
-  for (; s + 3 <= ks.NSW; s += 3) {
-    step(s, PA);
-    step(s + 1, PB);
-    step(s + 2, PC);
-  }
-  if (s < ks.NSW) step(s, PA);
-  if (s + 1 < ks.NSW) step(s + 1, PB);
+  for (; s + D <= ks.NSW; s += D) unroll_const<D>([&](auto u) { step(s + u, P[u]); });
+  unroll_const<D - 1>([&](auto u) {
+    if (s + u < ks.NSW) step(s + u, P[u]);
+  });
 
   // 16-token buffers: each column c < 16 takes its h lo partner from column
   // c + 16, so column c holds the whole sum over the wave's K half

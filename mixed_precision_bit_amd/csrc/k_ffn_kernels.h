@@ -121,12 +121,6 @@ __global__ __launch_bounds__(kThreads) void k_down(FfnParams p, int qmax, int pr
   }
 }
 
-template <int TC, bool DF>
-static size_t ffn_lds_bytes(int qmax) {
-  const size_t single = std::max<size_t>((256u << qmax) + stage_bytes<TC>(), kWaves * 16 * 64 * 4);
-  // DF: room for the full double-buffered stage of blocks below 8 bits
-  return DF ? std::max<size_t>(single, kDbTable4 + 2 * stage_bytes<TC>()) : single;
-}
 
 // ev0/ev1 (optional): the launch itself records them at the kernel's start and
 // end (hipExtLaunchKernelGGL), for timing the kernel alone.
@@ -136,15 +130,9 @@ static hipError_t launch_tc(const FfnParams& p, int qmax, hipStream_t s, hipEven
   const void* fn;
   if constexpr (GU) fn = (const void*)k_gate_up<TC, DF>;
   else fn = (const void*)k_down<TC, NT, DF>;
-  const hipError_t e =
-      raise_lds_limit(fn, (int)std::max<size_t>(ffn_lds_bytes<TC, DF>(8), kPairTableBytes + stage_bytes<TC>()), lds_raised);
+  const hipError_t e = raise_lds_limit(fn, (int)ffn_shmem<TC, DF>(8), lds_raised);
   if (e != hipSuccess) return e;
-  // every launch holds room for a 3-bit pair table and the stage (registers,
-  // not LDS, bound these kernels' occupancy: two workgroups per CU at one
-  // token chunk, one at four), so a block committed at 3 bits later, under a
-  // captured graph, still takes the pair path
-  constexpr size_t kPairLds = kPairTableBytes + stage_bytes<TC>();
-  const size_t shmem = std::max(ffn_lds_bytes<TC, DF>(qmax), kPairLds);
+  const size_t shmem = ffn_shmem<TC, DF>(qmax);
   const int pr3 = 1;
   // 128-token items take the XCD-interleaved order (decode_item_xcd)
   const int items = TC == 4 ? (p.max_items + 7) / 8 * 8 : p.max_items;

@@ -236,7 +236,7 @@ __device__ __forceinline__ void gate_up_unit(const FusedParams& P, int u, uint16
   const int item = u / P.ntile_gu, it = u - item * P.ntile_gu;
   int e, t0, nt, cnt;
   if (!unit_item(p, 0, item, slot, e, t0, nt, cnt)) return;
-  Item wi;
+  ItemRow wi;
   item_fields<true>(p, 2 * e, e, t0, p.tpi, wi);
   wi.nt = nt;
   const int q = wi.q;
@@ -288,7 +288,7 @@ __device__ __forceinline__ void down_unit(const FusedParams& P, int u, uint16_t*
   // h of group e is complete once all of its gate_up units are
   const uint32_t need = (uint32_t)((cnt + p.tpi - 1) / p.tpi) * P.ntile_gu;
   if (!wait_count(P, C_GU + e, need, flag)) return;
-  Item wi;
+  ItemRow wi;
   item_fields<true>(p, 2 * e + 1, e, t0, p.tpi_dn, wi);
   wi.nt = nt;
   const int q = wi.q;
