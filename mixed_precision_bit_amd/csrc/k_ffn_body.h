@@ -635,8 +635,11 @@ __device__ __forceinline__ void gate_up_body(const FfnParams& p, const It& wi, i
 // A block whose committed bitwidth is outside 3..qmax (the table region of
 // this launch was sized for qmax), or a table region not at LDS byte 0,
 // produces NaN instead of a silently wrong value.
-__device__ __forceinline__ void poison(float* dst, size_t ld, int rows, int cols) {
-  for (int i = threadIdx.x; i < rows * cols; i += blockDim.x) dst[(size_t)(i / cols) * ld + i % cols] = __builtin_nanf("");
+__device__ __forceinline__ void poison_y(const FfnParams& p, int ksi, int base, int nt, int n0) {
+  const int cols = min(128, p.H - n0);
+  float* y = p.y + (size_t)ksi * p.T * (p.K + p.S) * p.H + n0;
+  for (int i = threadIdx.x; i < nt * cols; i += blockDim.x)
+    y[(size_t)p.ent[base + i / cols] * p.H + i % cols] = __builtin_nanf("");
 }
 
 // ---------------------------------------------------------------- down
@@ -678,6 +681,11 @@ __device__ __forceinline__ void down_body(const FfnParams& p, const It& wi, int 
 
   StagePlan<TC> sp;
   const int st = tid >> 4, spc = tid & 15, hl = spc >> 3;
+  // the y row of each token chunk's entry in this lane's column (its (token,
+  // slot) index), read now so the epilogue's stores do not wait for it
+  int yent[TC];
+#pragma unroll
+  for (int c = 0; c < TC; ++c) yent[c] = ld_co<CO>(p.ent + base + min(kTok * c + r, nt - 1));
   {
     // one descriptor over both halves of h
     const size_t hbytes = (size_t)p.T * (p.K + p.S) * I * 2;
@@ -837,7 +845,7 @@ __device__ __forceinline__ void down_body(const FfnParams& p, const It& wi, int 
     if (kh == 0 && active && t < nt) {
       // h of a scaled token was carried as h 2^(-2 sc)
       const int sc = p.xsc ? ld_co<CO>(p.xsc + ld_co<CO>(p.ptok + base + t)) : 0;
-      float* yrow = p.y + (size_t)ksi * p.T * (p.K + p.S) * H + (size_t)(base + t) * H + n0 + 4 * g;
+      float* yrow = p.y + (size_t)ksi * p.T * (p.K + p.S) * H + (size_t)yent[c] * H + n0 + 4 * g;
 #pragma unroll
       for (int v4 = 0; v4 < 4; ++v4) {
         f32x4 o;
@@ -850,44 +858,39 @@ __device__ __forceinline__ void down_body(const FfnParams& p, const It& wi, int 
   }
 }
 
-// out[t][n..n+3] = sum_k w_tk * y[entry(t,k)] + sum_s y[entry(t,K+s)], in that
-// order (the same order for every output, so the result is deterministic).
+// out[t][n..n+3] = sum_k w_tk * y[t, k] + sum_s y[t, K + s], in that order
+// (the same order for every output, so the result is deterministic). y holds
+// one row per (token, slot), so a token's rows are known without reading the
+// grouping: the ids, weights and rows are all requested together (one round
+// trip); a dead slot's row (an out-of-range id) is read but not added.
 template <bool CO = false>
 __device__ __forceinline__ void combine4(const FfnParams& p, int t, int n) {
   const int KS = p.K + p.S;
   f32x4 s = (f32x4){};
-  // entries are taken 8 at a time: their ids, positions and weights are loaded
-  // together, then their rows of y, then summed in entry order (the loads
-  // overlap; the sum is the same)
   for (int k0 = 0; k0 < KS; k0 += 8) {
-    int pos[8];
     float w[8];
     bool live[8];
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
       const int k = k0 + j;
-      live[j] = false;
+      live[j] = k < KS;
       w[j] = 1.0f;
-      pos[j] = 0;
       if (k < p.K) {
         const int ex = ld_co<CO>(p.topk_idx + t * p.K + k);
         live[j] = ex >= 0 && ex < p.E;
         w[j] = ld_co<CO>(p.topk_w + t * p.K + k);
-        pos[j] = ld_co<CO>(p.inv + t * KS + k);
-      } else if (k < KS) {
-        live[j] = true;
-        pos[j] = ld_co<CO>(p.inv + t * KS + k);
       }
     }
+    const float* yt = p.y + (size_t)t * KS * p.H + n;
     f32x4 y[8];
 #pragma unroll
-    for (int j = 0; j < 8; ++j) y[j] = live[j] ? *(const f32x4*)(p.y + (size_t)pos[j] * p.H + n) : (f32x4){};
+    for (int j = 0; j < 8; ++j) y[j] = k0 + j < KS ? *(const f32x4*)(yt + (size_t)(k0 + j) * p.H) : (f32x4){};
     // partial sums of the other K ranges, added in range order
     const size_t slice = (size_t)p.T * KS * p.H;
     for (int r = 1; r < p.dn_split; ++r) {
 #pragma unroll
       for (int j = 0; j < 8; ++j)
-        if (live[j]) y[j] += *(const f32x4*)(p.y + r * slice + (size_t)pos[j] * p.H + n);
+        if (live[j]) y[j] += *(const f32x4*)(yt + r * slice + (size_t)(k0 + j) * p.H);
     }
 #pragma unroll
     for (int j = 0; j < 8; ++j) {

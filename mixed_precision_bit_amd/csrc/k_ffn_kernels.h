@@ -113,11 +113,7 @@ __global__ __launch_bounds__(kThreads) void k_down(FfnParams p, int qmax, int pr
     case 6: dn_modes<6, TC, NT, false, DF>(p, wi, it, lds, lut_bytes, mode, ksi); break;
     case 7: dn_modes<7, TC, NT, false, DF>(p, wi, it, lds, lut_bytes, mode, ksi); break;
     case 8: dn_modes<8, TC, NT, false, DF>(p, wi, it, lds, lut_bytes, mode, ksi); break;
-    default: {
-      const int n0 = it * 128;
-      poison(p.y + (size_t)ksi * p.T * (p.K + p.S) * p.H + (size_t)wi.base * p.H + n0, p.H, wi.nt,
-             min(128, p.H - n0));
-    }
+    default: poison_y(p, ksi, wi.base, wi.nt, it * 128);
   }
 }
 

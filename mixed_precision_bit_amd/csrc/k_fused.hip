@@ -215,7 +215,7 @@ __device__ __forceinline__ void group_unit(const FfnParams& p, int e, int* sm, i
         const int t = j / K, k = j - t * K;
         st_co<true>(p.ptok + pos, t);
         st_co<true>(p.pw + pos, ld_co<true>(p.topk_w + j));
-        st_co<true>(p.inv + t * KS + k, pos);
+        st_co<true>(p.ent + pos, t * KS + k);
       }
       run += tot;
       __syncthreads();
@@ -226,7 +226,7 @@ __device__ __forceinline__ void group_unit(const FfnParams& p, int e, int* sm, i
       const int pos = off + t;
       st_co<true>(p.ptok + pos, t);
       st_co<true>(p.pw + pos, 1.0f);
-      st_co<true>(p.inv + t * KS + K + s, pos);
+      st_co<true>(p.ent + pos, t * KS + K + s);
     }
   }
 }
@@ -318,11 +318,7 @@ __device__ __forceinline__ void down_unit(const FusedParams& P, int u, uint16_t*
       if (nt <= kDbTok) down_body<8, 1, true, true, true>(p, wi, it, lds, lut_bytes, tid, ksi);
       else down_body<8, 1, true>(p, wi, it, lds, lut_bytes, tid, ksi);
       break;
-    default: {
-      const int n0 = it * 128;
-      poison(p.y + (size_t)ksi * p.T * (p.K + p.S) * p.H + (size_t)wi.base * p.H + n0, p.H, nt,
-             min(128, p.H - n0));
-    }
+    default: poison_y(p, ksi, wi.base, nt, it * 128);
   }
   mark_done(ctr(P, C_DOWN));
 }

@@ -2,8 +2,9 @@
 //
 // Routed expert e receives the (token, k) pairs with topk_idx[t][k] == e, kept
 // in (t, k) order; shared experts receive every token with weight 1. Grouped
-// entries of expert e occupy positions offsets[e] .. offsets[e+1]-1; inv maps
-// each (t, slot) back to its position (slot k < K routed, K + s shared).
+// entries of expert e occupy positions offsets[e] .. offsets[e+1]-1; ent holds
+// each entry's (token, slot) index t (K + S) + slot (slot k < K routed, K + s
+// shared), the row of y the down projection writes for it.
 // Every workgroup builds the whole expert histogram in LDS (integer counts,
 // order-free), takes its own offset from it, then places its entries with a
 // ballot-ordered scan, so the grouping is identical on every run.
@@ -116,7 +117,7 @@ __global__ __launch_bounds__(256) void k_group(FfnParams p) {
         const int t = j / K, k = j - t * K;
         p.ptok[pos] = t;
         p.pw[pos] = p.topk_w[j];
-        p.inv[t * KS + k] = pos;
+        p.ent[pos] = t * KS + k;
       }
       run += tot;
       __syncthreads();
@@ -127,7 +128,7 @@ __global__ __launch_bounds__(256) void k_group(FfnParams p) {
       const int pos = off + t;
       p.ptok[pos] = t;
       p.pw[pos] = 1.0f;
-      p.inv[t * KS + K + s] = pos;
+      p.ent[pos] = t * KS + K + s;
     }
   }
 }
@@ -231,7 +232,7 @@ __global__ __launch_bounds__(256) void k_chunk_scatter(FfnParams p, const int32_
         const int t = j / K, k = j - t * K;
         p.ptok[pos] = t;
         p.pw[pos] = p.topk_w[j];
-        p.inv[t * KS + k] = pos;
+        p.ent[pos] = t * KS + k;
       }
       run += tot;
       __syncthreads();
@@ -242,7 +243,7 @@ __global__ __launch_bounds__(256) void k_chunk_scatter(FfnParams p, const int32_
       const int pos = off + t;
       p.ptok[pos] = t;
       p.pw[pos] = 1.0f;
-      p.inv[t * KS + K + sh] = pos;
+      p.ent[pos] = t * KS + K + sh;
     }
   }
 }

@@ -166,7 +166,7 @@ WsLayout ws_layout(int T, int H, int I, int E, int S, int K, bool bf16) {
   L.offsets = off; off += align256((NB + 1) * 4);
   L.ptok = off;    off += align256(P * 4);
   L.pw = off;      off += align256(P * 4);
-  L.inv = off;     off += align256(P * 4);
+  L.ent = off;     off += align256(P * 4);
   L.max_items = max_decode_items(T, E, S, K);
   L.items = off;   off += align256((size_t)L.max_items * 4);
   L.items_dn = off; off += align256((size_t)L.max_items * 4);
@@ -200,7 +200,7 @@ mpb::FfnParams ffn_params(const mpb::WsLayout& L, char* ws, const void* X_dev, i
   p.offsets = (int32_t*)(ws + L.offsets);
   p.ptok = (int32_t*)(ws + L.ptok);
   p.pw = (float*)(ws + L.pw);
-  p.inv = (int32_t*)(ws + L.inv);
+  p.ent = (int32_t*)(ws + L.ent);
   p.items = (int32_t*)(ws + L.items);
   p.items_dn = (int32_t*)(ws + L.items_dn);
   p.n_items = (int32_t*)(ws + L.n_items);

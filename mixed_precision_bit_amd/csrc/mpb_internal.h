@@ -39,7 +39,7 @@ struct FfnParams {
   int32_t* offsets;           // [NB+1]
   int32_t* ptok;              // [P] token of each grouped entry
   float* pw;                  // [P] routing weight of each entry
-  int32_t* inv;               // [T][K+S] entry position of (t, slot)
+  int32_t* ent;               // [P] (token, slot) of each grouped entry: t (K + S) + slot
   int32_t* items;             // [max_items] gate_up work items: (group << 16) | token split
   int32_t* items_dn;          // [max_items] down work items, same encoding
   int32_t* n_items;           // [2] number of valid items: gate_up, down
@@ -48,7 +48,7 @@ struct FfnParams {
   int tpi_dn;                 // down tokens per item: kChunkTokens
   uint16_t* hhi;              // [P][I] fp16 high part of h = SiLU(gate) * up
   uint16_t* hlo;              // [P][I] fp16 remainder h - hi
-  float* y;                   // [dn_split][P][H] per-entry down projection (partial sums over K ranges)
+  float* y;                   // [dn_split][T (K + S)][H] down projection of each (token, slot) (partial sums over K ranges)
   float* out;                 // [T][H]
   int dn_split;               // K ranges of the down projection (1: whole K per workgroup)
   int dn_hcs;                 // half-chunks (64 elements) per K range, even
@@ -77,7 +77,7 @@ inline int dn_range_hcs(int I, int n) {
 }
 
 struct WsLayout {
-  size_t counts, offsets, ptok, pw, inv, items, items_dn, n_items, ccnt, hhi, hlo, y, xh, xsc, total;
+  size_t counts, offsets, ptok, pw, ent, items, items_dn, n_items, ccnt, hhi, hlo, y, xh, xsc, total;
   int max_items;
 };
 // Upper bound on work items (one per tpi-token split of a group with tokens):
