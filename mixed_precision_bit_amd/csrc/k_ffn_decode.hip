@@ -9,7 +9,7 @@
 namespace mpb {
 
 // ---------------------------------------------------------------- combine
-// out[t] = sum_k w_tk * y[entry(t,k)] + sum_s y[entry(t,K+s)], in that order.
+// out[t] = sum_k w_tk * y[t, k] + sum_s y[t, K + s], in that order (y in (token, slot) rows).
 __global__ __launch_bounds__(256) void k_combine(FfnParams p) {
   const int H4 = p.H >> 2;
   const size_t gid = (size_t)blockIdx.x * 256 + threadIdx.x;
