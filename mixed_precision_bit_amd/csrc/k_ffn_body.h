@@ -66,7 +66,7 @@ static_assert(kDbTable4 + 2 * 2 * 4 * 32 * 256 <= 163840, "two 128-token stage b
 // table decides whether its activations stay resident).
 template <int TC, bool DF>
 __host__ __device__ constexpr uint32_t ffn_shmem(int qmax) {
-  constexpr uint32_t kSwiglu = kWaves * 16 * 64 * 4;  // the exchanged accumulators
+  constexpr uint32_t kSwiglu = TC * kWaves * 16 * 64 * 4;  // the exchanged accumulators of every chunk
   uint32_t b = (256u << qmax) + (uint32_t)stage_bytes<TC>();
   b = b > kSwiglu ? b : kSwiglu;
   const uint32_t pr = kPairTableBytes + (uint32_t)stage_bytes<TC>();
@@ -438,6 +438,11 @@ __device__ __forceinline__ void gate_up_body(const FfnParams& p, const It& wi, i
 #pragma unroll
     for (int c = 0; c < TC; ++c) sp.off[c] = kTok * c + st < nt ? (uint32_t)tok[c] * (uint32_t)H * 2u : 0u;
   };
+  // bf16 input: the epilogue's tokens (column r of each chunk), whose scale
+  // shifts it reads; requested now so that the epilogue waits for one load
+  int etok[TC];
+#pragma unroll
+  for (int c = 0; c < TC; ++c) etok[c] = p.xsc ? ld_co<CO>(p.ptok + base + min(kTok * c + r, nt - 1)) : 0;
   // stage byte offset of piece `pc` of token chunk c, row r, in buffer par
   auto rd_off = [&](int par, int c, int pc) -> uint32_t {
     if constexpr (HALF) return stage_off_db(par, kh, r & 15, pc);
@@ -594,34 +599,40 @@ __device__ __forceinline__ void gate_up_body(const FfnParams& p, const It& wi, i
     if (s + u < ks.NSW) step(s + u, P[u % D], u & 1);
   });
 
-  // SwiGLU, one token chunk at a time: every wave puts its accumulators in LDS
-  // (layout [wave][v][lane]), then wave w finishes v = 4 (w >> 1) .. + 3 of
-  // row half hr = w & 1 (columns it * 64 + 32 hr + ...), with gate = the
-  // partials of waves hr and hr + 4 and up = those of waves hr + 2 and hr + 6,
-  // each sum in that order; all eight waves share the SiLU work
+  // SwiGLU: every wave puts the accumulators of every token chunk in LDS
+  // (layout [chunk][wave][v][lane], TC x 32 KiB, which every launch holds),
+  // then wave w finishes v = 4 (w >> 1) .. + 3 of row half hr = w & 1
+  // (columns it * 64 + 32 hr + ...) of each chunk, with gate = the partials of
+  // waves hr and hr + 4 and up = those of waves hr + 2 and hr + 6, each sum in
+  // that order; all eight waves share the SiLU work, behind one barrier
   float* xb = (float*)lds;
   const int hr = w & 1, v4 = w >> 1;
+  // a token converted scaled by 2^-sc (bf16 beyond the fp16 range) gets gate
+  // and up scaled back, and h carried as h 2^(-2 sc)
+  int scs[TC];
+#pragma unroll
+  for (int c = 0; c < TC; ++c) scs[c] = p.xsc ? ld_co<CO>(p.xsc + etok[c]) : 0;
+#pragma unroll
+  for (int c = 0; c < TC; ++c)
+#pragma unroll
+    for (int v = 0; v < 16; ++v) xb[((c * kWaves + w) * 16 + v) * 64 + lane] = acc[c][v];
+  __syncthreads();
 #pragma unroll
   for (int c = 0; c < TC; ++c) {
-    if (c) __syncthreads();  // the previous chunk's partials have been read
-#pragma unroll
-    for (int v = 0; v < 16; ++v) xb[(w * 16 + v) * 64 + lane] = acc[c][v];
-    __syncthreads();
     const int t = kTok * c + r;
     if (t < nt) {
-      // acc[c][v] is row 8*(v/4) + 4*g + v%4 of a wave's 32 rows, token t.
-      // A token converted scaled by 2^-sc (bf16 beyond the fp16 range) gets
-      // gate and up scaled back, and h carried as h 2^(-2 sc).
-      const int sc = p.xsc ? ld_co<CO>(p.xsc + ld_co<CO>(p.ptok + base + t)) : 0;
+      // acc[c][v] is row 8*(v/4) + 4*g + v%4 of a wave's 32 rows, token t
+      const int sc = scs[c];
+      const float* xc = xb + c * kWaves * 16 * 64;
       const size_t o = (size_t)(base + t) * I + it * 64 + hr * 32 + 4 * g;
       uint16_t hv[4], lv[4];
 #pragma unroll
       for (int k = 0; k < 4; ++k) {
         const int v = 4 * v4 + k;
         const float gate =
-            __builtin_amdgcn_ldexpf(xb[(hr * 16 + v) * 64 + lane] + xb[((hr + 4) * 16 + v) * 64 + lane], sc);
+            __builtin_amdgcn_ldexpf(xc[(hr * 16 + v) * 64 + lane] + xc[((hr + 4) * 16 + v) * 64 + lane], sc);
         const float up =
-            __builtin_amdgcn_ldexpf(xb[((hr + 2) * 16 + v) * 64 + lane] + xb[((hr + 6) * 16 + v) * 64 + lane], sc);
+            __builtin_amdgcn_ldexpf(xc[((hr + 2) * 16 + v) * 64 + lane] + xc[((hr + 6) * 16 + v) * 64 + lane], sc);
         const split16 sp2 = split_hi_lo(__builtin_amdgcn_ldexpf(silu(gate) * up, -2 * sc));
         hv[k] = __builtin_bit_cast(uint16_t, sp2.hi);
         lv[k] = __builtin_bit_cast(uint16_t, sp2.lo);
