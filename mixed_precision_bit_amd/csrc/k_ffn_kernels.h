@@ -118,8 +118,8 @@ __global__ __launch_bounds__(kThreads) void k_down(FfnParams p, int qmax, int pr
 }
 
 
-// ev0/ev1 (optional): the launch itself records them at the kernel's start and
-// end (hipExtLaunchKernelGGL), for timing the kernel alone.
+// ev0/ev1 (optional, each may be null): the launch itself records them at the
+// kernel's start and end (hipExtLaunchKernelGGL), for timing the kernel alone.
 template <int TC, bool GU, bool NT, bool DF>
 static hipError_t launch_tc(const FfnParams& p, int qmax, hipStream_t s, hipEvent_t ev0, hipEvent_t ev1) {
   static unsigned long long lds_raised = 0;  // devices on which this kernel's LDS limit is raised
@@ -133,14 +133,14 @@ static hipError_t launch_tc(const FfnParams& p, int qmax, hipStream_t s, hipEven
   // 128-token items take the XCD-interleaved order (decode_item_xcd)
   const int items = TC == 4 ? (p.max_items + 7) / 8 * 8 : p.max_items;
   if constexpr (GU) {
-    if (ev0 && ev1)
+    if (ev0 || ev1)
       hipExtLaunchKernelGGL((k_gate_up<TC, DF>), dim3(items * (p.I >> 6)), dim3(kThreads), shmem, s, ev0, ev1, 0, p,
                             qmax, pr3);
     else
       hipLaunchKernelGGL((k_gate_up<TC, DF>), dim3(items * (p.I >> 6)), dim3(kThreads), shmem, s, p, qmax, pr3);
   } else {
     const dim3 grid(p.max_items * ((p.H + 127) >> 7) * p.dn_split);
-    if (ev0 && ev1)
+    if (ev0 || ev1)
       hipExtLaunchKernelGGL((k_down<TC, NT, DF>), grid, dim3(kThreads), shmem, s, ev0, ev1, 0, p, qmax, pr3);
     else
       hipLaunchKernelGGL((k_down<TC, NT, DF>), grid, dim3(kThreads), shmem, s, p, qmax, pr3);

@@ -13,7 +13,11 @@
 // (gate_up) or tpi_dn-token (down) split of every group with tokens. Each kernel gets its own list,
 // ordered by that kernel's committed bitwidth of the group, highest first
 // (then by group): workgroup time grows with the bitwidth, and starting the
-// longest ones first keeps the end of the launch short.
+// longest ones first keeps the end of the launch short. Groups of at least
+// wide_from tokens (when set) go to the wide lists instead, split into
+// tpi_w-token (gate_up) and tpi_dnw-token (down) items: first every full item
+// in the same order, then each group's last, partial item in that order (the
+// lighter workgroups come last, where a launch's final round runs).
 #include "mpb_device.h"
 #include "mpb_internal.h"
 
@@ -23,9 +27,80 @@ constexpr int kMaxGroups = 512 + 64;
 
 constexpr int kIdxCache = 8;  // topk ids kept in registers per thread between the two passes
 
+// Items of a group of cnt tokens in the lists: narrow gate_up, narrow down,
+// and the wide lists' full and partial items (a group is in the narrow or the
+// wide lists; a wide group has at most one partial item per list).
+struct GroupItems {
+  int gu, dn, gwf, gwp, dwf, dwp;
+};
+template <bool WIDE>
+__device__ __forceinline__ GroupItems group_items(const FfnParams& p, int cnt) {
+  const bool wide = WIDE && cnt >= p.wide_from;
+  GroupItems n;
+  n.gu = wide ? 0 : (cnt + p.tpi - 1) / p.tpi;
+  n.dn = wide ? 0 : (cnt + p.tpi_dn - 1) / p.tpi_dn;
+  n.gwf = wide ? cnt / p.tpi_w : 0;
+  n.gwp = wide && cnt % p.tpi_w ? 1 : 0;
+  n.dwf = wide ? cnt / p.tpi_dnw : 0;
+  n.dwp = wide && cnt % p.tpi_dnw ? 1 : 0;
+  return n;
+}
+
+// Sums over group j (count cnt, bitwidths qjg / qjd) that place group e's
+// entries and items: a[0] entry offset; positions before e in bitwidth order
+// a[1] narrow gate_up, a[2] narrow down, a[3] / a[4] wide gate_up full /
+// partial, a[5] / a[6] wide down full / partial; totals a[7] narrow gate_up,
+// a[8] narrow down, a[9] / a[10] wide gate_up full / partial, a[11] / a[12]
+// wide down full / partial.
+constexpr int kSums = 13;
+__host__ __device__ constexpr bool wide_sum(int i) { return (i >= 3 && i <= 6) || i >= 9; }
+template <bool WIDE>
+__device__ __forceinline__ void add_group(const FfnParams& p, int (&a)[kSums], int j, int cnt, int qjg, int qjd,
+                                          int e, int qg, int qd) {
+  const GroupItems n = group_items<WIDE>(p, cnt);
+  const bool before_g = qjg > qg || (qjg == qg && j < e);
+  const bool before_d = qjd > qd || (qjd == qd && j < e);
+  if (j < e) a[0] += cnt;
+  if (before_g) {
+    a[1] += n.gu;
+    a[3] += n.gwf;
+    a[4] += n.gwp;
+  }
+  if (before_d) {
+    a[2] += n.dn;
+    a[5] += n.dwf;
+    a[6] += n.dwp;
+  }
+  a[7] += n.gu;
+  a[8] += n.dn;
+  a[9] += n.gwf;
+  a[10] += n.gwp;
+  a[11] += n.dwf;
+  a[12] += n.dwp;
+}
+
+// Writes group e's item entries (and, from group 0, the totals).
+template <bool WIDE>
+__device__ __forceinline__ void put_items(const FfnParams& p, const int (&r)[kSums], int e, int mine, int tid) {
+  const GroupItems n = group_items<WIDE>(p, mine);
+  if (tid == 0 && e == 0) {
+    p.n_items[0] = r[7];
+    p.n_items[1] = r[8];
+    p.n_items[2] = r[9] + r[10];
+    p.n_items[3] = r[11] + r[12];
+  }
+  for (int sp = tid; sp < n.gu; sp += 256) p.items[r[1] + sp] = (e << 16) | sp;
+  for (int sp = tid; sp < n.dn; sp += 256) p.items_dn[r[2] + sp] = (e << 16) | sp;
+  for (int sp = tid; sp < n.gwf; sp += 256) p.items_w[r[3] + sp] = (e << 16) | sp;
+  for (int sp = tid; sp < n.dwf; sp += 256) p.items_dnw[r[5] + sp] = (e << 16) | sp;
+  if (tid == 0 && n.gwp) p.items_w[r[9] + r[4]] = (e << 16) | n.gwf;
+  if (tid == 0 && n.dwp) p.items_dnw[r[11] + r[6]] = (e << 16) | n.dwf;
+}
+
+template <bool WIDE>
 __global__ __launch_bounds__(256) void k_group(FfnParams p) {
   __shared__ int hist[kMaxGroups];
-  __shared__ int red[5][4];
+  __shared__ int red[kSums][4];
   __shared__ int wtot[4];
   const int e = blockIdx.x, tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int T = p.T, K = p.K, S = p.S, E = p.E, KS = K + S, TK = T * K;
@@ -54,47 +129,35 @@ __global__ __launch_bounds__(256) void k_group(FfnParams p) {
     if (x >= 0 && x < E) atomicAdd(&hist[x], 1);
   }
   __syncthreads();
-  // position of this group's entries (group order), of its items in both
+  // position of this group's entries (group order), of its items in the
   // bitwidth-ordered lists, and the item totals: sums over the groups, one per
   // thread, reduced
   const int mine = e < E ? hist[e] : T;
-  const int ni = (mine + p.tpi - 1) / p.tpi, ni_dn = (mine + p.tpi_dn - 1) / p.tpi_dn;
-  int a[5] = {0, 0, 0, 0, 0};  // offset, gate_up position, down position, gate_up total, down total
+  int a[kSums] = {};
 #pragma unroll
   for (int c = 0; c < 3; ++c) {
     const int j = tid + 256 * c;
-    if (j < p.NB) {
-      const int cnt = j < E ? hist[j] : T;
-      const int n = (cnt + p.tpi - 1) / p.tpi, n_dn = (cnt + p.tpi_dn - 1) / p.tpi_dn;
-      if (j < e) a[0] += cnt;
-      if (qjg[c] > qg || (qjg[c] == qg && j < e)) a[1] += n;
-      if (qjd[c] > qd || (qjd[c] == qd && j < e)) a[2] += n_dn;
-      a[3] += n;
-      a[4] += n_dn;
-    }
+    if (j < p.NB) add_group<WIDE>(p, a, j, j < E ? hist[j] : T, qjg[c], qjd[c], e, qg, qd);
   }
 #pragma unroll
-  for (int i = 0; i < 5; ++i) {
+  for (int i = 0; i < kSums; ++i) {
+    if (wide_sum(i) && !WIDE) continue;  // zero without wide items
 #pragma unroll
     for (int o = 32; o >= 1; o >>= 1) a[i] += __shfl_xor(a[i], o);
     if (lane == 0) red[i][w] = a[i];
   }
   __syncthreads();
-  int r[5];
+  int r[kSums];
 #pragma unroll
-  for (int i = 0; i < 5; ++i) r[i] = red[i][0] + red[i][1] + red[i][2] + red[i][3];
-  const int off = r[0], igu = r[1], idn = r[2];
+  for (int i = 0; i < kSums; ++i)
+    r[i] = wide_sum(i) && !WIDE ? 0 : red[i][0] + red[i][1] + red[i][2] + red[i][3];
+  const int off = r[0];
   if (tid == 0) {
     p.offsets[e] = off;
     p.counts[e] = mine;
     if (e == p.NB - 1) p.offsets[p.NB] = off + mine;
-    if (e == 0) {
-      p.n_items[0] = r[3];
-      p.n_items[1] = r[4];
-    }
   }
-  for (int sp = tid; sp < ni; sp += 256) p.items[igu + sp] = (e << 16) | sp;
-  for (int sp = tid; sp < ni_dn; sp += 256) p.items_dn[idn + sp] = (e << 16) | sp;
+  put_items<WIDE>(p, r, e, mine, tid);
   if (e < E) {
     int run = 0;
     for (int b0 = 0, c = 0; b0 < TK; b0 += 256, ++c) {
@@ -168,8 +231,9 @@ __global__ __launch_bounds__(256) void k_chunk_scan(FfnParams p, int32_t* ccnt, 
   p.counts[e] = run;
 }
 
+template <bool WIDE>
 __global__ __launch_bounds__(256) void k_chunk_scatter(FfnParams p, const int32_t* ccnt) {
-  __shared__ int red[5][4];
+  __shared__ int red[kSums][4];
   __shared__ int wtot[4];
   const int e = blockIdx.x, c = blockIdx.y, tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int T = p.T, K = p.K, E = p.E, KS = K + p.S, TK = T * K;
@@ -177,41 +241,29 @@ __global__ __launch_bounds__(256) void k_chunk_scatter(FfnParams p, const int32_
   // this group's offset and item positions as in k_group
   const int qg = p.q[2 * e], qd = p.q[2 * e + 1];
   const int mine = e < E ? p.counts[e] : T;
-  const int ni = (mine + p.tpi - 1) / p.tpi, ni_dn = (mine + p.tpi_dn - 1) / p.tpi_dn;
-  int a[5] = {0, 0, 0, 0, 0};
-  for (int j = tid; j < p.NB; j += 256) {
-    const int cnt = j < E ? p.counts[j] : T;
-    const int n = (cnt + p.tpi - 1) / p.tpi, n_dn = (cnt + p.tpi_dn - 1) / p.tpi_dn;
-    const int qjg = p.q[2 * j], qjd = p.q[2 * j + 1];
-    if (j < e) a[0] += cnt;
-    if (qjg > qg || (qjg == qg && j < e)) a[1] += n;
-    if (qjd > qd || (qjd == qd && j < e)) a[2] += n_dn;
-    a[3] += n;
-    a[4] += n_dn;
-  }
+  int a[kSums] = {};
+  for (int j = tid; j < p.NB; j += 256)
+    add_group<WIDE>(p, a, j, j < E ? p.counts[j] : T, p.q[2 * j], p.q[2 * j + 1], e, qg, qd);
 #pragma unroll
-  for (int i = 0; i < 5; ++i) {
+  for (int i = 0; i < kSums; ++i) {
+    if (wide_sum(i) && !WIDE) continue;  // zero without wide items
 #pragma unroll
     for (int o = 32; o >= 1; o >>= 1) a[i] += __shfl_xor(a[i], o);
     if (lane == 0) red[i][w] = a[i];
   }
   __syncthreads();
-  int r[5];
+  int r[kSums];
 #pragma unroll
-  for (int i = 0; i < 5; ++i) r[i] = red[i][0] + red[i][1] + red[i][2] + red[i][3];
+  for (int i = 0; i < kSums; ++i)
+    r[i] = wide_sum(i) && !WIDE ? 0 : red[i][0] + red[i][1] + red[i][2] + red[i][3];
   const int off = r[0];
   if (c == 0) {
     if (tid == 0) {
       p.offsets[e] = off;
       if (e >= E) p.counts[e] = mine;
       if (e == p.NB - 1) p.offsets[p.NB] = off + mine;
-      if (e == 0) {
-        p.n_items[0] = r[3];
-        p.n_items[1] = r[4];
-      }
     }
-    for (int sp = tid; sp < ni; sp += 256) p.items[r[1] + sp] = (e << 16) | sp;
-    for (int sp = tid; sp < ni_dn; sp += 256) p.items_dn[r[2] + sp] = (e << 16) | sp;
+    put_items<WIDE>(p, r, e, mine, tid);
   }
   if (e < E) {
     int run = off + ccnt[(size_t)c * E + e];
@@ -255,13 +307,17 @@ int group_chunks(int T, int K) {
 
 hipError_t launch_permute(const FfnParams& p, int32_t* ccnt, hipStream_t s) {
   const int nc = group_chunks(p.T, p.K);
+  // WIDE: the variants that also list the wide items (a layer and batch that use them)
+  const bool wide = p.wide_from > 0;
   if (nc == 0) {
-    hipLaunchKernelGGL(k_group, dim3(p.NB), dim3(256), 0, s, p);
+    if (wide) hipLaunchKernelGGL(k_group<true>, dim3(p.NB), dim3(256), 0, s, p);
+    else hipLaunchKernelGGL(k_group<false>, dim3(p.NB), dim3(256), 0, s, p);
     return hipGetLastError();
   }
   hipLaunchKernelGGL(k_chunk_hist, dim3(nc), dim3(256), 0, s, p, ccnt);
   hipLaunchKernelGGL(k_chunk_scan, dim3((p.E + 255) / 256), dim3(256), 0, s, p, ccnt, nc);
-  hipLaunchKernelGGL(k_chunk_scatter, dim3(p.NB, nc), dim3(256), 0, s, p, (const int32_t*)ccnt);
+  if (wide) hipLaunchKernelGGL(k_chunk_scatter<true>, dim3(p.NB, nc), dim3(256), 0, s, p, (const int32_t*)ccnt);
+  else hipLaunchKernelGGL(k_chunk_scatter<false>, dim3(p.NB, nc), dim3(256), 0, s, p, (const int32_t*)ccnt);
   return hipGetLastError();
 }
 

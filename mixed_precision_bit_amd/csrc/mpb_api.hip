@@ -170,7 +170,10 @@ WsLayout ws_layout(int T, int H, int I, int E, int S, int K, bool bf16) {
   L.max_items = max_decode_items(T, E, S, K);
   L.items = off;   off += align256((size_t)L.max_items * 4);
   L.items_dn = off; off += align256((size_t)L.max_items * 4);
-  L.n_items = off; off += 256;  // [2]
+  L.max_items_w = ffn_wide_from(T, H, I, E, S, K) ? max_wide_items(T, E, S, K) : 0;
+  L.items_w = off;  off += align256((size_t)L.max_items_w * 4);
+  L.items_dnw = off; off += align256((size_t)L.max_items_w * 4);
+  L.n_items = off; off += 256;  // [4]
   L.ccnt = off;    off += align256((size_t)group_chunks(T, K) * E * 4);
   L.hhi = off;     off += align256(P * (size_t)I * 2);
   L.hlo = off;     off += align256(P * (size_t)I * 2);
@@ -207,6 +210,13 @@ mpb::FfnParams ffn_params(const mpb::WsLayout& L, char* ws, const void* X_dev, i
   p.max_items = L.max_items;
   p.tpi = mpb::kChunkTokens * tc;
   p.tpi_dn = mpb::kChunkTokens;
+  // no wide items unless the caller enables them (ffn_impl)
+  p.items_w = (int32_t*)(ws + L.items_w);
+  p.items_dnw = (int32_t*)(ws + L.items_dnw);
+  p.max_items_w = L.max_items_w;
+  p.wide_from = 0;
+  p.tpi_w = mpb::kWideTokGu;
+  p.tpi_dnw = mpb::kWideTokDn;
   p.hhi = (uint16_t*)(ws + L.hhi);
   p.hlo = (uint16_t*)(ws + L.hlo);
   p.y = (float*)(ws + L.y);
@@ -405,11 +415,14 @@ int ffn_impl(const char* name, const void* X_dev, int x_dtype, int T, const int3
     return fail(MPB_E_WS, n + ": workspace " + std::to_string(ws_bytes) + " < " + std::to_string(L.total));
   }
   char* ws = (char*)ws_dev;
-  const int tc = mpb::ffn_token_chunks(T, g.E, g.K);
+  // with the wide kernels taking the large groups, the rest are small: they
+  // take 32-token items
+  const int tc = mpb::ffn_wide_from(T, g.H, g.I, g.E, g.S, g.K) ? 1 : mpb::ffn_token_chunks(T, g.E, g.K);
   mpb::FfnParams p = ffn_params(L, ws, X_dev, x_dtype, T, topk_idx_dev, topk_w_dev, planes_dev, luts_dev, q_dev,
                                 out_dev, tc);
   p.dn_split = mpb::dn_splits(T, g.H, g.I, g.E, g.S, g.K);
   p.dn_hcs = mpb::dn_range_hcs(g.I, p.dn_split);
+  p.wide_from = mpb::ffn_wide_from(T, g.H, g.I, g.E, g.S, g.K);
   hipStream_t s = (hipStream_t)stream;
   mark(0, s);
   hipError_t e = hipSuccess;
@@ -424,11 +437,25 @@ int ffn_impl(const char* name, const void* X_dev, int x_dtype, int T, const int3
     qmax_gu = std::max(qmax_gu, g.q[i]);
     qmax_dn = std::max(qmax_dn, g.q[i + 1]);
   }
-  // events 1 and 2 time the gate_up kernel itself: its launch records them
-  e = mpb::launch_gate_up(p, qmax_gu, tc, s, g_nev >= 5 ? g_ev[1] : nullptr, g_nev >= 5 ? g_ev[2] : nullptr);
+  // events 1 and 2 time the gate_up kernels themselves: their launches record
+  // them (the wide launch, when there is one, records the start, the other
+  // launch the end)
+  hipEvent_t e1 = g_nev >= 5 ? g_ev[1] : nullptr, e2 = g_nev >= 5 ? g_ev[2] : nullptr;
+  if (p.wide_from) {
+    e = mpb::launch_wide(p, true, qmax_gu, s, e1, nullptr);
+    if (e != hipSuccess) return hip_fail(e, (n + ": wide gate_up").c_str());
+    e1 = nullptr;
+  }
+  e = mpb::launch_gate_up(p, qmax_gu, tc, s, e1, e2);
   if (e != hipSuccess) return hip_fail(e, (n + ": gate_up").c_str());
-  // events 5 and 6 (optional) time the down kernel itself
-  e = mpb::launch_down(p, qmax_dn, tc == 1, s, g_nev == 7 ? g_ev[5] : nullptr, g_nev == 7 ? g_ev[6] : nullptr);
+  // events 5 and 6 (optional) time the down kernels themselves
+  hipEvent_t e5 = g_nev == 7 ? g_ev[5] : nullptr, e6 = g_nev == 7 ? g_ev[6] : nullptr;
+  if (p.wide_from) {
+    e = mpb::launch_wide(p, false, qmax_dn, s, e5, nullptr);
+    if (e != hipSuccess) return hip_fail(e, (n + ": wide down").c_str());
+    e5 = nullptr;
+  }
+  e = mpb::launch_down(p, qmax_dn, tc == 1, s, e5, e6);
   if (e != hipSuccess) return hip_fail(e, (n + ": down").c_str());
   mark(3, s);
   e = mpb::launch_combine(p, s);

@@ -42,10 +42,18 @@ struct FfnParams {
   int32_t* ent;               // [P] (token, slot) of each grouped entry: t (K + S) + slot
   int32_t* items;             // [max_items] gate_up work items: (group << 16) | token split
   int32_t* items_dn;          // [max_items] down work items, same encoding
-  int32_t* n_items;           // [2] number of valid items: gate_up, down
+  int32_t* n_items;           // [4] number of valid items: gate_up, down, wide gate_up, wide down
   int max_items;              // capacity of items (host bound)
   int tpi;                    // gate_up tokens per item: kChunkTokens * TC
   int tpi_dn;                 // down tokens per item: kChunkTokens
+  // wide items (groups of at least wide_from tokens; 0: none): the grouped-GEMM
+  // kernels of k_ffn_wide.hip take them, the kernels above only the other groups
+  int32_t* items_w;           // [max_items_w] wide gate_up items, same encoding (tpi_w tokens each)
+  int32_t* items_dnw;         // [max_items_w] wide down items (tpi_dnw tokens each)
+  int max_items_w;            // capacity of items_w and items_dnw
+  int wide_from;              // smallest group that takes the wide kernels (0: none)
+  int tpi_w;                  // wide gate_up tokens per item
+  int tpi_dnw;                // wide down tokens per item
   uint16_t* hhi;              // [P][I] fp16 high part of h = SiLU(gate) * up
   uint16_t* hlo;              // [P][I] fp16 remainder h - hi
   float* y;                   // [dn_split][T (K + S)][H] down projection of each (token, slot) (partial sums over K ranges)
@@ -77,8 +85,9 @@ inline int dn_range_hcs(int I, int n) {
 }
 
 struct WsLayout {
-  size_t counts, offsets, ptok, pw, ent, items, items_dn, n_items, ccnt, hhi, hlo, y, xh, xsc, total;
-  int max_items;
+  size_t counts, offsets, ptok, pw, ent, items, items_dn, items_w, items_dnw, n_items, ccnt, hhi, hlo, y, xh, xsc,
+      total;
+  int max_items, max_items_w;
 };
 // Upper bound on work items (one per tpi-token split of a group with tokens):
 // sum_g ceil(cnt_g / tpi) <= min(NB, P) + P / tpi for P grouped entries; the
@@ -88,6 +97,28 @@ inline int max_decode_items(int T, int E, int S, int K) {
   return (int)((P < NB ? P : NB) + P / kChunkTokens);
 }
 WsLayout ws_layout(int T, int H, int I, int E, int S, int K, bool bf16);
+
+// Wide items: a group of at least kWideFrom tokens runs as a grouped GEMM whose
+// workgroups dequantise a 128-row weight tile once per K step into LDS and
+// multiply it with kWideTokGu (gate_up) or kWideTokDn (down: h hi and lo, two
+// columns per token) tokens. Used where a layer's groups can reach that size
+// (batches of at least kWideBatch tokens: smaller ones hold too few such
+// groups to fill the chip with these long workgroups, and their 32-token items
+// finish sooner) and its down projection is not split over K ranges.
+constexpr int kWideFrom = 256;
+constexpr int kWideBatch = 2048;
+constexpr int kWideTokGu = 512;
+constexpr int kWideTokDn = 256;
+inline int ffn_wide_from(int T, int H, int I, int E, int S, int K) {
+  return T >= kWideBatch && dn_splits(T, H, I, E, S, K) == 1 ? kWideFrom : 0;
+}
+// Upper bound on wide items of either list: sum_g ceil(cnt_g / kWideTokDn) over
+// groups of at least kWideFrom entries.
+inline int max_wide_items(int T, int E, int S, int K) {
+  const long long P = (long long)T * (K + S), NB = (long long)E + S;
+  const long long g = P / kWideFrom;
+  return (int)(P / kWideTokDn + (g < NB ? g : NB));
+}
 
 // The FFN kernels stage activation and h rows through buffer descriptors with
 // 32-bit byte offsets, kNoRow standing for "no row" (reads as zeros): the
@@ -145,6 +176,9 @@ hipError_t launch_down_df(const FfnParams& p, int qmax, bool nt, hipStream_t s, 
 hipError_t launch_down(const FfnParams& p, int qmax, bool nt, hipStream_t s, hipEvent_t ev0 = nullptr,
                        hipEvent_t ev1 = nullptr);
 hipError_t launch_combine(const FfnParams& p, hipStream_t s);
+// The wide (grouped-GEMM) gate_up and down launches; no-ops when p.wide_from is 0.
+hipError_t launch_wide(const FfnParams& p, bool gu, int qmax, hipStream_t s, hipEvent_t ev0 = nullptr,
+                       hipEvent_t ev1 = nullptr);
 hipError_t launch_set_q(int32_t* q, int i, int b, hipStream_t s);
 
 // The whole layer in one persistent launch (k_fused.hip).

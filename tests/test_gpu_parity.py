@@ -579,9 +579,11 @@ def test_chunked_grouping_large_batch(layer_cache):
         i1, w1, o1, i2, w2, o2, _ = _separate_and_fused(D, Xb, "f16")
         X, z, r = oracle_route(L, Xb)
         assert np.array_equal(i1, z)
-        assert_close(o1, O.moe_ffn(X, z, r, L), f"T={T}")
-        assert_close(o2, O.moe_ffn(X, z, r, L), f"T={T} fused")
-        assert np.array_equal(o1.view(np.uint32), o2.view(np.uint32))
+        ref = O.moe_ffn(X, z, r, L)
+        assert_close(o1, ref, f"T={T}")
+        assert_close(o2, ref, f"T={T} fused")
+        if not _wide(L, T):
+            assert np.array_equal(o1.view(np.uint32), o2.view(np.uint32))
 
 
 def test_largest_batch_sampled(layer_cache):
@@ -597,9 +599,12 @@ def test_largest_batch_sampled(layer_cache):
     X, z, r = oracle_route(L, Xb)
     assert np.array_equal(i1, z)
     toks = np.unique(np.concatenate([np.arange(0, T, 1021), [T - 1]]))
-    assert_close(o1[toks], O.moe_ffn(X[toks], z[toks], r[toks], L), f"T={T} sampled")
+    ref = O.moe_ffn(X[toks], z[toks], r[toks], L)
+    assert_close(o1[toks], ref, f"T={T} sampled")
+    assert_close(o2[toks], ref, f"T={T} sampled, fused")
     assert np.array_equal(i1, i2)
-    assert np.array_equal(o1.view(np.uint32), o2.view(np.uint32))
+    if not _wide(L, T):
+        assert np.array_equal(o1.view(np.uint32), o2.view(np.uint32))
 
 
 def test_bf16_beyond_fp16_range_every_element(layer_cache):
@@ -831,6 +836,15 @@ def _separate_and_fused(D, Xb, xdtype):
             out2.cpu().numpy(), ws2)
 
 
+def _wide(L, T):
+    """moe_ffn runs groups of at least 256 tokens through the grouped-GEMM
+    kernels (weight tiles dequantised once per K step into LDS, 512 / 256
+    tokens per workgroup) in batches of at least 2048 tokens; moe_fused keeps
+    32-token items for every group, so the two agree bit for bit only below
+    that size (both are held to the oracle either way)."""
+    return T >= 2048
+
+
 def _prefill_items(L, T):
     """moe_ffn takes 128-token gate_up work items (four 32-token chunks per
     dequantised weight operand) once a routed group holds 96 tokens on
@@ -842,7 +856,9 @@ def _prefill_items(L, T):
 def test_fused_launch_equals_separate_calls(cfg, layer_cache):
     """moe_fused (one persistent launch, PagedWeight §3.3) gives bit for bit
     the routing and output of moe_route + moe_ffn, which the other tests hold
-    to the oracle; the small layers are also checked against the oracle here.
+    to the oracle, where both take the same FFN kernels; at the prefill size
+    (grouped-GEMM kernels for the large groups in moe_ffn) it is held to the
+    oracle itself. The small layers are also checked against the oracle here.
     Its counters are back at zero after the call."""
     L, D = dev_layer(layer_cache, cfg)
     Xb = S.make_tokens(cfg)
@@ -851,8 +867,13 @@ def test_fused_launch_equals_separate_calls(cfg, layer_cache):
     i1, w1, o1, i2, w2, o2, ws2 = _separate_and_fused(D, Xb, xdtype)
     assert np.array_equal(i1, i2)
     assert np.array_equal(w1.view(np.uint32), w2.view(np.uint32))
-    assert np.array_equal(o1.view(np.uint32), o2.view(np.uint32)), \
-        f"max |diff| {np.abs(o1.astype(np.float64) - o2).max()}"
+    if _wide(L, Xb.shape[0]):
+        X, z, r = oracle_route(L, Xb)
+        assert_close(o2, O.moe_ffn(X, z, r, L), f"cfg{cfg} fused")
+        assert_close(o1, o2.astype(np.float64), f"cfg{cfg} separate vs fused")
+    else:
+        assert np.array_equal(o1.view(np.uint32), o2.view(np.uint32)), \
+            f"max |diff| {np.abs(o1.astype(np.float64) - o2).max()}"
     assert int(ws2[:M().moe_fused_counter_bytes()].count_nonzero()) == 0, "counters not reset"
     if cfg in (0, 10, 11):
         X, z, r = oracle_route(L, Xb)
