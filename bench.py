@@ -32,7 +32,7 @@ HBM_PEAK_GBS = 8000.0
 MFMA_PEAK_TFLOPS = 2500.0  # dense fp16 MFMA
 METRIC = "MoE-layer tokens/s and achieved HBM GB/s (% of peak) at mixed bitwidths"
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_ffn_qwen15moe_decode.md")
-KERNEL_SRCS = ["k_ffn_decode.hip", "k_ffn_decode_df.hip", "k_ffn_kernels.h", "k_ffn_body.h", "mpb_device.h"]
+KERNEL_SRCS = ["k_ffn_decode.hip", "k_ffn_decode_df.hip", "k_ffn_kernels.h", "k_ffn_body.h", "mpb_device.h", "k_ffn_wide.hip"]
 
 
 def _code_only(text):

@@ -105,7 +105,7 @@ WsLayout ws_layout(int T, int H, int I, int E, int S, int K, bool bf16);
 // (batches of at least kWideBatch tokens: smaller ones hold too few such
 // groups to fill the chip with these long workgroups, and their 32-token items
 // finish sooner) and its down projection is not split over K ranges.
-constexpr int kWideFrom = 256;
+constexpr int kWideFrom = 96;
 constexpr int kWideBatch = 2048;
 constexpr int kWideTokGu = 512;
 constexpr int kWideTokDn = 256;

@@ -630,6 +630,42 @@ def test_bf16_beyond_fp16_range_every_element(layer_cache):
     assert np.array_equal(o1.view(np.uint32), o2.view(np.uint32))
 
 
+def test_bf16_beyond_fp16_range_wide_groups(layer_cache):
+    """The per-token power-of-two scale of bf16 activations beyond the fp16
+    range in a batch whose large groups take the grouped-GEMM kernels
+    (4000 tokens, Zipf-skewed router bias, H = I = 192: a ragged last row tile
+    of the down projection and an odd number of 64-K steps): tokens holding
+    values up to ~1e6 times their draw, and one far below the fp16 normal
+    range, among ordinary ones, every output element against the oracle."""
+    L, D = dev_layer(layer_cache, 11)
+    T = 4000
+    Xb = S.make_tokens(11, T=T, seed=8000 + T).copy()
+    X0, z0, _ = oracle_route(L, Xb)
+    cnt0 = np.bincount(z0.ravel(), minlength=L.E)
+    wide0 = np.nonzero(cnt0 >= WIDE_FROM)[0]
+    # scaled far up, a token goes to its unbiased best expert: take tokens whose
+    # unbiased best expert is a large group, so that they stay in one
+    best = np.argmax(X0 @ L.W_r.T, axis=1)
+    cand = [int(t) for t in np.nonzero(np.isin(best, wide0))[0]]
+    big = (cand[0], cand[len(cand) // 2], cand[-1])
+    small = next(t for t in range(T) if t not in big and int(z0[t, 0]) in wide0)
+    for t, f in zip(big + (small,), (1e6, 3e4, 1e5, 1e-30)):
+        Xb[t] = S.f32_to_bf16_bits((S.bf16_bits_to_f64(Xb[t]) * f).astype(np.float32))
+    X, z, r = oracle_route(L, Xb)
+    assert all(np.abs(X[t]).max() > 65504 for t in big)
+    cnt = np.bincount(z.ravel(), minlength=L.E)
+    wide = set(np.nonzero(cnt >= WIDE_FROM)[0].tolist())
+    assert _wide(L, T) and wide, "the batch must hold groups for the grouped-GEMM kernels"
+    assert all(int(z[t, 0]) in wide for t in big + (small,)), "the scaled tokens must sit in wide groups"
+    say(f"  wide groups {sorted(wide)}, sizes {sorted(cnt[list(wide)].tolist())}, scaled tokens {big + (small,)}")
+    gi, _, gout = run_layer(D, Xb, "bf16")
+    assert np.array_equal(gi, z)
+    ref = O.moe_ffn(X, z, r, L)
+    assert_close(gout, ref, "every token")
+    for t in big + (small,):
+        assert_close(gout[t], ref[t], f"token {t}", guard=None)
+
+
 @pytest.mark.parametrize("cfg", [12, 13, 14, 15, 16])
 def test_edge_shapes_every_element(cfg, layer_cache):
     """Extreme layer shapes, every element against the oracle on both paths:
@@ -836,8 +872,11 @@ def _separate_and_fused(D, Xb, xdtype):
             out2.cpu().numpy(), ws2)
 
 
+WIDE_FROM = 96  # smallest group of the grouped-GEMM kernels (batches of >= 2048 tokens)
+
+
 def _wide(L, T):
-    """moe_ffn runs groups of at least 256 tokens through the grouped-GEMM
+    """moe_ffn runs groups of at least 96 tokens through the grouped-GEMM
     kernels (weight tiles dequantised once per K step into LDS, 512 / 256
     tokens per workgroup) in batches of at least 2048 tokens; moe_fused keeps
     32-token items for every group, so the two agree bit for bit only below
