@@ -823,17 +823,21 @@ def test_abi_errors_after_init(layer_cache):
     torch.cuda.synchronize()
 
 
-def test_graph_replay_matches_eager(layer_cache):
+@pytest.mark.parametrize("cfg,T", [(10, None), (11, 4000)])
+def test_graph_replay_matches_eager(cfg, T, layer_cache):
     """moe_route + moe_ffn captured in a HIP graph: every replay, with eager
-    work and synchronisation in between, reproduces the eager result bitwise."""
-    L, D = dev_layer(layer_cache, 10)
-    Xb = S.make_tokens(10)
+    work and synchronisation in between, reproduces the eager result bitwise
+    (a small batch, and a 4000-token bf16 batch whose large groups take the
+    grouped-GEMM kernels)."""
+    L, D = dev_layer(layer_cache, cfg)
+    Xb = S.make_tokens(cfg, T=T, seed=None if T is None else 9100 + T)
+    xdt = L.cfg["xdtype"]
     X = to_dev_x(Xb)
     T = Xb.shape[0]
     idx, w = D.alloc_route(T)
     out, ws = D.alloc_ffn(T)
-    D.route(X, "f16", idx, w)
-    D.ffn(X, "f16", idx, w, out, ws)
+    D.route(X, xdt, idx, w)
+    D.ffn(X, xdt, idx, w, out, ws)
     torch.cuda.synchronize()
     eager = out.cpu().numpy().copy()
     s = torch.cuda.Stream()
@@ -841,8 +845,8 @@ def test_graph_replay_matches_eager(layer_cache):
     g = torch.cuda.CUDAGraph()
     with torch.cuda.stream(s):
         with torch.cuda.graph(g, stream=s):
-            D.route(X, "f16", idx, w)
-            D.ffn(X, "f16", idx, w, out, ws)
+            D.route(X, xdt, idx, w)
+            D.ffn(X, xdt, idx, w, out, ws)
     torch.cuda.current_stream().wait_stream(s)
     torch.cuda.synchronize()
     for rep in range(4):
