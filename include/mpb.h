@@ -124,13 +124,17 @@ int mpb_pack_table(int kind, const uint16_t* lut_dev, int N, int b, uint16_t* im
  * MPB_BF16); W_router_dev: [E][H] fp32; bias_dev: [E] fp32 added to the
  * logits, or NULL. Logits are accumulated in fp64 (every product of an
  * activation and a router weight is exact in fp64) in a fixed order. Writes
- * topk_idx_dev [T][K] int32 (descending logit, ties to the lower expert index)
- * and topk_w_dev [T][K] fp32 = softmax over all E experts restricted to the K
- * winners and renormalised (equal to a softmax over the K winning logits).
+ * topk_idx_dev [T][K] int32: the K largest exact logits in descending order,
+ * ties to the lower expert index (the fp64 order is checked against a bound
+ * on its rounding error; experts the bound cannot separate are ranked again
+ * on their exact sums), and topk_w_dev [T][K] fp32 = softmax over all E
+ * experts restricted to the K winners and renormalised (equal to a softmax
+ * over the K winning fp64 logits).
  * ws_dev: device workspace of ws_bytes >= moe_route_workspace_bytes(T, E)
- * (fp64 logits, summed in up to 8 hidden-dimension parts for small batches;
- * unused for batches of up to 128 tokens with E * H <= 16384, whose logits
- * stay on chip; contents not preserved). Needs
+ * (fp64 logits, summed in up to 8 hidden-dimension parts for small batches,
+ * and the norms that bound their rounding error; unused for batches of up to
+ * 128 tokens with E * H <= 16384, whose logits stay on chip; contents not
+ * preserved). Needs
  * 1 <= K <= min(E, 16), E <= 512, H a multiple of 64 up to 65536, T <= 2^20;
  * T == 0 is a no-op. Errors: MPB_E_ARG, MPB_E_SHAPE, MPB_E_WS, MPB_E_HIP.
  * Does not need mpb_init.

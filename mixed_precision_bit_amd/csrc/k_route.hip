@@ -18,7 +18,11 @@
 // is finished by one lane. Logits go to the workspace ([T][E] fp64).
 //
 // k_route_topk: one wave per token. Expert e is selected at position
-// rank(e) = #{experts that beat it} when rank(e) < K.
+// rank(e) = #{experts that beat it} when rank(e) < K. The logits' rounding
+// error is bounded from norms the logits kernels store beside them; a top-K
+// that the bound cannot certify is ranked again on exact logits
+// (topk_certify), so the selection and its order are those of the exact
+// logits, ties to the lower index.
 //
 // k_route_small (batches of up to kSmallT tokens, router matrices of up to
 // kSmallEH entries): one workgroup per token sums each of its logits whole
@@ -43,7 +47,8 @@ __global__ __launch_bounds__(256) void k_route_logits(const uint16_t* __restrict
   __shared__ double part[4][kTT * EW * 65];  // +1 column: the summing lanes read rows without bank conflicts
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const long long u = (long long)blockIdx.x * 4 + w;
-  logits_partials<XDT, EW, NPC>(X, W, T, H, E, ks, u, lane, part[w]);
+  logits_partials<XDT, EW, NPC>(X, W, T, H, E, ks, u, lane, part[w], route_ws_l1(logits, ks, T, E),
+                                route_ws_xinf(logits, ks, T, E));
   __syncthreads();
   logits_sum<EW>(T, E, ks, u, lane, part[w], logits);
 }
@@ -51,21 +56,30 @@ __global__ __launch_bounds__(256) void k_route_logits(const uint16_t* __restrict
 template <int XDT>
 __global__ __launch_bounds__(256) void k_route_logits_mfma(const uint16_t* __restrict__ X, const float* __restrict__ W,
                                                            int T, int H, int E, double* __restrict__ logits) {
-  logits_tile_mfma<XDT>(X, W, T, H, E, (long long)blockIdx.x * 4 + (threadIdx.x >> 6), threadIdx.x & 63, logits);
+  logits_tile_mfma<XDT>(X, W, T, H, E, (long long)blockIdx.x * 4 + (threadIdx.x >> 6), threadIdx.x & 63, logits,
+                        route_ws_l1(logits, 1, T, E), route_ws_xinf(logits, 1, T, E));
 }
 
-__global__ __launch_bounds__(256) void k_route_topk(const double* __restrict__ logits, const float* __restrict__ bias,
-                                                    int ks, int T, int E, int K, int32_t* __restrict__ idx_out,
+template <int XDT>
+__global__ __launch_bounds__(256) void k_route_topk(const double* __restrict__ logits, const uint16_t* __restrict__ X,
+                                                    const float* __restrict__ W, const float* __restrict__ bias,
+                                                    int ks, int T, int H, int E, int K, int32_t* __restrict__ idx_out,
                                                     float* __restrict__ w_out) {
   __shared__ double lg[4][kEMaxTopk];
   __shared__ double sel_v[4][16];
   __shared__ int sel_i[4][16];
+  __shared__ float l1[kEMaxTopk];
+  __shared__ ExactScratch sc[4];
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int t = blockIdx.x * 4 + w;
+  double* ws = const_cast<double*>(logits);
   topk_load(logits, bias, ks, t, T, E, lane, lg[w]);
+  topk_load_l1(route_ws_l1(ws, ks, T, E), ks, E, threadIdx.x, 256, l1);
+  const double xi = topk_xinf(route_ws_xinf(ws, ks, T, E), ks, t, T);
   __syncthreads();
   topk_rank(t, T, E, K, lane, lg[w], sel_v[w], sel_i[w]);
   __syncthreads();
+  topk_certify<XDT>(X, W, bias, t, T, H, E, K, lane, lg[w], l1, xi, sel_v[w], sel_i[w], sc[w]);
   topk_finish(t, T, K, lane, sel_v[w], sel_i[w], idx_out, w_out);
 }
 
@@ -76,17 +90,22 @@ __global__ __launch_bounds__(512) void k_route_small(const uint16_t* __restrict_
   __shared__ double lg[kEMaxTopk];
   __shared__ double sel_v[16];
   __shared__ int sel_i[16];
+  __shared__ float l1[kEMaxTopk];
+  __shared__ ExactScratch sc;
   const int t = blockIdx.x, lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const uint16_t* x = X + (size_t)t * H;
+  float xm = 0.0f;  // max-norm of the token (every wave covers all of it)
   for (int e0 = w * kSmallEW; e0 < E; e0 += 8 * kSmallEW) {
-    double a[kSmallEW];
+    double a[kSmallEW], n1[kSmallEW];
 #pragma unroll
-    for (int j = 0; j < kSmallEW; ++j) a[j] = 0.0;
+    for (int j = 0; j < kSmallEW; ++j) a[j] = n1[j] = 0.0;
 #pragma unroll 8
     for (int h = 4 * lane; h < H; h += 256) {
       const ushort4 xv = *(const ushort4*)(x + h);
-      const double x0 = x_to_f32<XDT>(xv.x), x1 = x_to_f32<XDT>(xv.y), x2 = x_to_f32<XDT>(xv.z),
-                   x3 = x_to_f32<XDT>(xv.w);
+      const float f0 = x_to_f32<XDT>(xv.x), f1 = x_to_f32<XDT>(xv.y), f2 = x_to_f32<XDT>(xv.z),
+                  f3 = x_to_f32<XDT>(xv.w);
+      xm = fmaxf(xm, fmaxf(fmaxf(fabsf(f0), fabsf(f1)), fmaxf(fabsf(f2), fabsf(f3))));
+      const double x0 = f0, x1 = f1, x2 = f2, x3 = f3;
 #pragma unroll
       for (int j = 0; j < kSmallEW; ++j) {
         const float4 wv = *(const float4*)(W + (size_t)min(e0 + j, E - 1) * H + h);
@@ -94,18 +113,28 @@ __global__ __launch_bounds__(512) void k_route_small(const uint16_t* __restrict_
         a[j] += x1 * (double)wv.y;
         a[j] += x2 * (double)wv.z;
         a[j] += x3 * (double)wv.w;
+        n1[j] += ((double)fabsf(wv.x) + (double)fabsf(wv.y)) + ((double)fabsf(wv.z) + (double)fabsf(wv.w));
       }
     }
 #pragma unroll
     for (int j = 0; j < kSmallEW; ++j) {
 #pragma unroll
-      for (int o = 32; o >= 1; o >>= 1) a[j] += __shfl_xor(a[j], o);
-      if (lane == 0 && e0 + j < E) lg[e0 + j] = a[j] + (bias ? (double)bias[e0 + j] : 0.0);
+      for (int o = 32; o >= 1; o >>= 1) {
+        a[j] += __shfl_xor(a[j], o);
+        n1[j] += __shfl_xor(n1[j], o);
+      }
+      if (lane == 0 && e0 + j < E) {
+        lg[e0 + j] = a[j] + (bias ? (double)bias[e0 + j] : 0.0);
+        l1[e0 + j] = (float)n1[j];
+      }
     }
   }
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) xm = fmaxf(xm, __shfl_xor(xm, o));
   __syncthreads();
   if (w == 0) topk_rank(t, T, E, K, lane, lg, sel_v, sel_i);
   __syncthreads();
+  if (w == 0) topk_certify<XDT>(X, W, bias, t, T, H, E, K, lane, lg, l1, (double)xm, sel_v, sel_i, sc);
   if (w == 0) topk_finish(t, T, K, lane, sel_v, sel_i, idx_out, w_out);
 }
 
@@ -151,10 +180,12 @@ hipError_t launch_routing_mass(const int32_t* idx, const float* w, int T, int E,
   return hipGetLastError();
 }
 
-// [ks][T][E] fp64 logit parts; ks <= 8 on the vector path (it depends on H,
-// which the size query does not take), 1 on the matrix-core path
+// [ks][T][E] fp64 logit parts, [ks][E] row 1-norms and [ks][T] token
+// max-norms; ks <= 8 on the vector path (it depends on H, which the size query
+// does not take), 1 on the matrix-core path
 size_t route_workspace_bytes(int T, int E) {
-  return ((size_t)(logits_use_mfma(T, E) ? 1 : 8) * T * E * 8 + 255) / 256 * 256;
+  const size_t ks = logits_use_mfma(T, E) ? 1 : 8;
+  return (ks * ((size_t)T * E + E + T) * 8 + 255) / 256 * 256;
 }
 
 template <int XDT>
@@ -195,7 +226,9 @@ hipError_t launch_route(const uint16_t* X, int xdt, const float* W, const float*
   else launch_logits<1>(X, W, T, H, E, ks, lg, s);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(k_route_topk, dim3((unsigned)((T + 3) / 4)), dim3(256), 0, s, lg, bias, ks, T, E, K, idx, w);
+  const dim3 grid((unsigned)((T + 3) / 4)), block(256);
+  if (xdt == 0) hipLaunchKernelGGL(k_route_topk<0>, grid, block, 0, s, lg, X, W, bias, ks, T, H, E, K, idx, w);
+  else hipLaunchKernelGGL(k_route_topk<1>, grid, block, 0, s, lg, X, W, bias, ks, T, H, E, K, idx, w);
   return hipGetLastError();
 }
 

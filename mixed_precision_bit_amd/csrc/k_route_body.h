@@ -21,6 +21,27 @@ __device__ __forceinline__ float x_to_f32(uint16_t v) {
   else return __builtin_bit_cast(float, (uint32_t)v << 16);
 }
 
+template <bool CO>
+__device__ __forceinline__ void st_f64(double* p, double v) {
+  if constexpr (CO) __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  else *p = v;
+}
+template <bool CO>
+__device__ __forceinline__ double ld_f64(const double* p) {
+  if constexpr (CO) return __hip_atomic_load(const_cast<double*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  else return *p;
+}
+
+// Router workspace (fp64): the logit parts [ks][T][E], then per hidden part
+// the 1-norms of the router rows [ks][E] and the max-norms of the tokens
+// [ks][T] that bound the logits' rounding error (see topk_certify).
+__host__ __device__ inline double* route_ws_l1(double* ws, int ks, int T, int E) {
+  return ws + (size_t)ks * T * E;
+}
+__host__ __device__ inline double* route_ws_xinf(double* ws, int ks, int T, int E) {
+  return ws + (size_t)ks * T * E + (size_t)ks * E;
+}
+
 // Hidden-dimension split of the vector-path logits: small batches give too
 // few (token tile, expert) units to fill the chip, so each logit is summed in
 // ks parts of the hidden pieces (by different waves) and the parts are added
@@ -37,10 +58,13 @@ __host__ __device__ inline int route_ksplit(int T, int H, int E) {
 // Logits, first half: wave unit u = (8-token tile, EW-expert group, hidden
 // part kp of ks) computes its 64 lanes' partial sums and writes them to part
 // ([8 EW][65] doubles, the wave's own LDS region). Units past the last one
-// write zeros.
-template <int XDT, int EW, int NPC>
+// write zeros. The units of the first token tile also store the 1-norms of
+// their router rows over part kp (wl1[kp][e]), those of the first expert
+// group the max-norms of their tokens over part kp (xinf[kp][t]).
+template <int XDT, int EW, int NPC, bool CO = false>
 __device__ __forceinline__ void logits_partials(const uint16_t* __restrict__ X, const float* __restrict__ W, int T,
-                                                int H, int E, int ks, long long u, int lane, double* part) {
+                                                int H, int E, int ks, long long u, int lane, double* part,
+                                                double* __restrict__ wl1, double* __restrict__ xinf) {
   const int ntt = (T + kTT - 1) / kTT, neg = (E + EW - 1) / EW;
   const bool live = u < (long long)ntt * neg * ks;
   const int tt = live ? (int)(u % ntt) : 0;
@@ -52,6 +76,12 @@ __device__ __forceinline__ void logits_partials(const uint16_t* __restrict__ X, 
   for (int k = 0; k < kTT; ++k)
 #pragma unroll
     for (int j = 0; j < EW; ++j) a[k][j] = 0.0;
+  double l1[EW];
+  float xm[kTT];
+#pragma unroll
+  for (int j = 0; j < EW; ++j) l1[j] = 0.0;
+#pragma unroll
+  for (int k = 0; k < kTT; ++k) xm[k] = 0.0f;
   if (live) {
     // pieces [p0, p1) of this part, NPC per pass, all loads of a pass in flight together
     const int npc = (H + 255) / 256, ppk = (npc + ks - 1) / ks;
@@ -75,11 +105,16 @@ __device__ __forceinline__ void logits_partials(const uint16_t* __restrict__ X, 
         xv[k] = *(const ushort4*)(X + (size_t)t * H + hc);
       }
 #pragma unroll
+      for (int j = 0; j < EW; ++j)
+        l1[j] += hin ? ((double)fabsf(wv[j].x) + (double)fabsf(wv[j].y)) +
+                           ((double)fabsf(wv[j].z) + (double)fabsf(wv[j].w))
+                     : 0.0;
+#pragma unroll
       for (int k = 0; k < kTT; ++k) {
-        const double x0 = hin ? (double)x_to_f32<XDT>(xv[k].x) : 0.0;
-        const double x1 = hin ? (double)x_to_f32<XDT>(xv[k].y) : 0.0;
-        const double x2 = hin ? (double)x_to_f32<XDT>(xv[k].z) : 0.0;
-        const double x3 = hin ? (double)x_to_f32<XDT>(xv[k].w) : 0.0;
+        const float f0 = hin ? x_to_f32<XDT>(xv[k].x) : 0.0f, f1 = hin ? x_to_f32<XDT>(xv[k].y) : 0.0f;
+        const float f2 = hin ? x_to_f32<XDT>(xv[k].z) : 0.0f, f3 = hin ? x_to_f32<XDT>(xv[k].w) : 0.0f;
+        xm[k] = fmaxf(xm[k], fmaxf(fmaxf(fabsf(f0), fabsf(f1)), fmaxf(fabsf(f2), fabsf(f3))));
+        const double x0 = f0, x1 = f1, x2 = f2, x3 = f3;
 #pragma unroll
         for (int j = 0; j < EW; ++j) {
           a[k][j] = fma(x0, (double)wv[j].x, a[k][j]);
@@ -94,6 +129,24 @@ __device__ __forceinline__ void logits_partials(const uint16_t* __restrict__ X, 
   for (int k = 0; k < kTT; ++k)
 #pragma unroll
     for (int j = 0; j < EW; ++j) part[(k * EW + j) * 65 + lane] = a[k][j];
+  if (live && tt == 0) {
+#pragma unroll
+    for (int j = 0; j < EW; ++j) {
+      double v = l1[j];
+#pragma unroll
+      for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o);
+      if (lane == 0 && e0 + j < E) st_f64<CO>(wl1 + (size_t)kp * E + e0 + j, v);
+    }
+  }
+  if (live && eg == 0) {
+#pragma unroll
+    for (int k = 0; k < kTT; ++k) {
+      float v = xm[k];
+#pragma unroll
+      for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
+      if (lane == 0 && t0 + k < T) st_f64<CO>(xinf + (size_t)kp * T + t0 + k, (double)v);
+    }
+  }
 }
 
 // Logits, second half (after a barrier): lane k EW + j sums the 64 partials of
@@ -129,7 +182,8 @@ typedef double f64x4 __attribute__((ext_vector_type(4)));
 
 template <int XDT, bool CO = false>
 __device__ __forceinline__ void logits_tile_mfma(const uint16_t* __restrict__ X, const float* __restrict__ W, int T,
-                                                 int H, int E, long long u, int lane, double* __restrict__ logits) {
+                                                 int H, int E, long long u, int lane, double* __restrict__ logits,
+                                                 double* __restrict__ wl1, double* __restrict__ xinf) {
   const int g = lane >> 4, c = lane & 15;
   const int ntt = (T + 15) >> 4, net = (E + 15) >> 4;
   if (u >= (long long)ntt * net) return;
@@ -138,6 +192,8 @@ __device__ __forceinline__ void logits_tile_mfma(const uint16_t* __restrict__ X,
   const uint16_t* xr = X + (size_t)t * H + 4 * g;
   const float* wr = W + (size_t)e * H + 4 * g;
   f64x4 acc = {0.0, 0.0, 0.0, 0.0};
+  double l1 = 0.0;  // this lane's share of the 1-norm of router row e and ...
+  float xm = 0.0f;  // ... of the max-norm of token t (the first tile row / column stores them)
   constexpr int kU = 8;  // 16-index steps per pass, loads of a pass in flight together
   for (int h0 = 0; h0 < H; h0 += 16 * kU) {
     ushort4 xv[kU];
@@ -151,12 +207,25 @@ __device__ __forceinline__ void logits_tile_mfma(const uint16_t* __restrict__ X,
 #pragma unroll
     for (int j = 0; j < kU; ++j) {
       if (h0 + 16 * j < H) {
+        l1 += ((double)fabsf(wv[j].x) + (double)fabsf(wv[j].y)) + ((double)fabsf(wv[j].z) + (double)fabsf(wv[j].w));
+        xm = fmaxf(xm, fmaxf(fmaxf(fabsf(x_to_f32<XDT>(xv[j].x)), fabsf(x_to_f32<XDT>(xv[j].y))),
+                             fmaxf(fabsf(x_to_f32<XDT>(xv[j].z)), fabsf(x_to_f32<XDT>(xv[j].w)))));
         acc = __builtin_amdgcn_mfma_f64_16x16x4f64((double)x_to_f32<XDT>(xv[j].x), (double)wv[j].x, acc, 0, 0, 0);
         acc = __builtin_amdgcn_mfma_f64_16x16x4f64((double)x_to_f32<XDT>(xv[j].y), (double)wv[j].y, acc, 0, 0, 0);
         acc = __builtin_amdgcn_mfma_f64_16x16x4f64((double)x_to_f32<XDT>(xv[j].z), (double)wv[j].z, acc, 0, 0, 0);
         acc = __builtin_amdgcn_mfma_f64_16x16x4f64((double)x_to_f32<XDT>(xv[j].w), (double)wv[j].w, acc, 0, 0, 0);
       }
     }
+  }
+  if (tt == 0) {
+    l1 += __shfl_xor(l1, 16);
+    l1 += __shfl_xor(l1, 32);
+    if (g == 0 && et * 16 + c < E) st_f64<CO>(wl1 + et * 16 + c, l1);
+  }
+  if (et == 0) {
+    xm = fmaxf(xm, __shfl_xor(xm, 16));
+    xm = fmaxf(xm, __shfl_xor(xm, 32));
+    if (g == 0 && tt * 16 + c < T) st_f64<CO>(xinf + tt * 16 + c, (double)xm);
   }
   const int ecol = et * 16 + c;
 #pragma unroll
@@ -188,6 +257,25 @@ __device__ __forceinline__ void topk_load(const double* __restrict__ logits, con
       }
       lg[e] = v + (bias ? (double)bias[e] : 0.0);
     }
+}
+
+// The router rows' 1-norms (sum of the hidden parts) into l1 (LDS, shared
+// by the workgroup: thread tid of nthr), and token t's max-norm.
+template <bool CO = false>
+__device__ __forceinline__ void topk_load_l1(const double* __restrict__ wl1, int ks, int E, int tid, int nthr,
+                                             float* l1) {
+  for (int e = tid; e < E; e += nthr) {
+    double v = 0.0;
+    for (int kp = 0; kp < ks; ++kp) v += ld_f64<CO>(wl1 + (size_t)kp * E + e);
+    l1[e] = (float)v;
+  }
+}
+template <bool CO = false>
+__device__ __forceinline__ double topk_xinf(const double* __restrict__ xinf, int ks, int t, int T) {
+  double v = 0.0;
+  if (t < T)
+    for (int kp = 0; kp < ks; ++kp) v = fmax(v, ld_f64<CO>(xinf + (size_t)kp * T + t));
+  return v;
 }
 
 __device__ __forceinline__ void topk_rank(int t, int T, int E, int K, int lane, const double* lg, double* sel_v,
@@ -227,6 +315,176 @@ __device__ __forceinline__ void topk_finish(int t, int T, int K, int lane, const
     idx_out[(size_t)t * K + lane] = id;
     w_out[(size_t)t * K + lane] = wt;
   }
+}
+
+// ---------------------------------------------------------------- exact order
+// Every fp64 logit is a sum of H exact products x_h w_h (an fp16 or bf16 times
+// an fp32 fits the 53-bit significand) and the bias, so whatever the order of
+// its additions its rounding error is at most gamma_n (||x||_inf ||w_e||_1 +
+// |bias_e|) with gamma_n = n u / (1 - n u), u = 2^-53 and n the number of
+// additions (Higham, Accuracy and Stability of Numerical Algorithms, §4.2; n
+// is taken as 2 (H + 64), which also covers a matrix-core sum rounded more
+// than once per step). The top-K of a token is certified when each winner's
+// interval lies above the next winner's and every other expert's interval
+// lies below all of them. Otherwise ("PagedWeight" §2.1 ranks the experts by
+// their logits; ties go to the lower index) the experts whose interval reaches
+// the winners are ranked on their exact logits: each product is an integer
+// times a power of two, summed exactly into kXL 32-bit digits of weight
+// 2^-282 .. 2^294 (which hold any fp16 or bf16 x fp32 product, any fp32 bias
+// and their sums), and the K largest are kept, equal values in index order.
+constexpr int kXL = 18;
+constexpr int kXEmin = -282;
+
+struct ExactScratch {           // one wave's, in LDS
+  unsigned long long acc[kXL];  // the candidate's digits, carries pending
+  uint32_t top[16][kXL];        // the exact top list: digits in [0, 2^32), the last one signed
+  int top_i[16];
+  int n;
+};
+
+// a finite value's bits as (-1)^neg m 2^e
+__device__ __forceinline__ void decode_f16(uint32_t b, uint64_t& m, int& e, bool& neg) {
+  const uint32_t ex = (b >> 10) & 31, f = b & 1023;
+  neg = (b >> 15) & 1;
+  m = ex ? (f | 1024u) : f;
+  e = ex ? (int)ex - 25 : -24;
+}
+__device__ __forceinline__ void decode_bf16(uint32_t b, uint64_t& m, int& e, bool& neg) {
+  const uint32_t ex = (b >> 7) & 255, f = b & 127;
+  neg = (b >> 15) & 1;
+  m = ex ? (f | 128u) : f;
+  e = ex ? (int)ex - 134 : -133;
+}
+__device__ __forceinline__ void decode_f32(uint32_t b, uint64_t& m, int& e, bool& neg) {
+  const uint32_t ex = (b >> 23) & 255, f = b & 0x7fffffu;
+  neg = b >> 31;
+  m = ex ? (f | 0x800000u) : f;
+  e = ex ? (int)ex - 150 : -149;
+}
+
+// acc += (-1)^neg P 2^e for P < 2^35 and kXEmin <= e <= 226 (inf and nan
+// inputs decode into that range too): three digits, LDS atomics
+__device__ __forceinline__ void exact_add(unsigned long long* acc, uint64_t P, int e, bool neg) {
+  const int off = e - kXEmin, k = off >> 5, r = off & 31;
+  const uint64_t lo = (uint32_t)(P << r);
+  const uint64_t rest = r ? P >> (32 - r) : P >> 32;
+  const uint64_t mid = (uint32_t)rest, hi = rest >> 32;
+  atomicAdd(acc + k, neg ? 0ull - lo : lo);
+  if (mid) atomicAdd(acc + k + 1, neg ? 0ull - mid : mid);
+  if (hi) atomicAdd(acc + k + 2, neg ? 0ull - hi : hi);
+}
+
+// the calling wave's LDS accesses before it are done before the ones after it
+__device__ __forceinline__ void wave_lds_fence() {
+  __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "workgroup");
+  __builtin_amdgcn_wave_barrier();
+}
+
+// Exact logit of (t, e) into sc.acc, by one whole wave.
+template <int XDT>
+__device__ __forceinline__ void exact_logit(const uint16_t* __restrict__ X, const float* __restrict__ W,
+                                            const float* __restrict__ bias, int t, int e, int H, int lane,
+                                            ExactScratch& sc) {
+  if (lane < kXL) sc.acc[lane] = 0ull;
+  wave_lds_fence();
+  const uint16_t* x = X + (size_t)t * H;
+  const uint32_t* w = (const uint32_t*)W + (size_t)e * H;
+  for (int h = lane; h < H; h += 64) {
+    uint64_t mx, mw;
+    int ex, ew;
+    bool sx, sw;
+    if constexpr (XDT == 0) decode_f16(x[h], mx, ex, sx);
+    else decode_bf16(x[h], mx, ex, sx);
+    decode_f32(w[h], mw, ew, sw);
+    if (mx && mw) exact_add(sc.acc, mx * mw, ex + ew, sx != sw);
+  }
+  if (lane == 0 && bias) {
+    uint64_t mb;
+    int eb;
+    bool sb;
+    decode_f32(__builtin_bit_cast(uint32_t, bias[e]), mb, eb, sb);
+    if (mb) exact_add(sc.acc, mb, eb, sb);
+  }
+  wave_lds_fence();
+}
+
+// a > b for digit lists in the top-list form
+__device__ __forceinline__ bool exact_greater(const uint32_t* a, const uint32_t* b) {
+  if (a[kXL - 1] != b[kXL - 1]) return (int32_t)a[kXL - 1] > (int32_t)b[kXL - 1];
+  for (int k = kXL - 2; k >= 0; --k)
+    if (a[k] != b[k]) return a[k] > b[k];
+  return false;
+}
+
+// Certificate of the top-K in sel_v / sel_i (after topk_rank) and, when it
+// fails, the exact ranking in their place. lg: token t's fp64 logits, l1:
+// ||w_e||_1 of every expert (float, LDS), xi: ||x_t||_inf. Called by the
+// whole wave of token t.
+template <int XDT>
+__device__ __forceinline__ void topk_certify(const uint16_t* __restrict__ X, const float* __restrict__ W,
+                                             const float* __restrict__ bias, int t, int T, int H, int E, int K,
+                                             int lane, const double* lg, const float* l1, double xi, double* sel_v,
+                                             int* sel_i, ExactScratch& sc) {
+  if (t >= T) return;
+  const double n = 2.0 * ((double)H + 64.0), u = 0x1p-53;
+  // the margin covers l1 rounded to float and the rounding of the bound itself
+  const double gam = n * u / (1.0 - n * u) * (1.0 + 0x1p-20);
+  auto bd = [&](int e) {
+    const int ec = min(max(e, 0), E - 1);
+    return gam * (xi * (double)l1[ec] + (bias ? fabs((double)bias[ec]) : 0.0));
+  };
+  double thr = 1e308;
+  bool ok = true;
+  for (int i = 0; i < K; ++i) {
+    const double lo = sel_v[i] - bd(sel_i[i]);
+    thr = fmin(thr, lo);
+    if (i + 1 < K && !(lo > sel_v[i + 1] + bd(sel_i[i + 1]))) ok = false;
+  }
+  auto winner = [&](int e) {
+    bool wn = false;
+    for (int i = 0; i < K; ++i) wn |= sel_i[i] == e;
+    return wn;
+  };
+  for (int e = lane; e < E; e += 64)
+    if (!winner(e) && !(lg[e] + bd(e) < thr)) ok = false;
+  if (__all(ok)) return;
+  // exact ranking of every expert whose interval reaches the winners'
+  if (lane == 0) sc.n = 0;
+  if (lane < 16) sc.top_i[lane] = 0;  // a valid id in any slot a nan logit leaves empty
+  wave_lds_fence();
+  for (int e = 0; e < E; ++e) {
+    if (!winner(e) && lg[e] + bd(e) < thr) continue;  // the same on every lane
+    exact_logit<XDT>(X, W, bias, t, e, H, lane, sc);
+    if (lane == 0) {
+      long long v[kXL];
+      for (int k = 0; k < kXL; ++k) v[k] = (long long)sc.acc[k];
+      for (int k = 0; k < kXL - 1; ++k) {
+        const long long c = v[k] >> 32;  // floor
+        v[k] -= c * 4294967296ll;
+        v[k + 1] += c;
+      }
+      uint32_t d[kXL];
+      for (int k = 0; k < kXL; ++k) d[k] = (uint32_t)v[k];
+      int pos = sc.n;
+      while (pos > 0 && exact_greater(d, sc.top[pos - 1])) --pos;
+      if (pos < K) {
+        for (int q = min(sc.n, K - 1); q > pos; --q) {
+          for (int k = 0; k < kXL; ++k) sc.top[q][k] = sc.top[q - 1][k];
+          sc.top_i[q] = sc.top_i[q - 1];
+        }
+        for (int k = 0; k < kXL; ++k) sc.top[pos][k] = d[k];
+        sc.top_i[pos] = e;
+        sc.n = min(sc.n + 1, K);
+      }
+    }
+    wave_lds_fence();
+  }
+  if (lane < K) {
+    const int e = sc.top_i[lane];
+    sel_i[lane] = e;
+    sel_v[lane] = lg[e];
+  }
+  wave_lds_fence();
 }
 
 }  // namespace mpb

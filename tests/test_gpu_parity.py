@@ -964,3 +964,98 @@ def test_fused_launch_graph_replays_and_commits(layer_cache):
     Xf, z, r = oracle_route(L, Xb)
     assert_close(out.cpu().numpy(), O.moe_ffn(Xf, z, r, L, q=q2), "fused replay after commits")
     assert int(ws[:M().moe_fused_counter_bytes()].count_nonzero()) == 0
+
+
+def _tie_rows(T, n):
+    """n tokens spread over the batch, the first and the last among them."""
+    return np.unique(np.linspace(0, T - 1, n).round().astype(np.int64))
+
+
+def _near_tie_x(T, H, j, xdt, rows, rng):
+    """Positive activations; column j is the smallest subnormal (2^-24 in
+    fp16, 2^-133 in bf16) in the given rows and 1.0 elsewhere, so a router
+    weight one ulp apart decides a sub-ulp near-tie in those rows and a
+    resolvable gap in the others."""
+    xa = np.abs(rng.standard_normal((T, H))).astype(np.float32)
+    if xdt == "f16":
+        Xb = xa.astype(np.float16).view(np.uint16)
+        one = np.float16(1.0).view(np.uint16)
+    else:
+        Xb = (xa.view(np.uint32) >> 16).astype(np.uint16)
+        one = np.uint16(0x3F80)
+    Xb[:, j] = one
+    Xb[rows, j] = 1
+    return np.ascontiguousarray(Xb)
+
+
+def _near_tie_rows(Wr, a, b, j, up):
+    """Router rows a and b equal except weight j of b, one ulp above or below."""
+    rng = np.random.default_rng(Wr.shape[1])
+    Wr[a] = (np.abs(rng.standard_normal(Wr.shape[1])) * 0.5 + 0.3).astype(np.float32)
+    Wr[b] = Wr[a]
+    Wr[b, j] = np.nextafter(Wr[a, j], np.float32(np.inf if up else -np.inf))
+
+
+@pytest.mark.parametrize("H,E,T", [(256, 24, 40), (1024, 24, 40), (256, 64, 4096)])
+def test_route_sub_ulp_near_tie_exact_order(H, E, T):
+    """Two router rows one ulp apart in one weight, met by the smallest fp16
+    subnormal: their fp64 logits tie but the exact logits do not, and the
+    top-K order must follow the exact ones ("PagedWeight" §2.1 ranks by the
+    logits; the one-launch small-batch router, the vector logits path and the
+    fp64 matrix-core path). The tokens of the other rows see a resolvable gap."""
+    K, a, b, j = 3, 5, 9, 17
+    rng = np.random.default_rng(H + T)
+    rows = _tie_rows(T, 8 if T > 64 else T)
+    for up in (True, False):
+        Wr = (rng.standard_normal((E, H)) / np.sqrt(H)).astype(np.float32)
+        _near_tie_rows(Wr, a, b, j, up)
+        Xb = _near_tie_x(T, H, j, "f16", rows, rng)
+        z, r, _ = O.route(S.f16_bits_to_f64(Xb), Wr, None, K)
+        assert (z[:, 0] == (b if up else a)).all() and (z[:, 1] == (a if up else b)).all()
+        idx = torch.empty((T, K), dtype=torch.int32, device="cuda")
+        w = torch.empty((T, K), dtype=torch.float32, device="cuda")
+        M().moe_route(to_dev_x(Xb), 0, torch.from_numpy(Wr).cuda(), None, K, idx, w, route_ws(T, E))
+        torch.cuda.synchronize()
+        got = idx.cpu().numpy()
+        bad = int((got != z).any(axis=1).sum())
+        say(f"H={H} E={E} T={T} ulp {'up' if up else 'down'}: {bad} of {T} tokens ordered differently")
+        assert bad == 0
+        assert_close(w.cpu().numpy(), r, "near-tie topk_w")
+
+
+@pytest.mark.parametrize("cfg", [10, 11, 3])
+def test_fused_sub_ulp_near_tie_exact_order(cfg, layer_cache):
+    """The fused launch ranks near-tied experts by their exact logits too
+    (router rows 1 and E-2, and their biases, equal but for one weight one ulp
+    apart, met by the smallest subnormal activation in sampled tokens):
+    vector-path logits in fp16 and in bf16, matrix-core logits with a bias."""
+    L, D = dev_layer(layer_cache, cfg)
+    H, E, K = D.H, D.E, D.K
+    xdt = L.cfg["xdtype"]
+    T = S.make_tokens(cfg).shape[0]
+    rng = np.random.default_rng(4242 + cfg)
+    a, b, j = 1, E - 2, 17
+    Wr = np.array(L.W_r, np.float32, copy=True)
+    _near_tie_rows(Wr, a, b, j, True)
+    bias = None if L.bias is None else np.array(L.bias, np.float32, copy=True)
+    if bias is not None:
+        bias[b] = bias[a]
+    Xb = _near_tie_x(T, H, j, xdt, _tie_rows(T, 8 if T > 64 else T), rng)
+    z, r, _ = O.route(S.x_bits_to_f64(Xb, xdt), Wr, bias, K)
+    assert (z[:, 0] == b).all()
+    W0, b0 = D.W_r.clone(), None if D.bias is None else D.bias.clone()
+    try:
+        D.W_r.copy_(torch.from_numpy(Wr))
+        if bias is not None:
+            D.bias.copy_(torch.from_numpy(bias))
+        say(f"fused near tie cfg{cfg}: T={T} H={H} E={E} K={K} {xdt}")
+        i1, w1, _, i2, w2, _, _ = _separate_and_fused(D, Xb, xdt)
+    finally:
+        D.W_r.copy_(W0)
+        if b0 is not None:
+            D.bias.copy_(b0)
+        torch.cuda.synchronize()
+    assert int((i2 != z).any(axis=1).sum()) == 0, "fused order"
+    assert int((i1 != z).any(axis=1).sum()) == 0, "separate order"
+    assert_close(w2, r, f"cfg{cfg} near-tie fused topk_w")
+    assert np.array_equal(w1.view(np.uint32), w2.view(np.uint32))
