@@ -30,6 +30,16 @@
 // (blocks 2, 3), so SiLU(gate) * up is formed in registers. Down adds each
 // token's hi and lo accumulators and writes the (token, slot) row of y that the
 // combine pass reads.
+//
+// h of the wide groups goes to panels laid out for down's operand loads: per
+// 32-token block of a group and 64-element step of I, 4 KiB of hi then 4 KiB
+// of lo, each [substep ks][half g][token r][8 fp16] holding h[r][64 s + 8 (4 g
+// + ks) + j]. A down operand load of 64 lanes (token r, half g) then reads 1
+// KiB in one piece: a load whose lanes reach 32 rows of a row-major array
+// touches 32 cache lines, and those line lookups, not the bytes, bounded the
+// loop (measured: the same loads over contiguous bytes took gate_up 586 ->
+// 479 us and down 632 -> 535 us at the 4096-token bf16 prefill layer). The
+// gate_up epilogue writes the panels with 512-byte stores.
 #include <hip/hip_ext.h>
 
 #include "k_ffn_body.h"
@@ -47,10 +57,18 @@ __device__ __forceinline__ uint32_t wa_off(int R, int o) {
   return (uint32_t)R * 128u + ((uint32_t)(o ^ ((R >> 1) & 7)) << 4);
 }
 
+// Element offset in the h panels: block blk, step s of I (NSI steps), half hl
+// (0 hi, 1 lo), element kk of the step, token r of the block.
+__device__ __forceinline__ size_t hpan_off(int blk, int NSI, int s, int hl, int kk, int r) {
+  const int o = kk >> 3;  // octet 4 g + ks
+  return ((((size_t)blk * NSI + s) * 2 + hl) << 11) + ((o & 3) << 9) + (((o >> 2) * 32 + r) << 3) + (kk & 7);
+}
+
 // Item and tile of workgroup blockIdx.x in the wide list of gate_up (gu) or
 // down: all tiles of an item run on one XCD (the dispatcher hands workgroup b
-// to XCD b % 8), so the item's activations are read through one L2.
-__device__ __forceinline__ bool wide_item(const FfnParams& p, bool gu, int ntile, int& tile, Item& m) {
+// to XCD b % 8), so the item's activations are read through one L2. blk0: the
+// item's first h panel block.
+__device__ __forceinline__ bool wide_item(const FfnParams& p, bool gu, int ntile, int& tile, Item& m, int& blk0) {
   const int k = blockIdx.x >> 3, li = k / ntile;
   tile = k - li * ntile;
   const int item = 8 * li + (blockIdx.x & 7);
@@ -60,6 +78,7 @@ __device__ __forceinline__ bool wide_item(const FfnParams& p, bool gu, int ntile
   const int tpi = gu ? p.tpi_w : p.tpi_dnw;
   const int e = v >> 16;
   item_fields<false>(p, 2 * e + (gu ? 0 : 1), e, (v & 0xffff) * tpi, tpi, m);
+  blk0 = p.wblk[e] + (v & 0xffff) * (tpi >> 5);
   return true;
 }
 
@@ -78,7 +97,8 @@ __device__ __forceinline__ void wide_table_image(const uint16_t* img, int w, int
 }
 
 template <int Q, bool GU>
-__device__ __forceinline__ void wide_body(const FfnParams& p, const Item& wi, int it, uint16_t* lds, uint32_t tb) {
+__device__ __forceinline__ void wide_body(const FfnParams& p, const Item& wi, int it, int blk0, uint16_t* lds,
+                                          uint32_t tb) {
   const int tid = threadIdx.x, lane = tid & 63, r = lane & 31, g = lane >> 5;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int Kd = GU ? p.H : p.I;
@@ -116,9 +136,12 @@ __device__ __forceinline__ void wide_body(const FfnParams& p, const Item& wi, in
   // ---- contraction role: columns 128 w .. 128 w + 127 in four blocks c of 32
   // (gate_up: tokens 128 w + 32 c + r; down: token 64 w + 32 (c / 2) + r, its
   // h hi for even c, h lo for odd c). Tokens past the item read the item's
-  // last token (in bounds; those columns are never stored).
+  // last token (gate_up) or its last panel block (down): in bounds, and those
+  // columns are never stored.
   rsrc_t brs;
   uint32_t boff[4];
+  constexpr uint32_t bstep = GU ? 128 : 8192;  // bytes from one step's operands to the next
+  constexpr uint32_t bks = GU ? 16 : 1024;      // bytes from one substep's operands to the next
   bool cl[4];  // wave-uniform: the column block holds a token of the item
   if constexpr (GU) {
     brs = rows_rsrc(p.xh, (size_t)p.T * p.H * 2);
@@ -129,21 +152,19 @@ __device__ __forceinline__ void wide_body(const FfnParams& p, const Item& wi, in
       boff[c] = (uint32_t)p.ptok[base + min(t, nt - 1)] * (uint32_t)p.H * 2u + 64u * g;
     }
   } else {
-    const size_t hbytes = (size_t)p.T * (p.K + p.S) * p.I * 2;
-    const char* a = (const char*)p.hhi;
-    const char* b = (const char*)p.hlo;
-    const char* lo = a < b ? a : b;
-    brs = rows_rsrc(lo, (size_t)((a < b ? b : a) - lo) + hbytes);
+    const int NSI = p.I >> 6;
+    brs = rows_rsrc(p.hpan, ((size_t)blk0 + ((nt + 31) >> 5)) * NSI * 8192);
 #pragma unroll
     for (int tc = 0; tc < 2; ++tc) {
-      const uint32_t row = (uint32_t)(base + min(64 * w + 32 * tc + r, nt - 1)) * (uint32_t)p.I * 2u + 64u * g;
-      boff[2 * tc] = (uint32_t)(a - lo) + row;
-      boff[2 * tc + 1] = (uint32_t)(b - lo) + row;
+      const uint32_t blk = (uint32_t)(blk0 + min(2 * w + tc, (nt - 1) >> 5));
+      boff[2 * tc] = blk * (uint32_t)NSI * 8192u + 16u * (uint32_t)lane;
+      boff[2 * tc + 1] = boff[2 * tc] + 4096u;
       cl[2 * tc] = cl[2 * tc + 1] = 64 * w + 32 * tc < nt;
     }
   }
   // B[c][ks]: column block c, substep ks = K octet 4 g + ks of the step (the
-  // lane's 64 bytes of the row, g = 0 the first half, g = 1 the second).
+  // lane's 64 bytes of the row, g = 0 the first half, g = 1 the second; for
+  // down, the panel's substep ks).
   // Every load of the K loop is issued unconditionally (column blocks without
   // tokens read the item's last token; steps past the end re-read the last
   // step, plane words past the row read zeros): a load under a branch leaves
@@ -155,7 +176,7 @@ __device__ __forceinline__ void wide_body(const FfnParams& p, const Item& wi, in
     for (int c = 0; c < 4; ++c)
 #pragma unroll
       for (int ks = 0; ks < 4; ++ks)
-        B[c][ks] = __builtin_bit_cast(f16x8, __builtin_amdgcn_raw_buffer_load_b128(brs, boff[c] + 16 * ks, 128 * s, 0));
+        B[c][ks] = __builtin_bit_cast(f16x8, __builtin_amdgcn_raw_buffer_load_b128(brs, boff[c] + bks * ks, bstep * s, 0));
   };
   // A operand of row block rb, substep ks: tile row 32 rb + r, piece 4 g + ks
   // (the swizzle does not depend on rb)
@@ -246,8 +267,7 @@ __device__ __forceinline__ void wide_body(const FfnParams& p, const Item& wi, in
       // a token converted scaled by 2^-sc (bf16 beyond the fp16 range): gate
       // and up scaled back, h carried as h 2^(-2 sc)
       const int sc = p.xsc ? p.xsc[p.ptok[base + t]] : 0;
-      uint16_t* hh = p.hhi + (size_t)(base + t) * p.I + it * 64 + 4 * g;
-      uint16_t* hl = p.hlo + (size_t)(base + t) * p.I + it * 64 + 4 * g;
+      const int blk = blk0 + 4 * w + c;  // panel block of token t, which is its row r
 #pragma unroll
       for (int rh = 0; rh < 2; ++rh)
 #pragma unroll
@@ -261,9 +281,9 @@ __device__ __forceinline__ void wide_body(const FfnParams& p, const Item& wi, in
             hv[k] = __builtin_bit_cast(uint16_t, h.hi);
             lv[k] = __builtin_bit_cast(uint16_t, h.lo);
           }
-          const int col = 32 * rh + 8 * v4;
-          *(uint64_t*)(hh + col) = __builtin_bit_cast(uint64_t, make_ushort4(hv[0], hv[1], hv[2], hv[3]));
-          *(uint64_t*)(hl + col) = __builtin_bit_cast(uint64_t, make_ushort4(lv[0], lv[1], lv[2], lv[3]));
+          uint16_t* hp = p.hpan + hpan_off(blk, p.I >> 6, it, 0, 32 * rh + 8 * v4 + 4 * g, r);
+          *(uint64_t*)hp = __builtin_bit_cast(uint64_t, make_ushort4(hv[0], hv[1], hv[2], hv[3]));
+          *(uint64_t*)(hp + 2048) = __builtin_bit_cast(uint64_t, make_ushort4(lv[0], lv[1], lv[2], lv[3]));
         }
     }
   } else {
@@ -296,23 +316,23 @@ template <bool GU>
 __global__ __launch_bounds__(kWideThreads) void k_wide(FfnParams p, int qmax) {
   extern __shared__ __attribute__((aligned(256))) uint16_t lds[];
   const int ntile = GU ? p.I >> 6 : (p.H + 127) >> 7;
-  int it;
+  int it, blk0;
   Item wi;
-  if (!wide_item(p, GU, ntile, it, wi)) return;
+  if (!wide_item(p, GU, ntile, it, wi, blk0)) return;
   const uint32_t tb = 256u << qmax;
   switch (wi.q < 3 || wi.q > qmax || !tables_at_zero(lds) ? 0 : wi.q) {
-    case 3: wide_body<3, GU>(p, wi, it, lds, tb); break;
-    case 4: wide_body<4, GU>(p, wi, it, lds, tb); break;
-    case 5: wide_body<5, GU>(p, wi, it, lds, tb); break;
-    case 6: wide_body<6, GU>(p, wi, it, lds, tb); break;
-    case 7: wide_body<7, GU>(p, wi, it, lds, tb); break;
-    case 8: wide_body<8, GU>(p, wi, it, lds, tb); break;
+    case 3: wide_body<3, GU>(p, wi, it, blk0, lds, tb); break;
+    case 4: wide_body<4, GU>(p, wi, it, blk0, lds, tb); break;
+    case 5: wide_body<5, GU>(p, wi, it, blk0, lds, tb); break;
+    case 6: wide_body<6, GU>(p, wi, it, blk0, lds, tb); break;
+    case 7: wide_body<7, GU>(p, wi, it, blk0, lds, tb); break;
+    case 8: wide_body<8, GU>(p, wi, it, blk0, lds, tb); break;
     default:
       if constexpr (GU) {
-        const size_t o = (size_t)wi.base * p.I + it * 64;
         for (int i = threadIdx.x; i < wi.nt * 64; i += blockDim.x) {
-          p.hhi[o + (size_t)(i >> 6) * p.I + (i & 63)] = 0x7e00;  // fp16 NaN
-          p.hlo[o + (size_t)(i >> 6) * p.I + (i & 63)] = 0;
+          const size_t o = hpan_off(blk0 + (i >> 11), p.I >> 6, it, 0, i & 63, (i >> 6) & 31);
+          p.hpan[o] = 0x7e00;  // fp16 NaN
+          p.hpan[o + 2048] = 0;
         }
       } else {
         poison_y(p, 0, wi.base, wi.nt, it * 128);

@@ -51,8 +51,9 @@ __device__ __forceinline__ GroupItems group_items(const FfnParams& p, int cnt) {
 // a[1] narrow gate_up, a[2] narrow down, a[3] / a[4] wide gate_up full /
 // partial, a[5] / a[6] wide down full / partial; totals a[7] narrow gate_up,
 // a[8] narrow down, a[9] / a[10] wide gate_up full / partial, a[11] / a[12]
-// wide down full / partial.
-constexpr int kSums = 13;
+// wide down full / partial; a[13] the 32-token h panel blocks of the wide
+// groups before e.
+constexpr int kSums = 14;
 __host__ __device__ constexpr bool wide_sum(int i) { return (i >= 3 && i <= 6) || i >= 9; }
 template <bool WIDE>
 __device__ __forceinline__ void add_group(const FfnParams& p, int (&a)[kSums], int j, int cnt, int qjg, int qjd,
@@ -60,7 +61,10 @@ __device__ __forceinline__ void add_group(const FfnParams& p, int (&a)[kSums], i
   const GroupItems n = group_items<WIDE>(p, cnt);
   const bool before_g = qjg > qg || (qjg == qg && j < e);
   const bool before_d = qjd > qd || (qjd == qd && j < e);
-  if (j < e) a[0] += cnt;
+  if (j < e) {
+    a[0] += cnt;
+    a[13] += n.gwf + n.gwp ? (cnt + 31) >> 5 : 0;
+  }
   if (before_g) {
     a[1] += n.gu;
     a[3] += n.gwf;
@@ -93,6 +97,7 @@ __device__ __forceinline__ void put_items(const FfnParams& p, const int (&r)[kSu
   for (int sp = tid; sp < n.dn; sp += 256) p.items_dn[r[2] + sp] = (e << 16) | sp;
   for (int sp = tid; sp < n.gwf; sp += 256) p.items_w[r[3] + sp] = (e << 16) | sp;
   for (int sp = tid; sp < n.dwf; sp += 256) p.items_dnw[r[5] + sp] = (e << 16) | sp;
+  if (tid == 0 && WIDE) p.wblk[e] = r[13];
   if (tid == 0 && n.gwp) p.items_w[r[9] + r[4]] = (e << 16) | n.gwf;
   if (tid == 0 && n.dwp) p.items_dnw[r[11] + r[6]] = (e << 16) | n.dwf;
 }

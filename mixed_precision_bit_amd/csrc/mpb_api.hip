@@ -173,10 +173,13 @@ WsLayout ws_layout(int T, int H, int I, int E, int S, int K, bool bf16) {
   L.max_items_w = ffn_wide_from(T, H, I, E, S, K) ? max_wide_items(T, E, S, K) : 0;
   L.items_w = off;  off += align256((size_t)L.max_items_w * 4);
   L.items_dnw = off; off += align256((size_t)L.max_items_w * 4);
+  L.wblk = off;    off += L.max_items_w ? align256(NB * 4) : 0;
   L.n_items = off; off += 256;  // [4]
   L.ccnt = off;    off += align256((size_t)group_chunks(T, K) * E * 4);
   L.hhi = off;     off += align256(P * (size_t)I * 2);
   L.hlo = off;     off += align256(P * (size_t)I * 2);
+  L.hpan_size = L.max_items_w ? hpan_bytes(T, I, E, S, K) : 0;
+  L.hpan = off;    off += align256(L.hpan_size);
   L.y = off;       off += align256(P * (size_t)H * 4 * dn_splits(T, H, I, E, S, K));
   L.xh = off;      off += bf16 ? align256((size_t)T * H * 2) : 0;
   L.xsc = off;     off += bf16 ? align256((size_t)T * 4) : 0;
@@ -219,6 +222,8 @@ mpb::FfnParams ffn_params(const mpb::WsLayout& L, char* ws, const void* X_dev, i
   p.tpi_dnw = mpb::kWideTokDn;
   p.hhi = (uint16_t*)(ws + L.hhi);
   p.hlo = (uint16_t*)(ws + L.hlo);
+  p.wblk = (int32_t*)(ws + L.wblk);
+  p.hpan = (uint16_t*)(ws + L.hpan);
   p.y = (float*)(ws + L.y);
   p.out = out_dev;
   p.dn_split = 1;

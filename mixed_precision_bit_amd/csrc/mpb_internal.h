@@ -56,6 +56,8 @@ struct FfnParams {
   int tpi_dnw;                // wide down tokens per item
   uint16_t* hhi;              // [P][I] fp16 high part of h = SiLU(gate) * up
   uint16_t* hlo;              // [P][I] fp16 remainder h - hi
+  int32_t* wblk;              // [NB] first h panel block of each wide group
+  uint16_t* hpan;             // h of the wide groups as down operand panels (k_ffn_wide.hip)
   float* y;                   // [dn_split][T (K + S)][H] down projection of each (token, slot) (partial sums over K ranges)
   float* out;                 // [T][H]
   int dn_split;               // K ranges of the down projection (1: whole K per workgroup)
@@ -85,8 +87,9 @@ inline int dn_range_hcs(int I, int n) {
 }
 
 struct WsLayout {
-  size_t counts, offsets, ptok, pw, ent, items, items_dn, items_w, items_dnw, n_items, ccnt, hhi, hlo, y, xh, xsc,
-      total;
+  size_t counts, offsets, ptok, pw, ent, items, items_dn, items_w, items_dnw, wblk, n_items, ccnt, hhi, hlo, hpan,
+      y, xh, xsc, total;
+  size_t hpan_size;  // bytes of the h panels (0 without wide items)
   int max_items, max_items_w;
 };
 // Upper bound on work items (one per tpi-token split of a group with tokens):
@@ -120,13 +123,22 @@ inline int max_wide_items(int T, int E, int S, int K) {
   return (int)(P / kWideTokDn + (g < NB ? g : NB));
 }
 
+// h panels of the wide groups: one per 32-token block of a group and 64-row
+// step of I, hi then lo, 4 KiB each; a group's blocks are consecutive. Upper
+// bound on the blocks: sum_g ceil(cnt_g / 32) <= P / 32 + NB.
+inline size_t hpan_bytes(int T, int I, int E, int S, int K) {
+  const size_t P = (size_t)T * (K + S);
+  return ((P + 31) / 32 + (size_t)E + S) * (size_t)I * 128;
+}
+
 // The FFN kernels stage activation and h rows through buffer descriptors with
 // 32-bit byte offsets, kNoRow standing for "no row" (reads as zeros): the
-// activations ([T][H] fp16) and the span of h's two halves must stay below it.
+// activations ([T][H] fp16), the span of h's two halves and the h panels must
+// stay below it.
 constexpr uint32_t kNoRow = 0xfffffff0u;
 inline bool rows_fit(const WsLayout& L, int T, int H, int I, int K, int S) {
   const size_t P = (size_t)T * (K + S);
-  return (size_t)T * H * 2 < kNoRow && (L.hlo - L.hhi) + P * I * 2 < kNoRow;
+  return (size_t)T * H * 2 < kNoRow && (L.hlo - L.hhi) + P * I * 2 < kNoRow && L.hpan_size < kNoRow;
 }
 
 // Raise a kernel's dynamic LDS limit to `bytes` on the current device, once
