@@ -353,12 +353,11 @@ __device__ __forceinline__ void logit_unit(const FusedParams& P, int u, uint16_t
   const int lane = tid & 63, w = tid >> 6;
   const long long wu = (long long)u * 8 + w;
   if (P.logit_mfma) {
-    logits_tile_mfma<XDT, true>(P.x, P.W, p.T, p.H, p.E, wu, lane, P.logits, route_ws_l1(P.logits, 1, p.T, p.E),
-                                route_ws_xinf(P.logits, 1, p.T, p.E));
+    logits_tile_mfma<XDT, true>(P.x, P.W, p.T, p.H, p.E, wu, lane, P.logits, route_ws_l1(P.logits, 1, p.T, p.E));
   } else {
     double* part = (double*)lds + w * (kTT * 65);
     logits_partials<XDT, 1, 2, true>(P.x, P.W, p.T, p.H, p.E, P.ks, wu, lane, part,
-                                     route_ws_l1(P.logits, P.ks, p.T, p.E), route_ws_xinf(P.logits, P.ks, p.T, p.E));
+                                     route_ws_l1(P.logits, P.ks, p.T, p.E));
     __syncthreads();
     logits_sum<1, true>(p.T, p.E, P.ks, wu, lane, part, P.logits);
   }
@@ -370,20 +369,23 @@ __device__ __forceinline__ void topk_unit(const FusedParams& P, int u, uint16_t*
   const FfnParams& p = P.f;
   const int lane = tid & 63, w = tid >> 6;
   if (wait_count(P, C_LOGIT, P.n_logit, flag)) {
-    // LDS: lg [8][512] fp64, sel_v [8][16] fp64, sel_i [8][16], l1 [512] fp32, exact scratch [8]
+    // LDS: lg [8][512] fp64, sel_v [8][17] fp64, sel_i [8][17], the norm maximum, exact scratch [8]
     double* lg = (double*)lds + w * 512;
-    double* sel_v = (double*)lds + 8 * 512 + w * 16;
-    int* sel_i = (int*)((double*)lds + 8 * 512 + 8 * 16) + w * 16;
-    float* l1 = (float*)((int*)((double*)lds + 8 * 512 + 8 * 16) + 8 * 16);
-    ExactScratch* sc = (ExactScratch*)(l1 + 512) + w;
+    double* sel_v = (double*)lds + 8 * 512 + w * 17;
+    int* sel_i = (int*)((double*)lds + 8 * 512 + 8 * 17) + w * 17;
+    unsigned* nmax = (unsigned*)((int*)((double*)lds + 8 * 512 + 8 * 17) + 8 * 17);
+    ExactScratch* sc = (ExactScratch*)((char*)nmax + 16) + w;
     const int t = u * 8 + w;
+    if (tid == 0) *nmax = 0u;
+    __syncthreads();
+    const float xi = topk_gather<XDT, true>(P.logits, P.x, P.bias, P.ks, t, p.T, p.H, p.E, lane, tid, kThreads, lg,
+                                            nmax);
     topk_load<true>(P.logits, P.bias, P.ks, t, p.T, p.E, lane, lg);
-    topk_load_l1<true>(route_ws_l1(P.logits, P.ks, p.T, p.E), P.ks, p.E, tid, kThreads, l1);
-    const double xi = topk_xinf<true>(route_ws_xinf(P.logits, P.ks, p.T, p.E), P.ks, t, p.T);
     __syncthreads();
     topk_rank(t, p.T, p.E, p.K, lane, lg, sel_v, sel_i);
     __syncthreads();
-    topk_certify<XDT>(P.x, P.W, P.bias, t, p.T, p.H, p.E, p.K, lane, lg, l1, xi, sel_v, sel_i, *sc);
+    topk_certify<XDT>(P.x, P.W, P.bias, t, p.T, p.H, p.E, p.K, lane, lg,
+                      logit_bound(p.H, xi, __uint_as_float(*nmax)), sel_v, sel_i, *sc);
     topk_finish<true>(t, p.T, p.K, lane, sel_v, sel_i, P.idx_out, P.w_out);
   }
   mark_done(ctr(P, C_TOPK));
@@ -479,7 +481,7 @@ size_t fused_lds_bytes(int qmax) {
   const size_t ffn = std::max<size_t>(std::max<size_t>((256u << qmax) + stage_bytes<1>(), kWaves * 16 * 64 * 4),
                                       kPairTableBytes + stage_bytes<1>());
   const size_t logit = 8 * kTT * 65 * 8;
-  constexpr size_t topk = 8 * 512 * 8 + 8 * 16 * 8 + 8 * 16 * 4 + 512 * 4 + 8 * sizeof(ExactScratch);
+  constexpr size_t topk = 8 * 512 * 8 + 8 * 17 * 8 + 8 * 17 * 4 + 16 + 8 * sizeof(ExactScratch);
   static_assert(topk <= kPairTableBytes + stage_bytes<1>(), "the router units fit the smallest FFN LDS");
   const size_t grp = (kMaxGroupsF + 48) * 4;
   return (std::max(std::max(ffn, logit), std::max(topk, grp)) + 255) / 256 * 256;

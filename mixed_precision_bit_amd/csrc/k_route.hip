@@ -47,8 +47,7 @@ __global__ __launch_bounds__(256) void k_route_logits(const uint16_t* __restrict
   __shared__ double part[4][kTT * EW * 65];  // +1 column: the summing lanes read rows without bank conflicts
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const long long u = (long long)blockIdx.x * 4 + w;
-  logits_partials<XDT, EW, NPC>(X, W, T, H, E, ks, u, lane, part[w], route_ws_l1(logits, ks, T, E),
-                                route_ws_xinf(logits, ks, T, E));
+  logits_partials<XDT, EW, NPC>(X, W, T, H, E, ks, u, lane, part[w], route_ws_l1(logits, ks, T, E));
   __syncthreads();
   logits_sum<EW>(T, E, ks, u, lane, part[w], logits);
 }
@@ -57,7 +56,7 @@ template <int XDT>
 __global__ __launch_bounds__(256) void k_route_logits_mfma(const uint16_t* __restrict__ X, const float* __restrict__ W,
                                                            int T, int H, int E, double* __restrict__ logits) {
   logits_tile_mfma<XDT>(X, W, T, H, E, (long long)blockIdx.x * 4 + (threadIdx.x >> 6), threadIdx.x & 63, logits,
-                        route_ws_l1(logits, 1, T, E), route_ws_xinf(logits, 1, T, E));
+                        route_ws_l1(logits, 1, T, E));
 }
 
 template <int XDT>
@@ -66,20 +65,21 @@ __global__ __launch_bounds__(256) void k_route_topk(const double* __restrict__ l
                                                     int ks, int T, int H, int E, int K, int32_t* __restrict__ idx_out,
                                                     float* __restrict__ w_out) {
   __shared__ double lg[4][kEMaxTopk];
-  __shared__ double sel_v[4][16];
-  __shared__ int sel_i[4][16];
-  __shared__ float l1[kEMaxTopk];
+  __shared__ double sel_v[4][17];
+  __shared__ int sel_i[4][17];
+  __shared__ unsigned nmax;
   __shared__ ExactScratch sc[4];
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int t = blockIdx.x * 4 + w;
-  double* ws = const_cast<double*>(logits);
+  if (threadIdx.x == 0) nmax = 0u;
+  __syncthreads();
+  const float xi = topk_gather<XDT>(logits, X, bias, ks, t, T, H, E, lane, threadIdx.x, 256, lg[w], &nmax);
   topk_load(logits, bias, ks, t, T, E, lane, lg[w]);
-  topk_load_l1(route_ws_l1(ws, ks, T, E), ks, E, threadIdx.x, 256, l1);
-  const double xi = topk_xinf(route_ws_xinf(ws, ks, T, E), ks, t, T);
   __syncthreads();
   topk_rank(t, T, E, K, lane, lg[w], sel_v[w], sel_i[w]);
   __syncthreads();
-  topk_certify<XDT>(X, W, bias, t, T, H, E, K, lane, lg[w], l1, xi, sel_v[w], sel_i[w], sc[w]);
+  topk_certify<XDT>(X, W, bias, t, T, H, E, K, lane, lg[w], logit_bound(H, xi, __uint_as_float(nmax)),
+                    sel_v[w], sel_i[w], sc[w]);
   topk_finish(t, T, K, lane, sel_v[w], sel_i[w], idx_out, w_out);
 }
 
@@ -88,11 +88,13 @@ __global__ __launch_bounds__(512) void k_route_small(const uint16_t* __restrict_
                                                      const float* __restrict__ bias, int T, int H, int E, int K,
                                                      int32_t* __restrict__ idx_out, float* __restrict__ w_out) {
   __shared__ double lg[kEMaxTopk];
-  __shared__ double sel_v[16];
-  __shared__ int sel_i[16];
-  __shared__ float l1[kEMaxTopk];
+  __shared__ double sel_v[17];
+  __shared__ int sel_i[17];
+  __shared__ unsigned nmax;
   __shared__ ExactScratch sc;
   const int t = blockIdx.x, lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  if (threadIdx.x == 0) nmax = 0u;
+  __syncthreads();
   const uint16_t* x = X + (size_t)t * H;
   float xm = 0.0f;  // max-norm of the token (every wave covers all of it)
   for (int e0 = w * kSmallEW; e0 < E; e0 += 8 * kSmallEW) {
@@ -125,7 +127,7 @@ __global__ __launch_bounds__(512) void k_route_small(const uint16_t* __restrict_
       }
       if (lane == 0 && e0 + j < E) {
         lg[e0 + j] = a[j] + (bias ? (double)bias[e0 + j] : 0.0);
-        l1[e0 + j] = (float)n1[j];
+        atomicMax(&nmax, __float_as_uint((float)(n1[j] + (bias ? fabs((double)bias[e0 + j]) : 0.0))));
       }
     }
   }
@@ -134,7 +136,9 @@ __global__ __launch_bounds__(512) void k_route_small(const uint16_t* __restrict_
   __syncthreads();
   if (w == 0) topk_rank(t, T, E, K, lane, lg, sel_v, sel_i);
   __syncthreads();
-  if (w == 0) topk_certify<XDT>(X, W, bias, t, T, H, E, K, lane, lg, l1, (double)xm, sel_v, sel_i, sc);
+  if (w == 0)
+    topk_certify<XDT>(X, W, bias, t, T, H, E, K, lane, lg, logit_bound(H, xm, __uint_as_float(nmax)), sel_v, sel_i,
+                      sc);
   if (w == 0) topk_finish(t, T, K, lane, sel_v, sel_i, idx_out, w_out);
 }
 
@@ -180,12 +184,12 @@ hipError_t launch_routing_mass(const int32_t* idx, const float* w, int T, int E,
   return hipGetLastError();
 }
 
-// [ks][T][E] fp64 logit parts, [ks][E] row 1-norms and [ks][T] token
-// max-norms; ks <= 8 on the vector path (it depends on H, which the size query
-// does not take), 1 on the matrix-core path
+// [ks][T][E] fp64 logit parts and [ks][E] row 1-norms; ks <= 8 on the vector
+// path (it depends on H, which the size query does not take), 1 on the
+// matrix-core path
 size_t route_workspace_bytes(int T, int E) {
-  const size_t ks = logits_use_mfma(T, E) ? 1 : 8;
-  return (ks * ((size_t)T * E + E + T) * 8 + 255) / 256 * 256;
+  const size_t ks = logits_use_mfma(T, E) ? 1 : kMaxParts;
+  return (ks * ((size_t)T * E + E) * 8 + 255) / 256 * 256;
 }
 
 template <int XDT>

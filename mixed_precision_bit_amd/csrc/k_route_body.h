@@ -33,14 +33,13 @@ __device__ __forceinline__ double ld_f64(const double* p) {
 }
 
 // Router workspace (fp64): the logit parts [ks][T][E], then per hidden part
-// the 1-norms of the router rows [ks][E] and the max-norms of the tokens
-// [ks][T] that bound the logits' rounding error (see topk_certify).
+// the 1-norms of the router rows [ks][E], which bound the logits' rounding
+// error (see topk_certify).
 __host__ __device__ inline double* route_ws_l1(double* ws, int ks, int T, int E) {
   return ws + (size_t)ks * T * E;
 }
-__host__ __device__ inline double* route_ws_xinf(double* ws, int ks, int T, int E) {
-  return ws + (size_t)ks * T * E + (size_t)ks * E;
-}
+
+constexpr int kMaxParts = 8;  // hidden parts of a logit at most
 
 // Hidden-dimension split of the vector-path logits: small batches give too
 // few (token tile, expert) units to fill the chip, so each logit is summed in
@@ -51,7 +50,7 @@ __host__ __device__ inline int route_ksplit(int T, int H, int E) {
   const long long units = (long long)((T + kTT - 1) / kTT) * E;
   const int npc = (H + 255) / 256;
   long long ks = 2048 / (units > 0 ? units : 1);
-  ks = ks < 1 ? 1 : ks > 8 ? 8 : ks;
+  ks = ks < 1 ? 1 : ks > kMaxParts ? kMaxParts : ks;
   return (int)(ks < npc ? ks : npc);
 }
 
@@ -59,12 +58,11 @@ __host__ __device__ inline int route_ksplit(int T, int H, int E) {
 // part kp of ks) computes its 64 lanes' partial sums and writes them to part
 // ([8 EW][65] doubles, the wave's own LDS region). Units past the last one
 // write zeros. The units of the first token tile also store the 1-norms of
-// their router rows over part kp (wl1[kp][e]), those of the first expert
-// group the max-norms of their tokens over part kp (xinf[kp][t]).
+// their router rows over part kp (wl1[kp][e]).
 template <int XDT, int EW, int NPC, bool CO = false>
 __device__ __forceinline__ void logits_partials(const uint16_t* __restrict__ X, const float* __restrict__ W, int T,
                                                 int H, int E, int ks, long long u, int lane, double* part,
-                                                double* __restrict__ wl1, double* __restrict__ xinf) {
+                                                double* __restrict__ wl1) {
   const int ntt = (T + kTT - 1) / kTT, neg = (E + EW - 1) / EW;
   const bool live = u < (long long)ntt * neg * ks;
   const int tt = live ? (int)(u % ntt) : 0;
@@ -76,12 +74,12 @@ __device__ __forceinline__ void logits_partials(const uint16_t* __restrict__ X, 
   for (int k = 0; k < kTT; ++k)
 #pragma unroll
     for (int j = 0; j < EW; ++j) a[k][j] = 0.0;
+  // the 1-norms: only the units that store them (wave-uniform) add them up;
+  // in the fused kernel every unit does (its register budget takes no branch)
+  const bool do_l1 = live && (CO || tt == 0);
   double l1[EW];
-  float xm[kTT];
 #pragma unroll
   for (int j = 0; j < EW; ++j) l1[j] = 0.0;
-#pragma unroll
-  for (int k = 0; k < kTT; ++k) xm[k] = 0.0f;
   if (live) {
     // pieces [p0, p1) of this part, NPC per pass, all loads of a pass in flight together
     const int npc = (H + 255) / 256, ppk = (npc + ks - 1) / ks;
@@ -104,17 +102,18 @@ __device__ __forceinline__ void logits_partials(const uint16_t* __restrict__ X, 
         const int t = t0 + k < T ? t0 + k : T - 1;
         xv[k] = *(const ushort4*)(X + (size_t)t * H + hc);
       }
+      if (do_l1)
 #pragma unroll
-      for (int j = 0; j < EW; ++j)
-        l1[j] += hin ? ((double)fabsf(wv[j].x) + (double)fabsf(wv[j].y)) +
-                           ((double)fabsf(wv[j].z) + (double)fabsf(wv[j].w))
-                     : 0.0;
+        for (int j = 0; j < EW; ++j)
+          l1[j] += hin ? ((double)fabsf(wv[j].x) + (double)fabsf(wv[j].y)) +
+                             ((double)fabsf(wv[j].z) + (double)fabsf(wv[j].w))
+                       : 0.0;
 #pragma unroll
       for (int k = 0; k < kTT; ++k) {
-        const float f0 = hin ? x_to_f32<XDT>(xv[k].x) : 0.0f, f1 = hin ? x_to_f32<XDT>(xv[k].y) : 0.0f;
-        const float f2 = hin ? x_to_f32<XDT>(xv[k].z) : 0.0f, f3 = hin ? x_to_f32<XDT>(xv[k].w) : 0.0f;
-        xm[k] = fmaxf(xm[k], fmaxf(fmaxf(fabsf(f0), fabsf(f1)), fmaxf(fabsf(f2), fabsf(f3))));
-        const double x0 = f0, x1 = f1, x2 = f2, x3 = f3;
+        const double x0 = hin ? (double)x_to_f32<XDT>(xv[k].x) : 0.0;
+        const double x1 = hin ? (double)x_to_f32<XDT>(xv[k].y) : 0.0;
+        const double x2 = hin ? (double)x_to_f32<XDT>(xv[k].z) : 0.0;
+        const double x3 = hin ? (double)x_to_f32<XDT>(xv[k].w) : 0.0;
 #pragma unroll
         for (int j = 0; j < EW; ++j) {
           a[k][j] = fma(x0, (double)wv[j].x, a[k][j]);
@@ -138,15 +137,6 @@ __device__ __forceinline__ void logits_partials(const uint16_t* __restrict__ X, 
       if (lane == 0 && e0 + j < E) st_f64<CO>(wl1 + (size_t)kp * E + e0 + j, v);
     }
   }
-  if (live && eg == 0) {
-#pragma unroll
-    for (int k = 0; k < kTT; ++k) {
-      float v = xm[k];
-#pragma unroll
-      for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
-      if (lane == 0 && t0 + k < T) st_f64<CO>(xinf + (size_t)kp * T + t0 + k, (double)v);
-    }
-  }
 }
 
 // Logits, second half (after a barrier): lane k EW + j sums the 64 partials of
@@ -163,11 +153,7 @@ __device__ __forceinline__ void logits_sum(int T, int E, int ks, long long u, in
   double s = 0.0;
 #pragma unroll 16
   for (int l = 0; l < 64; ++l) s += part[lane * 65 + l];
-  if (t < T && e < E) {
-    double* dst = logits + ((size_t)kp * T + t) * E + e;
-    if constexpr (CO) __hip_atomic_store(dst, s, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    else *dst = s;
-  }
+  if (t < T && e < E) st_f64<CO>(logits + ((size_t)kp * T + t) * E + e, s);
 }
 
 // Logits of large batches on the fp64 matrix cores: wave unit u is one 16-token x
@@ -183,7 +169,7 @@ typedef double f64x4 __attribute__((ext_vector_type(4)));
 template <int XDT, bool CO = false>
 __device__ __forceinline__ void logits_tile_mfma(const uint16_t* __restrict__ X, const float* __restrict__ W, int T,
                                                  int H, int E, long long u, int lane, double* __restrict__ logits,
-                                                 double* __restrict__ wl1, double* __restrict__ xinf) {
+                                                 double* __restrict__ wl1) {
   const int g = lane >> 4, c = lane & 15;
   const int ntt = (T + 15) >> 4, net = (E + 15) >> 4;
   if (u >= (long long)ntt * net) return;
@@ -192,8 +178,7 @@ __device__ __forceinline__ void logits_tile_mfma(const uint16_t* __restrict__ X,
   const uint16_t* xr = X + (size_t)t * H + 4 * g;
   const float* wr = W + (size_t)e * H + 4 * g;
   f64x4 acc = {0.0, 0.0, 0.0, 0.0};
-  double l1 = 0.0;  // this lane's share of the 1-norm of router row e and ...
-  float xm = 0.0f;  // ... of the max-norm of token t (the first tile row / column stores them)
+  double l1 = 0.0;  // this lane's share of the 1-norm of router row e (the first tile row only)
   constexpr int kU = 8;  // 16-index steps per pass, loads of a pass in flight together
   for (int h0 = 0; h0 < H; h0 += 16 * kU) {
     ushort4 xv[kU];
@@ -207,9 +192,8 @@ __device__ __forceinline__ void logits_tile_mfma(const uint16_t* __restrict__ X,
 #pragma unroll
     for (int j = 0; j < kU; ++j) {
       if (h0 + 16 * j < H) {
-        l1 += ((double)fabsf(wv[j].x) + (double)fabsf(wv[j].y)) + ((double)fabsf(wv[j].z) + (double)fabsf(wv[j].w));
-        xm = fmaxf(xm, fmaxf(fmaxf(fabsf(x_to_f32<XDT>(xv[j].x)), fabsf(x_to_f32<XDT>(xv[j].y))),
-                             fmaxf(fabsf(x_to_f32<XDT>(xv[j].z)), fabsf(x_to_f32<XDT>(xv[j].w)))));
+        if (tt == 0)
+          l1 += ((double)fabsf(wv[j].x) + (double)fabsf(wv[j].y)) + ((double)fabsf(wv[j].z) + (double)fabsf(wv[j].w));
         acc = __builtin_amdgcn_mfma_f64_16x16x4f64((double)x_to_f32<XDT>(xv[j].x), (double)wv[j].x, acc, 0, 0, 0);
         acc = __builtin_amdgcn_mfma_f64_16x16x4f64((double)x_to_f32<XDT>(xv[j].y), (double)wv[j].y, acc, 0, 0, 0);
         acc = __builtin_amdgcn_mfma_f64_16x16x4f64((double)x_to_f32<XDT>(xv[j].z), (double)wv[j].z, acc, 0, 0, 0);
@@ -222,11 +206,7 @@ __device__ __forceinline__ void logits_tile_mfma(const uint16_t* __restrict__ X,
     l1 += __shfl_xor(l1, 32);
     if (g == 0 && et * 16 + c < E) st_f64<CO>(wl1 + et * 16 + c, l1);
   }
-  if (et == 0) {
-    xm = fmaxf(xm, __shfl_xor(xm, 16));
-    xm = fmaxf(xm, __shfl_xor(xm, 32));
-    if (g == 0 && tt * 16 + c < T) st_f64<CO>(xinf + tt * 16 + c, (double)xm);
-  }
+
   const int ecol = et * 16 + c;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
@@ -241,41 +221,93 @@ __device__ __forceinline__ void logits_tile_mfma(const uint16_t* __restrict__ X,
 }
 
 // Top-K of token t by one wave, in three parts separated by barriers: add up
-// the logit's hidden parts and the bias into lg (E doubles of LDS), rank every expert (rank(e) = #experts that
-// beat it, ties to the lower index) into sel_v / sel_i (16 entries each), then
-// the softmax of the K winners summed in rank order.
+// the logit's hidden parts and the bias into lg (E doubles of LDS), rank every
+// expert (rank(e) = #experts that beat it, ties to the lower index) into sel_v
+// / sel_i (the K winners and the runner-up: 17 entries each), then the
+// softmax of the K winners summed in rank order.
 template <bool CO = false>
 __device__ __forceinline__ void topk_load(const double* __restrict__ logits, const float* __restrict__ bias, int ks,
                                           int t, int T, int E, int lane, double* lg) {
   if (t < T)
-    for (int e = lane; e < E; e += 64) {
+    for (int e = CO ? lane : lane + 64; e < E; e += 64) {  // outside CO, topk_gather loads the first
       double v = 0.0;
-      for (int kp = 0; kp < ks; ++kp) {
-        const double* a = logits + ((size_t)kp * T + t) * E + e;
-        if constexpr (CO) v += __hip_atomic_load(const_cast<double*>(a), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        else v += *a;
+      if constexpr (CO) {  // the fused kernel: no registers to spare
+        for (int kp = 0; kp < ks; ++kp) v += ld_f64<CO>(logits + ((size_t)kp * T + t) * E + e);
+      } else {
+        // every part's load in flight together (parts past ks re-read the
+        // last one and are not added), then the parts added in order
+        double a[kMaxParts];
+#pragma unroll
+        for (int kp = 0; kp < kMaxParts; ++kp) a[kp] = ld_f64<CO>(logits + ((size_t)min(kp, ks - 1) * T + t) * E + e);
+#pragma unroll
+        for (int kp = 0; kp < kMaxParts; ++kp) v = kp < ks ? v + a[kp] : v;
       }
       lg[e] = v + (bias ? (double)bias[e] : 0.0);
     }
 }
 
-// The router rows' 1-norms (sum of the hidden parts) into l1 (LDS, shared
-// by the workgroup: thread tid of nthr), and token t's max-norm.
-template <bool CO = false>
-__device__ __forceinline__ void topk_load_l1(const double* __restrict__ wl1, int ks, int E, int tid, int nthr,
-                                             float* l1) {
-  for (int e = tid; e < E; e += nthr) {
-    double v = 0.0;
-    for (int kp = 0; kp < ks; ++kp) v += ld_f64<CO>(wl1 + (size_t)kp * E + e);
-    l1[e] = (float)v;
+// The top-K step's reads besides the logits (topk_load), for the rounding
+// bound: max over the experts of ||w_e||_1 + |bias_e| (the 1-norms summed over
+// the hidden parts; thread tid of nthr takes experts tid, tid + nthr, ... and
+// raises *nmax, LDS, zero before: non-negative floats order as their bits),
+// and ||x_t||_inf from token t's row (the same value on every lane). Outside
+// the fused kernel the first expert of each role, every part and the first
+// 4096 elements of the row are requested at once with the logits of the
+// lane's first expert (one memory round trip): lg gets those logits here and
+// topk_load the rest (from expert 64 on).
+template <int XDT, bool CO = false>
+__device__ __forceinline__ float topk_gather(const double* __restrict__ logits, const uint16_t* __restrict__ X,
+                                             const float* __restrict__ bias, int ks, int t, int T, int H, int E,
+                                             int lane, int tid, int nthr, double* lg, unsigned* nmax) {
+  const double* wl1 = route_ws_l1(const_cast<double*>(logits), ks, T, E);
+  const int tc = min(t, T - 1);
+  const uint16_t* x = X + (size_t)tc * H;
+  auto amax4 = [](ushort4 v) {
+    return fmaxf(fmaxf(fabsf(x_to_f32<XDT>(v.x)), fabsf(x_to_f32<XDT>(v.y))),
+                 fmaxf(fabsf(x_to_f32<XDT>(v.z)), fabsf(x_to_f32<XDT>(v.w))));
+  };
+  float xi = 0.0f;
+  constexpr int kXR = 16;  // row pieces of 256 elements requested with the rest
+  if constexpr (CO) {      // the fused kernel: no registers to spare
+    for (int e = tid; e < E; e += nthr) {
+      double v = bias ? fabs((double)bias[e]) : 0.0;
+      for (int kp = 0; kp < ks; ++kp) v += ld_f64<CO>(wl1 + (size_t)kp * E + e);
+      atomicMax(nmax, __float_as_uint((float)v));
+    }
+    for (int h = 4 * lane; h < H; h += 256) xi = fmaxf(xi, amax4(*(const ushort4*)(x + h)));
+  } else {
+    const int el = min(lane, E - 1), en = min(tid, E - 1);
+    double a[kMaxParts], b[kMaxParts];
+    ushort4 xv[kXR];
+#pragma unroll
+    for (int kp = 0; kp < kMaxParts; ++kp) {
+      const size_t k = (size_t)min(kp, ks - 1);
+      a[kp] = logits[(k * T + tc) * E + el];
+      b[kp] = wl1[k * E + en];
+    }
+#pragma unroll
+    for (int i = 0; i < kXR; ++i) xv[i] = *(const ushort4*)(x + min(4 * lane + 256 * i, H - 4));  // repeats are harmless
+    const double bl = bias ? (double)bias[el] : 0.0, bn = bias ? fabs((double)bias[en]) : 0.0;
+    double v = 0.0, nv = bn;
+#pragma unroll
+    for (int kp = 0; kp < kMaxParts; ++kp) {
+      v = kp < ks ? v + a[kp] : v;
+      nv = kp < ks ? nv + b[kp] : nv;
+    }
+#pragma unroll
+    for (int i = 0; i < kXR; ++i) xi = fmaxf(xi, amax4(xv[i]));
+    if (t < T && lane < E) lg[lane] = v + bl;
+    if (tid < E) atomicMax(nmax, __float_as_uint((float)nv));
+    for (int h = 4 * lane + 256 * kXR; h < H; h += 256) xi = fmaxf(xi, amax4(*(const ushort4*)(x + h)));
+    for (int e = tid + nthr; e < E; e += nthr) {
+      double w = bias ? fabs((double)bias[e]) : 0.0;
+      for (int kp = 0; kp < ks; ++kp) w += wl1[(size_t)kp * E + e];
+      atomicMax(nmax, __float_as_uint((float)w));
+    }
   }
-}
-template <bool CO = false>
-__device__ __forceinline__ double topk_xinf(const double* __restrict__ xinf, int ks, int t, int T) {
-  double v = 0.0;
-  if (t < T)
-    for (int kp = 0; kp < ks; ++kp) v = fmax(v, ld_f64<CO>(xinf + (size_t)kp * T + t));
-  return v;
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) xi = fmaxf(xi, __shfl_xor(xi, o));
+  return xi;
 }
 
 __device__ __forceinline__ void topk_rank(int t, int T, int E, int K, int lane, const double* lg, double* sel_v,
@@ -289,7 +321,7 @@ __device__ __forceinline__ void topk_rank(int t, int T, int E, int K, int lane, 
       const double x = lg[j];
       rank += (x > v || (x == v && j < e)) ? 1 : 0;
     }
-    if (rank < K) {
+    if (rank <= K) {  // the K winners and the runner-up (sel_* hold K + 1 <= 17 entries)
       sel_v[rank] = v;
       sel_i[rank] = e;
     }
@@ -320,18 +352,20 @@ __device__ __forceinline__ void topk_finish(int t, int T, int K, int lane, const
 // ---------------------------------------------------------------- exact order
 // Every fp64 logit is a sum of H exact products x_h w_h (an fp16 or bf16 times
 // an fp32 fits the 53-bit significand) and the bias, so whatever the order of
-// its additions its rounding error is at most gamma_n (||x||_inf ||w_e||_1 +
-// |bias_e|) with gamma_n = n u / (1 - n u), u = 2^-53 and n the number of
-// additions (Higham, Accuracy and Stability of Numerical Algorithms, §4.2; n
-// is taken as 2 (H + 64), which also covers a matrix-core sum rounded more
-// than once per step). The top-K of a token is certified when each winner's
-// interval lies above the next winner's and every other expert's interval
-// lies below all of them. Otherwise ("PagedWeight" §2.1 ranks the experts by
-// their logits; ties go to the lower index) the experts whose interval reaches
-// the winners are ranked on their exact logits: each product is an integer
-// times a power of two, summed exactly into kXL 32-bit digits of weight
-// 2^-282 .. 2^294 (which hold any fp16 or bf16 x fp32 product, any fp32 bias
-// and their sums), and the K largest are kept, equal values in index order.
+// its additions its rounding error is at most gamma_n (||x_t||_inf ||w_e||_1 +
+// |bias_e|) <= B_t = gamma_n max(||x_t||_inf, 1) max_e (||w_e||_1 + |bias_e|)
+// with gamma_n = n u / (1 - n u), u = 2^-53 and n the number of additions
+// (Higham, Accuracy and Stability of Numerical Algorithms, §4.2; n is taken as
+// 2 (H + 64), which also covers a matrix-core sum rounded more than once per
+// step). The top-K of a token is certified when each winner's logit exceeds
+// the next one's, and the last winner's the runner-up's, by more than 2 B_t:
+// every other expert lies at or below the runner-up. Otherwise ("PagedWeight"
+// §2.1 ranks the experts by their logits; ties go to the lower index) the
+// experts within 2 B_t of the last winner or above it are ranked on their
+// exact logits: each product is an integer times a power of two, summed
+// exactly into kXL 32-bit digits of weight 2^-282 .. 2^294 (which hold any
+// fp16 or bf16 x fp32 product, any fp32 bias and their sums), and the K
+// largest are kept, equal values in index order.
 constexpr int kXL = 18;
 constexpr int kXEmin = -282;
 
@@ -416,44 +450,36 @@ __device__ __forceinline__ bool exact_greater(const uint32_t* a, const uint32_t*
   return false;
 }
 
-// Certificate of the top-K in sel_v / sel_i (after topk_rank) and, when it
-// fails, the exact ranking in their place. lg: token t's fp64 logits, l1:
-// ||w_e||_1 of every expert (float, LDS), xi: ||x_t||_inf. Called by the
-// whole wave of token t.
+// B_t of the comment above, from ||x_t||_inf and max_e (||w_e||_1 + |bias_e|)
+// (the margin covers that maximum rounded to float and the bound's own
+// rounding).
+__device__ __forceinline__ double logit_bound(int H, float xi, float nmax) {
+  const double n = 2.0 * ((double)H + 64.0), u = 0x1p-53;
+  return n * u / (1.0 - n * u) * (1.0 + 0x1p-20) * fmax((double)xi, 1.0) * (double)nmax;
+}
+
+// Certificate of the top-K in sel_v / sel_i (after topk_rank: winners and
+// runner-up) and, when it fails, the exact ranking in their place. lg: token
+// t's fp64 logits, B: their error bound. Called by the whole wave of token t;
+// lane i < K checks winner i against the next entry.
 template <int XDT>
 __device__ __forceinline__ void topk_certify(const uint16_t* __restrict__ X, const float* __restrict__ W,
                                              const float* __restrict__ bias, int t, int T, int H, int E, int K,
-                                             int lane, const double* lg, const float* l1, double xi, double* sel_v,
-                                             int* sel_i, ExactScratch& sc) {
+                                             int lane, const double* lg, double B, double* sel_v, int* sel_i,
+                                             ExactScratch& sc) {
   if (t >= T) return;
-  const double n = 2.0 * ((double)H + 64.0), u = 0x1p-53;
-  // the margin covers l1 rounded to float and the rounding of the bound itself
-  const double gam = n * u / (1.0 - n * u) * (1.0 + 0x1p-20);
-  auto bd = [&](int e) {
-    const int ec = min(max(e, 0), E - 1);
-    return gam * (xi * (double)l1[ec] + (bias ? fabs((double)bias[ec]) : 0.0));
-  };
-  double thr = 1e308;
-  bool ok = true;
-  for (int i = 0; i < K; ++i) {
-    const double lo = sel_v[i] - bd(sel_i[i]);
-    thr = fmin(thr, lo);
-    if (i + 1 < K && !(lo > sel_v[i + 1] + bd(sel_i[i + 1]))) ok = false;
-  }
-  auto winner = [&](int e) {
-    bool wn = false;
-    for (int i = 0; i < K; ++i) wn |= sel_i[i] == e;
-    return wn;
-  };
-  for (int e = lane; e < E; e += 64)
-    if (!winner(e) && !(lg[e] + bd(e) < thr)) ok = false;
+  const bool ok = !(lane < K && lane + 1 <= min(K, E - 1)) || sel_v[lane] - B > sel_v[lane + 1] + B;
   if (__all(ok)) return;
-  // exact ranking of every expert whose interval reaches the winners'
+  const double thr = sel_v[K - 1] - B;
+  const double vK = sel_v[K - 1];
+  const int iK = sel_i[K - 1];
+  auto winner = [&](int e) { return lg[e] > vK || (lg[e] == vK && e <= iK); };
+  // exact ranking of the winners and of every expert within reach of them
   if (lane == 0) sc.n = 0;
   if (lane < 16) sc.top_i[lane] = 0;  // a valid id in any slot a nan logit leaves empty
   wave_lds_fence();
   for (int e = 0; e < E; ++e) {
-    if (!winner(e) && lg[e] + bd(e) < thr) continue;  // the same on every lane
+    if (!winner(e) && lg[e] + B < thr) continue;  // the same on every lane
     exact_logit<XDT>(X, W, bias, t, e, H, lane, sc);
     if (lane == 0) {
       long long v[kXL];

@@ -63,9 +63,9 @@ def test_host_validation_without_device(L):
     assert L.moe_route(one, 0, one, None, 4, 256, 8, 17, one, one, one, 1 << 20, None) == -2  # K
     assert L.moe_route(one, 0, one, None, 0, 256, 8, 2, one, one, one, 0, None) == 0          # T = 0
     r256 = lambda n: (n + 255) // 256 * 256
-    # [8][4][8] fp64 parts, [8][8] row norms, [8][4] token norms
-    assert L.moe_route_workspace_bytes(4, 8) == r256(8 * (4 * 8 + 8 + 4) * 8)
-    assert L.moe_route_workspace_bytes(4096, 128) == r256((4096 * 128 + 128 + 4096) * 8)       # matrix-core path
+    # [8][4][8] fp64 parts and [8][8] router-row norms
+    assert L.moe_route_workspace_bytes(4, 8) == r256(8 * (4 * 8 + 8) * 8)
+    assert L.moe_route_workspace_bytes(4096, 128) == r256((4096 * 128 + 128) * 8)              # matrix-core path
     assert L.moe_route(one, 0, one, None, 4, 256, 8, 2, one, one, one, 255, None) == -5       # workspace
     assert L.moe_route(one, 0, one, None, 4, 256, 8, 2, one, one, None, 1 << 20, None) == -1  # null ws
     assert L.mpb_pack_block(one, 48, 128, (ctypes.c_void_p * 8)(*[1] * 8), None) == -2
