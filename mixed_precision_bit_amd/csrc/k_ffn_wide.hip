@@ -19,7 +19,9 @@
 //     stages, one barrier per step);
 //   * contraction: wave w multiplies all 128 rows (four 32-row blocks from the
 //     A stage) with its 128 columns (four 32-column blocks read straight from
-//     memory into registers a whole step ahead): sixteen 32x32x16 MFMAs per
+//     memory into registers: each substep's operands of the next step are
+//     requested into the registers its MFMAs have just read, which frees the
+//     registers of a second operand set): sixteen 32x32x16 MFMAs per
 //     16 K into 256 accumulators, the dequantisation of the next step placed
 //     between them. The K order inside a step is permuted (the same for both
 //     operands): 16-K substep ks takes K octets ks and 4 + ks, so that the
@@ -171,13 +173,12 @@ __device__ __forceinline__ void wide_body(const FfnParams& p, const Item& wi, in
   // the compiler an unknown count of loads in flight, and it then waits for
   // all of them, which would expose the full memory latency every step.
   typedef f16x8 Bops[4][4];
-  auto load_b = [&](Bops& B, int s) {
+  auto load_b1 = [&](Bops& B, int s, int ks) {
 #pragma unroll
     for (int c = 0; c < 4; ++c)
-#pragma unroll
-      for (int ks = 0; ks < 4; ++ks)
-        B[c][ks] = __builtin_bit_cast(f16x8, __builtin_amdgcn_raw_buffer_load_b128(brs, boff[c] + bks * ks, bstep * s, 0));
+      B[c][ks] = __builtin_bit_cast(f16x8, __builtin_amdgcn_raw_buffer_load_b128(brs, boff[c] + bks * ks, bstep * s, 0));
   };
+
   // A operand of row block rb, substep ks: tile row 32 rb + r, piece 4 g + ks
   // (the swizzle does not depend on rb)
   uint32_t ard[4];
@@ -190,8 +191,9 @@ __device__ __forceinline__ void wide_body(const FfnParams& p, const Item& wi, in
   uint32_t PR[2][Q];
   load_words(PR[0], 0);
   load_words(PR[1], 1);
-  Bops BB[2];
-  load_b(BB[0], 0);
+  Bops BB;
+#pragma unroll
+  for (int ks = 0; ks < 4; ++ks) load_b1(BB, 0, ks);
   wait_vmem_all();
   __syncthreads();
   {
@@ -215,8 +217,7 @@ __device__ __forceinline__ void wide_body(const FfnParams& p, const Item& wi, in
   // substeps (assembly, two lookup halves, stores); request step s + 3's
   // planes; one barrier. In the last step the dequantisation fills the idle
   // stage with unused values.
-  auto step = [&](int s, uint32_t (&Pn)[Q], Bops& Bc, Bops& Bn) {
-    load_b(Bn, min(s + 1, NS - 1));
+  auto step = [&](int s, uint32_t (&Pn)[Q], Bops& Bc) {
     const char* ab = abuf + (uint32_t)(s & 1) * kWideAStage;
     char* an = abuf + (uint32_t)((s + 1) & 1) * kWideAStage;
     f16x8 A[2][4];
@@ -235,6 +236,8 @@ __device__ __forceinline__ void wide_body(const FfnParams& p, const Item& wi, in
 #pragma unroll
         for (int rb = 0; rb < 4; ++rb) acc[rb][c] = mfma32(A[ks & 1][rb], Bc[c][ks], acc[rb][c]);
       }
+      // substep ks of the next step, into the registers these MFMAs have read
+      load_b1(Bc, min(s + 1, NS - 1), ks);
       if (ks == 0) assemble<Q>(Pn, O);
       if (ks == 1) {
         d[0] = lookup8(O[0], O[1], slot);
@@ -254,7 +257,7 @@ __device__ __forceinline__ void wide_body(const FfnParams& p, const Item& wi, in
   for (int s0 = 0; s0 < NS; s0 += 2)
     unroll_const<2>([&](auto u) {
       const int s = s0 + u;
-      if (s < NS) step(s, PR[(u + 1) % 2], BB[u], BB[(u + 1) % 2]);
+      if (s < NS) step(s, PR[(u + 1) % 2], BB);
     });
 
   // ---- epilogue. acc[rb][c][v] is tile row 32 rb + 8 (v / 4) + 4 g + v % 4,
