@@ -290,6 +290,19 @@ int mpb_dequant_block(const uint32_t* const* pages_host, const uint16_t* lut_b_d
                       int b, uint16_t* out_f16_dev, void* stream);
 
 /*
+ * The same dequantisation (§3.1, Eq. 2) read through a table image
+ * (mpb_pack_table of kind `kind` for this block, b bits, image_dev on the
+ * device) the way the FFN kernels stage and index it: a check that an image
+ * holds every table entry where those kernels look it up. Writes out_f16_dev
+ * [N][Kd] fp16 in canonical element order. Shapes as for mpb_table_image_bytes
+ * (N % 128 == 0 for kind 0, N % 64 == 0 for kind 1) and Kd % 64 == 0;
+ * MPB_E_ARG for a bad kind or a null pointer,
+ * MPB_E_RANGE (b), MPB_E_SHAPE, MPB_E_HIP.
+ */
+int mpb_dequant_block_image(const uint32_t* const* pages_host, const uint16_t* image_dev, int kind, int N,
+                            int Kd, int b, uint16_t* out_f16_dev, void* stream);
+
+/*
  * Page movement (§3.1 after Eq. 3, §3.3 "Asynchronous Page Movement",
  * Figure 4: an offload first lowers q_i, then moves the pages above it to CPU
  * memory; a reload first moves the pages back and raises q_i only once they

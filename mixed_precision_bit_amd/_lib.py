@@ -81,6 +81,7 @@ def lib() -> ctypes.CDLL:
             "mpb_dequant_block": (_I, [_P, _P, _I, _I, _I, _P, _P]),
             "mpb_table_image_bytes": (ctypes.c_int64, [_I, _I, _I]),
             "mpb_pack_table": (_I, [_I, _P, _I, _I, _P, _P]),
+            "mpb_dequant_block_image": (_I, [_P, _P, _I, _I, _I, _I, _P, _P]),
             "mpb_set_resident_planes": (_I, [_I, _I]),
             "mpb_get_resident_planes": (_I, [_I]),
             "mpb_offload_pages": (_I, [_I, _I, _P, _P, _P, _P, _P]),
@@ -221,6 +222,12 @@ def mpb_dequant_block(pages, lut, N, Kd, b, out, stream=None):
     arr = _host_ptrs([p.data_ptr() for p in pages[:b]])
     return _check("mpb_dequant_block", lib().mpb_dequant_block(arr, _ptr(lut), N, Kd, b, _ptr(out),
                                                                _stream(stream)))
+
+
+def mpb_dequant_block_image(pages, image, kind, N, Kd, b, out, stream=None):
+    arr = _host_ptrs([p.data_ptr() for p in pages[:b]])
+    return _check("mpb_dequant_block_image", lib().mpb_dequant_block_image(arr, _ptr(image), kind, N, Kd, b,
+                                                                           _ptr(out), _stream(stream)))
 
 
 def mpb_set_kernel_events(events):

@@ -5,6 +5,7 @@
 // read: a block at bitwidth q touches its first q pages and nothing else
 // ("PagedWeight", §3.1: one bit-plane is one weight page; §2.2: the top planes
 // form the lower-bitwidth weights).
+#include "k_ffn_body.h"
 #include "mpb_device.h"
 #include "mpb_internal.h"
 
@@ -133,6 +134,76 @@ hipError_t launch_dequant(const uint32_t* const* pages, const uint16_t* lut, int
   CPagePtrs pp;
   for (int p = 0; p < 8; ++p) pp.p[p] = p < b ? pages[p] : nullptr;
   hipLaunchKernelGGL(k_dequant, dim3(N / 32), dim3(64), 0, s, pp, lut, Kd / 32, b, out);
+  return hipGetLastError();
+}
+
+// Dequantisation through a table image, as the FFN kernels read it: one
+// 512-thread workgroup per image tile copies the tile's image to LDS with
+// their load_table_image, and wave w < 4 dequantises the rows that wave w of
+// an FFN workgroup looks up (kind 0, gate_up: (w / 2) N/2 + 64 t + 32 (w % 2) +
+// r; kind 1, down: 128 t + 32 w + r) with table slot lut_slot(r, w), writing
+// fp16 weights in canonical element order. Used to check mpb_pack_table's
+// images bit for bit against the canonical tables.
+template <int Q>
+__device__ void dequant_tile_image(const CPagePtrs& pages, const uint16_t* __restrict__ img, int kind, int N, int W,
+                                   uint16_t* __restrict__ out) {
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, r = lane & 31, g = lane >> 5;
+  const int t = blockIdx.x, NC = (W + 3) / 4, Kd = W * 32;
+  load_table_image<Q>(img + (size_t)t * (128u << Q), w, lane);
+  wait_vmem_all();
+  __syncthreads();
+  if (w >= 4) return;
+  const int row = kind == 0 ? (w >> 1) * (N / 2) + 64 * t + 32 * (w & 1) + r : 128 * t + 32 * w + r;
+  if (row >= N) return;  // past the last tile's rows (kind 1; whole waves, N % 64 == 0)
+  const uint32_t slot = lut_slot(r, w);
+  for (int c = g; c < NC; c += 2) {
+    uint4 P4[Q];
+#pragma unroll
+    for (int p = 0; p < Q; ++p) P4[p] = *(const uint4*)(pages.p[p] + page_word(row, 4 * c, NC));
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int word = 4 * c + j;
+      if (word >= W) break;
+      uint32_t P[Q];
+#pragma unroll
+      for (int p = 0; p < Q; ++p) P[p] = j == 0 ? P4[p].x : j == 1 ? P4[p].y : j == 2 ? P4[p].z : P4[p].w;
+      uint32_t O[8];
+      assemble<Q>(P, O);
+      uint16_t* dst = out + (size_t)row * Kd + word * 32;
+#pragma unroll
+      for (int m = 0; m < 4; ++m) *(f16x8*)(dst + 8 * m) = lookup8(O[2 * m], O[2 * m + 1], slot);
+    }
+  }
+}
+
+__global__ __launch_bounds__(512) void k_dequant_image(CPagePtrs pages, const uint16_t* __restrict__ img, int kind,
+                                                       int N, int W, int b, uint16_t* __restrict__ out) {
+  __shared__ __attribute__((aligned(256))) uint16_t lds[32768];
+  switch (tables_at_zero(lds) ? b : 0) {
+    case 3: dequant_tile_image<3>(pages, img, kind, N, W, out); break;
+    case 4: dequant_tile_image<4>(pages, img, kind, N, W, out); break;
+    case 5: dequant_tile_image<5>(pages, img, kind, N, W, out); break;
+    case 6: dequant_tile_image<6>(pages, img, kind, N, W, out); break;
+    case 7: dequant_tile_image<7>(pages, img, kind, N, W, out); break;
+    case 8: dequant_tile_image<8>(pages, img, kind, N, W, out); break;
+    default:  // table region misplaced: NaN for the tile's rows
+      if (threadIdx.x < 256) {
+        const int w = threadIdx.x >> 6, t = blockIdx.x;
+        for (int r = 0; r < 32; ++r) {
+          const int row = kind == 0 ? (w >> 1) * (N / 2) + 64 * t + 32 * (w & 1) + r : 128 * t + 32 * w + r;
+          if (row < N)
+            for (int i = threadIdx.x & 63; i < W * 32; i += 64) out[(size_t)row * W * 32 + i] = 0x7e00;
+        }
+      }
+  }
+}
+
+hipError_t launch_dequant_image(const uint32_t* const* pages, const uint16_t* img, int kind, int N, int Kd, int b,
+                                uint16_t* out, hipStream_t s) {
+  CPagePtrs pp;
+  for (int p = 0; p < 8; ++p) pp.p[p] = p < b ? pages[p] : nullptr;
+  const int tiles = kind == 0 ? N / 128 : (N + 127) / 128;
+  hipLaunchKernelGGL(k_dequant_image, dim3(tiles), dim3(512), 0, s, pp, img, kind, N, Kd / 32, b, out);
   return hipGetLastError();
 }
 

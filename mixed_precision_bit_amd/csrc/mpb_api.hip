@@ -340,6 +340,23 @@ int mpb_dequant_block(const uint32_t* const* pages_host, const uint16_t* lut_b_d
   return fail(MPB_E_HIP, "mpb_dequant_block: unexpected exception");
 }
 
+int mpb_dequant_block_image(const uint32_t* const* pages_host, const uint16_t* image_dev, int kind, int N, int Kd,
+                            int b, uint16_t* out_f16_dev, void* stream) try {
+  if (!pages_host || !image_dev || !out_f16_dev) return fail(MPB_E_ARG, "mpb_dequant_block_image: null pointer");
+  if (kind != 0 && kind != 1) return fail(MPB_E_ARG, "mpb_dequant_block_image: kind must be 0 or 1");
+  if (b < 3 || b > 8) return fail(MPB_E_RANGE, "mpb_dequant_block_image: b outside 3..8");
+  for (int p = 0; p < b; ++p)
+    if (!pages_host[p]) return fail(MPB_E_ARG, "mpb_dequant_block_image: null page pointer");
+  if (N <= 0 || N % (kind == 0 ? 128 : 64) || Kd <= 0 || Kd % 64)
+    return fail(MPB_E_SHAPE, "mpb_dequant_block_image: need N % 128 == 0 (kind 0) or N % 64 == 0 (kind 1), "
+                             "and Kd % 64 == 0");
+  hipError_t e = mpb::launch_dequant_image(pages_host, image_dev, kind, N, Kd, b, out_f16_dev, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "mpb_dequant_block_image");
+  return MPB_OK;
+} catch (...) {
+  return fail(MPB_E_HIP, "mpb_dequant_block_image: unexpected exception");
+}
+
 int moe_routing_mass(const int32_t* topk_idx_dev, const float* topk_w_dev, int T, int E, int K, double* mass_dev,
                      void* stream) try {
   if (T < 0 || T > (1 << 20)) return fail(MPB_E_SHAPE, "moe_routing_mass: T outside 0..2^20");

@@ -159,6 +159,8 @@ hipError_t launch_pack(const uint32_t* canon, int N, int Kd, uint32_t* const* pa
 hipError_t launch_pack_table(const uint16_t* lut, int kind, int N, int b, uint16_t* img, hipStream_t s);
 hipError_t launch_dequant(const uint32_t* const* pages, const uint16_t* lut, int N, int Kd, int b,
                           uint16_t* out, hipStream_t s);
+hipError_t launch_dequant_image(const uint32_t* const* pages, const uint16_t* img, int kind, int N, int Kd, int b,
+                                uint16_t* out, hipStream_t s);
 size_t route_workspace_bytes(int T, int E);
 hipError_t launch_routing_mass(const int32_t* idx, const float* w, int T, int E, int K, double* mass,
                                hipStream_t s);

@@ -29,7 +29,8 @@ def test_header_declares_the_calls():
     names = declared_functions()
     for n in ("moe_route", "moe_route_workspace_bytes", "moe_ffn", "set_committed_bits", "mpb_init", "mpb_pack_block",
               "mpb_committed_bytes", "mpb_dequant_block", "mpb_last_error", "mpb_table_image_bytes",
-              "mpb_pack_table", "moe_routing_mass", "mpb_offload_pages", "mpb_reload_pages", "mpb_page_state"):
+              "mpb_pack_table", "moe_routing_mass", "mpb_offload_pages", "mpb_reload_pages", "mpb_page_state",
+              "mpb_dequant_block_image"):
         assert n in names
 
 
@@ -79,6 +80,11 @@ def test_host_validation_without_device(L):
     assert L.mpb_table_image_bytes(2, 256, 3) == -1               # kind
     assert L.mpb_table_image_bytes(1, 256, 9) == -3               # b
     assert L.mpb_pack_table(1, None, 256, 4, one, None) == -1
+    pg = (ctypes.c_void_p * 8)(*[1] * 8)
+    assert L.mpb_dequant_block_image(pg, one, 2, 256, 128, 4, one, None) == -1               # kind
+    assert L.mpb_dequant_block_image(pg, one, 0, 192, 128, 4, one, None) == -2               # gate_up: N % 128
+    assert L.mpb_dequant_block_image(pg, one, 1, 256, 128, 9, one, None) == -3               # b
+    assert L.mpb_dequant_block_image(pg, None, 1, 256, 128, 4, one, None) == -1              # null image
     assert L.moe_routing_mass(one, one, 4, 0, 1, one, None) == -2     # E
     assert L.moe_routing_mass(one, one, 4, 8, 9, one, None) == -2     # K > E
     assert L.moe_routing_mass(one, one, 4, 8, 2, None, None) == -1    # null output

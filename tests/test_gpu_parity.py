@@ -71,6 +71,30 @@ def test_dequant_bit_exact_all_bitwidths(N, Kd):
         assert np.array_equal(got, ref), f"b={b}: {np.count_nonzero(got != ref)} mismatches"
 
 
+@pytest.mark.parametrize("N,Kd,kind", [(256, 2048, 0), (2816, 64, 1), (192, 128, 1), (1408, 192, 0)])
+def test_dequant_through_table_image_bit_exact(N, Kd, kind):
+    """mpb_pack_table's image read the way the FFN kernels stage and index it
+    (mpb_dequant_block_image) gives, bit for bit, the weights of the canonical
+    tables ("PagedWeight" §3.1, Eq. 2) and of the oracle, at every bitwidth, for
+    gate_up (kind 0: rows of the gate and up halves paired in a tile) and down
+    (kind 1, with a last tile partly past N)."""
+    blk = S.make_block(91, N + Kd + kind, N, Kd)
+    canon = torch.from_numpy(blk.planes.view(np.int32)).cuda()
+    nw = M().mpb_plane_page_bytes(N, Kd) // 4
+    pages = [torch.empty(nw, dtype=torch.int32, device="cuda") for _ in range(8)]
+    M().mpb_pack_block(canon, N, Kd, pages)
+    for b in S.BITS:
+        lut = torch.from_numpy(blk.luts[b - 3].view(np.int16)).cuda()
+        img = torch.empty(M().mpb_table_image_bytes(kind, N, b) // 2, dtype=torch.int16, device="cuda")
+        M().mpb_pack_table(kind, lut, N, b, img)
+        out = torch.empty((N, Kd), dtype=torch.int16, device="cuda")
+        M().mpb_dequant_block_image(pages, img, kind, N, Kd, b, out)
+        torch.cuda.synchronize()
+        got = out.cpu().numpy().view(np.uint16)
+        ref = O.dequant(blk.planes, blk.luts[b - 3], b).astype(np.float16).view(np.uint16)
+        assert np.array_equal(got, ref), f"b={b}: {np.count_nonzero(got != ref)} mismatches"
+
+
 def test_pack_round_trip_integer_table():
     rng = np.random.default_rng(11)
     N, Kd = 96, 192
