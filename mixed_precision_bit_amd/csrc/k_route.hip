@@ -67,18 +67,17 @@ __global__ __launch_bounds__(256) void k_route_topk(const double* __restrict__ l
   __shared__ double lg[4][kEMaxTopk];
   __shared__ double sel_v[4][17];
   __shared__ int sel_i[4][17];
-  __shared__ unsigned nmax;
+  __shared__ unsigned nmaxw[4];
   __shared__ ExactScratch sc[4];
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int t = blockIdx.x * 4 + w;
-  if (threadIdx.x == 0) nmax = 0u;
-  __syncthreads();
-  const float xi = topk_gather<XDT>(logits, X, bias, ks, t, T, H, E, lane, threadIdx.x, 256, lg[w], &nmax);
+  const float xi = topk_gather<XDT>(logits, X, bias, ks, t, T, H, E, lane, threadIdx.x, 256, lg[w], &nmaxw[w]);
+  const float nm = __uint_as_float(nmaxw[w]);
   topk_load(logits, bias, ks, t, T, E, lane, lg[w]);
   __syncthreads();
   topk_rank(t, T, E, K, lane, lg[w], sel_v[w], sel_i[w]);
   __syncthreads();
-  topk_certify<XDT>(X, W, bias, t, T, H, E, K, lane, lg[w], logit_bound(H, xi, __uint_as_float(nmax)),
+  topk_certify<XDT>(X, W, bias, t, T, H, E, K, lane, lg[w], logit_bound(H, xi, nm),
                     sel_v[w], sel_i[w], sc[w]);
   topk_finish(t, T, K, lane, sel_v[w], sel_i[w], idx_out, w_out);
 }

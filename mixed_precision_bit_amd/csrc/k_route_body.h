@@ -248,13 +248,15 @@ __device__ __forceinline__ void topk_load(const double* __restrict__ logits, con
 
 // The top-K step's reads besides the logits (topk_load), for the rounding
 // bound: max over the experts of ||w_e||_1 + |bias_e| (the 1-norms summed over
-// the hidden parts; thread tid of nthr takes experts tid, tid + nthr, ... and
-// raises *nmax, LDS, zero before: non-negative floats order as their bits),
-// and ||x_t||_inf from token t's row (the same value on every lane). Outside
-// the fused kernel the first expert of each role, every part and the first
-// 4096 elements of the row are requested at once with the logits of the
-// lane's first expert (one memory round trip): lg gets those logits here and
-// topk_load the rest (from expert 64 on).
+// the hidden parts) into *nmax, and ||x_t||_inf from token t's row (the same
+// value on every lane). Outside the fused kernel the wave finds the maximum
+// itself and stores it in its own *nmax: its first expert's logit and norm
+// parts and the first 4096 elements of the row are requested at once (one
+// memory round trip; lg gets those logits here, topk_load the rest from
+// expert 64 on), and both maxima are reduced across the wave together. In the
+// fused kernel (CO: no registers to spare) thread tid of nthr takes experts
+// tid, tid + nthr, ... and raises the workgroup's *nmax (LDS, zero before;
+// non-negative floats order as their bits).
 template <int XDT, bool CO = false>
 __device__ __forceinline__ float topk_gather(const double* __restrict__ logits, const uint16_t* __restrict__ X,
                                              const float* __restrict__ bias, int ks, int t, int T, int H, int E,
@@ -276,18 +278,18 @@ __device__ __forceinline__ float topk_gather(const double* __restrict__ logits, 
     }
     for (int h = 4 * lane; h < H; h += 256) xi = fmaxf(xi, amax4(*(const ushort4*)(x + h)));
   } else {
-    const int el = min(lane, E - 1), en = min(tid, E - 1);
+    const int el = min(lane, E - 1);
     double a[kMaxParts], b[kMaxParts];
     ushort4 xv[kXR];
 #pragma unroll
     for (int kp = 0; kp < kMaxParts; ++kp) {
       const size_t k = (size_t)min(kp, ks - 1);
       a[kp] = logits[(k * T + tc) * E + el];
-      b[kp] = wl1[k * E + en];
+      b[kp] = wl1[k * E + el];
     }
 #pragma unroll
     for (int i = 0; i < kXR; ++i) xv[i] = *(const ushort4*)(x + min(4 * lane + 256 * i, H - 4));  // repeats are harmless
-    const double bl = bias ? (double)bias[el] : 0.0, bn = bias ? fabs((double)bias[en]) : 0.0;
+    const double bl = bias ? (double)bias[el] : 0.0, bn = fabs(bl);
     double v = 0.0, nv = bn;
 #pragma unroll
     for (int kp = 0; kp < kMaxParts; ++kp) {
@@ -297,13 +299,20 @@ __device__ __forceinline__ float topk_gather(const double* __restrict__ logits, 
 #pragma unroll
     for (int i = 0; i < kXR; ++i) xi = fmaxf(xi, amax4(xv[i]));
     if (t < T && lane < E) lg[lane] = v + bl;
-    if (tid < E) atomicMax(nmax, __float_as_uint((float)nv));
+    float nm = (float)nv;
     for (int h = 4 * lane + 256 * kXR; h < H; h += 256) xi = fmaxf(xi, amax4(*(const ushort4*)(x + h)));
-    for (int e = tid + nthr; e < E; e += nthr) {
+    for (int e = lane + 64; e < E; e += 64) {
       double w = bias ? fabs((double)bias[e]) : 0.0;
       for (int kp = 0; kp < ks; ++kp) w += wl1[(size_t)kp * E + e];
-      atomicMax(nmax, __float_as_uint((float)w));
+      nm = fmaxf(nm, (float)w);
     }
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) {
+      xi = fmaxf(xi, __shfl_xor(xi, o));
+      nm = fmaxf(nm, __shfl_xor(nm, o));
+    }
+    *nmax = __float_as_uint(nm);  // the wave's own slot
+    return xi;
   }
 #pragma unroll
   for (int o = 32; o >= 1; o >>= 1) xi = fmaxf(xi, __shfl_xor(xi, o));
