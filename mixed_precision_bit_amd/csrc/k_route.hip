@@ -59,7 +59,7 @@ __global__ __launch_bounds__(256) void k_route_logits_mfma(const uint16_t* __res
                         route_ws_l1(logits, 1, T, E));
 }
 
-template <int XDT>
+template <int XDT, int KP>
 __global__ __launch_bounds__(256) void k_route_topk(const double* __restrict__ logits, const uint16_t* __restrict__ X,
                                                     const float* __restrict__ W, const float* __restrict__ bias,
                                                     int ks, int T, int H, int E, int K, int32_t* __restrict__ idx_out,
@@ -71,9 +71,10 @@ __global__ __launch_bounds__(256) void k_route_topk(const double* __restrict__ l
   __shared__ ExactScratch sc[4];
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int t = blockIdx.x * 4 + w;
-  const float xi = topk_gather<XDT>(logits, X, bias, ks, t, T, H, E, lane, threadIdx.x, 256, lg[w], &nmaxw[w]);
+  const float xi = topk_gather<XDT, false, KP>(logits, X, bias, ks, t, T, H, E, lane, threadIdx.x, 256, lg[w],
+                                               &nmaxw[w]);
   const float nm = __uint_as_float(nmaxw[w]);
-  topk_load(logits, bias, ks, t, T, E, lane, lg[w]);
+  topk_load<false, KP>(logits, bias, ks, t, T, E, lane, lg[w]);
   __syncthreads();
   topk_rank(t, T, E, K, lane, lg[w], sel_v[w], sel_i[w]);
   __syncthreads();
@@ -230,8 +231,16 @@ hipError_t launch_route(const uint16_t* X, int xdt, const float* W, const float*
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const dim3 grid((unsigned)((T + 3) / 4)), block(256);
-  if (xdt == 0) hipLaunchKernelGGL(k_route_topk<0>, grid, block, 0, s, lg, X, W, bias, ks, T, H, E, K, idx, w);
-  else hipLaunchKernelGGL(k_route_topk<1>, grid, block, 0, s, lg, X, W, bias, ks, T, H, E, K, idx, w);
+  // the matrix-core path has one hidden part: its top-K loads no others
+  if (ks == 1) {
+    if (xdt == 0) hipLaunchKernelGGL((k_route_topk<0, 1>), grid, block, 0, s, lg, X, W, bias, ks, T, H, E, K, idx, w);
+    else hipLaunchKernelGGL((k_route_topk<1, 1>), grid, block, 0, s, lg, X, W, bias, ks, T, H, E, K, idx, w);
+  } else {
+    if (xdt == 0)
+      hipLaunchKernelGGL((k_route_topk<0, kMaxParts>), grid, block, 0, s, lg, X, W, bias, ks, T, H, E, K, idx, w);
+    else
+      hipLaunchKernelGGL((k_route_topk<1, kMaxParts>), grid, block, 0, s, lg, X, W, bias, ks, T, H, E, K, idx, w);
+  }
   return hipGetLastError();
 }
 

@@ -225,7 +225,8 @@ __device__ __forceinline__ void logits_tile_mfma(const uint16_t* __restrict__ X,
 // expert (rank(e) = #experts that beat it, ties to the lower index) into sel_v
 // / sel_i (the K winners and the runner-up: 17 entries each), then the
 // softmax of the K winners summed in rank order.
-template <bool CO = false>
+// KP: the most hidden parts the launch can have (1 on the matrix-core path)
+template <bool CO = false, int KP = kMaxParts>
 __device__ __forceinline__ void topk_load(const double* __restrict__ logits, const float* __restrict__ bias, int ks,
                                           int t, int T, int E, int lane, double* lg) {
   if (t < T)
@@ -236,11 +237,11 @@ __device__ __forceinline__ void topk_load(const double* __restrict__ logits, con
       } else {
         // every part's load in flight together (parts past ks re-read the
         // last one and are not added), then the parts added in order
-        double a[kMaxParts];
+        double a[KP];
 #pragma unroll
-        for (int kp = 0; kp < kMaxParts; ++kp) a[kp] = ld_f64<CO>(logits + ((size_t)min(kp, ks - 1) * T + t) * E + e);
+        for (int kp = 0; kp < KP; ++kp) a[kp] = ld_f64<CO>(logits + ((size_t)min(kp, ks - 1) * T + t) * E + e);
 #pragma unroll
-        for (int kp = 0; kp < kMaxParts; ++kp) v = kp < ks ? v + a[kp] : v;
+        for (int kp = 0; kp < KP; ++kp) v = kp < ks ? v + a[kp] : v;
       }
       lg[e] = v + (bias ? (double)bias[e] : 0.0);
     }
@@ -257,7 +258,7 @@ __device__ __forceinline__ void topk_load(const double* __restrict__ logits, con
 // fused kernel (CO: no registers to spare) thread tid of nthr takes experts
 // tid, tid + nthr, ... and raises the workgroup's *nmax (LDS, zero before;
 // non-negative floats order as their bits).
-template <int XDT, bool CO = false>
+template <int XDT, bool CO = false, int KP = kMaxParts>
 __device__ __forceinline__ float topk_gather(const double* __restrict__ logits, const uint16_t* __restrict__ X,
                                              const float* __restrict__ bias, int ks, int t, int T, int H, int E,
                                              int lane, int tid, int nthr, double* lg, unsigned* nmax) {
@@ -279,10 +280,10 @@ __device__ __forceinline__ float topk_gather(const double* __restrict__ logits, 
     for (int h = 4 * lane; h < H; h += 256) xi = fmaxf(xi, amax4(*(const ushort4*)(x + h)));
   } else {
     const int el = min(lane, E - 1);
-    double a[kMaxParts], b[kMaxParts];
+    double a[KP], b[KP];
     ushort4 xv[kXR];
 #pragma unroll
-    for (int kp = 0; kp < kMaxParts; ++kp) {
+    for (int kp = 0; kp < KP; ++kp) {
       const size_t k = (size_t)min(kp, ks - 1);
       a[kp] = logits[(k * T + tc) * E + el];
       b[kp] = wl1[k * E + el];
@@ -292,7 +293,7 @@ __device__ __forceinline__ float topk_gather(const double* __restrict__ logits, 
     const double bl = bias ? (double)bias[el] : 0.0, bn = fabs(bl);
     double v = 0.0, nv = bn;
 #pragma unroll
-    for (int kp = 0; kp < kMaxParts; ++kp) {
+    for (int kp = 0; kp < KP; ++kp) {
       v = kp < ks ? v + a[kp] : v;
       nv = kp < ks ? nv + b[kp] : nv;
     }
