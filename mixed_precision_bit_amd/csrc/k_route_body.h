@@ -320,16 +320,20 @@ __device__ __forceinline__ float topk_gather(const double* __restrict__ logits, 
   return xi;
 }
 
+// A nan logit (a non-finite activation) ranks as -inf, so the order is total
+// and every rank is taken once; topk_certify then ranks such a token on its
+// exact sums (nan gaps never certify).
 __device__ __forceinline__ void topk_rank(int t, int T, int E, int K, int lane, const double* lg, double* sel_v,
                                           int* sel_i) {
   if (t >= T) return;
+  auto key = [](double v) { return v != v ? -__builtin_inf() : v; };
   for (int e = lane; e < E; e += 64) {
-    const double v = lg[e];
+    const double v = lg[e], kv = key(v);
     int rank = 0;
 #pragma unroll 4
     for (int j = 0; j < E; ++j) {
-      const double x = lg[j];
-      rank += (x > v || (x == v && j < e)) ? 1 : 0;
+      const double x = key(lg[j]);
+      rank += (x > kv || (x == kv && j < e)) ? 1 : 0;
     }
     if (rank <= K) {  // the K winners and the runner-up (sel_* hold K + 1 <= 17 entries)
       sel_v[rank] = v;

@@ -1052,6 +1052,33 @@ def test_route_sub_ulp_near_tie_exact_order(H, E, T, K):
         assert_close(w.cpu().numpy(), r, "near-tie topk_w")
 
 
+@pytest.mark.parametrize("H,E,T,K", [(256, 24, 40, 3), (1024, 24, 40, 4), (256, 64, 4096, 8), (64, 12, 9, 2)])
+def test_route_non_finite_tokens(H, E, T, K):
+    """Tokens holding an inf or a nan activation get K distinct expert ids in
+    range (a nan logit ranks lowest, and such a token is ranked on its exact
+    sums); the finite tokens of the same batch are routed as the oracle routes
+    them (the vector, matrix-core and one-launch router paths)."""
+    rng = np.random.default_rng(7 + H + T)
+    Wr = (rng.standard_normal((E, H)) / np.sqrt(H)).astype(np.float32)
+    xa = rng.standard_normal((T, H)).astype(np.float16)
+    bad = np.arange(0, T, 4)
+    xa[bad[0::3], 5] = np.float16(np.inf)
+    xa[bad[1::3], 7] = np.float16(-np.inf)
+    xa[bad[2::3], 3] = np.float16(np.nan)
+    Xb = np.ascontiguousarray(xa.view(np.uint16))
+    idx = torch.empty((T, K), dtype=torch.int32, device="cuda")
+    w = torch.empty((T, K), dtype=torch.float32, device="cuda")
+    M().moe_route(to_dev_x(Xb), 0, torch.from_numpy(Wr).cuda(), None, K, idx, w, route_ws(T, E))
+    torch.cuda.synchronize()
+    got = idx.cpu().numpy()
+    assert ((got >= 0) & (got < E)).all()
+    assert all(len(set(row.tolist())) == K for row in got)
+    good = np.setdiff1d(np.arange(T), bad)
+    z, r, _ = O.route(S.f16_bits_to_f64(Xb[good]), Wr, None, K)
+    assert np.array_equal(got[good], z)
+    assert_close(w.cpu().numpy()[good], r, "finite tokens' topk_w")
+
+
 @pytest.mark.parametrize("cfg", [10, 11, 3])
 def test_fused_sub_ulp_near_tie_exact_order(cfg, layer_cache):
     """The fused launch ranks near-tied experts by their exact logits too
