@@ -1079,6 +1079,28 @@ def test_route_non_finite_tokens(H, E, T, K):
     assert_close(w.cpu().numpy()[good], r, "finite tokens' topk_w")
 
 
+@pytest.mark.parametrize("cfg", [10, 11])
+def test_fused_non_finite_tokens_match_separate(cfg, layer_cache):
+    """With inf and nan activations in some tokens, the one-launch path routes
+    every token as moe_route does (ids and weights bit for bit, nan included)
+    and gives the finite tokens the same outputs as moe_ffn."""
+    L, D = dev_layer(layer_cache, cfg)
+    xdt = L.cfg["xdtype"]
+    Xb = np.array(S.make_tokens(cfg), copy=True)
+    T = Xb.shape[0]
+    bad = np.arange(1, T, 5)
+    inf_bits, nan_bits = (0x7C00, 0x7E00) if xdt == "f16" else (0x7F80, 0x7FC0)
+    Xb[bad[0::2], 3] = inf_bits
+    Xb[bad[1::2], 6] = nan_bits
+    i1, w1, o1, i2, w2, o2, _ = _separate_and_fused(D, Xb, xdt)
+    assert ((i1 >= 0) & (i1 < L.E)).all()
+    assert np.array_equal(i1, i2)
+    assert np.array_equal(w1.view(np.uint32), w2.view(np.uint32))
+    good = np.setdiff1d(np.arange(T), bad)
+    assert np.isfinite(o1[good]).all()
+    assert np.array_equal(o1[good].view(np.uint32), o2[good].view(np.uint32))
+
+
 @pytest.mark.parametrize("cfg", [10, 11, 3])
 def test_fused_sub_ulp_near_tie_exact_order(cfg, layer_cache):
     """The fused launch ranks near-tied experts by their exact logits too
