@@ -320,20 +320,29 @@ __device__ __forceinline__ float topk_gather(const double* __restrict__ logits, 
   return xi;
 }
 
+// the calling wave's LDS accesses before it are done before the ones after it
+__device__ __forceinline__ void wave_lds_fence() {
+  __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "workgroup");
+  __builtin_amdgcn_wave_barrier();
+}
+
 // A nan logit (a non-finite activation) ranks as -inf, so the order is total
-// and every rank is taken once; topk_certify then ranks such a token on its
-// exact sums (nan gaps never certify).
-__device__ __forceinline__ void topk_rank(int t, int T, int E, int K, int lane, const double* lg, double* sel_v,
+// and every rank is taken once. The wave replaces its token's nan logits by
+// -inf in place first, so the pairwise count below compares plain values and
+// topk_certify sees the same order (two -inf never certify as a gap).
+__device__ __forceinline__ void topk_rank(int t, int T, int E, int K, int lane, double* lg, double* sel_v,
                                           int* sel_i) {
   if (t >= T) return;
-  auto key = [](double v) { return v != v ? -__builtin_inf() : v; };
+  for (int e = lane; e < E; e += 64)
+    if (lg[e] != lg[e]) lg[e] = -__builtin_inf();
+  wave_lds_fence();
   for (int e = lane; e < E; e += 64) {
-    const double v = lg[e], kv = key(v);
+    const double v = lg[e];
     int rank = 0;
 #pragma unroll 4
     for (int j = 0; j < E; ++j) {
-      const double x = key(lg[j]);
-      rank += (x > kv || (x == kv && j < e)) ? 1 : 0;
+      const double x = lg[j];
+      rank += (x > v || (x == v && j < e)) ? 1 : 0;
     }
     if (rank <= K) {  // the K winners and the runner-up (sel_* hold K + 1 <= 17 entries)
       sel_v[rank] = v;
@@ -422,12 +431,6 @@ __device__ __forceinline__ void exact_add(unsigned long long* acc, uint64_t P, i
   if (hi) atomicAdd(acc + k + 2, neg ? 0ull - hi : hi);
 }
 
-// the calling wave's LDS accesses before it are done before the ones after it
-__device__ __forceinline__ void wave_lds_fence() {
-  __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "workgroup");
-  __builtin_amdgcn_wave_barrier();
-}
-
 // Exact logit of (t, e) into sc.acc, by one whole wave.
 template <int XDT>
 __device__ __forceinline__ void exact_logit(const uint16_t* __restrict__ X, const float* __restrict__ W,
@@ -490,7 +493,7 @@ __device__ __forceinline__ void topk_certify(const uint16_t* __restrict__ X, con
   auto winner = [&](int e) { return lg[e] > vK || (lg[e] == vK && e <= iK); };
   // exact ranking of the winners and of every expert within reach of them
   if (lane == 0) sc.n = 0;
-  if (lane < 16) sc.top_i[lane] = 0;  // a valid id in any slot a nan logit leaves empty
+  if (lane < 16) sc.top_i[lane] = 0;  // the K winners fill every slot; a valid id regardless
   wave_lds_fence();
   for (int e = 0; e < E; ++e) {
     if (!winner(e) && lg[e] + B < thr) continue;  // the same on every lane
